@@ -1,0 +1,125 @@
+"""Seeded input generator: determinism, structure, distributions; and the
+oracle run end to end on the tiny workload and scaled-down workloads."""
+import math
+
+import numpy as np
+import pytest
+
+from mla_inputs import WORKLOADS, bf16_bits_from_f32, generate, small_variant
+from oracle import formats, mla
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125, -2.5, 3.3e38],
+                 dtype=np.float32)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0)
+    # 1 + 1.5*2^-8 rounds up to 1 + 2^-7
+    got = formats.bf16_to_f64(bf16_bits_from_f32(x))
+    assert got[0] == 1.0 and got[1] == 1.0 and got[2] == 1.0078125
+    assert got[3] == 1.0078125 and got[4] == -2.5
+    assert abs(got[5] - 3.3e38) / 3.3e38 < 2 ** -8
+
+
+def test_generator_is_deterministic_and_seeded():
+    w = small_variant(WORKLOADS["v2_b32_l4k_bf16"], batch=2, kv_len=96)
+    a, b = generate(w), generate(w)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    c = generate(w, seed=1)
+    assert not np.array_equal(a["c_kv"], c["c_kv"])
+
+
+def test_generator_fields_are_independent_of_other_sizes():
+    w1 = small_variant(WORKLOADS["v2_b32_l4k_bf16"], batch=2, kv_len=64)
+    w2 = small_variant(WORKLOADS["v2_b32_l4k_bf16"], batch=2, kv_len=128)
+    a, b = generate(w1), generate(w2)
+    assert np.array_equal(a["w_uk"], b["w_uk"])
+    assert np.array_equal(a["q_nope"], b["q_nope"])
+
+
+def test_generator_shapes_and_distributions():
+    w = small_variant(WORKLOADS["v2_b32_l4k_bf16"], batch=4, kv_len=512)
+    g = generate(w)
+    assert g["w_uk"].shape == (128, 128, 512) and g["w_uk"].dtype == np.uint16
+    assert g["q_nope"].shape == (4, 128, 128) and g["q_rope"].shape == (4, 128, 64)
+    assert g["c_kv"].shape == (2048, 512) and g["k_r"].shape == (2048, 64)
+    wv = formats.bf16_to_f64(g["w_uk"])
+    assert abs(wv.std() * math.sqrt(512) - 1) < 0.01 and abs(wv.mean()) < 1e-3
+    cv = formats.bf16_to_f64(g["c_kv"])
+    assert abs(cv.std() - 1) < 0.01 and abs(cv.mean()) < 0.01
+    assert np.array_equal(g["q_pos"], np.full(4, 511))
+
+
+def test_paged_structure():
+    w = small_variant(WORKLOADS["v2_paged_b128_bf16"], batch=16, len_range=(100, 900))
+    g = generate(w, with_cache_rows=False)
+    L = g["seq_lens"]
+    assert L.min() >= 100 and L.max() <= 900
+    pt = g["page_table"]
+    n_pages = (L + 63) // 64
+    used = np.concatenate([pt[b, :n_pages[b]] for b in range(16)])
+    assert np.array_equal(np.sort(used), np.arange(n_pages.sum()))   # a permutation
+    assert not np.array_equal(used, np.arange(n_pages.sum()))         # shuffled
+    for b in range(16):
+        assert np.all(pt[b, n_pages[b]:] == -1)
+
+
+def test_full_paged_lengths_log_uniform():
+    g = generate(WORKLOADS["v2_paged_b128_bf16"], with_cache_rows=False)
+    L = g["seq_lens"].astype(np.float64)
+    assert L.min() >= 512 and L.max() <= 32768
+    lg = np.log(L)
+    assert abs(lg.mean() - 0.5 * (math.log(512) + math.log(32768))) < 0.4
+
+
+def test_outlier_rows():
+    w = small_variant(WORKLOADS["v2_long_b4_l128k_bf16"], batch=2, kv_len=3000)
+    g = generate(w)
+    c = formats.bf16_to_f64(g["c_kv"]).reshape(2, 3000, 512)
+    big = np.abs(c).max(axis=2) > 6.0
+    # round(0.01 * 3000) = 30 scaled rows per sequence (a few unscaled rows may
+    # exceed 6 by chance only with negligible probability)
+    rms = np.sqrt((c ** 2).mean(axis=2))
+    assert np.all((rms > 4).sum(axis=1) == 30)
+    assert big.sum(axis=1).min() >= 30
+
+
+def test_oracle_tiny_workload_runs_and_is_finite():
+    w = WORKLOADS["tiny_fp32"]
+    g = generate(w)
+    out = mla.decode_workload(g, w)
+    assert np.all(np.isfinite(out["o"])) and out["o"].shape == (1, 4, 16)
+    assert out["latent"].shape == (1, 4, 32)
+
+
+def test_oracle_rope_applied_on_tiny_workload():
+    """The tiny workload carries raw q^R / k^R; the oracle rotates them."""
+    w = WORKLOADS["tiny_fp32"]
+    g = generate(w)
+    d = mla.logical_inputs(g, w)
+    raw = g["k_r"].astype(np.float64)
+    np.testing.assert_array_equal(d["kr_rows"][0], raw[0])      # position 0
+    assert not np.allclose(d["kr_rows"][5], raw[5])
+    np.testing.assert_allclose(np.linalg.norm(d["kr_rows"], axis=1),
+                               np.linalg.norm(raw, axis=1), rtol=1e-12)
+
+
+def test_oracle_fp8_inputs_are_quantised_per_token():
+    w = small_variant(WORKLOADS["v2_fp8_t4_b64_l8k"], batch=2, kv_len=80)
+    g = generate(w)
+    d = mla.logical_inputs(g, w)
+    src = np.concatenate([formats.bf16_to_f64(g["c_kv"]), formats.bf16_to_f64(g["k_r"])], 1)
+    deq = np.concatenate([d["c_rows"], d["kr_rows"]], 1)
+    rel = np.linalg.norm(deq - src) / np.linalg.norm(src)
+    assert 0.005 < rel < 0.05          # e4m3 has 3 mantissa bits
+    assert d["fp8_codes"].shape == (160, 576) and d["fp8_scales"].shape == (160,)
+
+
+def test_oracle_sampled_heads_match_full():
+    w = small_variant(WORKLOADS["v2_b32_l4k_bf16"], batch=2, kv_len=70, n_heads=8,
+                      d_head=16, d_latent=32, d_rope=8)
+    g = generate(w)
+    full = mla.decode_workload(g, w)
+    part = mla.decode_workload(g, w, seqs=[1], heads=[3, 5])
+    np.testing.assert_array_equal(part["o"][1, [3, 5]], full["o"][1, [3, 5]])
+    assert np.isnan(part["o"][0]).all()
