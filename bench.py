@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs:
+    mla_absorb_q -> mla_decode_attn (split-KV attention + LSE combine)
+    -> mla_up_proj_v
+with every input already resident in HBM.  The latent cache is replicated
+(>= 768 MB in total) and the replicas are used round-robin, so each step
+reads its cache from HBM rather than from the 256 MB memory-side cache.
+
+Prints ONE JSON line.  `value` is decode tokens/s (B*T query tokens per
+step / step time).  `roofline` describes the dominant kernel (the attention
+kernel), timed with HIP events on the stream it runs on; `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+DEFAULT_WORKLOAD = "v2_b32_l4k_bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc", "decode_mfma.hip")
+
+
+def algorithmic(w, seq_lens):
+    """Bytes and flops the absorbed method must move / compute per attention
+    launch: the latent cache rows, the absorbed queries, the latent output
+    and the LSE; 2 * rows * L * (d_c + d_h^R + d_c) flops per sequence."""
+    D = w.d_latent + w.d_rope
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+    row_bytes = D * esz + (4 if w.kv_dtype == "fp8" else 0)
+    total_tokens = int(sum(seq_lens))
+    q_bytes = w.batch * w.q_tokens * w.n_heads * D * (4 if w.q_dtype == "f32" else 2)
+    out_bytes = w.batch * w.q_tokens * w.n_heads * (w.d_latent + 1) * 4
+    cache_bytes = total_tokens * row_bytes
+    flops = 0
+    for L in seq_lens:
+        # causal: query tau sees L - T + tau + 1 tokens
+        for tau in range(w.q_tokens):
+            n = L - w.q_tokens + tau + 1
+            flops += 2 * w.n_heads * n * (D + w.d_latent)
+    return cache_bytes, q_bytes + out_bytes, flops
+
+
+def traffic_for_current_kernel():
+    """HBM traffic per launch measured with rocprofv3 counters, if the
+    counters were taken on the current decode kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if rec.get("decode_src_sha256") == src_hash:
+            return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(w, gen, budget_s: float):
+    """Time the CPU oracle (as it is) on a bounded sample: whole-length
+    (sequence, head) evaluations, scaled to the full step."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla as omla
+    t0 = time.perf_counter()
+    n_eval = 0
+    seqs = list(range(w.batch))
+    h = 0
+    b_i = 0
+    d = None
+    cur_b = None
+    while True:
+        b = seqs[b_i % len(seqs)]
+        if b != cur_b:
+            d = omla.logical_inputs(gen, w, seqs=[b])
+            cur_b = b
+        omla.decode(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_rows"], d["kr_rows"],
+                    d["row_offsets"], d["seq_lens"], w.q_tokens, seqs=[b], heads=[h])
+        n_eval += 1
+        h += 1
+        if h == w.n_heads:
+            h = 0
+            b_i += 1
+        if time.perf_counter() - t0 >= budget_s and n_eval >= 2:
+            break
+    elapsed = time.perf_counter() - t0
+    per_eval = elapsed / n_eval                       # one (sequence, head) incl. all T
+    full_step = per_eval * w.batch * w.n_heads
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": w.batch * w.q_tokens / full_step,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{n_eval} whole-length (sequence, head) evaluations of the literal "
+                   f"fp64 oracle in {elapsed:.1f} s, scaled to B*n_h = "
+                   f"{w.batch * w.n_heads} evaluations per step"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the cpu_baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from head_latent_attention_11_amd.runner import DecodeBuffers
+    from mla_inputs import WORKLOADS, generate
+
+    w = WORKLOADS[args.workload]
+    gen = generate(w)
+    seq_lens = [int(x) for x in gen["seq_lens"]]
+    cache_b, io_b, flops = algorithmic(w, seq_lens)
+    replicas = max(1, -(-768 * 2 ** 20 // max(cache_b, 1)))
+    torch.cuda.set_device(0)
+    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=replicas)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        buf.step(replica=i % replicas)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        buf.absorb()
+        e[1].record(stream)
+        buf.attend(replica=i % replicas)
+        e[2].record(stream)
+        buf.up_proj()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    absorb_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    up_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    attn_s = attn_ms * 1e-3
+    bytes_alg = cache_b + io_b
+    achieved_gbps = bytes_alg / attn_s / 1e9
+    tflops = flops / attn_s / 1e12
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16"]          # the MFMA precision issued
+    t_hbm = bytes_alg / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (mfma_peak * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4)}
+    tr = traffic_for_current_kernel() if w.name == DEFAULT_WORKLOAD else None
+    roof["traffic"] = tr["hbm_bytes_per_launch"] if tr else None
+    roof["kernel"] = "attention (decode_mfma_kernel + combine_kernel), per mla_decode_attn call"
+    roof["bytes_alg_per_launch"] = bytes_alg
+    roof["flops_alg_per_launch"] = flops
+
+    out = {
+        "metric": "MLA decode tokens/s and latent-cache GB/s (% of HBM/MFMA roofline)",
+        "value": round(w.batch * w.q_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype if w.kv_dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) latent cache and queries, N(0,1/d_c) weights)",
+        "config": {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens,
+                   "kv_len": w.kv_len or None, "n_heads": w.n_heads, "d_head": w.d_head,
+                   "d_latent": w.d_latent, "d_rope": w.d_rope, "kv_dtype": w.kv_dtype,
+                   "layout": w.layout, "cache_replicas": replicas},
+        "latent_cache_GBps": round(cache_b / attn_s / 1e9, 1),
+        "attn_us": round(attn_ms * 1e3, 2),
+        "absorb_us": round(absorb_ms * 1e3, 2),
+        "up_proj_us": round(up_ms * 1e3, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, gen, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

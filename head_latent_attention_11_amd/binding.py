@@ -1,0 +1,179 @@
+"""ctypes binding of libmla.so (argument marshalling only).
+
+Each function takes torch tensors that live on the GPU (torch provides the
+device memory and the stream), passes their raw pointers to the C ABI
+declared in include/mla.h, and raises MLAError on a negative status.  All
+computation happens in the HIP kernels of libmla.so; if the library is not
+built, loading fails with an error instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+
+EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
+            "mla_decode_attn", "mla_up_proj_v", "mla_status_string", "mla_version")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class MLADims(ctypes.Structure):
+    """mirror of mla_dims_t"""
+    _fields_ = [
+        ("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+    ]
+
+    @classmethod
+    def make(cls, n_heads, d_head, d_latent, d_rope, kv_dtype="bf16",
+             q_dtype="bf16", softmax_scale=0.0, rope_base=0.0, page_size=64):
+        kv = DTYPE_CODES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
+        qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else q_dtype
+        return cls(n_heads, d_head, d_latent, d_rope, page_size, kv, qd,
+                   softmax_scale, rope_base)
+
+    @classmethod
+    def from_workload(cls, w):
+        return cls.make(w.n_heads, w.d_head, w.d_latent, w.d_rope, w.kv_dtype,
+                        w.q_dtype, 0.0, w.rope_base, w.page_size)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m head_latent_attention_11_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pdims = ctypes.POINTER(MLADims)
+    lib.mla_absorb_q.argtypes = [pdims, vp, vp, vp, vp, vp, i32, vp]
+    lib.mla_cache_append.argtypes = [pdims, vp, vp, vp, vp, vp, i32, i32, i32, i64,
+                                     i32, vp, vp, i32, vp]
+    lib.mla_decode_workspace_size.argtypes = [pdims, vp, i32, i32, i32,
+                                              ctypes.POINTER(sz)]
+    lib.mla_decode_attn.argtypes = [pdims, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
+                                    i32, vp, sz, vp, vp, vp]
+    lib.mla_up_proj_v.argtypes = [pdims, vp, vp, vp, i32, i32, vp]
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_version.argtypes = []
+    for f in EXPORTED:
+        if f not in ("mla_status_string",):
+            getattr(lib, f).restype = i32
+    lib.mla_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mla_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().mla_version())
+
+
+def _ptr(t) -> Optional[int]:
+    """Raw device pointer of a tensor (None stays NULL; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmla must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream) if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MLAError(int(status), where)
+
+
+def absorb_q(dims: MLADims, q_nope, q_rope, w_uk, q_pos, q_abs, n_tokens: int,
+             stream=None):
+    lib = load_library()
+    _check(lib.mla_absorb_q(ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                            _ptr(q_pos), _ptr(q_abs), int(n_tokens), _stream(stream)),
+           "mla_absorb_q")
+
+
+def cache_append(dims: MLADims, new_c, new_kr, seq_idx, pos, page_table, batch: int,
+                 max_pages: int, max_len: int, cache_rows: int, apply_rope: bool,
+                 cache, kv_scale, n_rows: int, stream=None):
+    lib = load_library()
+    _check(lib.mla_cache_append(ctypes.byref(dims), _ptr(new_c), _ptr(new_kr),
+                                _ptr(seq_idx), _ptr(pos), _ptr(page_table), int(batch),
+                                int(max_pages), int(max_len), int(cache_rows),
+                                int(bool(apply_rope)), _ptr(cache), _ptr(kv_scale),
+                                int(n_rows), _stream(stream)),
+           "mla_cache_append")
+
+
+def _lens_host(seq_lens_host: Sequence[int]):
+    arr = (ctypes.c_int32 * len(seq_lens_host))(*[int(x) for x in seq_lens_host])
+    return arr
+
+
+def decode_workspace_size(dims: MLADims, seq_lens_host: Sequence[int], q_tokens: int,
+                          num_splits: int = 0) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    lens = _lens_host(seq_lens_host)
+    _check(lib.mla_decode_workspace_size(ctypes.byref(dims), ctypes.cast(lens, ctypes.c_void_p),
+                                         len(seq_lens_host), int(q_tokens), int(num_splits),
+                                         ctypes.byref(out)),
+           "mla_decode_workspace_size")
+    return int(out.value)
+
+
+def decode_attn(dims: MLADims, q_abs, cache, kv_scale, page_table, max_pages: int,
+                max_len: int, seq_lens, seq_lens_host: Sequence[int], q_tokens: int,
+                num_splits: int, workspace, ws_bytes: int, out_latent, out_lse,
+                stream=None, _lens_cache=None):
+    lib = load_library()
+    lens = _lens_cache if _lens_cache is not None else _lens_host(seq_lens_host)
+    _check(lib.mla_decode_attn(ctypes.byref(dims), _ptr(q_abs), _ptr(cache), _ptr(kv_scale),
+                               _ptr(page_table), int(max_pages), int(max_len), _ptr(seq_lens),
+                               ctypes.cast(lens, ctypes.c_void_p), len(seq_lens_host),
+                               int(q_tokens), int(num_splits), _ptr(workspace), int(ws_bytes),
+                               _ptr(out_latent), _ptr(out_lse), _stream(stream)),
+           "mla_decode_attn")
+
+
+def up_proj_v(dims: MLADims, latent, w_uv, out, n_tokens: int, stream=None,
+              out_dtype: Optional[int] = None):
+    """out_dtype defaults to the dtype of ``out`` (float32 -> F32, else BF16)."""
+    lib = load_library()
+    if out_dtype is None:
+        import torch
+        out_dtype = F32 if (not isinstance(out, int) and out.dtype == torch.float32) else BF16
+    _check(lib.mla_up_proj_v(ctypes.byref(dims), _ptr(latent), _ptr(w_uv), _ptr(out),
+                             int(out_dtype), int(n_tokens), _stream(stream)),
+           "mla_up_proj_v")

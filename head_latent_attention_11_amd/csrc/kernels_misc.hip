@@ -1,0 +1,410 @@
+// Query absorption, cache append, split combine and value up-projection.
+//
+// Sources: "DeepSeek-V2: Strong, Economical, Efficient", section 2.1.2 and
+// Appendix C (W^UK absorbed into the query side, W^UV applied after the
+// latent sum), section 2.1.3 (decoupled RoPE, cached shared k^R);
+// "DeepSeek-V3 Technical Report" notes, MLA section (head-block layout of
+// W^UK / W^UV; attention-output equation whose sum over tokens is what the
+// split combine re-associates).
+#include <math.h>
+
+#include "mla_common.hpp"
+#include "plan_device.hpp"
+
+namespace mla {
+
+// ============================================================ RoPE helper
+// Interleaved pairs (2k, 2k+1) rotated by pos * base^(-2k/d); angle and
+// rotation in double precision.
+__device__ inline void rope_pair(float x0, float x1, int pos, int k, int d,
+                                 float base, float* y0, float* y1) {
+  double theta = pow((double)base, -2.0 * (double)k / (double)d);
+  double ang = (double)pos * theta;
+  double s, c;
+  sincos(ang, &s, &c);
+  *y0 = (float)((double)x0 * c - (double)x1 * s);
+  *y1 = (float)((double)x0 * s + (double)x1 * c);
+}
+
+template <typename T> __device__ inline float load_f(const T* p, size_t i);
+template <> __device__ inline float load_f<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ inline float load_f<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+template <typename T> __device__ inline void store_f(T* p, size_t i, float v);
+template <> __device__ inline void store_f<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ inline void store_f<uint16_t>(uint16_t* p, size_t i, float v) {
+  p[i] = f32_to_bf16_bits(v);
+}
+
+// ====================================================== absorb: MFMA path
+// q_abs[n, i, 0:512] = W^UK_i^T q_nope[n, i, :], d_h = 128.  One workgroup
+// per (head i, block of 128 latent columns); wave w owns 32 columns.  The
+// W^UK_i column block is staged transposed in LDS so that each MFMA operand
+// lane holds 8 consecutive d_h values.  D^T[cols x tokens] = W^T q^T.
+constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsDh + 8;
+
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
+    uint16_t* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
+  constexpr int DC = 512, DR = 64, D = DC + DR;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kAbsCols * kAbsLdsRow];
+  const int head = blockIdx.x >> 2, cb = blockIdx.x & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  // stage W^UK[head][r][cb*128 + c] -> wt[c][r]
+  const uint16_t* wsrc = w_uk + (size_t)head * kAbsDh * DC + cb * kAbsCols;
+  for (int ch = tid; ch < kAbsDh * (kAbsCols / 8); ch += 256) {
+    const int r = ch / (kAbsCols / 8), c8 = (ch % (kAbsCols / 8)) * 8;
+    u32x4 v = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wt[(c8 + 2 * e) * kAbsLdsRow + r] = uint16_t(v[e] & 0xFFFF);
+      wt[(c8 + 2 * e + 1) * kAbsLdsRow + r] = uint16_t(v[e] >> 16);
+    }
+  }
+  __syncthreads();
+
+  const int col = wave * 32 + l32;   // A-operand row (latent column in block)
+  for (int t0 = 0; t0 < n_tok; t0 += 32) {
+    const int tok = t0 + l32;         // B-operand column
+    floatx16 acc = {};
+#pragma unroll
+    for (int k = 0; k < kAbsDh / 16; ++k) {
+      bf16x8 a = *(const bf16x8*)(wt + col * kAbsLdsRow + 16 * k + 8 * h);
+      bf16x8 b = {};
+      if (tok < n_tok)
+        b = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    // acc[r]: row (column in block) 8(r/4) + 4h + r%4, column = token l32
+    if (tok < n_tok) {
+      uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 pk;
+        pk[0] = uint32_t(f32_to_bf16_bits(acc[4 * j])) | uint32_t(f32_to_bf16_bits(acc[4 * j + 1])) << 16;
+        pk[1] = uint32_t(f32_to_bf16_bits(acc[4 * j + 2])) | uint32_t(f32_to_bf16_bits(acc[4 * j + 3])) << 16;
+        *(u32x2*)(dst + 8 * j + 4 * h) = pk;
+      }
+    }
+  }
+
+  // the RoPE part q_abs[..., 512:576] is written by the cb == 0 workgroups
+  if (cb == 0) {
+    for (int idx = tid; idx < n_tok * (DR / 2); idx += 256) {
+      const int tok = idx / (DR / 2), k = idx % (DR / 2);
+      const uint16_t* src = q_rope + ((size_t)tok * n_h + head) * DR + 2 * k;
+      float x0 = bf16_bits_to_f32(src[0]), x1 = bf16_bits_to_f32(src[1]);
+      if (q_pos) rope_pair(x0, x1, q_pos[tok], k, DR, rope_base, &x0, &x1);
+      uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * k;
+      dst[0] = f32_to_bf16_bits(x0);
+      dst[1] = f32_to_bf16_bits(x1);
+    }
+  }
+}
+
+// =================================================== absorb: general path
+template <typename T>
+__global__ __launch_bounds__(256) void absorb_general_kernel(
+    const T* __restrict__ q_nope, const T* __restrict__ q_rope,
+    const T* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
+    T* __restrict__ q_abs, int n_tok, int n_h, int d_h, int d_c, int d_r,
+    float rope_base) {
+  const int D = d_c + d_r;
+  const size_t total = (size_t)n_tok * n_h * D;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int e = int(idx % D);
+    const size_t row = idx / D;            // tok * n_h + head
+    const int head = int(row % n_h), tok = int(row / n_h);
+    float v;
+    if (e < d_c) {
+      float acc = 0.f;
+      const T* q = q_nope + row * d_h;
+      const T* w = w_uk + (size_t)head * d_h * d_c + e;
+      for (int r = 0; r < d_h; ++r) acc = fmaf(load_f(q, r), load_f(w, (size_t)r * d_c), acc);
+      v = acc;
+    } else {
+      const int k = (e - d_c) >> 1;
+      const T* q = q_rope + row * d_r;
+      float x0 = load_f(q, 2 * k), x1 = load_f(q, 2 * k + 1);
+      if (q_pos) rope_pair(x0, x1, q_pos[tok], k, d_r, rope_base, &x0, &x1);
+      v = ((e - d_c) & 1) ? x1 : x0;
+    }
+    store_f(q_abs, idx, v);
+  }
+}
+
+// ================================================================ append
+// One wave per new row.  Source rows are F32 (F32 cache) or BF16.
+template <typename SrcT, int KV>
+__global__ __launch_bounds__(256) void append_kernel(
+    const SrcT* __restrict__ new_c, const SrcT* __restrict__ new_kr,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
+    long long cache_rows, int apply_rope, void* __restrict__ cache,
+    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, float rope_base) {
+  const int lane = threadIdx.x & 63;
+  const int D = d_c + d_r;
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += gridDim.x * 4) {
+    const int sq = seq_idx[r], p = pos[r];
+    if (sq < 0 || sq >= B || p < 0) continue;
+    long long row;
+    if (page_table) {
+      if (p / kPage >= max_pages) continue;
+      const int page = page_table[(size_t)sq * max_pages + p / kPage];
+      if (page < 0) continue;
+      row = (long long)page * kPage + p % kPage;
+    } else {
+      if (p >= max_len) continue;
+      row = (long long)sq * max_len + p;
+    }
+    if (row >= cache_rows) continue;
+
+    // gather this lane's elements (at most 10 per lane: D <= 640)
+    float v[10];
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 10; ++k) {
+      const int e = lane + 64 * k;
+      float x = 0.f;
+      if (e < d_c) {
+        x = load_f(new_c, (size_t)r * d_c + e);
+      } else if (e < D) {
+        const int q = e - d_c;
+        if (apply_rope) {
+          const int kp = q >> 1;
+          float x0 = load_f(new_kr, (size_t)r * d_r + 2 * kp);
+          float x1 = load_f(new_kr, (size_t)r * d_r + 2 * kp + 1);
+          float y0, y1;
+          rope_pair(x0, x1, p, kp, d_r, rope_base, &y0, &y1);
+          x = (q & 1) ? y1 : y0;
+        } else {
+          x = load_f(new_kr, (size_t)r * d_r + q);
+        }
+      }
+      v[k] = x;
+      amax = fmaxf(amax, fabsf(x));
+    }
+    if (KV == MLA_F32) {
+      float* dst = (float*)cache + row * D;
+#pragma unroll
+      for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = v[k];
+    } else if (KV == MLA_BF16) {
+      uint16_t* dst = (uint16_t*)cache + row * D;
+#pragma unroll
+      for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = f32_to_bf16_bits(v[k]);
+    } else {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+      const float s = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+      uint8_t* dst = (uint8_t*)cache + row * D;
+#pragma unroll
+      for (int k = 0; k < 10; ++k)
+        if (lane + 64 * k < D) dst[lane + 64 * k] = uint8_t(f32_to_e4m3(__fdiv_rn(v[k], s)));
+      if (lane == 0) kv_scale[row] = s;
+    }
+  }
+}
+
+// =============================================================== combine
+// LSE combine of the split partials of one (query token, head) row:
+// lse = ln sum_s e^{lse_s};  latent = sum_s e^{lse_s - lse} latent_s.
+// Exact re-association of the sum in the attention-output equation.
+__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+  const int rows = a.n_h * a.T;
+  const int nq = blockIdx.x / a.n_h, head = blockIdx.x % a.n_h;
+  const int b = nq / a.T, tau = nq % a.T;
+  const int L = a.seq_lens[b];
+  const int ns = splits_of(L, a.num_splits, a.chunk);
+  if (ns <= 1) return;
+  const int first = first_item_of(a.seq_lens, b, a.num_splits, a.chunk);
+  const int row = tau * a.n_h + head;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[(size_t)(first + s) * rows + row]);
+  float* out = a.out_latent + ((size_t)nq * a.n_h + head) * a.d_c;
+  if (mx == -INFINITY) {
+    for (int d = threadIdx.x; d < a.d_c; d += blockDim.x) out[d] = 0.f;
+    if (threadIdx.x == 0) a.out_lse[(size_t)nq * a.n_h + head] = -INFINITY;
+    return;
+  }
+  float wsum = 0.f;
+  for (int s = 0; s < ns; ++s) wsum += expf(a.part_lse[(size_t)(first + s) * rows + row] - mx);
+  const float inv = 1.0f / wsum;
+  for (int d4 = threadIdx.x * 4; d4 < a.d_c; d4 += blockDim.x * 4) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      const size_t it = (size_t)(first + s) * rows + row;
+      const float w = expf(a.part_lse[it] - mx) * inv;
+      const floatx4 v = *(const floatx4*)(a.part_o + it * a.d_c + d4);
+      acc += w * v;
+    }
+    *(floatx4*)(out + d4) = acc;
+  }
+  if (threadIdx.x == 0) a.out_lse[(size_t)nq * a.n_h + head] = mx + logf(wsum);
+}
+
+// ===================================================== up-projection: MFMA
+// out[n, i, :] = W^UV_i latent[n, i, :], d_h = 128, d_c = 512.  One
+// workgroup per (head i, block of 32 tokens); wave w owns d_h rows
+// 32w..32w+31.  The fp32 latent is split into bf16 hi + lo parts so the
+// bf16 MFMA keeps (nearly) fp32 accuracy: W (hi + lo) with W exact in bf16.
+template <typename OutT>
+__global__ __launch_bounds__(256) void up_proj_mfma_kernel(
+    const float* __restrict__ latent, const uint16_t* __restrict__ w_uv,
+    OutT* __restrict__ out, int n_tok, int n_h) {
+  constexpr int DC = 512, DH = 128;
+  const int head = blockIdx.x, t0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int m = wave * 32 + l32;        // d_h row held as A-operand row
+  const int tok = t0 + l32;             // token held as B-operand column
+  const uint16_t* wrow = w_uv + ((size_t)head * DH + m) * DC;
+  const float* lrow = latent + ((size_t)tok * n_h + head) * DC;
+  floatx16 acc_hi = {}, acc_lo = {};
+#pragma unroll 4
+  for (int k = 0; k < DC / 16; ++k) {
+    bf16x8 a = *(const bf16x8*)(wrow + 16 * k + 8 * h);
+    bf16x8 bh = {}, bl = {};
+    if (tok < n_tok) {
+      const floatx4 x0 = *(const floatx4*)(lrow + 16 * k + 8 * h);
+      const floatx4 x1 = *(const floatx4*)(lrow + 16 * k + 8 * h + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const uint16_t hb = f32_to_bf16_bits(x);
+        const float hi = bf16_bits_to_f32(hb);
+        const uint16_t lb = f32_to_bf16_bits(x - hi);
+        bh[e] = __builtin_bit_cast(__bf16, hb);
+        bl[e] = __builtin_bit_cast(__bf16, lb);
+      }
+    }
+    acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc_hi, 0, 0, 0);
+    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc_lo, 0, 0, 0);
+  }
+  if (tok < n_tok) {
+    OutT* dst = out + ((size_t)tok * n_h + head) * DH + wave * 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const floatx4 v = {acc_hi[4 * j] + acc_lo[4 * j], acc_hi[4 * j + 1] + acc_lo[4 * j + 1],
+                         acc_hi[4 * j + 2] + acc_lo[4 * j + 2], acc_hi[4 * j + 3] + acc_lo[4 * j + 3]};
+      if constexpr (sizeof(OutT) == 4) {
+        *(floatx4*)(dst + 8 * j + 4 * h) = v;
+      } else {
+        u32x2 pk;
+        pk[0] = uint32_t(f32_to_bf16_bits(v[0])) | uint32_t(f32_to_bf16_bits(v[1])) << 16;
+        pk[1] = uint32_t(f32_to_bf16_bits(v[2])) | uint32_t(f32_to_bf16_bits(v[3])) << 16;
+        *(u32x2*)(dst + 8 * j + 4 * h) = pk;
+      }
+    }
+  }
+}
+
+// =========================================== up-projection: general path
+template <typename T, typename OutT>
+__global__ __launch_bounds__(256) void up_proj_general_kernel(
+    const float* __restrict__ latent, const T* __restrict__ w_uv,
+    OutT* __restrict__ out, int n_tok, int n_h, int d_h, int d_c) {
+  const size_t total = (size_t)n_tok * n_h * d_h;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int r = int(idx % d_h);
+    const size_t row = idx / d_h;         // tok * n_h + head
+    const int head = int(row % n_h);
+    const float* x = latent + row * d_c;
+    const T* w = w_uv + ((size_t)head * d_h + r) * d_c;
+    float acc = 0.f;
+    for (int c = 0; c < d_c; ++c) acc = fmaf(load_f(w, c), x[c], acc);
+    store_f(out, idx, acc);
+  }
+}
+
+// ================================================================ launchers
+hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
+                         const void* q_rope, const void* w_uk,
+                         const int32_t* q_pos, void* q_abs, int n_tok,
+                         float rope_base, hipStream_t st) {
+  if (fast) {
+    hipLaunchKernelGGL(absorb_mfma_kernel, dim3(d.n_heads * 4), dim3(256), 0, st,
+                       (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                       (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
+                       d.n_heads, rope_base);
+  } else {
+    const size_t total = (size_t)n_tok * d.n_heads * (d.d_latent + d.d_rope);
+    const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
+    if (d.q_dtype == MLA_F32)
+      hipLaunchKernelGGL(absorb_general_kernel<float>, dim3(grid), dim3(256), 0, st,
+                         (const float*)q_nope, (const float*)q_rope, (const float*)w_uk,
+                         q_pos, (float*)q_abs, n_tok, d.n_heads, d.d_head,
+                         d.d_latent, d.d_rope, rope_base);
+    else
+      hipLaunchKernelGGL(absorb_general_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
+                         (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
+                         d.n_heads, d.d_head, d.d_latent, d.d_rope, rope_base);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new_kr,
+                         const int32_t* seq_idx, const int32_t* pos,
+                         const int32_t* page_table, int B, int max_pages,
+                         int max_len, long long cache_rows, int apply_rope,
+                         void* cache, float* kv_scale, int n_rows,
+                         float rope_base, hipStream_t st) {
+  const int grid = std::min((n_rows + 3) / 4, 16384);
+  if (d.kv_dtype == MLA_F32)
+    hipLaunchKernelGGL((append_kernel<float, MLA_F32>), dim3(grid), dim3(256), 0, st,
+                       (const float*)new_c, (const float*)new_kr, seq_idx, pos,
+                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
+                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
+  else if (d.kv_dtype == MLA_BF16)
+    hipLaunchKernelGGL((append_kernel<uint16_t, MLA_BF16>), dim3(grid), dim3(256), 0, st,
+                       (const uint16_t*)new_c, (const uint16_t*)new_kr, seq_idx, pos,
+                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
+                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
+  else
+    hipLaunchKernelGGL((append_kernel<uint16_t, MLA_FP8_E4M3>), dim3(grid), dim3(256), 0, st,
+                       (const uint16_t*)new_c, (const uint16_t*)new_kr, seq_idx, pos,
+                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
+                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.T * a.n_h), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_proj(const mla_dims_t& d, bool fast, const float* latent,
+                          const void* w_uv, void* out, bool out_f32, int n_tok,
+                          hipStream_t st) {
+  if (fast) {
+    const dim3 grid(d.n_heads, (n_tok + 31) / 32);
+    if (out_f32)
+      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(256), 0, st,
+                         latent, (const uint16_t*)w_uv, (float*)out, n_tok, d.n_heads);
+    else
+      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(256), 0, st,
+                         latent, (const uint16_t*)w_uv, (uint16_t*)out, n_tok, d.n_heads);
+  } else {
+    const size_t total = (size_t)n_tok * d.n_heads * d.d_head;
+    const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
+#define MLA_UP(WT, OT)                                                              \
+    hipLaunchKernelGGL((up_proj_general_kernel<WT, OT>), dim3(grid), dim3(256), 0, st, \
+                       latent, (const WT*)w_uv, (OT*)out, n_tok, d.n_heads, d.d_head,  \
+                       d.d_latent)
+    if (d.q_dtype == MLA_F32) {
+      if (out_f32) MLA_UP(float, float); else MLA_UP(float, uint16_t);
+    } else {
+      if (out_f32) MLA_UP(uint16_t, float); else MLA_UP(uint16_t, uint16_t);
+    }
+#undef MLA_UP
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,272 @@
+// C ABI of the MLA decode library: argument validation, split planning and
+// kernel launches.  Every check runs on the host before the first HIP call,
+// so invalid arguments never touch the device.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "mla_common.hpp"
+
+namespace mla {
+hipError_t launch_absorb(const mla_dims_t&, bool, const void*, const void*, const void*,
+                         const int32_t*, void*, int, float, hipStream_t);
+hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int32_t*,
+                         const int32_t*, const int32_t*, int, int, int, long long, int,
+                         void*, float*, int, float, hipStream_t);
+hipError_t launch_combine(const DecodeArgs&, hipStream_t);
+hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
+                          int, hipStream_t);
+hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
+}  // namespace mla
+
+using namespace mla;
+
+namespace {
+
+constexpr int32_t kVersion = 10000;   // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Dimension and dtype checks shared by every entry point.
+int32_t check_dims(const mla_dims_t* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->n_heads < 1 || d->n_heads > 4096) return MLA_ERR_DIMS;
+  if (d->d_head < 1 || d->d_head > 256) return MLA_ERR_DIMS;
+  if (d->d_latent < 4 || d->d_latent > 512 || (d->d_latent & 3)) return MLA_ERR_DIMS;
+  if (d->d_rope < 0 || d->d_rope > 128 || (d->d_rope & 1)) return MLA_ERR_DIMS;
+  if (d->page_size != kPage) return MLA_ERR_DIMS;
+  if (d->q_dtype != MLA_F32 && d->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d->kv_dtype != MLA_F32 && d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3)
+    return MLA_ERR_DTYPE;
+  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
+  if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return MLA_ERR_ARG;
+  return MLA_OK;
+}
+
+// The matrix-core path: DeepSeek-V2 / V3 MLA shapes with bf16 operands.
+bool fast_shape(const mla_dims_t* d) {
+  return d->d_head == 128 && d->d_latent == 512 && d->d_rope == 64 &&
+         d->n_heads % 32 == 0 && d->q_dtype == MLA_BF16;
+}
+
+bool fast_decode(const mla_dims_t* d, int T) {
+  return fast_shape(d) && (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) &&
+         ((int64_t)d->n_heads * T) % 128 == 0;
+}
+
+float rope_base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.f; }
+
+float softmax_scale_of(const mla_dims_t* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale
+                                : 1.0f / sqrtf((float)(d->d_head + d->d_rope));
+}
+
+int32_t status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+struct Plan {
+  int num_splits;   // > 0: per-sequence equal splits
+  int chunk;        // global chunk when num_splits == 0
+  int n_items;
+  int row_blocks;
+  bool any_split;
+  size_t ws_bytes;
+};
+
+// Split-KV plan.  num_splits > 0 cuts each sequence into at most that many
+// chunks of equal size (multiple of 64 tokens).  num_splits == 0 picks one
+// chunk length for all sequences so that the work items fill the GPU about
+// once: chunk = ceil(total tokens * row blocks / 256 CUs), rounded up to 64
+// and at least 256 tokens.
+int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
+                  int num_splits, Plan* p) {
+  if (B < 1 || T < 1 || T > 1024) return MLA_ERR_ARG;
+  if (num_splits < 0 || num_splits > 4096) return MLA_ERR_ARG;
+  const bool fast = fast_decode(d, T);
+  const int64_t rows = (int64_t)d->n_heads * T;
+  const int64_t rb = fast ? rows / 128 : rows;
+  int64_t total = 0;
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < 1 || lens[b] < T) return MLA_ERR_SEQLEN;
+    total += lens[b];
+  }
+  p->num_splits = num_splits;
+  p->row_blocks = (int)rb;
+  p->chunk = 0;
+  if (num_splits == 0) {
+    const int64_t target_items = std::max<int64_t>(1, (kNumCU + rb - 1) / rb);
+    int64_t c = (total + target_items - 1) / target_items;
+    c = ((c + kPage - 1) / kPage) * kPage;
+    c = std::max<int64_t>(c, kMinChunk);
+    c = std::min<int64_t>(c, 1 << 30);
+    p->chunk = (int)c;
+  }
+  int64_t items = 0;
+  bool any = false;
+  for (int b = 0; b < B; ++b) {
+    const int ns = splits_of(lens[b], p->num_splits, p->chunk);
+    items += ns;
+    any = any || ns > 1;
+  }
+  if (items * rb > INT32_MAX / 2) return MLA_ERR_ARG;
+  p->n_items = (int)items;
+  p->any_split = any;
+  p->ws_bytes = any ? (size_t)items * rows * (d->d_latent + 1) * sizeof(float) + 256 : 0;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_version(void) { return kVersion; }
+
+const char* mla_status_string(int32_t s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_DIMS: return "dimension fields inconsistent or out of range";
+    case MLA_ERR_DTYPE: return "unknown or unsupported dtype combination";
+    case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MLA_ERR_SEQLEN: return "a sequence length is < 1, < T, or beyond the cache capacity";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_ERR_ARG: return "invalid count, size or flag argument";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                     const void* w_uk, const int32_t* q_pos, void* q_abs,
+                     int32_t n_tokens, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !w_uk || !q_abs || (dims->d_rope > 0 && !q_rope)) return MLA_ERR_NULL;
+  if (n_tokens < 1) return MLA_ERR_ARG;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_abs) ||
+      (q_rope && !aligned16(q_rope)))
+    return MLA_ERR_ALIGN;
+  const bool fast = fast_shape(dims);
+  return status_of(launch_absorb(*dims, fast, q_nope, q_rope, w_uk, q_pos, q_abs, n_tokens,
+                                 rope_base_of(dims), (hipStream_t)stream));
+}
+
+int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* new_kr,
+                         const int32_t* seq_idx, const int32_t* pos,
+                         const int32_t* page_table, int32_t batch, int32_t max_pages,
+                         int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                         void* cache, float* kv_scale, int32_t n_rows, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!new_c || !seq_idx || !pos || !cache || (dims->d_rope > 0 && !new_kr))
+    return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_FP8_E4M3) {
+    if (!kv_scale) return MLA_ERR_NULL;
+  } else if (kv_scale) {
+    return MLA_ERR_ARG;
+  }
+  if (n_rows < 1 || batch < 1 || cache_rows < 1) return MLA_ERR_ARG;
+  if (apply_rope != 0 && apply_rope != 1) return MLA_ERR_ARG;
+  if (page_table) {
+    if (max_pages < 1) return MLA_ERR_ARG;
+  } else {
+    if (max_len < 1) return MLA_ERR_ARG;
+    if ((int64_t)batch * max_len > cache_rows) return MLA_ERR_ARG;
+  }
+  if (dims->d_latent + dims->d_rope > 640) return MLA_ERR_DIMS;
+  if (!aligned16(new_c) || !aligned16(cache) || (new_kr && !aligned16(new_kr)))
+    return MLA_ERR_ALIGN;
+  return status_of(launch_append(*dims, new_c, new_kr, seq_idx, pos, page_table, batch,
+                                 max_pages, max_len, cache_rows, apply_rope, cache,
+                                 kv_scale, n_rows, rope_base_of(dims), (hipStream_t)stream));
+}
+
+int32_t mla_decode_workspace_size(const mla_dims_t* dims, const int32_t* seq_lens_host,
+                                  int32_t batch, int32_t q_tokens, int32_t num_splits,
+                                  size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!seq_lens_host || !bytes) return MLA_ERR_NULL;
+  Plan p;
+  st = make_plan(dims, seq_lens_host, batch, q_tokens, num_splits, &p);
+  if (st != MLA_OK) return st;
+  *bytes = p.ws_bytes;
+  return MLA_OK;
+}
+
+int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* cache,
+                        const float* kv_scale, const int32_t* page_table, int32_t max_pages,
+                        int32_t max_len, const int32_t* seq_lens,
+                        const int32_t* seq_lens_host, int32_t batch, int32_t q_tokens,
+                        int32_t num_splits, void* workspace, size_t ws_bytes,
+                        float* out_latent, float* out_lse, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!q_abs || !cache || !seq_lens || !seq_lens_host || !out_latent || !out_lse)
+    return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_FP8_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(out_latent) ||
+      !aligned16(out_lse) || (workspace && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  Plan p;
+  st = make_plan(dims, seq_lens_host, batch, q_tokens, num_splits, &p);
+  if (st != MLA_OK) return st;
+  const int64_t cap = page_table ? (int64_t)max_pages * kPage : (int64_t)max_len;
+  if (page_table ? max_pages < 1 : max_len < 1) return MLA_ERR_ARG;
+  for (int b = 0; b < batch; ++b)
+    if (seq_lens_host[b] > cap) return MLA_ERR_SEQLEN;
+  if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return MLA_ERR_WORKSPACE;
+
+  DecodeArgs a = {};
+  a.q_abs = q_abs;
+  a.cache = cache;
+  a.kv_scale = kv_scale;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  const int64_t rows = (int64_t)dims->n_heads * q_tokens;
+  a.part_o = p.any_split ? (float*)workspace : nullptr;
+  a.part_lse = p.any_split ? (float*)workspace + (size_t)p.n_items * rows * dims->d_latent
+                           : nullptr;
+  a.out_latent = out_latent;
+  a.out_lse = out_lse;
+  a.B = batch;
+  a.T = q_tokens;
+  a.n_h = dims->n_heads;
+  a.d_c = dims->d_latent;
+  a.d_r = dims->d_rope;
+  a.max_pages = page_table ? max_pages : 0;
+  a.max_len = page_table ? 0 : max_len;
+  a.num_splits = p.num_splits;
+  a.chunk = p.chunk;
+  a.n_items = p.n_items;
+  a.row_blocks = p.row_blocks;
+  a.q_dtype = dims->q_dtype;
+  a.kv_dtype = dims->kv_dtype;
+  a.scale_log2 = softmax_scale_of(dims) * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = fast_decode(dims, q_tokens) ? launch_decode_mfma(a, s)
+                                             : launch_decode_general(a, s);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  if (p.any_split) {
+    e = launch_combine(a, s);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  }
+  return MLA_OK;
+}
+
+int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent, const void* w_uv,
+                      void* out, int32_t out_dtype, int32_t n_tokens, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!latent || !w_uv || !out) return MLA_ERR_NULL;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (n_tokens < 1) return MLA_ERR_ARG;
+  if (!aligned16(latent) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  return status_of(launch_up_proj(*dims, fast_shape(dims), latent, w_uv, out,
+                                  out_dtype == MLA_F32, n_tokens, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Shared definitions of the MLA decode library (device and host side).
+//
+// Number formats: bfloat16 is the top half of an IEEE binary32; the fp8
+// cache uses OCP FP8 E4M3 ("e4m3fn": bias 7, 3 mantissa bits, max 448,
+// no infinities).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 64;            // tokens per page of a paged cache
+constexpr int kNumCU = 256;          // MI355X compute units
+constexpr int kNumXCD = 8;           // accelerator complex dies (own L2 each)
+constexpr int kMinChunk = 256;       // smallest automatic KV chunk (tokens)
+
+// ---------------------------------------------------------------- formats
+__host__ __device__ inline float bf16_bits_to_f32(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = uint32_t(b) << 16;
+  return v.f;
+}
+
+// float -> bfloat16 bits, round to nearest, ties to even (finite inputs).
+__host__ __device__ inline uint16_t f32_to_bf16_bits(float f) {
+  union { uint32_t u; float f; } v;
+  v.f = f;
+  uint32_t u = v.u;
+  if ((u & 0x7F800000u) == 0x7F800000u) return uint16_t((u >> 16) | ((u & 0xFFFF) ? 0x40 : 0));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// E4M3 code -> float (exact).  Codes 0x7F / 0xFF (NaN) never occur in a
+// cache written by the append kernel.
+__host__ __device__ inline float e4m3_to_f32(uint32_t code) {
+  uint32_t em = code & 0x7Fu;
+  float mag;
+  if (em >= 8) {
+    union { uint32_t u; float f; } v;
+    v.u = ((em >> 3) + 120u) << 23 | (em & 7u) << 20;
+    mag = v.f;
+  } else {
+    mag = float(em) * 0.001953125f;   // m * 2^-9 (subnormal)
+  }
+  return (code & 0x80u) ? -mag : mag;
+}
+
+// float -> nearest E4M3 code, ties to even mantissa, |x| >= 448 saturates.
+__host__ __device__ inline uint32_t f32_to_e4m3(float x) {
+  union { uint32_t u; float f; } v;
+  v.f = x;
+  uint32_t sign = (v.u >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.0f)) {
+    code = 0x7E;
+  } else if (a < 0.015625f) {                // below 2^-6: subnormal grid
+    code = uint32_t(rintf(a * 512.0f));      // exact scaling; ties to even
+  } else {
+    union { uint32_t u; float f; } w;
+    w.f = a;
+    uint32_t e = (w.u >> 23) - 127u + 7u;    // biased E4M3 exponent, 1..15
+    uint32_t mant = w.u & 0x7FFFFFu;
+    uint32_t q = mant >> 20, rem = mant & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    if (q == 8) { q = 0; ++e; }
+    code = (e << 3) | q;                     // a < 448 keeps this <= 0x7E
+  }
+  return code | sign;
+}
+
+// ------------------------------------------------------------ split planner
+// Tokens per KV chunk of sequence b.  num_splits > 0: each sequence is cut
+// into at most num_splits chunks of equal size rounded up to the page size;
+// otherwise every sequence uses the global chunk `chunk`.
+__host__ __device__ inline int chunk_of(int L, int num_splits, int chunk) {
+  if (num_splits > 0) {
+    int c = (L + num_splits - 1) / num_splits;
+    return ((c + kPage - 1) / kPage) * kPage;
+  }
+  return chunk;
+}
+
+__host__ __device__ inline int splits_of(int L, int num_splits, int chunk) {
+  int c = chunk_of(L, num_splits, chunk);
+  return (L + c - 1) / c;
+}
+
+// Logical work index of a workgroup so that consecutive logical indices run
+// on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ inline int xcd_logical_index(int g, int G) {
+  int q = G / kNumXCD, r = G % kNumXCD;
+  int x = g % kNumXCD;
+  return x * q + (x < r ? x : r) + g / kNumXCD;
+}
+
+// Arguments of the attention kernels (passed by value).
+struct DecodeArgs {
+  const void* q_abs;          // [B*T, n_h, D] bf16 (fast) / q_dtype (general)
+  const void* cache;          // contiguous [B, max_len, D] or paged
+  const float* kv_scale;      // fp8: one float per cache row
+  const int32_t* page_table;  // [B, max_pages] or nullptr
+  const int32_t* seq_lens;    // [B]
+  float* part_o;              // [n_items, rows, d_c] partial latent outputs
+  float* part_lse;            // [n_items, rows]
+  float* out_latent;          // [B*T, n_h, d_c]
+  float* out_lse;             // [B*T, n_h]
+  int32_t B, T, n_h, d_c, d_r;
+  int32_t max_pages, max_len;
+  int32_t num_splits, chunk, n_items, row_blocks;
+  int32_t q_dtype, kv_dtype;
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+}  // namespace mla

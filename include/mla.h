@@ -1,0 +1,203 @@
+/*
+ * mla.h -- C ABI of the MLA decode library (libmla.so, AMD gfx950 / MI355X).
+ *
+ * One decode step of Multi-head Latent Attention over the compressed latent
+ * KV cache, with W^UK absorbed into the query and W^UV applied after the
+ * latent-space weighted sum.  Sources, cited by page title and section /
+ * equation:
+ *   "DeepSeek-V2: Strong, Economical, Efficient" -- section 2.1.2 (low-rank
+ *     key-value joint compression; only c^KV is cached; W^UK can be absorbed
+ *     into the query side and W^UV into the output side), section 2.1.3
+ *     (decoupled RoPE: per-head q^R, one shared k^R per token, cached next to
+ *     c^KV), Appendix C (full formulas; absorption by associativity of the
+ *     matrix products), section 3.2.1 (n_h = 128, d_h = 128, d_c = 512,
+ *     d_h^R = 64).
+ *   "DeepSeek-V3 Technical Report" notes, MLA section -- the equations for
+ *     k^C, k^R, v^C, q^C, q^R and the attention-output equation
+ *     o_{t,i} = sum_{j<=t} softmax_j(q_{t,i}.k_{j,i} / sqrt(d_h + d_h^R)) v^C_{j,i}.
+ *
+ * With the absorbed query q~_{t,i} = [W^UK_i^T q^C_{t,i} ; q^R_{t,i}] and the
+ * cache row K_j = [c^KV_j ; k^R_j] (d_c + d_h^R elements), the score is
+ * q~.K_j / sqrt(d_h + d_h^R), the latent output is
+ * latent_{t,i} = sum_j p_j c^KV_j, and o_{t,i} = W^UV_i latent_{t,i}.
+ *
+ * Conventions common to every call
+ *   - All pointers are DEVICE pointers unless the name ends in _host.
+ *   - All tensors are dense, row-major, and start 16-byte aligned.
+ *   - The caller allocates and owns every buffer, including the workspace.
+ *     The library allocates no memory and keeps no state between calls.
+ *   - Every call enqueues work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns without synchronising.  Results are ready when the
+ *     stream reaches that point.
+ *   - Return value: MLA_OK (0) when the work was enqueued, else a negative
+ *     mla_status_t.  All argument checks run on the host before any HIP call;
+ *     on error nothing is enqueued and no buffer is touched.
+ *   - Weights W^UK / W^UV are stored [n_h, d_h, d_c]: head i is the row block
+ *     [i*d_h, (i+1)*d_h) of the d_h n_h x d_c matrix.
+ *   - Query tokens are numbered n = b*T + tau (sequence b, query tau < T).
+ *     A sequence of KV length L_b holds its T query tokens as its last T
+ *     rows; query tau sits at position L_b - T + tau and attends to cache
+ *     rows 0 .. L_b - T + tau (the sum includes the current token).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_DIMS = -2,        /* dimension fields inconsistent or out of range */
+  MLA_ERR_DTYPE = -3,       /* unknown or unsupported dtype combination */
+  MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MLA_ERR_SEQLEN = -5,      /* some L_b < 1, L_b < T, or L_b beyond capacity */
+  MLA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+  MLA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement */
+  MLA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a kernel launch */
+  MLA_ERR_ARG = -9          /* a count, size or flag argument is invalid */
+} mla_status_t;
+
+typedef enum mla_dtype {
+  MLA_F32 = 0,      /* IEEE binary32 */
+  MLA_BF16 = 1,     /* bfloat16 */
+  MLA_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("e4m3fn", max 448), KV cache only */
+} mla_dtype_t;
+
+/* Problem dimensions and number formats (a plain value struct). */
+typedef struct mla_dims {
+  int32_t n_heads;     /* n_h */
+  int32_t d_head;      /* d_h   (per-head dim of q^C, k^C, v^C) */
+  int32_t d_latent;    /* d_c   (KV compression dim) */
+  int32_t d_rope;      /* d_h^R (decoupled RoPE dim, even) */
+  int32_t page_size;   /* tokens per page of a paged cache; must be 64 */
+  int32_t kv_dtype;    /* cache format: MLA_F32, MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t q_dtype;     /* format of queries, weights, q_abs and o:
+                          MLA_F32 or MLA_BF16 */
+  float softmax_scale; /* 0 -> 1/sqrt(d_head + d_rope) */
+  float rope_base;     /* RoPE base; 0 -> 10000 */
+} mla_dims_t;
+
+/* Supported combinations:
+ *   fast path (MFMA): n_h % 32 == 0, (n_h*T) % 128 == 0, d_h = 128,
+ *       d_c = 512, d_h^R = 64, q_dtype = BF16, kv_dtype = BF16 or FP8_E4M3;
+ *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
+ *       d_h^R <= 128 (even),
+ *       every q_dtype / kv_dtype combination (e.g. the all-fp32 problems).
+ * RoPE uses interleaved pairs (2k, 2k+1) rotated by pos * base^(-2k/d_h^R).
+ */
+
+/* ------------------------------------------------------------------------ */
+/* Query absorption: "DeepSeek-V2", section 2.1.2 and Appendix C (W^UK is
+ * absorbed into the query); decoupled RoPE of q^R, section 2.1.3.
+ *
+ *   q_abs[n, i, 0:d_c]        = W^UK_i^T q_nope[n, i, :]      (fp32 accumulate)
+ *   q_abs[n, i, d_c:d_c+d_r]  = RoPE(q_rope[n, i, :], q_pos[n])   if q_pos
+ *                             = q_rope[n, i, :]                   if q_pos NULL
+ *
+ * q_nope [n_tokens, n_h, d_h], q_rope [n_tokens, n_h, d_h^R],
+ * w_uk [n_h, d_h, d_c]: q_dtype.  q_pos [n_tokens] int32 or NULL.
+ * q_abs [n_tokens, n_h, d_c + d_h^R]: q_dtype, written (round to nearest).
+ * n_tokens >= 1.                                                          */
+int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope,
+                     const void* q_rope, const void* w_uk,
+                     const int32_t* q_pos, void* q_abs, int32_t n_tokens,
+                     void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Cache append: writes cache rows [c^KV | k^R] of new tokens ("DeepSeek-V2",
+ * section 2.1.3: c^KV and the shared, rotated k^R are the cached vectors;
+ * "DeepSeek-V3 Technical Report" notes, MLA section, the boxed vectors).
+ *
+ * new_c [n_rows, d_c], new_kr [n_rows, d_h^R]: F32 when kv_dtype is F32,
+ * else BF16.  Row r belongs to sequence seq_idx[r] at position pos[r]
+ * (device int32 arrays of n_rows).  apply_rope != 0 rotates k^R at pos[r]
+ * before it is stored.
+ *
+ * Layouts (D = d_c + d_h^R):
+ *   contiguous (page_table == NULL): cache [B, max_len, D]; row =
+ *       seq * max_len + pos.
+ *   paged: cache [num_pages, page_size, D]; page_table [B, max_pages] int32;
+ *       row = page_table[seq*max_pages + pos/page_size]*page_size
+ *             + pos % page_size.
+ * cache_rows is the capacity of the cache in rows (B*max_len or
+ * num_pages*page_size).  A row whose target falls outside [0, cache_rows),
+ * or whose position lies outside the sequence's pages, is skipped: the
+ * kernel never writes outside the cache.
+ *
+ * kv_dtype FP8_E4M3: per row, s = amax|row| / 448 (float32, s = 1 if the row
+ * is zero); each element stores the E4M3 code nearest to x / s (ties to
+ * even, saturating at 448); kv_scale[row] = s.  kv_scale must be NULL for
+ * other formats.                                                          */
+int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c,
+                         const void* new_kr, const int32_t* seq_idx,
+                         const int32_t* pos, const int32_t* page_table,
+                         int32_t batch, int32_t max_pages, int32_t max_len,
+                         int64_t cache_rows, int32_t apply_rope, void* cache,
+                         float* kv_scale, int32_t n_rows, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Workspace of mla_decode_attn for the given host copy of the lengths and
+ * split request (same planner as mla_decode_attn).  *bytes receives the
+ * exact size; 0 when no sequence is split.                                */
+int32_t mla_decode_workspace_size(const mla_dims_t* dims,
+                                  const int32_t* seq_lens_host, int32_t batch,
+                                  int32_t q_tokens, int32_t num_splits,
+                                  size_t* bytes);
+
+/* ------------------------------------------------------------------------ */
+/* Attention over the latent cache ("DeepSeek-V3 Technical Report" notes,
+ * MLA section, attention-output equation, evaluated in absorbed form):
+ *
+ *   s_j = scale * q_abs[n, i, :] . cache_row_j        (j <= L_b - T + tau)
+ *   out_latent[n, i, :] = sum_j softmax(s)_j * cache_row_j[0:d_c]
+ *   out_lse[n, i]       = ln sum_j exp(s_j)
+ *
+ * q_abs [B*T, n_h, D] q_dtype; cache as in mla_cache_append (kv_scale for
+ * FP8 only).  seq_lens [B] int32 on the device; seq_lens_host: the same
+ * values on the host (used to plan the split-KV work; they must agree).
+ * num_splits = 0: the library splits long sequences into KV chunks to fill
+ * the GPU; num_splits = S > 0: each sequence is cut into at most S chunks of
+ * equal size (rounded up to 64 tokens).  Chunks are reduced with an LSE
+ * combine.  workspace/ws_bytes: at least mla_decode_workspace_size() bytes
+ * (may be NULL/0 when that size is 0).  out_latent [B*T, n_h, d_c] fp32,
+ * out_lse [B*T, n_h] fp32.  Requires 1 <= T <= L_b for every b, and L_b <=
+ * max_len (contiguous) or L_b <= max_pages*page_size (paged).             */
+int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs,
+                        const void* cache, const float* kv_scale,
+                        const int32_t* page_table, int32_t max_pages,
+                        int32_t max_len, const int32_t* seq_lens,
+                        const int32_t* seq_lens_host, int32_t batch,
+                        int32_t q_tokens, int32_t num_splits, void* workspace,
+                        size_t ws_bytes, float* out_latent, float* out_lse,
+                        void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Value up-projection after the latent sum ("DeepSeek-V2", section 2.1.2 and
+ * Appendix C: W^UV is applied to the latent output instead of forming
+ * v^C for every cached token):
+ *
+ *   out[n, i, :] = W^UV_i latent[n, i, :]          (fp32 accumulate)
+ *
+ * latent [n_tokens, n_h, d_c] fp32; w_uv [n_h, d_h, d_c] q_dtype;
+ * out [n_tokens, n_h, d_h] in out_dtype (MLA_F32, or MLA_BF16 rounded to
+ * nearest).                                                               */
+int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent,
+                      const void* w_uv, void* out, int32_t out_dtype,
+                      int32_t n_tokens, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_string(int32_t status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

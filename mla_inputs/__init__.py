@@ -60,6 +60,7 @@ class Workload:
     d_rope: int
     kv_len: int = 0            # uniform length; 0 when len_range is used
     len_range: Tuple[int, int] = (0, 0)   # log-uniform [lo, hi]
+    lengths: Tuple[int, ...] = ()          # explicit per-sequence lengths
     kv_dtype: str = "bf16"     # "f32" | "bf16" | "fp8"
     q_dtype: str = "bf16"      # "f32" | "bf16"
     layout: str = "contiguous"  # "contiguous" | "paged"
@@ -179,7 +180,11 @@ def generate(w: Workload, seed: Optional[int] = None,
     out["q_nope"] = _gauss(rng["q_nope"], (B * T, H, w.d_head), 1.0, w.q_dtype)
     out["q_rope"] = _gauss(rng["q_rope"], (B * T, H, w.d_rope), 1.0, w.q_dtype)
 
-    if w.kv_len > 0:
+    if w.lengths:
+        if len(w.lengths) != B:
+            raise ValueError("lengths must list one length per sequence")
+        seq_lens = np.asarray(w.lengths, dtype=np.int32)
+    elif w.kv_len > 0:
         seq_lens = np.full(B, w.kv_len, dtype=np.int32)
     else:
         lo, hi = w.len_range

@@ -100,6 +100,36 @@ def decode(q_nope: np.ndarray, q_rope: np.ndarray, w_uk: np.ndarray,
     return {"o": o, "latent": lat, "lse": lse}
 
 
+def absorbed_query(q_nope: np.ndarray, q_rope: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """The absorbed query of [V2] Appendix C: by associativity,
+    q^C_i . (W^UK_i c) = (W^UK_i^T q^C_i) . c, so the per-head query against
+    the cache row [c ; k^R] is [W^UK_i^T q^C_i ; q^R_i].
+
+    q_nope [N, n_h, d_h], q_rope [N, n_h, d_h^R] (rotated), w_uk [n_h, d_h, d_c]
+    -> [N, n_h, d_c + d_h^R] (float64).
+    """
+    n_tok, H, _ = q_nope.shape
+    out = np.empty((n_tok, H, w_uk.shape[2] + q_rope.shape[2]))
+    for i in range(H):
+        out[:, i, :w_uk.shape[2]] = q_nope[:, i, :] @ w_uk[i]
+        out[:, i, w_uk.shape[2]:] = q_rope[:, i, :]
+    return out
+
+
+def up_project(latent: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """o_{n,i} = W^UV_i latent_{n,i}: the value up-projection applied after
+    the latent-space weighted sum ([V2] Appendix C; exact because
+    sum_j p_j W^UV_i c_j = W^UV_i sum_j p_j c_j).
+
+    latent [N, n_h, d_c], w_uv [n_h, d_h, d_c] -> [N, n_h, d_h] (float64).
+    """
+    n_tok, H, _ = latent.shape
+    out = np.empty((n_tok, H, w_uv.shape[1]))
+    for i in range(H):
+        out[:, i, :] = latent[:, i, :] @ w_uv[i].T
+    return out
+
+
 def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
@@ -108,7 +138,7 @@ def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def logical_inputs(gen: Dict[str, np.ndarray], workload) -> Dict[str, np.ndarray]:
+def logical_inputs(gen: Dict[str, np.ndarray], workload, seqs=None) -> Dict[str, np.ndarray]:
     """Decode the generator's stored inputs into the oracle's float64 operands.
 
     Applies the steps that precede attention in the method, the oracle's way:
@@ -117,6 +147,8 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload) -> Dict[str, np.ndarray
       * for the fp8 cache, the per-token E4M3 quantisation of the source rows
         (float32 decisions, see ``formats``) followed by exact dequantisation:
         the dequantised cache *is* the attention input.
+    ``seqs`` limits the cache rows decoded to those sequences (the returned
+    row_offsets then index the compacted rows).
     """
     w = workload
     d = {
@@ -128,10 +160,24 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload) -> Dict[str, np.ndarray
         "row_offsets": gen["row_offsets"],
     }
     src_dt = "f32" if w.kv_dtype == "f32" else "bf16"
-    c = _to_f64(gen["c_kv"], src_dt)
-    kr = _to_f64(gen["k_r"], src_dt)
+    offs = np.asarray(gen["row_offsets"], dtype=np.int64)
+    if seqs is None:
+        idx = slice(None)
+        row_pos = gen["row_pos"]
+    else:
+        seqs = sorted(set(int(b) for b in seqs))
+        idx = np.concatenate([np.arange(offs[b], offs[b + 1]) for b in seqs])
+        row_pos = gen["row_pos"][idx]
+        new_offs = np.zeros_like(offs)
+        start = 0
+        for b in seqs:
+            new_offs[b] = start
+            start += offs[b + 1] - offs[b]
+        d["row_offsets"] = new_offs
+    c = _to_f64(gen["c_kv"][idx], src_dt)
+    kr = _to_f64(gen["k_r"][idx], src_dt)
     if w.rope:
-        kr = _rope(kr, gen["row_pos"], w.rope_base)
+        kr = _rope(kr, row_pos, w.rope_base)
         qpos = np.repeat(gen["q_pos"], w.n_heads).reshape(-1, w.n_heads)
         d["q_rope"] = _rope(d["q_rope"], qpos, w.rope_base)
     if w.kv_dtype == "fp8":
@@ -146,7 +192,7 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload) -> Dict[str, np.ndarray
 
 def decode_workload(gen: Dict[str, np.ndarray], workload, seqs=None, heads=None):
     """Oracle outputs for a generated workload (optionally a sample of it)."""
-    d = logical_inputs(gen, workload)
+    d = logical_inputs(gen, workload, seqs)
     return decode(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_rows"],
                   d["kr_rows"], d["row_offsets"], d["seq_lens"],
                   workload.q_tokens, seqs=seqs, heads=heads)

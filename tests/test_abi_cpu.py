@@ -1,0 +1,149 @@
+"""The C-ABI library loads, exports what include/mla.h declares, and rejects
+invalid arguments with the documented status codes before any HIP call (so
+these run without a GPU).  Also checks the host split planner through
+mla_decode_workspace_size."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+LIB = os.path.join(ROOT, "head_latent_attention_11_amd", "libmla.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmla.so not built")
+
+OK, NULL, DIMS, DTYPE, ALIGN, SEQLEN, WS, UNSUP, LAUNCH, ARG = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+FAKE = 0x10000          # a 16-byte aligned non-null address, never dereferenced
+MIS = 0x10008           # misaligned
+
+
+@pytest.fixture(scope="module")
+def mla():
+    from head_latent_attention_11_amd import binding
+    return binding.load_library(LIB), binding
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int32_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+
+
+def test_header_declarations_found():
+    names = _declared()
+    assert set(names) >= {"mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
+                          "mla_decode_attn", "mla_up_proj_v", "mla_status_string"}
+
+
+def test_library_exports_every_declared_symbol(mla):
+    lib, _ = mla
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(mla):
+    lib, b = mla
+    for code in (OK, NULL, DIMS, DTYPE, ALIGN, SEQLEN, WS, UNSUP, LAUNCH, ARG, -1234):
+        assert isinstance(b.status_string(code), str) and b.status_string(code)
+    assert b.version() >= 10000
+
+
+def _v2(b, **kw):
+    return b.MLADims.make(128, 128, 512, 64, **kw)
+
+
+def _decode(lib, b, dims, lens, T=1, q=FAKE, cache=FAKE, scale=None, pt=None, max_pages=0,
+            max_len=8192, seq=FAKE, ws=None, wsb=0, out=FAKE, lse=FAKE, splits=0):
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    return lib.mla_decode_attn(ctypes.byref(dims), q, cache, scale, pt, max_pages, max_len, seq,
+                               ctypes.cast(arr, ctypes.c_void_p), len(lens), T, splits, ws,
+                               wsb, out, lse, None)
+
+
+def test_decode_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    assert _decode(lib, b, d, [100], q=None) == NULL
+    assert _decode(lib, b, d, [100], out=None) == NULL
+    assert _decode(lib, b, d, [100], q=MIS) == ALIGN
+    assert _decode(lib, b, d, [0]) == SEQLEN                  # L_b = 0
+    assert _decode(lib, b, d, [3], T=4) == SEQLEN             # T > L_b
+    assert _decode(lib, b, d, [9000], max_len=8192) == SEQLEN  # beyond capacity
+    assert _decode(lib, b, d, [100], T=0) == ARG
+    assert _decode(lib, b, d, [100], splits=-1) == ARG
+    assert _decode(lib, b, d, [4096] * 32) == WS              # needs a workspace
+    assert _decode(lib, b, d, [4096] * 32, ws=FAKE, wsb=16) == WS
+    fp8 = _v2(b, kv_dtype="fp8")
+    assert _decode(lib, b, fp8, [100]) == NULL                # fp8 needs kv_scale
+    bad = _v2(b, page_size=32)
+    assert _decode(lib, b, bad, [100]) == DIMS
+    bad = _v2(b, kv_dtype=7)
+    assert _decode(lib, b, bad, [100]) == DTYPE
+    bad = b.MLADims.make(128, 128, 512, 63)
+    assert _decode(lib, b, bad, [100]) == DIMS                # odd RoPE dim
+    bad = b.MLADims.make(128, 128, 513, 64)
+    assert _decode(lib, b, bad, [100]) == DIMS
+    bad = _v2(b, softmax_scale=-1.0)
+    assert _decode(lib, b, bad, [100]) == ARG
+    # paged: capacity is max_pages * 64
+    assert _decode(lib, b, d, [200], pt=FAKE, max_pages=3) == SEQLEN
+    assert _decode(lib, b, d, [200], pt=FAKE, max_pages=0) == ARG
+    assert lib.mla_decode_attn(None, FAKE, FAKE, None, None, 0, 10, FAKE, FAKE, 1, 1, 0,
+                               None, 0, FAKE, FAKE, None) == NULL
+
+
+def test_absorb_append_upproj_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    assert lib.mla_absorb_q(ctypes.byref(d), None, FAKE, FAKE, None, FAKE, 4, None) == NULL
+    assert lib.mla_absorb_q(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 0, None) == ARG
+    assert lib.mla_absorb_q(ctypes.byref(d), FAKE, FAKE, MIS, None, FAKE, 4, None) == ALIGN
+    assert lib.mla_up_proj_v(ctypes.byref(d), FAKE, None, FAKE, 0, 4, None) == NULL
+    assert lib.mla_up_proj_v(ctypes.byref(d), FAKE, FAKE, MIS, 0, 4, None) == ALIGN
+    assert lib.mla_up_proj_v(ctypes.byref(d), FAKE, FAKE, FAKE, 2, 4, None) == DTYPE
+    assert lib.mla_up_proj_v(ctypes.byref(d), FAKE, FAKE, FAKE, 0, -1, None) == ARG
+    ap = lib.mla_cache_append
+    assert ap(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 0, FAKE, None,
+              0, None) == ARG                                  # n_rows = 0
+    assert ap(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, 2, 0, 64, 128, 0, FAKE, None,
+              8, None) == NULL
+    assert ap(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 2, 0, 64, 100, 0, FAKE, None,
+              8, None) == ARG                                  # B*max_len > rows
+    assert ap(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 0, FAKE, FAKE,
+              8, None) == ARG                                  # scale on a bf16 cache
+    fp8 = _v2(b, kv_dtype="fp8")
+    assert ap(ctypes.byref(fp8), FAKE, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 0, FAKE, None,
+              8, None) == NULL                                 # fp8 needs the scale array
+    assert ap(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 2, FAKE, None,
+              8, None) == ARG                                  # apply_rope not 0/1
+    assert ap(ctypes.byref(d), MIS, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 0, FAKE, None,
+              8, None) == ALIGN
+
+
+def _ws(lib, dims, lens, T=1, splits=0):
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    out = ctypes.c_size_t(0)
+    st = lib.mla_decode_workspace_size(ctypes.byref(dims), ctypes.cast(arr, ctypes.c_void_p),
+                                       len(lens), T, splits, ctypes.byref(out))
+    return st, out.value
+
+
+def test_split_planner_sizes(mla):
+    lib, b = mla
+    d = _v2(b)
+    rows, dc = 128, 512
+    # 32 x 4096 tokens, 1 row block: chunk 512 -> 8 splits each = 256 items
+    st, n = _ws(lib, d, [4096] * 32)
+    assert st == OK and n == 256 * rows * (dc + 1) * 4 + 256
+    # 64 x 8192, T = 4 (4 row blocks): chunk 8192 -> no split, no workspace
+    st, n = _ws(lib, _v2(b, kv_dtype="fp8"), [8192] * 64, T=4)
+    assert st == OK and n == 0
+    # explicit 64 splits of 131072 tokens: 4 * 64 items
+    st, n = _ws(lib, d, [131072] * 4, splits=64)
+    assert st == OK and n == 256 * rows * (dc + 1) * 4 + 256
+    # a short sequence is never split below 256 tokens
+    st, n = _ws(lib, d, [200])
+    assert st == OK and n == 0
+    st, _ = _ws(lib, d, [5], T=6)
+    assert st == SEQLEN

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases compare every output element with the oracle; the full-size
+workloads (in the launch configuration the benchmark times) compare sampled
+(sequence, head) rows that the oracle computes one by one.  NaN poisoning:
+the cache (including unused page slots and page tails), the outputs and the
+split workspace are filled with NaN before the step, so any read of an
+unwritten slot or a masked tile entering the PV product shows up as NaN.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import (LSE_ABS, MAX_ABS_BF16, REL_L2_BF16, REL_L2_FP8, REL_L2_FP32_TARGET,
+                         check, rel_l2, sample_mask, say, to_np)
+from mla_inputs import WORKLOADS, generate, small_variant
+from oracle import formats
+from oracle import mla as omla
+
+pytestmark = pytest.mark.gpu
+
+V2 = WORKLOADS["v2_b32_l4k_bf16"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from head_latent_attention_11_amd import binding
+    binding.load_library()
+    torch.cuda.set_device(0)
+
+
+def _buffers(w, gen, **kw):
+    from head_latent_attention_11_amd.runner import DecodeBuffers
+    return DecodeBuffers(w, gen, device="cuda", **kw)
+
+
+def _gates(w):
+    return (REL_L2_FP8, None) if w.kv_dtype == "fp8" else (REL_L2_BF16, MAX_ABS_BF16)
+
+
+def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None):
+    say(f"case {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout} "
+        f"splits={w.num_splits if num_splits is None else num_splits} seqs={seqs} heads={heads}")
+    gen = generate(w) if gen is None else gen
+    buf = _buffers(w, gen, num_splits=num_splits)
+    buf.step()
+    torch.cuda.synchronize()
+    o, lat, lse = to_np(buf.o), to_np(buf.latent), to_np(buf.lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lat)), "NaN/Inf in GPU output"
+    assert np.all(np.isfinite(lse))
+    ref = omla.decode_workload(gen, w, seqs=seqs, heads=heads)
+    mask = sample_mask((w.batch * w.q_tokens, w.n_heads),
+                       range(w.batch) if seqs is None else seqs,
+                       range(w.n_heads) if heads is None else heads, w.q_tokens)
+    rel, mabs = _gates(w)
+    check("o", o[mask], ref["o"][mask], rel, mabs)
+    check("latent", lat[mask], ref["latent"][mask], rel, mabs)
+    dl = float(np.max(np.abs(lse[mask] - ref["lse"][mask])))
+    say(f"  lse: max-abs {dl:.3e} (gate {LSE_ABS:.0e})")
+    assert dl <= LSE_ABS
+    if w.q_dtype == "f32" and w.kv_dtype == "f32":
+        check("o (fp32 target)", o[mask], ref["o"][mask], REL_L2_FP32_TARGET)
+    return buf, gen, ref
+
+
+# ----------------------------------------------------------- small cases
+SMALL = [
+    WORKLOADS["tiny_fp32"],
+    small_variant(V2, name="v2_ragged_auto", batch=4, kv_len=0, lengths=(1, 33, 700, 64)),
+    small_variant(V2, name="v2_ragged_split5", batch=4, kv_len=0, lengths=(1, 33, 700, 64),
+                  num_splits=5),
+    small_variant(V2, name="v2_paged", batch=5, kv_len=0, lengths=(40, 900, 64, 65, 333),
+                  layout="paged"),
+    small_variant(V2, name="v2_outliers_split7", batch=2, kv_len=0, lengths=(3000, 2900),
+                  num_splits=7, outlier_frac=0.01, outlier_scale=8.0),
+    small_variant(V2, name="bf16_t4", batch=2, q_tokens=4, kv_len=0, lengths=(129, 64)),
+    small_variant(V2, name="fp8_t4", batch=4, q_tokens=4, kv_len=0, lengths=(300, 77, 4, 130),
+                  kv_dtype="fp8"),
+    small_variant(V2, name="fp8_t4_split3", batch=4, q_tokens=4, kv_len=0,
+                  lengths=(300, 77, 4, 130), kv_dtype="fp8", num_splits=3),
+    small_variant(V2, name="fp8_t1_paged", batch=2, kv_len=0, lengths=(100, 520),
+                  kv_dtype="fp8", layout="paged"),
+    small_variant(V2, name="general_n16_bf16", batch=2, n_heads=16, kv_len=0,
+                  lengths=(50, 300)),
+    small_variant(V2, name="general_n16_fp8_rope", batch=2, n_heads=16, kv_len=0,
+                  lengths=(70, 129), kv_dtype="fp8", rope=True),
+    small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_bf16cache", kv_dtype="bf16",
+                  batch=2, kv_len=0, lengths=(64, 300), num_splits=2),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_decode_parity_small(w):
+    _run_compare(w)
+
+
+# ------------------------------------------------- full-size workloads
+FULL = [
+    (WORKLOADS["v2_b32_l4k_bf16"], [0, 17, 31], [0, 1, 64, 127]),
+    (WORKLOADS["v2_b64_l8k_bf16"], [5, 63], [3, 100]),
+    (WORKLOADS["v2_fp8_t4_b64_l8k"], [0, 63], [0, 64, 127]),
+    (WORKLOADS["v2_long_b4_l128k_bf16"], [0, 3], [0, 77]),
+]
+
+
+@pytest.mark.parametrize("w,seqs,heads", FULL, ids=[f[0].name for f in FULL])
+def test_decode_parity_full_size(w, seqs, heads):
+    _run_compare(w, seqs=seqs, heads=heads)
+
+
+def test_decode_parity_full_size_paged():
+    w = WORKLOADS["v2_paged_b128_bf16"]
+    gen = generate(w)
+    L = gen["seq_lens"]
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 5})
+    _run_compare(w, gen=gen, seqs=seqs, heads=[0, 77, 127])
+
+
+# ------------------------------------------------------ properties
+def test_split_invariance_and_determinism():
+    w = small_variant(V2, name="split_inv", batch=2, kv_len=0, lengths=(2000, 1500))
+    gen = generate(w)
+    ref = omla.decode_workload(gen, w)
+    outs = {}
+    for ns in (1, 2, 7, 0):
+        buf = _buffers(w, gen, num_splits=ns)
+        buf.step()
+        torch.cuda.synchronize()
+        outs[ns] = (to_np(buf.latent), to_np(buf.o))
+        check(f"latent splits={ns}", outs[ns][0], ref["latent"], REL_L2_BF16, MAX_ABS_BF16)
+        buf.step()                                    # same plan again: bitwise equal
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(buf.latent), outs[ns][0])
+        assert np.array_equal(to_np(buf.o), outs[ns][1])
+    for ns in (2, 7, 0):
+        r = rel_l2(outs[ns][0], outs[1][0])
+        say(f"  splits={ns} vs unsplit: rel-L2 {r:.2e}")
+        assert r <= 2e-3
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Token order is logical order whatever the physical page order, so the
+    same plan gives bitwise-identical results (token permutation invariance
+    of the page table)."""
+    base = small_variant(V2, name="perm", batch=3, kv_len=0, lengths=(700, 64, 200))
+    gen = generate(base)
+    paged = dataclasses.replace(base, layout="paged")
+    genp = generate(paged)
+    for k in ("c_kv", "k_r", "q_nope", "q_rope", "w_uk", "w_uv"):
+        assert np.array_equal(gen[k], genp[k])
+    a = _buffers(base, gen)
+    b = _buffers(paged, genp)
+    a.step()
+    b.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(a.latent), to_np(b.latent))
+    assert np.array_equal(to_np(a.o), to_np(b.o))
+
+
+def test_reference_restart_on_large_score_jump():
+    """A late token whose score exceeds the first tile's max by far more than
+    2^64 (log2 units) forces the kernel to restart its work item with a higher
+    reference; the result must still match the oracle."""
+    w = small_variant(V2, name="restart", batch=2, kv_len=0, lengths=(1000, 900))
+    gen = generate(w)
+    c = formats.bf16_to_f64(gen["c_kv"])
+    c[700] *= 64.0                  # sequence 0, late tile
+    c[1000 + 500] *= 64.0           # sequence 1
+    from mla_inputs import bf16_bits_from_f32
+    gen["c_kv"] = bf16_bits_from_f32(c.astype(np.float32))
+    _run_compare(w, gen=gen)
+
+
+# --------------------------------------------------- append, bit exact
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_cache_append_bit_exact(layout, kv):
+    w = small_variant(V2, name=f"append_{kv}_{layout}", batch=3, kv_len=0,
+                      lengths=(65, 200, 3), layout=layout, kv_dtype=kv,
+                      q_dtype="f32" if kv == "f32" else "bf16")
+    say(f"case append kv={kv} layout={layout}")
+    gen = generate(w)
+    buf = _buffers(w, gen)
+    torch.cuda.synchronize()
+    rows = omla.cache_row_index(gen["row_seq"], gen["row_pos"], gen.get("page_table"),
+                                w.page_size, buf.max_len)
+    cache = buf.cache.cpu()
+    if kv == "fp8":
+        d = omla.logical_inputs(gen, w)
+        got = cache.numpy()[rows]
+        assert np.array_equal(got, d["fp8_codes"])
+        assert np.array_equal(buf.kv_scale.cpu().numpy()[rows], d["fp8_scales"])
+    elif kv == "bf16":
+        got = cache.view(torch.int16).numpy().view(np.uint16)[rows]
+        assert np.array_equal(got, np.concatenate([gen["c_kv"], gen["k_r"]], 1))
+    else:
+        got = cache.numpy()[rows]
+        assert np.array_equal(got, np.concatenate([gen["c_kv"], gen["k_r"]], 1))
+    # every slot not written must still hold the NaN poison
+    written = np.zeros(buf.cache_rows, dtype=bool)
+    written[rows] = True
+    rest = cache.numpy()[~written] if kv != "bf16" else cache.float().numpy()[~written]
+    if kv == "fp8":
+        assert np.all(rest == 0x7F)
+    else:
+        assert np.all(np.isnan(rest))
+
+
+def test_cache_append_rope_matches_oracle():
+    w = WORKLOADS["tiny_fp32"]
+    gen = generate(w)
+    buf = _buffers(w, gen)
+    torch.cuda.synchronize()
+    d = omla.logical_inputs(gen, w)
+    got = buf.cache.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(got[:, :w.d_latent], d["c_rows"], rtol=0, atol=0)
+    np.testing.assert_allclose(got[:, w.d_latent:], d["kr_rows"], rtol=1e-6, atol=1e-6)
+
+
+def test_fp8_every_code_decodes_exactly():
+    """L = 1: the softmax weight is exactly 1, so the latent output is the
+    stored row itself; rows built from all 254 finite E4M3 codes with scale 1
+    must come back as their exact values."""
+    from head_latent_attention_11_amd.runner import DecodeBuffers
+    w = small_variant(V2, name="codes", batch=2, kv_len=0, lengths=(1, 1), kv_dtype="fp8")
+    gen = generate(w)
+    buf = DecodeBuffers(w, gen)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    row = np.zeros((2, 576), dtype=np.uint8)
+    row[0, :254] = codes
+    row[1, :254] = codes[::-1]
+    row[:, 254:508] = codes
+    row[:, 508:512] = codes[:4]
+    buf.cache[:2] = torch.from_numpy(row).cuda()
+    buf.kv_scale[:2] = 1.0
+    buf.step()
+    torch.cuda.synchronize()
+    lat = to_np(buf.latent)                       # [2, 128, 512]
+    exp = formats.e4m3_to_f64(row[:, :512])
+    for b in range(2):
+        assert np.array_equal(lat[b], np.broadcast_to(exp[b], lat[b].shape)), b
+
+
+# ------------------------------------------- absorb and up-projection
+@pytest.mark.parametrize("w", [V2, WORKLOADS["tiny_fp32"],
+                               small_variant(V2, name="n16", n_heads=16)],
+                         ids=["v2_mfma", "tiny_fp32_rope", "general_n16"])
+def test_absorb_q_parity(w):
+    w = small_variant(w, batch=min(w.batch, 37), kv_len=0, lengths=(64,) * min(w.batch, 37))
+    gen = generate(w)
+    buf = _buffers(w, gen)
+    buf.absorb()
+    torch.cuda.synchronize()
+    d = omla.logical_inputs(gen, w)
+    ref = omla.absorbed_query(d["q_nope"], d["q_rope"], d["w_uk"])
+    got = to_np(buf.q_abs)
+    # q_abs is stored in the query format: bf16 rounding (2^-9 relative)
+    tol = 1e-6 if w.q_dtype == "f32" else 4e-3
+    check("q_abs", got, ref, tol)
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-3)) < (1e-5 if w.q_dtype == "f32" else 8e-3)
+
+
+@pytest.mark.parametrize("w", [V2, WORKLOADS["tiny_fp32"],
+                               small_variant(V2, name="n16", n_heads=16)],
+                         ids=["v2_mfma", "tiny_fp32", "general_n16"])
+def test_up_proj_parity(w):
+    """Latent inputs are drawn here (seeded), never taken from the HIP path."""
+    n_tok = 45
+    rng = np.random.default_rng(77)
+    latent = (rng.standard_normal((n_tok, w.n_heads, w.d_latent)) * 0.05).astype(np.float32)
+    gen = generate(small_variant(w, batch=1, kv_len=64, lengths=()))
+    from head_latent_attention_11_amd import binding as B
+    from head_latent_attention_11_amd.runner import to_device
+    dims = B.MLADims.from_workload(w)
+    kind = "f32" if w.q_dtype == "f32" else "bf16"
+    w_uv = to_device(gen["w_uv"], kind, "cuda")
+    lat_d = torch.from_numpy(latent).cuda()
+    out = torch.full((n_tok, w.n_heads, w.d_head), float("nan"), dtype=w_uv.dtype, device="cuda")
+    out32 = torch.full((n_tok, w.n_heads, w.d_head), float("nan"), dtype=torch.float32,
+                       device="cuda")
+    B.up_proj_v(dims, lat_d, w_uv, out, n_tok)
+    B.up_proj_v(dims, lat_d, w_uv, out32, n_tok)
+    torch.cuda.synchronize()
+    w_uv64 = formats.bf16_to_f64(gen["w_uv"]) if kind == "bf16" else gen["w_uv"].astype(np.float64)
+    ref = omla.up_project(latent.astype(np.float64), w_uv64)
+    got = to_np(out)
+    check("o", got, ref, 1e-6 if kind == "f32" else 4e-3)
+    check("o (fp32 out)", to_np(out32), ref, 1e-5)

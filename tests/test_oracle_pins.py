@@ -405,3 +405,33 @@ def test_kv_cache_accounting_matches_pages():
     assert mla_el / (2 * w.d_head) == e["gqa_equivalent_groups"]
     assert 2 * mla_el == e["bf16_bytes_per_token"]
     assert mla_el + 4 == e["fp8_bytes_per_token_with_fp32_scale"]
+
+
+# ------------------------------------------- absorbed query and up-projection
+def test_absorbed_query_reproduces_unabsorbed_scores():
+    """q~ . [c_j ; k^R_j] must equal q . k_j with k_j = [W^UK_i c_j ; k^R_j]
+    materialised from the definition."""
+    rng = np.random.default_rng(31)
+    n_h, d_h, d_c, d_r, L, N = 3, 6, 10, 4, 7, 2
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    qn = rng.standard_normal((N, n_h, d_h)); qr = rng.standard_normal((N, n_h, d_r))
+    C = rng.standard_normal((L, d_c)); KR = rng.standard_normal((L, d_r))
+    qa = mla.absorbed_query(qn, qr, w_uk)
+    assert qa.shape == (N, n_h, d_c + d_r)
+    for n in range(N):
+        for i in range(n_h):
+            direct = np.array([sum(qn[n, i, r] * sum(w_uk[i, r, c] * C[j, c] for c in range(d_c))
+                                   for r in range(d_h)) + qr[n, i] @ KR[j] for j in range(L)])
+            np.testing.assert_allclose(np.concatenate([C, KR], 1) @ qa[n, i], direct, rtol=1e-12)
+
+
+def test_up_project_matches_literal_values():
+    """W^UV applied to the oracle's latent output equals the literal o."""
+    p = _rand_problem(np.random.default_rng(32), n_h=3, d_h=5, d_c=9, d_r=2, L=13, T=2)
+    out = _run(p)
+    np.testing.assert_allclose(mla.up_project(out["latent"], p["w_uv"]), out["o"], rtol=1e-12)
+    # and against the worked example
+    g = _golden()
+    w_uk, w_uv, C, KR, qn, qr = _golden_operands(g)
+    lat = np.array(g["expected_T1"]["latent"])[None]
+    np.testing.assert_allclose(mla.up_project(lat, w_uv)[0], g["expected_T1"]["o"], atol=1e-13)
