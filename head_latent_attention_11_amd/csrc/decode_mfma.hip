@@ -18,17 +18,27 @@
 //     item (36 MFMA operands of 8 bf16 = 144 VGPRs) and its output
 //     accumulator O^T (512 x 32 fp32 = 256 registers) stays in the matrix
 //     accumulators.
-//   * KV tiles of 32 tokens are staged in LDS (double buffered, rows padded
-//     to 1168 bytes so the 16-byte operand reads of 16 consecutive tokens hit
-//     distinct banks).  fp8 tiles are decoded to bf16 while staging; the
-//     per-token scale multiplies the score and is folded into P for the PV
-//     product, so the fp8 values themselves enter the bf16 MFMA exactly.
-//   * S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 so that each
-//     lane holds one head's 16 token scores: the per-head max and sum need
-//     no cross-lane reduction except with the partner lane (lane ^ 32).  The
-//     probability registers are then already in the operand layout of the PV
-//     product O^T += C^T P^T (token order inside the K dimension is chosen to
-//     match the score layout).
+//   * KV tiles of 32 tokens go through a 3-buffer LDS ring (rows padded to
+//     1168 bytes so the 16-byte operand reads of 16 consecutive tokens hit
+//     distinct banks).  While tile i+2 streams in, a wave takes the softmax
+//     of tile i, the scores of tile i+1 and the PV product of tile i, so the
+//     matrix pipe has independent work while the softmax runs.
+//     bf16 tiles move HBM -> LDS with buffer loads that write LDS directly
+//     (no VGPR staging); a load range that ends at the last valid token makes
+//     the hardware write zeros for masked tokens, so they enter the PV
+//     product as exact zeros.  fp8 tiles are decoded to bf16 while staged
+//     through VGPRs; the per-token scale multiplies the score and is folded
+//     into P for the PV product, so the fp8 values enter the bf16 MFMA
+//     exactly.
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one head's 16 token scores
+//     in each lane: the per-head max and sum need no cross-lane reduction
+//     except with the partner lane (lane ^ 32).  The probability registers
+//     are then already in the B-operand layout of O^T += C^T P^T (the token
+//     order inside the K dimension is chosen to match the score layout), and
+//     the A operand C^T comes from the transposing LDS read
+//     (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
+//     i%4 of the 8-byte chunks addressed by lanes 4k + i/4, k = 0..3, i.e.
+//     four token rows of 16 latent dims come back as 16 dims of 4 tokens).
 //   * Softmax in the log2 domain against a per-row reference m_ref instead
 //     of a running max: m_ref is the max of the first tile in which the row
 //     sees a token, and p = 2^(s - m_ref) is accumulated without rescaling
@@ -46,14 +56,28 @@ namespace mla {
 
 namespace {
 constexpr int DC = 512, DR = 64, D = DC + DR;
+constexpr int ROWS_WG = 128;             // query rows per workgroup (4 waves x 32)
 constexpr int TILE = 32;                 // tokens per staged tile
 constexpr int LROW = 1168;               // LDS bytes per token row (1152 + 16 pad)
-constexpr int NCH = 72;                  // 16-byte bf16 chunks per row
-constexpr int NSTG = TILE * NCH / 256;   // staging chunks per thread (9)
+constexpr int NBUF = 4;                  // LDS ring of tiles
+constexpr int NLOADS = 37;               // direct loads of 64 x 16 B per tile
+constexpr int TILE_BYTES = NLOADS * 1024;
+constexpr int NLD = 10;                  // loads per wave per tile (wave 0: 10, others: 9)
+constexpr int NCH = 72;                  // 16-byte chunks per bf16 row
+constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte staging chunks per thread (9)
+constexpr uint32_t kOOB = 0x40000000u;   // buffer offset past any valid range
 constexpr float kNegInf = -INFINITY;
+// s_waitcnt immediates (gfx9 encoding): vmcnt <= N, other counters unconstrained
+constexpr int kWaitVm9 = 9 | (7 << 4) | (15 << 8);
+constexpr int kWaitVm10 = 10 | (7 << 4) | (15 << 8);
 }  // namespace
 
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x2 lds_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (shortx4 __attribute__((address_space(3)))*)(p)));
+}
 
 // 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
 __device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
@@ -65,17 +89,44 @@ __device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
   return r;
 }
 
+// S^T[token, head] of one tile for the wave's 32 heads; kb points at this
+// lane's operand (token l%32, dims 16k + 8(l/32)).
+__device__ __forceinline__ floatx16 qk_tile(const uint8_t* kb, const bf16x8 (&qf)[D / 16]) {
+  floatx16 sa = {};
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k)
+    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kb + 32 * k), qf[k], sa, 0, 0, 0);
+  return sa;
+}
+
+// O^T[dim, head] += sum_tok C^T[dim, tok] P^T[tok, head] over a 32-token
+// tile; vb is this lane's transposed-read base in the tile.
+__device__ __forceinline__ void pv_tile(const uint8_t* vb, const bf16x8 pf0, const bf16x8 pf1,
+                                        floatx16 (&o)[DC / 32]) {
+#pragma unroll
+  for (int db = 0; db < DC / 32; ++db) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x2 lo = lds_tr16(vb + (16 * ks) * LROW + 64 * db);
+      const u32x2 hi = lds_tr16(vb + (16 * ks + 8) * LROW + 64 * db);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks ? pf1 : pf0, o[db], 0, 0, 0);
+    }
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][TILE * LROW];
-  __shared__ float s_scale[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
+  __shared__ float s_scale[NBUF][TILE];
   __shared__ int s_restart;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int g = xcd_logical_index(blockIdx.x, gridDim.x);
-  const int item = g / a.row_blocks, rb = g % a.row_blocks;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31, g = lane >> 4, j = lane & 15;
+  const int gi = xcd_logical_index(blockIdx.x, gridDim.x);
+  const int item = gi / a.row_blocks, rb = gi % a.row_blocks;
   const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
   if (loc.b < 0) return;
   const int b = loc.b;
@@ -84,12 +135,13 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int t0 = loc.s * c;
   const int t_end = min(L, t0 + c);                       // item end
   const int rows = a.n_h * a.T;
-  const int row = rb * 128 + wave * 32 + l32;             // this lane's row
+  const int row = rb * ROWS_WG + wave * 32 + l32;         // this lane's row
   const int tau = row / a.n_h, head = row % a.n_h;
   const int lim = min(t_end - 1, L - a.T + tau);          // last visible token
-  const int tau_max = (rb * 128 + 127) / a.n_h;
+  const int tau_max = (rb * ROWS_WG + ROWS_WG - 1) / a.n_h;
   const int t_stage = min(t_end, L - a.T + tau_max + 1);  // tokens any row sees
   const int nq = b * a.T + tau;
+  const int ntiles = (t_stage > t0) ? (t_stage - t0 + TILE - 1) / TILE : 0;
 
   // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims)
   bf16x8 qf[D / 16];
@@ -99,136 +151,165 @@ void decode_mfma_kernel(DecodeArgs a) {
     for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qrow + 16 * k + 8 * h);
   }
 
+  const uint8_t* cache = (const uint8_t*)a.cache;
+  constexpr int ROWB = FP8 ? D : 2 * D;                   // bytes per cache row
+  const size_t seq_row0 = (size_t)b * a.max_len;
+  const int32_t* ptab = a.page_table ? a.page_table + (size_t)b * a.max_pages : nullptr;
+
+  // ---- staging.  bf16: LDS 16-byte chunk q of a tile holds token q / 73,
+  // chunk q % 73 of its row (chunk 72 is the row padding, filled with zero
+  // by an out-of-range offset).  Load n of wave w fills chunks
+  // 64 (w + 4n) .. +63; the last (37th) load of a tile belongs to wave 0.
+  // fp8: 8-byte chunk ci = tid + 256 i of the tile goes to LDS bytes
+  // 16 ci + 16 (ci / 72) as 8 bf16.
+  // LDS chunk q = 64 (w + 4n) + lane  <-  memory chunk q - q/73 of the tile
+  // (q/73 = (449 q) >> 15 for q < 2368); the padding chunk of each row and
+  // chunks past the tile take an out-of-range offset.
+  const int qbase = 64 * wave + lane;
+#define MLA_VOFF(n_)                                                                       \
+  ({                                                                                     \
+    const int q__ = qbase + 256 * (n_), tk__ = (q__ * 449) >> 15;                        \
+    (q__ - 73 * tk__ == NCH || tk__ >= TILE) ? kOOB : uint32_t(16 * (q__ - tk__));      \
+  })
+  u32x2 stg8[FP8 ? NSTG8 : 1];
+  float stg_scale = 0.f;
+
+  // Issue the loads of the tile starting at token ts into ring slot buf.  A
+  // tile never crosses a page (ts is a multiple of 32, pages hold 64 tokens).
+#define MLA_ISSUE_TILE(ts_, buf_)                                                          \
+  do {                                                                                   \
+    const int ts__ = (ts_);                                                              \
+    const int nv__ = max(0, min(TILE, t_stage - ts__));                                  \
+    const size_t r0__ = nv__ == 0 ? 0                                                    \
+                      : ptab ? (size_t)ptab[ts__ / kPage] * kPage + (ts__ % kPage)       \
+                             : seq_row0 + ts__;                                          \
+    const __amdgpu_buffer_rsrc_t rs__ = __builtin_amdgcn_make_buffer_rsrc(               \
+        (void*)(cache + r0__ * ROWB), (short)0, nv__ * ROWB, 0x00020000);                \
+    if constexpr (!FP8) {                                                                \
+      _Pragma("unroll") for (int n = 0; n < NLD - 1; ++n)                                \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
+            rs__, (void __attribute__((address_space(3)))*)(&s_kv[(buf_)][1024 * (wave + 4 * n)]), \
+            16, MLA_VOFF(n), 0, 0, 0);                                                   \
+      if (wave == 0)                                                                     \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
+            rs__, (void __attribute__((address_space(3)))*)(&s_kv[(buf_)][1024 * 36]),   \
+            16, MLA_VOFF(NLD - 1), 0, 0, 0);                                             \
+    } else {                                                                             \
+      _Pragma("unroll") for (int i = 0; i < NSTG8; ++i)                                  \
+        stg8[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs__, 8 * tid, 2048 * i, 0)); \
+      if (tid < TILE) stg_scale = (tid < nv__) ? a.kv_scale[r0__ + tid] : 0.f;           \
+    }                                                                                    \
+  } while (0)
+  // fp8: decode the staged registers into ring slot buf
+#define MLA_STORE_FP8_TILE(buf_)                                                           \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NSTG8; ++i) {                                  \
+      const int ci = tid + 256 * i;                                                      \
+      *(u32x4*)(&s_kv[(buf_)][16 * ci + 16 * (ci / NCH)]) = fp8x8_to_bf16x8(stg8[i]);    \
+    }                                                                                    \
+    if (tid < TILE) s_scale[(buf_)][tid] = stg_scale;                                    \
+  } while (0)
+  // bf16: wait until at most one tile's loads of this wave are in flight
+#define MLA_WAIT_ONE_TILE_IN_FLIGHT()                                                      \
+  do {                                                                                   \
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(kWaitVm10);                                \
+    else __builtin_amdgcn_s_waitcnt(kWaitVm9);                                           \
+  } while (0)
+
+  // ---- per-lane LDS offsets of the MFMA operands
+  const int qk_off = l32 * LROW + 16 * h;                                  // + 32 k
+  const int pv_off = ((j >> 2) + 4 * h) * LROW + (16 * (g & 1) + 4 * (j & 3)) * 2;
+
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
 
-  const uint8_t* cache = (const uint8_t*)a.cache;
-  constexpr int ESZ = FP8 ? 1 : 2;
-
-  // first cache row of the tile starting at token ts (a tile never crosses
-  // a page: ts is a multiple of 32 and pages hold 64 tokens)
-  auto tile_row = [&](int ts) -> size_t {
-    if (a.page_table)
-      return (size_t)a.page_table[(size_t)b * a.max_pages + ts / kPage] * kPage + (ts % kPage);
-    return (size_t)b * a.max_len + ts;
-  };
-
-  // Staging: a 32-token tile is one contiguous run of cache rows (a tile
-  // never crosses a page), read with buffer loads whose range ends at the
-  // last valid token: loads past it return zero, so masked tokens enter
-  // the PV product as exact zeros.  Chunk ci of the tile sits at byte
-  // CH*ci in memory and at 16*ci + 16*(ci/72) in LDS (rows padded).
-  constexpr int CH = FP8 ? 8 : 16;     // bytes per staged chunk
-  u32x4 stg16[FP8 ? 1 : NSTG];
-  u32x2 stg8[FP8 ? NSTG : 1];
-  float stg_scale = 0.f;
-
-  auto stage_load = [&](int ts) {
-    const size_t r0 = tile_row(ts);
-    const int nvalid = min(TILE, t_stage - ts);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(cache + r0 * (size_t)(D * ESZ)), (short)0, nvalid * D * ESZ, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < NSTG; ++i) {
-      if (FP8)
-        stg8[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, CH * tid, CH * 256 * i, 0));
-      else
-        stg16[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, CH * tid, CH * 256 * i, 0));
-    }
-    if (FP8 && tid < TILE) stg_scale = (tid < nvalid) ? a.kv_scale[r0 + tid] : 0.f;
-  };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NSTG; ++i) {
-      const int ci = tid + 256 * i;
-      u32x4 v = FP8 ? fp8x8_to_bf16x8(stg8[i]) : stg16[i];
-      *(u32x4*)(&s_kv[buf][16 * ci + 16 * (ci / NCH)]) = v;
-    }
-    if (FP8 && tid < TILE) s_scale[buf][tid] = stg_scale;
-  };
-
-  const int ntiles = (t_stage > t0) ? (t_stage - t0 + TILE - 1) / TILE : 0;
   if (tid == 0) s_restart = 0;
   for (;;) {                          // attempts (a restart is rare)
 #pragma unroll
-  for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
-  l_run = 0.f;
-  if (ntiles > 0) {
-    stage_load(t0);
-    stage_store(0);
-  }
-  __syncthreads();
-
-  int restart = 0;
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const int ts = t0 + it * TILE;
-    if (it + 1 < ntiles) stage_load(ts + TILE);
-
-    const uint8_t* kb = s_kv[cur];
-    // ---- S^T[token, head] = sum_d K[token, d] Q[head, d]
-    floatx16 sa = {};
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) {
-      const bf16x8 a0 = *(const bf16x8*)(kb + l32 * LROW + 32 * k + 16 * h);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[k], sa, 0, 0, 0);
-    }
-    // ---- scores of this lane's head: register r holds token
-    //      8*(r/4) + 4*h + r%4 of the tile
-    float s[16];
-    float mt = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tl = 8 * (r >> 2) + 4 * h + (r & 3);
-      float v = sa[r] * a.scale_log2;
-      if (FP8) v *= s_scale[cur][tl];
-      s[r] = (ts + tl <= lim) ? v : kNegInf;
-      mt = fmaxf(mt, s[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    m_seen = fmaxf(m_seen, mt);
-    if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
-    if (mt > m_ref + 64.0f) s_restart = 1;
-    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] - m_use);
-      if (FP8) {
-        l_run += p;
-        pf[r >> 3][r & 7] = (__bf16)(p * s_scale[cur][8 * (r >> 2) + 4 * h + (r & 3)]);
-      } else {
-        // the normaliser sums exactly the rounded weights used in P C
-        const __bf16 pb = (__bf16)p;
-        l_run += (float)pb;
-        pf[r >> 3][r & 7] = pb;
+    for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
+    l_run = 0.f;
+    int restart = 0;
+    if (ntiles > 0) {
+      // prologue: tiles 0 and 1 resident, (bf16) tile 2 in flight
+      MLA_ISSUE_TILE(t0, 0);
+      if constexpr (FP8) MLA_STORE_FP8_TILE(0);
+      if (ntiles > 1) {
+        MLA_ISSUE_TILE(t0 + TILE, 1);
+        if constexpr (FP8) MLA_STORE_FP8_TILE(1);
       }
-    }
-    // ---- O^T[dim, head] += sum_tok C^T[dim, tok] P^T[tok, head]
-#pragma unroll
-    for (int db = 0; db < DC / 32; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tl = 16 * ks + 8 * (e >> 2) + 4 * h + (e & 3);
-          vf[e] = *(const __bf16*)(kb + tl * LROW + (32 * db + l32) * 2);
+      if constexpr (!FP8) {
+        if (ntiles > 2) {
+          MLA_ISSUE_TILE(t0 + 2 * TILE, 2);
+          MLA_WAIT_ONE_TILE_IN_FLIGHT();
+        } else {
+          __builtin_amdgcn_s_waitcnt(0);
         }
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+      }
+      __syncthreads();
+      // Step it works on tile it in ring slot it & 3 while (bf16) tiles
+      // it+1, it+2 are in flight and tile it+3 is issued, or (fp8) tile it+2
+      // is staged through VGPRs.
+      for (int it = 0; it < ntiles; ++it) {
+        const int ts = t0 + it * TILE;
+        const uint8_t* tile = s_kv[it & 3];
+        if constexpr (!FP8) {
+          MLA_ISSUE_TILE(ts + 3 * TILE, (it + 3) & 3);
+        } else {
+          MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
+        }
+        const floatx16 s_cur = qk_tile(tile + qk_off, qf);
+        // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4
+        float sv[16];
+        float mt = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tl = 8 * (r >> 2) + 4 * h + (r & 3);
+          float v = s_cur[r] * a.scale_log2;
+          if (FP8) v *= s_scale[it & 3][tl];
+          sv[r] = (ts + tl <= lim) ? v : kNegInf;
+          mt = fmaxf(mt, sv[r]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        m_seen = fmaxf(m_seen, mt);
+        if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
+        if (mt > m_ref + 64.0f) s_restart = 1;
+        const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+        bf16x8 pf0, pf1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
+          __bf16 pb;
+          if (FP8) {
+            l_run += p;
+            pb = (__bf16)(p * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)]);
+          } else {
+            // the normaliser sums exactly the rounded weights used in P C
+            pb = (__bf16)p;
+            l_run += (float)pb;
+          }
+          if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
+        }
+        pv_tile(tile + pv_off, pf0, pf1, o);
+        if constexpr (!FP8) {
+          MLA_WAIT_ONE_TILE_IN_FLIGHT();   // tile it+2 landed (it+3 may fly)
+        } else {
+          MLA_STORE_FP8_TILE((it + 2) & 3);
+        }
+        __syncthreads();
+        restart = s_restart;               // uniform: read after the barrier
+        if (restart) break;
       }
     }
-
-    if (it + 1 < ntiles) stage_store(cur ^ 1);
-    __syncthreads();
-    restart = s_restart;              // uniform: read after the barrier
-    if (restart) break;
+    if (!restart) break;
+    __builtin_amdgcn_s_waitcnt(0);    // no load of this attempt still in flight
+    __syncthreads();                  // everyone has read the flag
+    if (tid == 0) s_restart = 0;
+    m_ref = m_seen;
   }
-  if (!restart) break;
-  __syncthreads();                    // everyone has read the flag
-  if (tid == 0) s_restart = 0;
-  m_ref = m_seen;
-  }
+#undef MLA_ISSUE_TILE
+#undef MLA_STORE_FP8_TILE
+#undef MLA_WAIT_ONE_TILE_IN_FLIGHT
+#undef MLA_VOFF
 
   // ---- normalise and write (the final output, or this split's partial)
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -246,15 +327,16 @@ void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < DC / 32; ++db) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      floatx4 v = {o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-      *(floatx4*)(dst + 32 * db + 8 * j + 4 * h) = v * inv;
+    for (int jj = 0; jj < 4; ++jj) {
+      floatx4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
+      *(floatx4*)(dst + 32 * db + 8 * jj + 4 * h) = v * inv;
     }
   }
   if (h == 0) *dlse = lse;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  // a.row_blocks counts blocks of ROWS_WG query rows
   const int grid = a.n_items * a.row_blocks;
   if (a.kv_dtype == MLA_FP8_E4M3)
     hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(256), 0, st, a);

@@ -39,55 +39,81 @@ template <> __device__ inline void store_f<uint16_t>(uint16_t* p, size_t i, floa
 
 // ====================================================== absorb: MFMA path
 // q_abs[n, i, 0:512] = W^UK_i^T q_nope[n, i, :], d_h = 128.  One workgroup
-// per (head i, block of 128 latent columns); wave w owns 32 columns.  The
-// W^UK_i column block is staged transposed in LDS so that each MFMA operand
-// lane holds 8 consecutive d_h values.  D^T[cols x tokens] = W^T q^T.
-constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsDh + 8;
+// per (head i, block of 128 latent columns); wave w owns 32 columns and
+// computes D^T[cols x tokens] = W^T q^T.  The 128 x 128 W^UK_i block is
+// staged row-major in LDS with 16-byte writes and read back column-wise
+// with the gfx950 transposing LDS read: within each group of 16 lanes,
+// ds_read_b64_tr_b16 hands lane i element i%4 of the 8-byte chunks
+// addressed by lanes 4k + i/4 (k = 0..3), so four rows of 16 elements come
+// back as 16 columns of 4.
+constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsCols + 8;
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+__device__ inline shortx4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (shortx4 __attribute__((address_space(3)))*)(p));
+}
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
     uint16_t* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kAbsCols * kAbsLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
   const int head = blockIdx.x >> 2, cb = blockIdx.x & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, j = lane & 15;
 
-  // stage W^UK[head][r][cb*128 + c] -> wt[c][r]
+  // stage W^UK[head][r][cb*128 : cb*128 + 128] row-major (16-byte chunks)
   const uint16_t* wsrc = w_uk + (size_t)head * kAbsDh * DC + cb * kAbsCols;
-  for (int ch = tid; ch < kAbsDh * (kAbsCols / 8); ch += 256) {
-    const int r = ch / (kAbsCols / 8), c8 = (ch % (kAbsCols / 8)) * 8;
-    u32x4 v = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
+  u32x4 stg[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wt[(c8 + 2 * e) * kAbsLdsRow + r] = uint16_t(v[e] & 0xFFFF);
-      wt[(c8 + 2 * e + 1) * kAbsLdsRow + r] = uint16_t(v[e] >> 16);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int ch = tid + 256 * i, r = ch >> 4, c8 = (ch & 15) * 8;
+    stg[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ch = tid + 256 * i, r = ch >> 4, c8 = (ch & 15) * 8;
+    *(u32x4*)(ws + r * kAbsLdsRow + c8) = stg[i];
   }
   __syncthreads();
 
-  const int col = wave * 32 + l32;   // A-operand row (latent column in block)
+  // A operand (W^T, lane: column 32*wave + l32, d_h values 16k + 8h + e)
+  bf16x8 af[kAbsDh / 16];
+  const int colbase = wave * 32 + 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+  for (int k = 0; k < kAbsDh / 16; ++k) {
+    const int r0 = 16 * k + 8 * h;
+    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(ws + (r0 + (j >> 2)) * kAbsLdsRow + colbase));
+    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(ws + (r0 + 4 + (j >> 2)) * kAbsLdsRow + colbase));
+    af[k] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+
   for (int t0 = 0; t0 < n_tok; t0 += 32) {
     const int tok = t0 + l32;         // B-operand column
-    floatx16 acc = {};
+    bf16x8 bq[kAbsDh / 16];
 #pragma unroll
     for (int k = 0; k < kAbsDh / 16; ++k) {
-      bf16x8 a = *(const bf16x8*)(wt + col * kAbsLdsRow + 16 * k + 8 * h);
-      bf16x8 b = {};
+      bq[k] = bf16x8{};
       if (tok < n_tok)
-        b = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        bq[k] = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
     }
-    // acc[r]: row (column in block) 8(r/4) + 4h + r%4, column = token l32
+    floatx16 acc = {};
+#pragma unroll
+    for (int k = 0; k < kAbsDh / 16; ++k)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bq[k], acc, 0, 0, 0);
+    // acc[r]: column-in-block 8(r/4) + 4h + r%4 of wave's 32, token l32
     if (tok < n_tok) {
       uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int jj = 0; jj < 4; ++jj) {
         u32x2 pk;
-        pk[0] = uint32_t(f32_to_bf16_bits(acc[4 * j])) | uint32_t(f32_to_bf16_bits(acc[4 * j + 1])) << 16;
-        pk[1] = uint32_t(f32_to_bf16_bits(acc[4 * j + 2])) | uint32_t(f32_to_bf16_bits(acc[4 * j + 3])) << 16;
-        *(u32x2*)(dst + 8 * j + 4 * h) = pk;
+        pk[0] = uint32_t(f32_to_bf16_bits(acc[4 * jj])) | uint32_t(f32_to_bf16_bits(acc[4 * jj + 1])) << 16;
+        pk[1] = uint32_t(f32_to_bf16_bits(acc[4 * jj + 2])) | uint32_t(f32_to_bf16_bits(acc[4 * jj + 3])) << 16;
+        *(u32x2*)(dst + 8 * jj + 4 * h) = pk;
       }
     }
   }
@@ -249,44 +275,76 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
 
 // ===================================================== up-projection: MFMA
 // out[n, i, :] = W^UV_i latent[n, i, :], d_h = 128, d_c = 512.  One
-// workgroup per (head i, block of 32 tokens); wave w owns d_h rows
-// 32w..32w+31.  The fp32 latent is split into bf16 hi + lo parts so the
-// bf16 MFMA keeps (nearly) fp32 accuracy: W (hi + lo) with W exact in bf16.
+// workgroup of 2 waves per (head i, half of the d_h rows, block of 32
+// tokens); wave w owns d_h rows 64*half + 32*w .. +31.  The latent block
+// (32 tokens x 512 fp32) is staged in LDS as bf16 hi + lo parts
+// (x = hi + lo + O(2^-17 x)), so the bf16 MFMA keeps nearly fp32 accuracy
+// with W^UV exact in bf16.  All W^UV operand loads are issued up front.
+constexpr int kUpLds = 512 + 8;       // padded bf16 row of the latent block
+
 template <typename OutT>
-__global__ __launch_bounds__(256) void up_proj_mfma_kernel(
+__global__ __launch_bounds__(128) void up_proj_mfma_kernel(
     const float* __restrict__ latent, const uint16_t* __restrict__ w_uv,
     OutT* __restrict__ out, int n_tok, int n_h) {
   constexpr int DC = 512, DH = 128;
-  const int head = blockIdx.x, t0 = blockIdx.y * 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[32 * kUpLds];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[32 * kUpLds];
+  const int head = blockIdx.x >> 1, half = blockIdx.x & 1, t0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int m = wave * 32 + l32;        // d_h row held as A-operand row
-  const int tok = t0 + l32;             // token held as B-operand column
+  const int m = half * 64 + wave * 32 + l32;        // d_h row (A-operand row)
   const uint16_t* wrow = w_uv + ((size_t)head * DH + m) * DC;
-  const float* lrow = latent + ((size_t)tok * n_h + head) * DC;
-  floatx16 acc_hi = {}, acc_lo = {};
-#pragma unroll 4
-  for (int k = 0; k < DC / 16; ++k) {
-    bf16x8 a = *(const bf16x8*)(wrow + 16 * k + 8 * h);
-    bf16x8 bh = {}, bl = {};
-    if (tok < n_tok) {
-      const floatx4 x0 = *(const floatx4*)(lrow + 16 * k + 8 * h);
-      const floatx4 x1 = *(const floatx4*)(lrow + 16 * k + 8 * h + 4);
+
+  bf16x8 wa[DC / 16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? x0[e] : x1[e - 4];
-        const uint16_t hb = f32_to_bf16_bits(x);
-        const float hi = bf16_bits_to_f32(hb);
-        const uint16_t lb = f32_to_bf16_bits(x - hi);
-        bh[e] = __builtin_bit_cast(__bf16, hb);
-        bl[e] = __builtin_bit_cast(__bf16, lb);
-      }
+  for (int k = 0; k < DC / 16; ++k) wa[k] = *(const bf16x8*)(wrow + 16 * k + 8 * h);
+
+  // stage latent[t0 + t][head][:] (4096 chunks of 4 floats, 2 rounds)
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    floatx4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ch = tid + 128 * (16 * round + i);   // 0 .. 4095
+      const int t = ch >> 7, c4 = (ch & 127) * 4;
+      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (t0 + t < n_tok)
+        v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
     }
-    acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc_hi, 0, 0, 0);
-    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc_lo, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int ch = tid + 128 * (16 * round + i);
+      const int t = ch >> 7, c4 = (ch & 127) * 4;
+      u32x2 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint32_t hb[2], lb[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float x = v[i][2 * e + q];
+          hb[q] = f32_to_bf16_bits(x);
+          lb[q] = f32_to_bf16_bits(x - bf16_bits_to_f32((uint16_t)hb[q]));
+        }
+        hi[e] = hb[0] | hb[1] << 16;
+        lo[e] = lb[0] | lb[1] << 16;
+      }
+      *(u32x2*)(s_hi + t * kUpLds + c4) = hi;
+      *(u32x2*)(s_lo + t * kUpLds + c4) = lo;
+    }
   }
+  __syncthreads();
+
+  floatx16 acc_hi = {}, acc_lo = {};
+#pragma unroll
+  for (int k = 0; k < DC / 16; ++k) {
+    const bf16x8 bh = *(const bf16x8*)(s_hi + l32 * kUpLds + 16 * k + 8 * h);
+    const bf16x8 bl = *(const bf16x8*)(s_lo + l32 * kUpLds + 16 * k + 8 * h);
+    acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bh, acc_hi, 0, 0, 0);
+    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bl, acc_lo, 0, 0, 0);
+  }
+  const int tok = t0 + l32;
   if (tok < n_tok) {
-    OutT* dst = out + ((size_t)tok * n_h + head) * DH + wave * 32;
+    OutT* dst = out + ((size_t)tok * n_h + head) * DH + half * 64 + wave * 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const floatx4 v = {acc_hi[4 * j] + acc_lo[4 * j], acc_hi[4 * j + 1] + acc_lo[4 * j + 1],
@@ -383,12 +441,12 @@ hipError_t launch_up_proj(const mla_dims_t& d, bool fast, const float* latent,
                           const void* w_uv, void* out, bool out_f32, int n_tok,
                           hipStream_t st) {
   if (fast) {
-    const dim3 grid(d.n_heads, (n_tok + 31) / 32);
+    const dim3 grid(d.n_heads * 2, (n_tok + 31) / 32);
     if (out_f32)
-      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(128), 0, st,
                          latent, (const uint16_t*)w_uv, (float*)out, n_tok, d.n_heads);
     else
-      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(128), 0, st,
                          latent, (const uint16_t*)w_uv, (uint16_t*)out, n_tok, d.n_heads);
   } else {
     const size_t total = (size_t)n_tok * d.n_heads * d.d_head;

@@ -27,6 +27,7 @@ using namespace mla;
 namespace {
 
 constexpr int32_t kVersion = 10000;   // 1.0.0
+constexpr int64_t kRowsPerWorkgroup = 128;  // query rows per attention workgroup (fast path)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -54,7 +55,7 @@ bool fast_shape(const mla_dims_t* d) {
 
 bool fast_decode(const mla_dims_t* d, int T) {
   return fast_shape(d) && (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) &&
-         ((int64_t)d->n_heads * T) % 128 == 0;
+         ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
 }
 
 float rope_base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.f; }
@@ -86,7 +87,7 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
   if (num_splits < 0 || num_splits > 4096) return MLA_ERR_ARG;
   const bool fast = fast_decode(d, T);
   const int64_t rows = (int64_t)d->n_heads * T;
-  const int64_t rb = fast ? rows / 128 : rows;
+  const int64_t rb = fast ? rows / kRowsPerWorkgroup : rows;
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     if (lens[b] < 1 || lens[b] < T) return MLA_ERR_SEQLEN;

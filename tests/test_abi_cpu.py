@@ -133,7 +133,7 @@ def test_split_planner_sizes(mla):
     lib, b = mla
     d = _v2(b)
     rows, dc = 128, 512
-    # 32 x 4096 tokens, 1 row block: chunk 512 -> 8 splits each = 256 items
+    # 32 x 4096 tokens, 1 row block of 128 rows: chunk 512 -> 8 splits each
     st, n = _ws(lib, d, [4096] * 32)
     assert st == OK and n == 256 * rows * (dc + 1) * 4 + 256
     # 64 x 8192, T = 4 (4 row blocks): chunk 8192 -> no split, no workspace
