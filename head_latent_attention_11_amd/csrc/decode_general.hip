@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void decode_general_kernel(DecodeArgs a) {
     dst = a.out_latent + ((size_t)nq * a.n_h + head) * a.d_c;
     dlse = a.out_lse + (size_t)nq * a.n_h + head;
   } else {
-    dst = a.part_o + ((size_t)item * rows + row) * a.d_c;
+    dst = (float*)a.part_o + ((size_t)item * rows + row) * a.d_c;
     dlse = a.part_lse + (size_t)item * rows + row;
   }
   if (tid < a.d_c) dst[tid] = acc0 * inv;

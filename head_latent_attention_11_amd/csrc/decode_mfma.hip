@@ -315,24 +315,32 @@ void decode_mfma_kernel(DecodeArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const float lse = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
-  float* dst;
-  float* dlse;
   if (loc.ns == 1) {
-    dst = a.out_latent + ((size_t)nq * a.n_h + head) * DC;
-    dlse = a.out_lse + (size_t)nq * a.n_h + head;
-  } else {
-    dst = a.part_o + ((size_t)item * rows + row) * DC;
-    dlse = a.part_lse + (size_t)item * rows + row;
-  }
+    float* dst = a.out_latent + ((size_t)nq * a.n_h + head) * DC;
 #pragma unroll
-  for (int db = 0; db < DC / 32; ++db) {
+    for (int db = 0; db < DC / 32; ++db) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      floatx4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
-      *(floatx4*)(dst + 32 * db + 8 * jj + 4 * h) = v * inv;
+      for (int jj = 0; jj < 4; ++jj) {
+        floatx4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
+        *(floatx4*)(dst + 32 * db + 8 * jj + 4 * h) = v * inv;
+      }
     }
+    if (h == 0) a.out_lse[(size_t)nq * a.n_h + head] = lse;
+  } else {
+    // split partial, normalised, stored as bf16 (combined in fp32)
+    uint16_t* dst = (uint16_t*)a.part_o + ((size_t)item * rows + row) * DC;
+#pragma unroll
+    for (int db = 0; db < DC / 32; ++db) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bf16x2 p01 = {(__bf16)(o[db][4 * jj] * inv), (__bf16)(o[db][4 * jj + 1] * inv)};
+        const bf16x2 p23 = {(__bf16)(o[db][4 * jj + 2] * inv), (__bf16)(o[db][4 * jj + 3] * inv)};
+        *(u32x2*)(dst + 32 * db + 8 * jj + 4 * h) =
+            u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+      }
+    }
+    if (h == 0) a.part_lse[(size_t)item * rows + row] = lse;
   }
-  if (h == 0) *dlse = lse;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {

@@ -50,6 +50,11 @@ constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsCols + 8;
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
+// two floats -> packed bf16 pair (hardware round to nearest even)
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
 __device__ inline shortx4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (shortx4 __attribute__((address_space(3)))*)(p));
@@ -66,6 +71,14 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, j = lane & 15;
 
+  // first token block's query operands, issued before the W^UK staging
+  bf16x8 bq0[kAbsDh / 16];
+#pragma unroll
+  for (int k = 0; k < kAbsDh / 16; ++k) {
+    bq0[k] = bf16x8{};
+    if (l32 < n_tok)
+      bq0[k] = *(const bf16x8*)(q_nope + ((size_t)l32 * n_h + head) * kAbsDh + 16 * k + 8 * h);
+  }
   // stage W^UK[head][r][cb*128 : cb*128 + 128] row-major (16-byte chunks)
   const uint16_t* wsrc = w_uk + (size_t)head * kAbsDh * DC + cb * kAbsCols;
   u32x4 stg[8];
@@ -97,9 +110,12 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     bf16x8 bq[kAbsDh / 16];
 #pragma unroll
     for (int k = 0; k < kAbsDh / 16; ++k) {
-      bq[k] = bf16x8{};
-      if (tok < n_tok)
-        bq[k] = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
+      bq[k] = bq0[k];
+      if (t0 > 0) {
+        bq[k] = bf16x8{};
+        if (tok < n_tok)
+          bq[k] = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
+      }
     }
     floatx16 acc = {};
 #pragma unroll
@@ -109,12 +125,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     if (tok < n_tok) {
       uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        u32x2 pk;
-        pk[0] = uint32_t(f32_to_bf16_bits(acc[4 * jj])) | uint32_t(f32_to_bf16_bits(acc[4 * jj + 1])) << 16;
-        pk[1] = uint32_t(f32_to_bf16_bits(acc[4 * jj + 2])) | uint32_t(f32_to_bf16_bits(acc[4 * jj + 3])) << 16;
-        *(u32x2*)(dst + 8 * jj + 4 * h) = pk;
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        *(u32x2*)(dst + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
+                                               pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
     }
   }
 
@@ -265,7 +278,14 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
     for (int s = 0; s < ns; ++s) {
       const size_t it = (size_t)(first + s) * rows + row;
       const float w = expf(a.part_lse[it] - mx) * inv;
-      const floatx4 v = *(const floatx4*)(a.part_o + it * a.d_c + d4);
+      floatx4 v;
+      if (a.part_bf16) {
+        const u32x2 pk = *(const u32x2*)((const uint16_t*)a.part_o + it * a.d_c + d4);
+        v = floatx4{bf16_bits_to_f32(uint16_t(pk[0])), bf16_bits_to_f32(uint16_t(pk[0] >> 16)),
+                    bf16_bits_to_f32(uint16_t(pk[1])), bf16_bits_to_f32(uint16_t(pk[1] >> 16))};
+      } else {
+        v = *(const floatx4*)((const float*)a.part_o + it * a.d_c + d4);
+      }
       acc += w * v;
     }
     *(floatx4*)(out + d4) = acc;
@@ -275,62 +295,51 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
 
 // ===================================================== up-projection: MFMA
 // out[n, i, :] = W^UV_i latent[n, i, :], d_h = 128, d_c = 512.  One
-// workgroup of 2 waves per (head i, half of the d_h rows, block of 32
-// tokens); wave w owns d_h rows 64*half + 32*w .. +31.  The latent block
-// (32 tokens x 512 fp32) is staged in LDS as bf16 hi + lo parts
-// (x = hi + lo + O(2^-17 x)), so the bf16 MFMA keeps nearly fp32 accuracy
-// with W^UV exact in bf16.  All W^UV operand loads are issued up front.
+// workgroup of 4 waves per (head i, block of 32 tokens); wave w owns d_h
+// rows 32w .. 32w+31.  All global loads are issued first: each lane's 32
+// W^UV operands (the workgroup streams W^UV_i once) and its share of the
+// latent block (32 tokens x 512 fp32), which is then staged in LDS as bf16
+// hi + lo parts (x = hi + lo + O(2^-17 x)), so the bf16 MFMA keeps nearly
+// fp32 accuracy with W^UV exact in bf16.
 constexpr int kUpLds = 512 + 8;       // padded bf16 row of the latent block
 
 template <typename OutT>
-__global__ __launch_bounds__(128) void up_proj_mfma_kernel(
+__global__ __launch_bounds__(256) void up_proj_mfma_kernel(
     const float* __restrict__ latent, const uint16_t* __restrict__ w_uv,
     OutT* __restrict__ out, int n_tok, int n_h) {
   constexpr int DC = 512, DH = 128;
   __shared__ __attribute__((aligned(16))) uint16_t s_hi[32 * kUpLds];
   __shared__ __attribute__((aligned(16))) uint16_t s_lo[32 * kUpLds];
-  const int head = blockIdx.x >> 1, half = blockIdx.x & 1, t0 = blockIdx.y * 32;
+  const int head = blockIdx.x, t0 = blockIdx.y * 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int m = half * 64 + wave * 32 + l32;        // d_h row (A-operand row)
+  const int m = wave * 32 + l32;                    // d_h row (A-operand row)
   const uint16_t* wrow = w_uv + ((size_t)head * DH + m) * DC;
 
   bf16x8 wa[DC / 16];
 #pragma unroll
   for (int k = 0; k < DC / 16; ++k) wa[k] = *(const bf16x8*)(wrow + 16 * k + 8 * h);
-
-  // stage latent[t0 + t][head][:] (4096 chunks of 4 floats, 2 rounds)
+  // latent block: 4096 chunks of 4 floats, 16 per thread
+  floatx4 v[16];
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    floatx4 v[16];
+  for (int i = 0; i < 16; ++i) {
+    const int ch = tid + 256 * i, t = ch >> 7, c4 = (ch & 127) * 4;
+    v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
+  }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ch = tid + 128 * (16 * round + i);   // 0 .. 4095
-      const int t = ch >> 7, c4 = (ch & 127) * 4;
-      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (t0 + t < n_tok)
-        v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
+  for (int i = 0; i < 16; ++i) {
+    const int ch = tid + 256 * i, t = ch >> 7, c4 = (ch & 127) * 4;
+    u32x2 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float x0 = v[i][2 * e], x1 = v[i][2 * e + 1];
+      const bf16x2 hb = bf16x2{(__bf16)x0, (__bf16)x1};
+      hi[e] = __builtin_bit_cast(uint32_t, hb);
+      lo[e] = pack_bf16x2(x0 - (float)hb[0], x1 - (float)hb[1]);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ch = tid + 128 * (16 * round + i);
-      const int t = ch >> 7, c4 = (ch & 127) * 4;
-      u32x2 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint32_t hb[2], lb[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float x = v[i][2 * e + q];
-          hb[q] = f32_to_bf16_bits(x);
-          lb[q] = f32_to_bf16_bits(x - bf16_bits_to_f32((uint16_t)hb[q]));
-        }
-        hi[e] = hb[0] | hb[1] << 16;
-        lo[e] = lb[0] | lb[1] << 16;
-      }
-      *(u32x2*)(s_hi + t * kUpLds + c4) = hi;
-      *(u32x2*)(s_lo + t * kUpLds + c4) = lo;
-    }
+    *(u32x2*)(s_hi + t * kUpLds + c4) = hi;
+    *(u32x2*)(s_lo + t * kUpLds + c4) = lo;
   }
   __syncthreads();
 
@@ -344,18 +353,15 @@ __global__ __launch_bounds__(128) void up_proj_mfma_kernel(
   }
   const int tok = t0 + l32;
   if (tok < n_tok) {
-    OutT* dst = out + ((size_t)tok * n_h + head) * DH + half * 64 + wave * 32;
+    OutT* dst = out + ((size_t)tok * n_h + head) * DH + wave * 32;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const floatx4 v = {acc_hi[4 * j] + acc_lo[4 * j], acc_hi[4 * j + 1] + acc_lo[4 * j + 1],
+      const floatx4 r = {acc_hi[4 * j] + acc_lo[4 * j], acc_hi[4 * j + 1] + acc_lo[4 * j + 1],
                          acc_hi[4 * j + 2] + acc_lo[4 * j + 2], acc_hi[4 * j + 3] + acc_lo[4 * j + 3]};
       if constexpr (sizeof(OutT) == 4) {
-        *(floatx4*)(dst + 8 * j + 4 * h) = v;
+        *(floatx4*)(dst + 8 * j + 4 * h) = r;
       } else {
-        u32x2 pk;
-        pk[0] = uint32_t(f32_to_bf16_bits(v[0])) | uint32_t(f32_to_bf16_bits(v[1])) << 16;
-        pk[1] = uint32_t(f32_to_bf16_bits(v[2])) | uint32_t(f32_to_bf16_bits(v[3])) << 16;
-        *(u32x2*)(dst + 8 * j + 4 * h) = pk;
+        *(u32x2*)(dst + 8 * j + 4 * h) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
       }
     }
   }
@@ -441,12 +447,12 @@ hipError_t launch_up_proj(const mla_dims_t& d, bool fast, const float* latent,
                           const void* w_uv, void* out, bool out_f32, int n_tok,
                           hipStream_t st) {
   if (fast) {
-    const dim3 grid(d.n_heads * 2, (n_tok + 31) / 32);
+    const dim3 grid(d.n_heads, (n_tok + 31) / 32);
     if (out_f32)
-      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(128), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(256), 0, st,
                          latent, (const uint16_t*)w_uv, (float*)out, n_tok, d.n_heads);
     else
-      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(128), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(256), 0, st,
                          latent, (const uint16_t*)w_uv, (uint16_t*)out, n_tok, d.n_heads);
   } else {
     const size_t total = (size_t)n_tok * d.n_heads * d.d_head;

@@ -73,6 +73,7 @@ struct Plan {
   int n_items;
   int row_blocks;
   bool any_split;
+  bool part_bf16;
   size_t ws_bytes;
 };
 
@@ -114,7 +115,12 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
   if (items * rb > INT32_MAX / 2) return MLA_ERR_ARG;
   p->n_items = (int)items;
   p->any_split = any;
-  p->ws_bytes = any ? (size_t)items * rows * (d->d_latent + 1) * sizeof(float) + 256 : 0;
+  // partials: fp32 LSE per (item, row), then the latent partials (bf16 on
+  // the matrix-core path, fp32 on the general path)
+  const size_t part_elem = fast ? 2 : 4;
+  const size_t lse_bytes = ((size_t)items * rows * sizeof(float) + 255) / 256 * 256;
+  p->part_bf16 = fast;
+  p->ws_bytes = any ? lse_bytes + (size_t)items * rows * d->d_latent * part_elem : 0;
   return MLA_OK;
 }
 
@@ -228,9 +234,10 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   const int64_t rows = (int64_t)dims->n_heads * q_tokens;
-  a.part_o = p.any_split ? (float*)workspace : nullptr;
-  a.part_lse = p.any_split ? (float*)workspace + (size_t)p.n_items * rows * dims->d_latent
-                           : nullptr;
+  const size_t lse_bytes = ((size_t)p.n_items * rows * sizeof(float) + 255) / 256 * 256;
+  a.part_lse = p.any_split ? (float*)workspace : nullptr;
+  a.part_o = p.any_split ? (void*)((char*)workspace + lse_bytes) : nullptr;
+  a.part_bf16 = p.part_bf16 ? 1 : 0;
   a.out_latent = out_latent;
   a.out_lse = out_lse;
   a.B = batch;

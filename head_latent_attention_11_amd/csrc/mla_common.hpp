@@ -112,8 +112,10 @@ struct DecodeArgs {
   const float* kv_scale;      // fp8: one float per cache row
   const int32_t* page_table;  // [B, max_pages] or nullptr
   const int32_t* seq_lens;    // [B]
-  float* part_o;              // [n_items, rows, d_c] partial latent outputs
+  void* part_o;               // [n_items, rows, d_c] partial latent outputs
+                              // (bf16 when part_bf16, else fp32)
   float* part_lse;            // [n_items, rows]
+  int32_t part_bf16;
   float* out_latent;          // [B*T, n_h, d_c]
   float* out_lse;             // [B*T, n_h]
   int32_t B, T, n_h, d_c, d_r;

@@ -135,13 +135,13 @@ def test_split_planner_sizes(mla):
     rows, dc = 128, 512
     # 32 x 4096 tokens, 1 row block of 128 rows: chunk 512 -> 8 splits each
     st, n = _ws(lib, d, [4096] * 32)
-    assert st == OK and n == 256 * rows * (dc + 1) * 4 + 256
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 2   # fp32 LSE + bf16 partials
     # 64 x 8192, T = 4 (4 row blocks): chunk 8192 -> no split, no workspace
     st, n = _ws(lib, _v2(b, kv_dtype="fp8"), [8192] * 64, T=4)
     assert st == OK and n == 0
     # explicit 64 splits of 131072 tokens: 4 * 64 items
     st, n = _ws(lib, d, [131072] * 4, splits=64)
-    assert st == OK and n == 256 * rows * (dc + 1) * 4 + 256
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 2
     # a short sequence is never split below 256 tokens
     st, n = _ws(lib, d, [200])
     assert st == OK and n == 0

@@ -136,10 +136,14 @@ def test_split_invariance_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(to_np(buf.latent), outs[ns][0])
         assert np.array_equal(to_np(buf.o), outs[ns][1])
+    # A split run stores each chunk's partial latent in bf16 before the LSE
+    # combine: one extra rounding of at most 2^-8 relative per element on top
+    # of the unsplit result, whose own operands are bf16.  The two results may
+    # therefore differ by up to about one bf16 unit roundoff (2^-8) in rel-L2.
     for ns in (2, 7, 0):
         r = rel_l2(outs[ns][0], outs[1][0])
         say(f"  splits={ns} vs unsplit: rel-L2 {r:.2e}")
-        assert r <= 2e-3
+        assert r <= 2.0 ** -8
 
 
 def test_paged_equals_contiguous_bitwise():
