@@ -67,9 +67,6 @@ constexpr int NCH = 72;                  // 16-byte chunks per bf16 row
 constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte staging chunks per thread (9)
 constexpr uint32_t kOOB = 0x40000000u;   // buffer offset past any valid range
 constexpr float kNegInf = -INFINITY;
-// s_waitcnt immediates (gfx9 encoding): vmcnt <= N, other counters unconstrained
-constexpr int kWaitVm9 = 9 | (7 << 4) | (15 << 8);
-constexpr int kWaitVm10 = 10 | (7 << 4) | (15 << 8);
 }  // namespace
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -89,30 +86,38 @@ __device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
   return r;
 }
 
-// S^T[token, head] of one tile for the wave's 32 heads; kb points at this
-// lane's operand (token l%32, dims 16k + 8(l/32)).
-__device__ __forceinline__ floatx16 qk_tile(const uint8_t* kb, const bf16x8 (&qf)[D / 16]) {
-  floatx16 sa = {};
-#pragma unroll
-  for (int k = 0; k < D / 16; ++k)
-    sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kb + 32 * k), qf[k], sa, 0, 0, 0);
-  return sa;
+// One tile's S^T[token, head] for the wave's 32 heads (36 MFMAs over the
+// 576 dims; kb is this lane's operand address: token l%32, dims 16k +
+// 8(l/32)), and O^T[dim, head] += C^T[dim, tok] P^T[tok, head] (32 MFMAs;
+// vb is this lane's transposed-read address).  Both are software-pipelined
+// sequences (several LDS reads in flight ahead of the matrix pipe) written
+// out by gen_decode_asm.py; they wait for all of their reads before they end.
+#include "decode_mfma_asm.inc"
+
+__device__ __forceinline__ floatx16 qk_tile(const uint8_t* kb, const bf16x8 (&q)[D / 16]) {
+  floatx16 s;
+  const uint32_t ad = (uint32_t)(uintptr_t)kb;
+  asm volatile(MLA_ASM_QK_TILE
+               : "=&v"(s)
+               : "v"(ad), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]),
+                 "v"(q[6]), "v"(q[7]), "v"(q[8]), "v"(q[9]), "v"(q[10]), "v"(q[11]), "v"(q[12]),
+                 "v"(q[13]), "v"(q[14]), "v"(q[15]), "v"(q[16]), "v"(q[17]), "v"(q[18]),
+                 "v"(q[19]), "v"(q[20]), "v"(q[21]), "v"(q[22]), "v"(q[23]), "v"(q[24]),
+                 "v"(q[25]), "v"(q[26]), "v"(q[27]), "v"(q[28]), "v"(q[29]), "v"(q[30]),
+                 "v"(q[31]), "v"(q[32]), "v"(q[33]), "v"(q[34]), "v"(q[35])
+               : "memory", MLA_ASM_QK_CLOBBERS);
+  return s;
 }
 
-// O^T[dim, head] += sum_tok C^T[dim, tok] P^T[tok, head] over a 32-token
-// tile; vb is this lane's transposed-read base in the tile.
 __device__ __forceinline__ void pv_tile(const uint8_t* vb, const bf16x8 pf0, const bf16x8 pf1,
                                         floatx16 (&o)[DC / 32]) {
-#pragma unroll
-  for (int db = 0; db < DC / 32; ++db) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x2 lo = lds_tr16(vb + (16 * ks) * LROW + 64 * db);
-      const u32x2 hi = lds_tr16(vb + (16 * ks + 8) * LROW + 64 * db);
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks ? pf1 : pf0, o[db], 0, 0, 0);
-    }
-  }
+  const uint32_t ad = (uint32_t)(uintptr_t)vb;
+  asm volatile(MLA_ASM_PV_TILE
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
+               : "v"(ad), "v"(pf0), "v"(pf1)
+               : "memory", MLA_ASM_PV_CLOBBERS);
 }
 
 template <bool FP8>
@@ -129,17 +134,18 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int item = gi / a.row_blocks, rb = gi % a.row_blocks;
   const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
   if (loc.b < 0) return;
-  const int b = loc.b;
-  const int L = a.seq_lens[b];
+  const int b = __builtin_amdgcn_readfirstlane(loc.b);
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
   const int c = chunk_of(L, a.num_splits, a.chunk);
-  const int t0 = loc.s * c;
+  const int t0 = __builtin_amdgcn_readfirstlane(loc.s) * c;
   const int t_end = min(L, t0 + c);                       // item end
   const int rows = a.n_h * a.T;
   const int row = rb * ROWS_WG + wave * 32 + l32;         // this lane's row
   const int tau = row / a.n_h, head = row % a.n_h;
   const int lim = min(t_end - 1, L - a.T + tau);          // last visible token
   const int tau_max = (rb * ROWS_WG + ROWS_WG - 1) / a.n_h;
-  const int t_stage = min(t_end, L - a.T + tau_max + 1);  // tokens any row sees
+  const int t_stage =                                     // tokens any row sees
+      __builtin_amdgcn_readfirstlane(min(t_end, L - a.T + tau_max + 1));
   const int nq = b * a.T + tau;
   const int ntiles = (t_stage > t0) ? (t_stage - t0 + TILE - 1) / TILE : 0;
 
@@ -153,8 +159,10 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   const uint8_t* cache = (const uint8_t*)a.cache;
   constexpr int ROWB = FP8 ? D : 2 * D;                   // bytes per cache row
-  const size_t seq_row0 = (size_t)b * a.max_len;
-  const int32_t* ptab = a.page_table ? a.page_table + (size_t)b * a.max_pages : nullptr;
+  const int seq_row0 = b * a.max_len;
+  typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+  const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
 
   // ---- staging.  bf16: LDS 16-byte chunk q of a tile holds token q / 73,
   // chunk q % 73 of its row (chunk 72 is the row padding, filled with zero
@@ -176,27 +184,40 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   // Issue the loads of the tile starting at token ts into ring slot buf.  A
   // tile never crosses a page (ts is a multiple of 32, pages hold 64 tokens).
+  // Everything that addresses the tile is wave-uniform: the page id comes
+  // through the scalar cache and the buffer descriptor lives in SGPRs.
+  // bf16 tiles are copied HBM -> LDS by buffer loads with the LDS-write
+  // option, issued from inline assembly: the compiler then keeps no
+  // bookkeeping of them (it would otherwise wait for every in-flight tile
+  // before each LDS read, since it cannot tell the ring slots apart), and
+  // the kernel's own vmcnt waits and barriers order them.
 #define MLA_ISSUE_TILE(ts_, buf_)                                                          \
   do {                                                                                   \
     const int ts__ = (ts_);                                                              \
     const int nv__ = max(0, min(TILE, t_stage - ts__));                                  \
-    const size_t r0__ = nv__ == 0 ? 0                                                    \
-                      : ptab ? (size_t)ptab[ts__ / kPage] * kPage + (ts__ % kPage)       \
-                             : seq_row0 + ts__;                                          \
-    const __amdgpu_buffer_rsrc_t rs__ = __builtin_amdgcn_make_buffer_rsrc(               \
-        (void*)(cache + r0__ * ROWB), (short)0, nv__ * ROWB, 0x00020000);                \
+    int r0__ = 0;                                                                        \
+    if (nv__ > 0)                                                                        \
+      r0__ = ptab ? ptab[ts__ / kPage] * kPage + (ts__ % kPage) : seq_row0 + ts__;      \
+    r0__ = __builtin_amdgcn_readfirstlane(r0__);                                         \
+    const uint64_t ad__ = (uint64_t)(cache + (size_t)r0__ * ROWB);                       \
+    const u32x4 rs__ = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad__),        \
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad__ >> 32)) & 0xFFFFu, \
+                        (uint32_t)__builtin_amdgcn_readfirstlane(nv__ * ROWB),           \
+                        0x00020000u};                                                    \
     if constexpr (!FP8) {                                                                \
+      const uint32_t lb__ = lds_ring + (buf_) * TILE_BYTES + 1024 * wave;                \
       _Pragma("unroll") for (int n = 0; n < NLD - 1; ++n)                                \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
-            rs__, (void __attribute__((address_space(3)))*)(&s_kv[(buf_)][1024 * (wave + 4 * n)]), \
-            16, MLA_VOFF(n), 0, 0, 0);                                                   \
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
+                     :: "s"(lb__ + 4096 * n), "v"(MLA_VOFF(n)), "s"(rs__) : "memory");   \
       if (wave == 0)                                                                     \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                        \
-            rs__, (void __attribute__((address_space(3)))*)(&s_kv[(buf_)][1024 * 36]),   \
-            16, MLA_VOFF(NLD - 1), 0, 0, 0);                                             \
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
+                     :: "s"(lds_ring + (buf_) * TILE_BYTES + 1024 * 36),                 \
+                        "v"(MLA_VOFF(NLD - 1)), "s"(rs__) : "memory");                   \
     } else {                                                                             \
+      const __amdgpu_buffer_rsrc_t rb__ = __builtin_amdgcn_make_buffer_rsrc(             \
+          (void*)(cache + (size_t)r0__ * ROWB), (short)0, nv__ * ROWB, 0x00020000);      \
       _Pragma("unroll") for (int i = 0; i < NSTG8; ++i)                                  \
-        stg8[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs__, 8 * tid, 2048 * i, 0)); \
+        stg8[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rb__, 8 * tid, 2048 * i, 0)); \
       if (tid < TILE) stg_scale = (tid < nv__) ? a.kv_scale[r0__ + tid] : 0.f;           \
     }                                                                                    \
   } while (0)
@@ -210,10 +231,10 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (tid < TILE) s_scale[(buf_)][tid] = stg_scale;                                    \
   } while (0)
   // bf16: wait until at most one tile's loads of this wave are in flight
-#define MLA_WAIT_ONE_TILE_IN_FLIGHT()                                                      \
+#define MLA_WAIT_TWO_TILES_IN_FLIGHT()                                                     \
   do {                                                                                   \
-    if (wave == 0) __builtin_amdgcn_s_waitcnt(kWaitVm10);                                \
-    else __builtin_amdgcn_s_waitcnt(kWaitVm9);                                           \
+    if (wave == 0) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");                     \
+    else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");                               \
   } while (0)
 
   // ---- per-lane LDS offsets of the MFMA operands
@@ -223,27 +244,39 @@ void decode_mfma_kernel(DecodeArgs a) {
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
 
+  // Prologue of an attempt: issue tiles 0..2 (bf16; tiles 0 and 1 for fp8,
+  // which are decoded into the ring right away).
+#define MLA_PROLOGUE()                                                                     \
+  do {                                                                                   \
+    if (ntiles > 0) {                                                                    \
+      MLA_ISSUE_TILE(t0, 0);                                                             \
+      if constexpr (FP8) MLA_STORE_FP8_TILE(0);                                          \
+      if (ntiles > 1) {                                                                  \
+        MLA_ISSUE_TILE(t0 + TILE, 1);                                                    \
+        if constexpr (FP8) MLA_STORE_FP8_TILE(1);                                        \
+      }                                                                                  \
+      if (!FP8 && ntiles > 2) MLA_ISSUE_TILE(t0 + 2 * TILE, 2);                          \
+    }                                                                                    \
+  } while (0)
+
   if (tid == 0) s_restart = 0;
+  MLA_PROLOGUE();
+  // The query loads were issued before the first tiles, so their latency
+  // overlaps; let them land here.  (The compiler waits for them with vmcnt
+  // counts that do not know of the tile loads; issued later, those can
+  // only make such a wait longer, never shorter.)
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
+
   for (;;) {                          // attempts (a restart is rare)
 #pragma unroll
     for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
     l_run = 0.f;
     int restart = 0;
     if (ntiles > 0) {
-      // prologue: tiles 0 and 1 resident, (bf16) tile 2 in flight
-      MLA_ISSUE_TILE(t0, 0);
-      if constexpr (FP8) MLA_STORE_FP8_TILE(0);
-      if (ntiles > 1) {
-        MLA_ISSUE_TILE(t0 + TILE, 1);
-        if constexpr (FP8) MLA_STORE_FP8_TILE(1);
-      }
       if constexpr (!FP8) {
-        if (ntiles > 2) {
-          MLA_ISSUE_TILE(t0 + 2 * TILE, 2);
-          MLA_WAIT_ONE_TILE_IN_FLIGHT();
-        } else {
-          __builtin_amdgcn_s_waitcnt(0);
-        }
+        if (ntiles > 2) MLA_WAIT_TWO_TILES_IN_FLIGHT();    // tile 0 landed
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       __syncthreads();
       // Step it works on tile it in ring slot it & 3 while (bf16) tiles
@@ -291,7 +324,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
         pv_tile(tile + pv_off, pf0, pf1, o);
         if constexpr (!FP8) {
-          MLA_WAIT_ONE_TILE_IN_FLIGHT();   // tile it+2 landed (it+3 may fly)
+          MLA_WAIT_TWO_TILES_IN_FLIGHT();  // tile it+1 landed (it+2, it+3 may fly)
         } else {
           MLA_STORE_FP8_TILE((it + 2) & 3);
         }
@@ -301,45 +334,70 @@ void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     if (!restart) break;
-    __builtin_amdgcn_s_waitcnt(0);    // no load of this attempt still in flight
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load of this attempt in flight
     __syncthreads();                  // everyone has read the flag
     if (tid == 0) s_restart = 0;
     m_ref = m_seen;
+    MLA_PROLOGUE();
   }
 #undef MLA_ISSUE_TILE
+#undef MLA_PROLOGUE
 #undef MLA_STORE_FP8_TILE
-#undef MLA_WAIT_ONE_TILE_IN_FLIGHT
+#undef MLA_WAIT_TWO_TILES_IN_FLIGHT
 #undef MLA_VOFF
 
-  // ---- normalise and write (the final output, or this split's partial)
+  // ---- normalise and write (the final output, or this split's partial).
+  // O^T sits in the MFMA layout (lane: one row, 4-dim pieces); each wave
+  // stages its 32 rows in LDS and writes them back as whole rows, so every
+  // store instruction covers 1 KB of contiguous memory.  The wave's rows are
+  // consecutive in the output (row = tau * n_h + head).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile loads past the end still write LDS
+  __syncthreads();                                   // every wave is done with the ring
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const float lse = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
+  constexpr int EROW = 1040;                         // staged row: 1 KB + 16 B padding
+  static_assert(4 * 32 * EROW <= NBUF * TILE_BYTES, "output staging must fit the ring");
+  uint8_t* stg = &s_kv[0][0] + wave * (32 * EROW);
+  const int row0 = rb * ROWS_WG + wave * 32;         // first row of this wave
   if (loc.ns == 1) {
-    float* dst = a.out_latent + ((size_t)nq * a.n_h + head) * DC;
+    const size_t g0 = (size_t)b * rows + row0;
+    uint8_t* dst = (uint8_t*)(a.out_latent + g0 * DC);
 #pragma unroll
-    for (int db = 0; db < DC / 32; ++db) {
+    for (int p = 0; p < 2; ++p) {                    // fp32 rows: two halves of 256 dims
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        floatx4 v = {o[db][4 * jj], o[db][4 * jj + 1], o[db][4 * jj + 2], o[db][4 * jj + 3]};
-        *(floatx4*)(dst + 32 * db + 8 * jj + 4 * h) = v * inv;
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const floatx16& ob = o[8 * p + db];
+          const floatx4 v = {ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]};
+          *(floatx4*)(stg + l32 * EROW + 4 * (32 * db + 8 * jj + 4 * h)) = v * inv;
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        *(floatx4*)(dst + (size_t)r * (4 * DC) + 1024 * p + 16 * lane) =
+            *(const floatx4*)(stg + r * EROW + 16 * lane);
     }
-    if (h == 0) a.out_lse[(size_t)nq * a.n_h + head] = lse;
+    if (h == 0) a.out_lse[g0 + l32] = lse;
   } else {
     // split partial, normalised, stored as bf16 (combined in fp32)
-    uint16_t* dst = (uint16_t*)a.part_o + ((size_t)item * rows + row) * DC;
+    const size_t g0 = (size_t)item * rows + row0;
+    uint8_t* dst = (uint8_t*)a.part_o + g0 * (2 * DC);
 #pragma unroll
     for (int db = 0; db < DC / 32; ++db) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const bf16x2 p01 = {(__bf16)(o[db][4 * jj] * inv), (__bf16)(o[db][4 * jj + 1] * inv)};
         const bf16x2 p23 = {(__bf16)(o[db][4 * jj + 2] * inv), (__bf16)(o[db][4 * jj + 3] * inv)};
-        *(u32x2*)(dst + 32 * db + 8 * jj + 4 * h) =
+        *(u32x2*)(stg + l32 * EROW + 2 * (32 * db + 8 * jj + 4 * h)) =
             u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
       }
     }
-    if (h == 0) a.part_lse[(size_t)item * rows + row] = lse;
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      *(u32x4*)(dst + (size_t)r * (2 * DC) + 16 * lane) = *(const u32x4*)(stg + r * EROW + 16 * lane);
+    if (h == 0) a.part_lse[g0 + l32] = lse;
   }
 }
 

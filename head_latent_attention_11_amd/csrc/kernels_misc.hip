@@ -253,44 +253,105 @@ __global__ __launch_bounds__(256) void append_kernel(
 // LSE combine of the split partials of one (query token, head) row:
 // lse = ln sum_s e^{lse_s};  latent = sum_s e^{lse_s - lse} latent_s.
 // Exact re-association of the sum in the attention-output equation.
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+// One wave per row, four rows per workgroup.  The split LSEs are read lane-
+// parallel and reduced with cross-lane operations; each lane then owns 8
+// latent dims and streams the partials with several loads in flight.
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int R = blockIdx.x * 4 + (threadIdx.x >> 6);      // global row (nq * n_h + head)
   const int rows = a.n_h * a.T;
-  const int nq = blockIdx.x / a.n_h, head = blockIdx.x % a.n_h;
-  const int b = nq / a.T, tau = nq % a.T;
+  if (R >= a.B * rows) return;
+  const int b = R / rows, row = R % rows;
   const int L = a.seq_lens[b];
   const int ns = splits_of(L, a.num_splits, a.chunk);
-  if (ns <= 1) return;
-  const int first = first_item_of(a.seq_lens, b, a.num_splits, a.chunk);
-  const int row = tau * a.n_h + head;
+  if (ns <= 1) return;                                    // written by the attention kernel
+  // first work item of sequence b: splits of the sequences before it
+  int first = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    const int bb = b0 + lane;
+    first += (bb < b) ? splits_of(a.seq_lens[bb], a.num_splits, a.chunk) : 0;
+  }
+  first = wave_sum_i(first);
+  const float* lse_p = a.part_lse + (size_t)first * rows + row;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_lse[(size_t)(first + s) * rows + row]);
-  float* out = a.out_latent + ((size_t)nq * a.n_h + head) * a.d_c;
-  if (mx == -INFINITY) {
-    for (int d = threadIdx.x; d < a.d_c; d += blockDim.x) out[d] = 0.f;
-    if (threadIdx.x == 0) a.out_lse[(size_t)nq * a.n_h + head] = -INFINITY;
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse_p[(size_t)s * rows]);
+  mx = wave_max(mx);
+  float* out = a.out_latent + (size_t)R * a.d_c;
+  const int d0 = 8 * lane;                                // this lane's 8 dims
+  if (mx == -INFINITY) {                                  // no visible token at all
+    for (int d = d0; d < min(d0 + 8, a.d_c); d += 4) *(floatx4*)(out + d) = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0) a.out_lse[R] = -INFINITY;
     return;
   }
   float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) wsum += expf(a.part_lse[(size_t)(first + s) * rows + row] - mx);
+  for (int s = lane; s < ns; s += 64) wsum += expf(lse_p[(size_t)s * rows] - mx);
+  wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
-  for (int d4 = threadIdx.x * 4; d4 < a.d_c; d4 += blockDim.x * 4) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      const size_t it = (size_t)(first + s) * rows + row;
-      const float w = expf(a.part_lse[it] - mx) * inv;
-      floatx4 v;
-      if (a.part_bf16) {
-        const u32x2 pk = *(const u32x2*)((const uint16_t*)a.part_o + it * a.d_c + d4);
-        v = floatx4{bf16_bits_to_f32(uint16_t(pk[0])), bf16_bits_to_f32(uint16_t(pk[0] >> 16)),
-                    bf16_bits_to_f32(uint16_t(pk[1])), bf16_bits_to_f32(uint16_t(pk[1] >> 16))};
-      } else {
-        v = *(const floatx4*)((const float*)a.part_o + it * a.d_c + d4);
+  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const size_t pstride = (size_t)rows * a.d_c;            // elements between splits
+  if (a.part_bf16) {                                      // fast path: d_c = 512
+    const uint16_t* src = (const uint16_t*)a.part_o + ((size_t)first * rows + row) * a.d_c + d0;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int n = min(64, ns - s0);
+      const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
+      int s = 0;
+      for (; s + 4 <= n; s += 4) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(src + (size_t)(s0 + s + u) * pstride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __shfl(w_l, s + u, 64);
+          acc0 += w * floatx4{__builtin_bit_cast(float, v[u][0] << 16), __builtin_bit_cast(float, v[u][0] & 0xFFFF0000u),
+                              __builtin_bit_cast(float, v[u][1] << 16), __builtin_bit_cast(float, v[u][1] & 0xFFFF0000u)};
+          acc1 += w * floatx4{__builtin_bit_cast(float, v[u][2] << 16), __builtin_bit_cast(float, v[u][2] & 0xFFFF0000u),
+                              __builtin_bit_cast(float, v[u][3] << 16), __builtin_bit_cast(float, v[u][3] & 0xFFFF0000u)};
+        }
       }
-      acc += w * v;
+      for (; s < n; ++s) {
+        const u32x4 v = *(const u32x4*)(src + (size_t)(s0 + s) * pstride);
+        const float w = __shfl(w_l, s, 64);
+        acc0 += w * floatx4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xFFFF0000u),
+                            __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xFFFF0000u)};
+        acc1 += w * floatx4{__builtin_bit_cast(float, v[2] << 16), __builtin_bit_cast(float, v[2] & 0xFFFF0000u),
+                            __builtin_bit_cast(float, v[3] << 16), __builtin_bit_cast(float, v[3] & 0xFFFF0000u)};
+      }
     }
-    *(floatx4*)(out + d4) = acc;
+    *(floatx4*)(out + d0) = acc0;
+    *(floatx4*)(out + d0 + 4) = acc1;
+  } else {                                                // general path: fp32, d_c % 4 == 0
+    const float* src = (const float*)a.part_o + ((size_t)first * rows + row) * a.d_c;
+    const bool has0 = d0 < a.d_c, has1 = d0 + 4 < a.d_c;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int n = min(64, ns - s0);
+      const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
+      for (int s = 0; s < n; ++s) {
+        const float w = __shfl(w_l, s, 64);
+        const float* ps = src + (size_t)(s0 + s) * pstride;
+        if (has0) acc0 += w * *(const floatx4*)(ps + d0);
+        if (has1) acc1 += w * *(const floatx4*)(ps + d0 + 4);
+      }
+    }
+    if (has0) *(floatx4*)(out + d0) = acc0;
+    if (has1) *(floatx4*)(out + d0 + 4) = acc1;
   }
-  if (threadIdx.x == 0) a.out_lse[(size_t)nq * a.n_h + head] = mx + logf(wsum);
+  if (lane == 0) a.out_lse[R] = mx + logf(wsum);
 }
 
 // ===================================================== up-projection: MFMA
@@ -439,7 +500,7 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.T * a.n_h), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((a.B * a.T * a.n_h + 3) / 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

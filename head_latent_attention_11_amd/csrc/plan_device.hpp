@@ -62,21 +62,4 @@ __device__ inline ItemLoc locate_item(const int32_t* __restrict__ seq_lens,
   return r;
 }
 
-// First work item of sequence b (threads of the block cooperate).
-__device__ inline int first_item_of(const int32_t* __restrict__ seq_lens, int b,
-                                    int num_splits, int chunk) {
-  __shared__ int s_part[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int acc = 0;
-  for (int bb = tid; bb < b; bb += blockDim.x) acc += splits_of(seq_lens[bb], num_splits, chunk);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) s_part[wave] = acc;
-  __syncthreads();
-  int tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += s_part[w];
-  __syncthreads();
-  return tot;
-}
-
 }  // namespace mla
