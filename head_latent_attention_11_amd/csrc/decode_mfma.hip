@@ -142,7 +142,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int rows = a.n_h * a.T;
   const int row = rb * ROWS_WG + wave * 32 + l32;         // this lane's row
   const int tau = row / a.n_h, head = row % a.n_h;
-  const int lim = min(t_end - 1, L - a.T + tau);          // last visible token
+  // last visible token; the 32 rows of a wave share tau (n_h % 32 == 0)
+  const int lim = __builtin_amdgcn_readfirstlane(min(t_end - 1, L - a.T + tau));
   const int tau_max = (rb * ROWS_WG + ROWS_WG - 1) / a.n_h;
   const int t_stage =                                     // tokens any row sees
       __builtin_amdgcn_readfirstlane(min(t_end, L - a.T + tau_max + 1));
@@ -291,36 +292,62 @@ void decode_mfma_kernel(DecodeArgs a) {
           MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
         }
         const floatx16 s_cur = qk_tile(tile + qk_off, qf);
-        // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4
+        // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4.
+        // The 32 rows of a wave share one query token, so the visibility
+        // limit is wave-uniform and only a tile that crosses it is masked.
         float sv[16];
-        float mt = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tl = 8 * (r >> 2) + 4 * h + (r & 3);
-          float v = s_cur[r] * a.scale_log2;
-          if (FP8) v *= s_scale[it & 3][tl];
-          sv[r] = (ts + tl <= lim) ? v : kNegInf;
-          mt = fmaxf(mt, sv[r]);
+        for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
+        if constexpr (FP8) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] *= s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)];
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        if (ts + TILE - 1 > lim) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
+        }
+        // max of the raw scores over the row's 32 tokens (lane pair l, l^32)
+        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                             fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                           __builtin_bit_cast(uint32_t, mx), false, false);
+          mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+        }
+        const float mt = mx * a.scale_log2;            // log2 domain (scale > 0)
         m_seen = fmaxf(m_seen, mt);
         if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
         if (mt > m_ref + 64.0f) s_restart = 1;
         const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
         bf16x8 pf0, pf1;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sv[r] - m_use);
-          __bf16 pb;
-          if (FP8) {
+          for (int r = 0; r < 16; ++r) {
+            // product rounded before the subtraction (no contraction), as
+            // in m_ref: the maximum score gives exactly 2^0, so an L = 1 row
+            // returns its value exactly
+#pragma clang fp contract(off)
+            const float p = __builtin_amdgcn_exp2f(sv[r] * a.scale_log2 - m_use);
             l_run += p;
-            pb = (__bf16)(p * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)]);
-          } else {
-            // the normaliser sums exactly the rounded weights used in P C
-            pb = (__bf16)p;
-            l_run += (float)pb;
+            const __bf16 pb = (__bf16)(p * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)]);
+            if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
           }
-          if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
+        } else {
+          // (fma: p of the maximum score is 2^(-rounding error of m_ref),
+          // which rounds to exactly 1 in bf16)
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const bf16x2 pb = {(__bf16)__builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -m_use)),
+                               (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[r + 1], a.scale_log2, -m_use))};
+            // the normaliser sums exactly the rounded weights used in P C
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, one, l_run, false);
+            if (r < 8) { pf0[r] = pb[0]; pf0[r + 1] = pb[1]; }
+            else { pf1[r - 8] = pb[0]; pf1[r - 7] = pb[1]; }
+          }
         }
         pv_tile(tile + pv_off, pf0, pf1, o);
         if constexpr (!FP8) {
