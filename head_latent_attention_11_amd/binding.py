@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(PKG, "libmla.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+PREC_BF16, PREC_FP32 = 0, 1
+PRECISION_CODES = {"bf16": PREC_BF16, "fp32": PREC_FP32}
 
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_up_proj_v", "mla_status_string", "mla_version")
@@ -35,21 +37,26 @@ class MLADims(ctypes.Structure):
         ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-        ("rope_base", ctypes.c_float),
+        ("rope_base", ctypes.c_float), ("precision", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, n_heads, d_head, d_latent, d_rope, kv_dtype="bf16",
-             q_dtype="bf16", softmax_scale=0.0, rope_base=0.0, page_size=64):
+             q_dtype="bf16", softmax_scale=0.0, rope_base=0.0, page_size=64,
+             precision="bf16"):
         kv = DTYPE_CODES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
         qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else q_dtype
+        pr = PRECISION_CODES[precision] if isinstance(precision, str) else precision
         return cls(n_heads, d_head, d_latent, d_rope, page_size, kv, qd,
-                   softmax_scale, rope_base)
+                   softmax_scale, rope_base, pr)
 
     @classmethod
-    def from_workload(cls, w):
+    def from_workload(cls, w, precision="bf16"):
         return cls.make(w.n_heads, w.d_head, w.d_latent, w.d_rope, w.kv_dtype,
-                        w.q_dtype, 0.0, w.rope_base, w.page_size)
+                        w.q_dtype, 0.0, w.rope_base, w.page_size, precision)
+
+    def qabs_is_f32(self) -> bool:
+        return self.q_dtype == F32 or self.precision == PREC_FP32
 
 
 _lib = None

@@ -76,6 +76,17 @@ __device__ inline u32x2 lds_tr16(const uint8_t* p) {
                                        (shortx4 __attribute__((address_space(3)))*)(p)));
 }
 
+// max(x[l], x[l ^ 32]) in every lane l.  v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second; with x
+// in both, one comes back as the lower halves and the other as the upper
+// halves.  Written as assembly: the compiler's builtin for this instruction
+// takes its two results as equal when its two inputs are, which they are not.
+__device__ inline float pair_max32(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+  return fmaxf(lo, hi);
+}
+
 // 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
 __device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
   u32x4 r;
@@ -312,11 +323,7 @@ void decode_mfma_kernel(DecodeArgs a) {
                          fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
                              fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
-                                                           __builtin_bit_cast(uint32_t, mx), false, false);
-          mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-        }
+        mx = pair_max32(mx);
         const float mt = mx * a.scale_log2;            // log2 domain (scale > 0)
         m_seen = fmaxf(m_seen, mt);
         if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here

@@ -60,10 +60,11 @@ __device__ inline shortx4 lds_read_tr16(const uint16_t* p) {
       (shortx4 __attribute__((address_space(3)))*)(p));
 }
 
+template <typename OutT>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
-    uint16_t* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
+    OutT* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
   __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
   const int head = blockIdx.x >> 2, cb = blockIdx.x & 3;
@@ -123,11 +124,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bq[k], acc, 0, 0, 0);
     // acc[r]: column-in-block 8(r/4) + 4h + r%4 of wave's 32, token l32
     if (tok < n_tok) {
-      uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
+      OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *(u32x2*)(dst + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
-                                               pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (sizeof(OutT) == 4)
+          *(floatx4*)(dst + 8 * jj + 4 * h) =
+              floatx4{acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
+        else
+          *(u32x2*)(dst + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
+                                                 pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
+      }
     }
   }
 
@@ -138,19 +144,24 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
       const uint16_t* src = q_rope + ((size_t)tok * n_h + head) * DR + 2 * k;
       float x0 = bf16_bits_to_f32(src[0]), x1 = bf16_bits_to_f32(src[1]);
       if (q_pos) rope_pair(x0, x1, q_pos[tok], k, DR, rope_base, &x0, &x1);
-      uint16_t* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * k;
-      dst[0] = f32_to_bf16_bits(x0);
-      dst[1] = f32_to_bf16_bits(x1);
+      OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * k;
+      if constexpr (sizeof(OutT) == 4) {
+        dst[0] = x0;
+        dst[1] = x1;
+      } else {
+        dst[0] = f32_to_bf16_bits(x0);
+        dst[1] = f32_to_bf16_bits(x1);
+      }
     }
   }
 }
 
 // =================================================== absorb: general path
-template <typename T>
+template <typename T, typename OutT>
 __global__ __launch_bounds__(256) void absorb_general_kernel(
     const T* __restrict__ q_nope, const T* __restrict__ q_rope,
     const T* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
-    T* __restrict__ q_abs, int n_tok, int n_h, int d_h, int d_c, int d_r,
+    OutT* __restrict__ q_abs, int n_tok, int n_h, int d_h, int d_c, int d_r,
     float rope_base) {
   const int D = d_c + d_r;
   const size_t total = (size_t)n_tok * n_h * D;
@@ -452,24 +463,36 @@ hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
                          const void* q_rope, const void* w_uk,
                          const int32_t* q_pos, void* q_abs, int n_tok,
                          float rope_base, hipStream_t st) {
+  const bool out_f32 = d.q_dtype == MLA_F32 || d.precision == MLA_PREC_FP32;
   if (fast) {
-    hipLaunchKernelGGL(absorb_mfma_kernel, dim3(d.n_heads * 4), dim3(256), 0, st,
-                       (const uint16_t*)q_nope, (const uint16_t*)q_rope,
-                       (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
-                       d.n_heads, rope_base);
+    if (out_f32)
+      hipLaunchKernelGGL(absorb_mfma_kernel<float>, dim3(d.n_heads * 4), dim3(256), 0, st,
+                         (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok,
+                         d.n_heads, rope_base);
+    else
+      hipLaunchKernelGGL(absorb_mfma_kernel<uint16_t>, dim3(d.n_heads * 4), dim3(256), 0, st,
+                         (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
+                         d.n_heads, rope_base);
   } else {
     const size_t total = (size_t)n_tok * d.n_heads * (d.d_latent + d.d_rope);
     const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
     if (d.q_dtype == MLA_F32)
-      hipLaunchKernelGGL(absorb_general_kernel<float>, dim3(grid), dim3(256), 0, st,
+      hipLaunchKernelGGL((absorb_general_kernel<float, float>), dim3(grid), dim3(256), 0, st,
                          (const float*)q_nope, (const float*)q_rope, (const float*)w_uk,
                          q_pos, (float*)q_abs, n_tok, d.n_heads, d.d_head,
                          d.d_latent, d.d_rope, rope_base);
+    else if (out_f32)
+      hipLaunchKernelGGL((absorb_general_kernel<uint16_t, float>), dim3(grid), dim3(256), 0,
+                         st, (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok, d.n_heads,
+                         d.d_head, d.d_latent, d.d_rope, rope_base);
     else
-      hipLaunchKernelGGL(absorb_general_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
-                         (const uint16_t*)q_nope, (const uint16_t*)q_rope,
-                         (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
-                         d.n_heads, d.d_head, d.d_latent, d.d_rope, rope_base);
+      hipLaunchKernelGGL((absorb_general_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256),
+                         0, st, (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok, d.n_heads,
+                         d.d_head, d.d_latent, d.d_rope, rope_base);
   }
   return hipGetLastError();
 }

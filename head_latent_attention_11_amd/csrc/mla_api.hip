@@ -44,6 +44,7 @@ int32_t check_dims(const mla_dims_t* d) {
     return MLA_ERR_DTYPE;
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return MLA_ERR_ARG;
+  if (d->precision != MLA_PREC_BF16 && d->precision != MLA_PREC_FP32) return MLA_ERR_ARG;
   return MLA_OK;
 }
 
@@ -54,8 +55,14 @@ bool fast_shape(const mla_dims_t* d) {
 }
 
 bool fast_decode(const mla_dims_t* d, int T) {
-  return fast_shape(d) && (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) &&
+  return fast_shape(d) && d->precision == MLA_PREC_BF16 &&
+         (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) &&
          ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
+}
+
+// Format of the absorbed query.
+int32_t qabs_dtype(const mla_dims_t* d) {
+  return d->precision == MLA_PREC_FP32 ? MLA_F32 : d->q_dtype;
 }
 
 float rope_base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.f; }
@@ -251,7 +258,7 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   a.chunk = p.chunk;
   a.n_items = p.n_items;
   a.row_blocks = p.row_blocks;
-  a.q_dtype = dims->q_dtype;
+  a.q_dtype = qabs_dtype(dims);
   a.kv_dtype = dims->kv_dtype;
   a.scale_log2 = softmax_scale_of(dims) * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;

@@ -36,11 +36,12 @@ def to_device(arr: np.ndarray, kind: str, device) -> torch.Tensor:
 class DecodeBuffers:
     def __init__(self, w, gen: Dict[str, np.ndarray], device="cuda",
                  num_splits: Optional[int] = None, poison: bool = True,
-                 cache_replicas: int = 1):
+                 cache_replicas: int = 1, precision: str = "bf16"):
         self.w = w
         self.device = torch.device(device)
         dev = self.device
-        self.dims = B.MLADims.from_workload(w)
+        self.precision = precision
+        self.dims = B.MLADims.from_workload(w, precision)
         qk = "f32" if w.q_dtype == "f32" else "bf16"
         self.w_uk = to_device(gen["w_uk"], qk, dev)
         self.w_uv = to_device(gen["w_uv"], qk, dev)
@@ -97,7 +98,8 @@ class DecodeBuffers:
         del new_c, new_kr, seq_idx, pos
 
         # ---- outputs and workspace
-        self.q_abs = torch.empty((self.n_tok, w.n_heads, D), dtype=self.w_uk.dtype, device=dev)
+        qabs_dtype = torch.float32 if self.dims.qabs_is_f32() else self.w_uk.dtype
+        self.q_abs = torch.empty((self.n_tok, w.n_heads, D), dtype=qabs_dtype, device=dev)
         self.latent = torch.empty((self.n_tok, w.n_heads, w.d_latent), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.n_tok, w.n_heads), dtype=torch.float32, device=dev)
         # o is written in fp32: the parity gates are absolute (max-abs) and the

@@ -80,11 +80,30 @@ typedef struct mla_dims {
                           MLA_F32 or MLA_BF16 */
   float softmax_scale; /* 0 -> 1/sqrt(d_head + d_rope) */
   float rope_base;     /* RoPE base; 0 -> 10000 */
+  int32_t precision;   /* MLA_PREC_BF16 or MLA_PREC_FP32, see below */
 } mla_dims_t;
+
+/* Arithmetic of the absorbed query and the attention (inputs and weights are
+ * always read in q_dtype / kv_dtype):
+ *   MLA_PREC_BF16: the absorbed query is stored in q_dtype and, on the
+ *     matrix-core path, the softmax weights enter the P.C product as bf16
+ *     (each rounded to 8 significant bits; the normaliser sums exactly the
+ *     rounded weights).  Fastest; scores and weights carry bf16 rounding.
+ *   MLA_PREC_FP32: the absorbed query is stored as fp32 whatever q_dtype
+ *     is, and scores, weights and the weighted sum are formed in fp32.  For
+ *     inputs whose score range makes bf16 rounding of the query or of the
+ *     weights visible in the output (e.g. a few cache rows far larger than
+ *     the rest).                                                            */
+typedef enum mla_precision {
+  MLA_PREC_BF16 = 0,
+  MLA_PREC_FP32 = 1
+} mla_precision_t;
 
 /* Supported combinations:
  *   fast path (MFMA): n_h % 32 == 0, (n_h*T) % 128 == 0, d_h = 128,
- *       d_c = 512, d_h^R = 64, q_dtype = BF16, kv_dtype = BF16 or FP8_E4M3;
+ *       d_c = 512, d_h^R = 64, q_dtype = BF16, kv_dtype = BF16 or FP8_E4M3,
+ *       precision = MLA_PREC_BF16 (the query absorption also uses matrix
+ *       cores with MLA_PREC_FP32);
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
  *       d_h^R <= 128 (even),
  *       every q_dtype / kv_dtype combination (e.g. the all-fp32 problems).
@@ -101,7 +120,8 @@ typedef struct mla_dims {
  *
  * q_nope [n_tokens, n_h, d_h], q_rope [n_tokens, n_h, d_h^R],
  * w_uk [n_h, d_h, d_c]: q_dtype.  q_pos [n_tokens] int32 or NULL.
- * q_abs [n_tokens, n_h, d_c + d_h^R]: q_dtype, written (round to nearest).
+ * q_abs [n_tokens, n_h, d_c + d_h^R]: q_dtype (F32 when precision is
+ * MLA_PREC_FP32), written (round to nearest).
  * n_tokens >= 1.                                                          */
 int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope,
                      const void* q_rope, const void* w_uk,
@@ -157,7 +177,8 @@ int32_t mla_decode_workspace_size(const mla_dims_t* dims,
  *   out_latent[n, i, :] = sum_j softmax(s)_j * cache_row_j[0:d_c]
  *   out_lse[n, i]       = ln sum_j exp(s_j)
  *
- * q_abs [B*T, n_h, D] q_dtype; cache as in mla_cache_append (kv_scale for
+ * q_abs [B*T, n_h, D] as written by mla_absorb_q (q_dtype, or F32 when
+ * precision is MLA_PREC_FP32); cache as in mla_cache_append (kv_scale for
  * FP8 only).  seq_lens [B] int32 on the device; seq_lens_host: the same
  * values on the host (used to plan the split-KV work; they must agree).
  * num_splits = 0: the library splits long sequences into KV chunks to fill

