@@ -28,8 +28,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 DEFAULT_WORKLOAD = "v2_b32_l4k_bf16"
+ATTN_PER_GRAPH = 20                     # attention calls captured per graph
+COPY_PROBE_BYTES = 512 * 2 ** 20        # calibration copy of the traffic probe
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc", "decode_mfma.hip")
+_CSRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
+                  ("decode_mfma.hip", "decode_mfma_asm.inc", "kernels_misc.hip",
+                   "mla_common.hpp", "plan_device.hpp", "mla_api.hip")]
 
 
 def algorithmic(w, seq_lens):
@@ -52,14 +57,24 @@ def algorithmic(w, seq_lens):
     return cache_bytes, q_bytes + out_bytes, flops
 
 
-def traffic_for_current_kernel():
-    """HBM traffic per launch measured with rocprofv3 counters, if the
-    counters were taken on the current decode kernel source."""
+def kernel_sources_sha256() -> str:
+    """Digest of the attention kernels' sources (decode + combine): counters
+    taken on other sources do not describe the kernels being timed."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for_current_kernel(workload: str):
+    """HBM traffic per attention call measured with rocprofv3 counters
+    (bench_traffic.py), if taken on this workload and on the current kernel
+    sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        src_hash = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if rec.get("decode_src_sha256") == src_hash:
+        if rec.get("workload") == workload and rec.get("sources_sha256") == kernel_sources_sha256():
             return rec
     except (OSError, ValueError):
         pass
@@ -117,6 +132,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a calibration copy and a few attention calls for "
+                         "rocprofv3 counter runs (see bench_traffic.py), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -153,8 +171,30 @@ def main():
         return g
 
     step_graphs = [capture(lambda r=r: buf.step(replica=r)) for r in range(replicas)]
-    attn_graphs = [capture(lambda r=r: buf.attend(replica=r)) for r in range(replicas)]
+    # the attention call alone: ATTN_PER_GRAPH calls (replicas round-robin) per
+    # graph, so the gap between graph launches is amortised and the per-call
+    # time is the kernels' own (decode + combine)
+    def attn_calls():
+        for i in range(ATTN_PER_GRAPH):
+            buf.attend(replica=i % replicas)
+    attn_graph = capture(attn_calls)
     stream = torch.cuda.current_stream()
+
+    if args.traffic_probe:
+        # For rocprofv3 counter runs: a plain copy of known size (the
+        # calibration kernel), then a few attention calls.  Nothing is timed.
+        src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        for i in range(3):
+            buf.attend(replica=i % replicas)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_PROBE_BYTES,
+                          "workload": w.name, "sources_sha256": kernel_sources_sha256(),
+                          "bytes_alg_per_launch": cache_b + io_b}), flush=True)
+        return
 
     for i in range(args.warmup):
         step_graphs[i % replicas].replay()
@@ -174,16 +214,17 @@ def main():
     ms_step_events = e0.elapsed_time(e1) / args.steps
 
     # ---- the attention launches alone, back to back (same stream)
-    for i in range(args.warmup):
-        attn_graphs[i % replicas].replay()
+    n_rep = max(1, -(-args.steps // ATTN_PER_GRAPH))
+    for i in range(max(1, args.warmup // ATTN_PER_GRAPH)):
+        attn_graph.replay()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a0.record(stream)
-    for i in range(args.steps):
-        attn_graphs[i % replicas].replay()
+    for i in range(n_rep):
+        attn_graph.replay()
     a1.record(stream)
     torch.cuda.synchronize()
-    attn_ms = a0.elapsed_time(a1) / args.steps
+    attn_ms = a0.elapsed_time(a1) / (n_rep * ATTN_PER_GRAPH)
     attn_s = attn_ms * 1e-3
     bytes_alg = cache_b + io_b
     achieved_gbps = bytes_alg / attn_s / 1e9
@@ -197,7 +238,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4)}
-    tr = traffic_for_current_kernel() if w.name == DEFAULT_WORKLOAD else None
+    tr = traffic_for_current_kernel(w.name)
     roof["traffic"] = tr["hbm_bytes_per_launch"] if tr else None
     roof["kernel"] = ("mla_decode_attn (decode_mfma_kernel + combine_kernel when split), "
                       "per call, HIP-event timed over back-to-back graph replays")
