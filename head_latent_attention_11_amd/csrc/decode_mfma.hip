@@ -243,21 +243,41 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (tid < TILE) s_scale[(buf_)][tid] = stg_scale;                                    \
   } while (0)
   // bf16: wait until at most one tile's loads of this wave are in flight
-#define MLA_WAIT_TWO_TILES_IN_FLIGHT()                                                     \
+#define MLA_WAIT_ONE_TILE_IN_FLIGHT()                                                      \
   do {                                                                                   \
-    if (wave == 0) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");                     \
-    else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");                               \
+    if (wave == 0) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");                     \
+    else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");                                \
   } while (0)
+  // bf16: buffer descriptor of the tile starting at token ts (as in
+  // MLA_ISSUE_TILE), for loads issued from the step's assembly blocks
+#define MLA_TILE_RSRC(ts_, rs_)                                                            \
+  u32x4 rs_;                                                                             \
+  {                                                                                      \
+    const int ts__ = (ts_);                                                              \
+    const int nv__ = max(0, min(TILE, t_stage - ts__));                                  \
+    int r0__ = 0;                                                                        \
+    if (nv__ > 0)                                                                        \
+      r0__ = ptab ? ptab[ts__ / kPage] * kPage + (ts__ % kPage) : seq_row0 + ts__;      \
+    r0__ = __builtin_amdgcn_readfirstlane(r0__);                                         \
+    const uint64_t ad__ = (uint64_t)(cache + (size_t)r0__ * ROWB);                       \
+    rs_ = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad__),                \
+                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad__ >> 32)) & 0xFFFFu, \
+                (uint32_t)__builtin_amdgcn_readfirstlane(nv__ * ROWB), 0x00020000u};     \
+  }
 
   // ---- per-lane LDS offsets of the MFMA operands
   const int qk_off = l32 * LROW + 16 * h;                                  // + 32 k
   const int pv_off = ((j >> 2) + 4 * h) * LROW + (16 * (g & 1) + 4 * (j & 3)) * 2;
+  // lane offsets of this wave's tile loads (the same for every tile)
+  uint32_t voff[NLD];
+#pragma unroll
+  for (int n = 0; n < NLD; ++n) voff[n] = MLA_VOFF(n);
 
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
 
-  // Prologue of an attempt: issue tiles 0..2 (bf16; tiles 0 and 1 for fp8,
-  // which are decoded into the ring right away).
+  // Prologue of an attempt: issue tiles 0 and 1 (fp8: decoded into the ring
+  // right away).
 #define MLA_PROLOGUE()                                                                     \
   do {                                                                                   \
     if (ntiles > 0) {                                                                    \
@@ -267,7 +287,6 @@ void decode_mfma_kernel(DecodeArgs a) {
         MLA_ISSUE_TILE(t0 + TILE, 1);                                                    \
         if constexpr (FP8) MLA_STORE_FP8_TILE(1);                                        \
       }                                                                                  \
-      if (!FP8 && ntiles > 2) MLA_ISSUE_TILE(t0 + 2 * TILE, 2);                          \
     }                                                                                    \
   } while (0)
 
@@ -285,52 +304,130 @@ void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
     l_run = 0.f;
     int restart = 0;
-    if (ntiles > 0) {
-      if constexpr (!FP8) {
-        if (ntiles > 2) MLA_WAIT_TWO_TILES_IN_FLIGHT();    // tile 0 landed
+    if constexpr (!FP8) {
+      // Step it: scores of tile it; the PV product of tile it-1 with the
+      // softmax of tile it interleaved (one assembly block); the loads of
+      // tile it+2 spread through both blocks; wait for tile it+1.  Ring
+      // slots in use during step it: it-1 (PV), it (QK), it+1 (landing),
+      // it+2 (loading).  Step 0 has no previous tile: its PV product
+      // multiplies tile 0 by zero weights (adds exactly zero; the tile
+      // holds finite values).  The last tile's PV product runs after the
+      // loop.
+      if (ntiles > 0) {
+        if (ntiles > 1) MLA_WAIT_ONE_TILE_IN_FLIGHT();   // tile 0 landed
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        bf16x8 pf_prev = {}, pf_prev1 = {};
+        for (int it = 0; it < ntiles; ++it) {
+          const int ts = t0 + it * TILE;
+          MLA_TILE_RSRC(ts + 2 * TILE, rs_n);
+          const uint32_t lb_n = lds_ring + ((it + 2) & 3) * TILE_BYTES + 1024 * wave;
+          floatx16 s_cur;
+          {
+            const uint32_t ad = (uint32_t)(uintptr_t)(s_kv[it & 3] + qk_off);
+            asm volatile(MLA_ASM_QK_TILE_DMA
+                         : "=&v"(s_cur)
+                         : "v"(ad), "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
+                           "v"(qf[5]), "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]),
+                           "v"(qf[10]), "v"(qf[11]), "v"(qf[12]), "v"(qf[13]), "v"(qf[14]),
+                           "v"(qf[15]), "v"(qf[16]), "v"(qf[17]), "v"(qf[18]), "v"(qf[19]),
+                           "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]), "v"(qf[24]),
+                           "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]),
+                           "v"(qf[30]), "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]),
+                           "v"(qf[35]), "s"(rs_n), "s"(lb_n), "v"(voff[0]), "v"(voff[1]),
+                           "v"(voff[2]), "v"(voff[3]), "v"(voff[4])
+                         : "memory", MLA_ASM_QK_CLOBBERS);
+          }
+          // register r holds token 8*(r/4) + 4h + r%4.  The 32 rows of a
+          // wave share one query token, so the visibility limit is
+          // wave-uniform and only a tile that crosses it is masked.
+          float sv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
+          if (ts + TILE - 1 > lim) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
+          }
+          float mt;
+          if (m_ref == kNegInf) {
+            // the first tile in which the row sees a token sets the reference
+            float tmp0;
+            asm volatile(MLA_ASM_SOFTMAX_MAX
+                         : "=&v"(mt), "=&v"(tmp0)
+                         : "v"(sv[0]), "v"(sv[1]), "v"(sv[2]), "v"(sv[3]), "v"(sv[4]),
+                           "v"(sv[5]), "v"(sv[6]), "v"(sv[7]), "v"(sv[8]), "v"(sv[9]),
+                           "v"(sv[10]), "v"(sv[11]), "v"(sv[12]), "v"(sv[13]), "v"(sv[14]),
+                           "v"(sv[15]), "v"(a.scale_log2));
+            m_ref = mt;                          // O and l are still zero here
+          }
+          const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+          const uint32_t vb = (uint32_t)(uintptr_t)(s_kv[(it > 0 ? it - 1 : 0) & 3] + pv_off);
+          uint32_t pk[8];
+          float tmp;
+          asm volatile(MLA_ASM_PV_SOFTMAX_TILE_DMA
+                       : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
+                         "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
+                         "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
+                         "+a"(o[15]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3]),
+                         "+v"(sv[4]), "+v"(sv[5]), "+v"(sv[6]), "+v"(sv[7]), "+v"(sv[8]),
+                         "+v"(sv[9]), "+v"(sv[10]), "+v"(sv[11]), "+v"(sv[12]), "+v"(sv[13]),
+                         "+v"(sv[14]), "+v"(sv[15]), "=&v"(pk[0]), "=&v"(pk[1]), "=&v"(pk[2]),
+                         "=&v"(pk[3]), "=&v"(pk[4]), "=&v"(pk[5]), "=&v"(pk[6]), "=&v"(pk[7]),
+                         "=&v"(mt), "=&v"(tmp), "+v"(l_run)
+                       : "v"(vb), "v"(pf_prev), "v"(pf_prev1), "v"(neg_m), "v"(a.scale_log2),
+                         "s"(rs_n), "s"(lb_n), "v"(voff[5]), "v"(voff[6]), "v"(voff[7]),
+                         "v"(voff[8])
+                       : "memory", MLA_ASM_PV_CLOBBERS);
+          if (wave == 0)                         // the tile's 37th load
+            asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(lds_ring + ((it + 2) & 3) * TILE_BYTES), "v"(voff[NLD - 1]),
+                            "s"(rs_n), "i"(1024 * 36) : "memory");
+          pf_prev = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+          pf_prev1 = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+          m_seen = fmaxf(m_seen, mt);
+          if (mt > m_ref + 64.0f) s_restart = 1;
+          MLA_WAIT_ONE_TILE_IN_FLIGHT();     // tile it+1 landed (it+2 may fly)
+          __syncthreads();
+          restart = s_restart;               // uniform: read after the barrier
+          if (restart) break;
+        }
+        if (!restart) pv_tile(s_kv[(ntiles - 1) & 3] + pv_off, pf_prev, pf_prev1, o);
       }
-      __syncthreads();
-      // Step it works on tile it in ring slot it & 3 while (bf16) tiles
-      // it+1, it+2 are in flight and tile it+3 is issued, or (fp8) tile it+2
-      // is staged through VGPRs.
-      for (int it = 0; it < ntiles; ++it) {
-        const int ts = t0 + it * TILE;
-        const uint8_t* tile = s_kv[it & 3];
-        if constexpr (!FP8) {
-          MLA_ISSUE_TILE(ts + 3 * TILE, (it + 3) & 3);
-        } else {
+    } else {
+      // Step it works on tile it in ring slot it & 3 while tile it+2 is
+      // staged through VGPRs.
+      if (ntiles > 0) {
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+          const int ts = t0 + it * TILE;
+          const uint8_t* tile = s_kv[it & 3];
           MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
-        }
-        const floatx16 s_cur = qk_tile(tile + qk_off, qf);
-        // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4.
-        // The 32 rows of a wave share one query token, so the visibility
-        // limit is wave-uniform and only a tile that crosses it is masked.
-        float sv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
-        if constexpr (FP8) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[r] *= s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)];
-        }
-        if (ts + TILE - 1 > lim) {
+          const floatx16 s_cur = qk_tile(tile + qk_off, qf);
+          // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4.
+          // The 32 rows of a wave share one query token, so the visibility
+          // limit is wave-uniform and only a tile that crosses it is masked.
+          float sv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
-        }
-        // max of the raw scores over the row's 32 tokens (lane pair l, l^32)
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                             fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-        mx = pair_max32(mx);
-        const float mt = mx * a.scale_log2;            // log2 domain (scale > 0)
-        m_seen = fmaxf(m_seen, mt);
-        if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
-        if (mt > m_ref + 64.0f) s_restart = 1;
-        const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-        bf16x8 pf0, pf1;
-        if constexpr (FP8) {
+            sv[r] = s_cur[r] * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)];
+          if (ts + TILE - 1 > lim) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
+          }
+          // max of the raw scores over the row's 32 tokens (lane pair l, l^32)
+          float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                               fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+          mx = pair_max32(mx);
+          const float mt = mx * a.scale_log2;            // log2 domain (scale > 0)
+          m_seen = fmaxf(m_seen, mt);
+          if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
+          if (mt > m_ref + 64.0f) s_restart = 1;
+          const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+          bf16x8 pf0, pf1;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             // product rounded before the subtraction (no contraction), as
@@ -342,29 +439,12 @@ void decode_mfma_kernel(DecodeArgs a) {
             const __bf16 pb = (__bf16)(p * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)]);
             if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
           }
-        } else {
-          // (fma: p of the maximum score is 2^(-rounding error of m_ref),
-          // which rounds to exactly 1 in bf16)
-          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const bf16x2 pb = {(__bf16)__builtin_amdgcn_exp2f(fmaf(sv[r], a.scale_log2, -m_use)),
-                               (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[r + 1], a.scale_log2, -m_use))};
-            // the normaliser sums exactly the rounded weights used in P C
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pb, one, l_run, false);
-            if (r < 8) { pf0[r] = pb[0]; pf0[r + 1] = pb[1]; }
-            else { pf1[r - 8] = pb[0]; pf1[r - 7] = pb[1]; }
-          }
-        }
-        pv_tile(tile + pv_off, pf0, pf1, o);
-        if constexpr (!FP8) {
-          MLA_WAIT_TWO_TILES_IN_FLIGHT();  // tile it+1 landed (it+2, it+3 may fly)
-        } else {
+          pv_tile(tile + pv_off, pf0, pf1, o);
           MLA_STORE_FP8_TILE((it + 2) & 3);
+          __syncthreads();
+          restart = s_restart;               // uniform: read after the barrier
+          if (restart) break;
         }
-        __syncthreads();
-        restart = s_restart;               // uniform: read after the barrier
-        if (restart) break;
       }
     }
     if (!restart) break;
@@ -377,7 +457,8 @@ void decode_mfma_kernel(DecodeArgs a) {
 #undef MLA_ISSUE_TILE
 #undef MLA_PROLOGUE
 #undef MLA_STORE_FP8_TILE
-#undef MLA_WAIT_TWO_TILES_IN_FLIGHT
+#undef MLA_WAIT_ONE_TILE_IN_FLIGHT
+#undef MLA_TILE_RSRC
 #undef MLA_VOFF
 
   // ---- normalise and write (the final output, or this split's partial).

@@ -1,14 +1,18 @@
 #!/usr/bin/env python3
 """Writes decode_mfma_asm.inc: the software-pipelined LDS-read / MFMA
-sequences of the attention kernel's two contractions, as inline-assembly
-string literals.
+sequences of the attention kernel's tile steps, as inline-assembly string
+literals.
 
 The compiler keeps a single LDS operand read in flight in front of each
 matrix instruction; these sequences keep several in flight (the reads of the
 next P instructions are issued before waiting for the current one), so the
-LDS latency hides behind the matrix pipe.  Each sequence waits for all of
-its own reads before it ends and finishes with enough independent cycles
-for a vector instruction to read the matrix results.
+LDS latency hides behind the matrix pipe.  The softmax of a tile is
+interleaved with the PV product of the previous tile, and the loads of the
+tile after next are spread through both sequences, so the vector ALU and the
+memory pipeline work while the matrix pipe runs.  Each sequence waits for
+all of its own LDS reads before it ends (its buffer loads complete into LDS
+and are waited for by the kernel) and finishes with enough independent
+cycles for a vector instruction to read the matrix results.
 
 Run from this directory after changing the tile layout constants below
 (they must match decode_mfma.hip):  python3 gen_decode_asm.py
@@ -20,6 +24,8 @@ QK_BUFS = 8
 PV_STEPS = 32        # 16 latent blocks x 2 token halves
 PV_AHEAD = 4
 PV_BUFS = 6
+QK_DMA = 5           # tile loads interleaved with the QK sequence
+PV_DMA = 4           # ... and with the PV + softmax sequence (9 per wave)
 NOPS = "s_nop 7\\n\\ts_nop 7\\n\\t"   # 16 wait states: XDL result -> VALU read
 
 
@@ -32,9 +38,19 @@ def quad(base, i, nbuf):
     return r
 
 
-def qk():
+def dma(n, rsrc, ldsbase, voff):
+    """Load n of this wave's share of a tile: 64 lanes x 16 bytes from the
+    cache (buffer descriptor rsrc, lane offset voff) straight into LDS at
+    ldsbase + 4096 n (M0 holds the LDS address)."""
+    return [f"s_add_u32 m0, {ldsbase}, {4096 * n}", "s_nop 0",
+            f"buffer_load_dwordx4 {voff}, {rsrc}, 0 offen lds"]
+
+
+def qk(with_dma=False):
     # operands: %0 S (floatx16, out), %1 base address, %2..%37 query
-    # fragments; operand buffers are the fixed VGPRs v[224:255]
+    # fragments; with_dma: %38 buffer descriptor, %39 LDS base of this
+    # wave's loads, %40..%44 lane offsets of loads 0..4 (one load after
+    # every fourth MFMA).  Operand buffers are the fixed VGPRs v[224:255].
     out = []
     for k in range(QK_AHEAD):
         r = quad(QK_TMP, k, QK_BUFS)
@@ -48,7 +64,21 @@ def qk():
         c = "0" if k == 0 else "%0"
         r = quad(QK_TMP, k, QK_BUFS)
         out.append(f"v_mfma_f32_32x32x16_bf16 %0, v[{r}:{r + 3}], %{2 + k}, {c}")
+        if with_dma and k % 4 == 3 and k // 4 < QK_DMA:
+            n = k // 4
+            out += dma(n, "%38", "%39", f"%{40 + n}")
     return out
+
+
+def pv_reads(m, base):
+    """The two transposed reads of PV step m (32-dim block m // 2, token
+    half m % 2) relative to the base address operand."""
+    db, ks = m // 2, m % 2
+    r = quad(PV_TMP, m, PV_BUFS)
+    lo = (16 * ks) * LROW + 64 * db
+    hi = (16 * ks + 8) * LROW + 64 * db
+    return [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], {base} offset:{lo}",
+            f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], {base} offset:{hi}"]
 
 
 def pv():
@@ -56,21 +86,12 @@ def pv():
     # probabilities of token halves 0 / 1; operand buffers are the fixed
     # VGPRs v[232:255]
     out = []
-
-    def reads(m):
-        db, ks = m // 2, m % 2
-        r = quad(PV_TMP, m, PV_BUFS)
-        lo = (16 * ks) * LROW + 64 * db
-        hi = (16 * ks + 8) * LROW + 64 * db
-        return [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], %16 offset:{lo}",
-                f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], %16 offset:{hi}"]
-
     for m in range(PV_AHEAD):
-        out += reads(m)
+        out += pv_reads(m, "%16")
     for m in range(PV_STEPS):
         n = m + PV_AHEAD
         if n < PV_STEPS:
-            out += reads(n)
+            out += pv_reads(n, "%16")
         out.append(f"s_waitcnt lgkmcnt({2 * min(PV_AHEAD, PV_STEPS - 1 - m)})")
         db, ks = m // 2, m % 2
         r = quad(PV_TMP, m, PV_BUFS)
@@ -78,8 +99,97 @@ def pv():
     return out
 
 
+def max_valu(S, MT, TMP, SCALE):
+    """Scaled max of the 16 raw scores and of the lane pair (l, l ^ 32).
+    v_permlane32_swap exchanges the upper half of its first operand with
+    the lower half of its second: with the max in both, the larger of the
+    two results is the pair's max."""
+    valu = [f"v_max3_f32 {TMP}, {S(0)}, {S(1)}, {S(2)}"]
+    for r in range(3, 15, 2):
+        valu.append(f"v_max3_f32 {TMP}, {TMP}, {S(r)}, {S(r + 1)}")
+    valu.append(f"v_max_f32 {TMP}, {TMP}, {S(15)}")
+    valu.append(f"v_mov_b32 {MT}, {TMP}")
+    valu.append("s_nop 1")
+    valu.append(f"v_permlane32_swap_b32 {TMP}, {MT}")
+    valu.append("s_nop 1")
+    valu.append(f"v_max_f32 {TMP}, {TMP}, {MT}")
+    valu.append(f"v_mul_f32 {MT}, {TMP}, {SCALE}")
+    return valu
+
+
+def weights_valu(S, PK, LRUN, NEGM, SCALE):
+    """p_r = 2^(s_r * scale - m_ref) (one fma, no rounding in between);
+    pairs packed to bf16; normaliser += both rounded weights of each pair.
+    Each v_exp result is read at least two instructions later."""
+    fma = [f"v_fma_f32 {S(r)}, {S(r)}, {SCALE}, {NEGM}" for r in range(16)]
+    exp = [f"v_exp_f32 {S(r)}, {S(r)}" for r in range(16)]
+    seq = fma[:2]
+    for r in range(2, 16):
+        seq += [fma[r], exp[r - 2]]
+    seq += exp[14:]
+    seq.append("s_nop 1")
+    seq += [f"v_cvt_pk_bf16_f32 {PK(i)}, {S(2 * i)}, {S(2 * i + 1)}" for i in range(8)]
+    seq += [f"v_dot2c_f32_bf16 {LRUN}, 0x3f803f80, {PK(i)}" for i in range(8)]
+    return seq
+
+
+def softmax_max():
+    """operands: %0 scaled max (out), %1 a temporary, %2..%17 scores, %18 scale."""
+    return max_valu(lambda r: f"%{2 + r}", "%0", "%1", "%18") + ["s_nop 1"]
+
+
+def softmax_valu(S, PK, MT, TMP, LRUN, NEGM, SCALE):
+    """One tile's softmax (bf16 weights).  The weights need only the fixed
+    reference, not this tile's max, so the max (for the restart check) and
+    the weights are independent chains."""
+    return max_valu(S, MT, TMP, SCALE) + weights_valu(S, PK, LRUN, NEGM, SCALE)
+
+
+def pv_softmax(with_dma=False):
+    """PV of the previous tile interleaved with the softmax of the current.
+
+    operands: %0..%15 O blocks (accumulators), %16..%31 the current tile's
+    scores s_0..s_15 (in; overwritten), %32..%39 the current tile's packed
+    bf16 weight pairs (out), %40 its scaled max (out), %41 a temporary,
+    %42 the running normaliser (in/out), %43 base address of the previous
+    tile's transposed reads, %44 / %45 the previous tile's weights (token
+    halves 0 / 1), %46 -m_ref, %47 the scale (log2 domain).  with_dma:
+    %48 buffer descriptor, %49 LDS base of this wave's loads, %50..%53 lane
+    offsets of loads 5..8 (one load after every eighth MFMA).  Operand
+    buffers: v[232:255].
+    """
+    valu = softmax_valu(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
+                        "%40", "%41", "%42", "%46", "%47")
+    out = []
+    for m in range(PV_AHEAD):
+        out += pv_reads(m, "%43")
+    vi = 0
+    for m in range(PV_STEPS):
+        n = m + PV_AHEAD
+        if n < PV_STEPS:
+            out += pv_reads(n, "%43")
+        out.append(f"s_waitcnt lgkmcnt({2 * min(PV_AHEAD, PV_STEPS - 1 - m)})")
+        db, ks = m // 2, m % 2
+        r = quad(PV_TMP, m, PV_BUFS)
+        out.append(f"v_mfma_f32_32x32x16_bf16 %{db}, v[{r}:{r + 3}], %{44 + ks}, %{db}")
+        if with_dma and m % 8 == 3 and m // 8 < PV_DMA:
+            k = m // 8
+            out += dma(QK_DMA + k, "%48", "%49", f"%{50 + k}")
+        take = 2 if m < PV_STEPS - 1 else len(valu) - vi
+        for _ in range(take):
+            if vi < len(valu):
+                out.append(valu[vi])
+                vi += 1
+    assert vi == len(valu)
+    return out
+
+
 def clobbers(base, n):
     return ", ".join(f'"v{base + i}"' for i in range(n))
+
+
+def emit_plain(name, lines):
+    return f"#define {name} \\\n" + " \\\n".join(f'  "{l}\\n\\t"' for l in lines) + "\n"
 
 
 def emit(name, lines):
@@ -89,10 +199,13 @@ def emit(name, lines):
 
 if __name__ == "__main__":
     txt = ["// Generated by gen_decode_asm.py -- do not edit by hand.",
-           "// Inline-assembly bodies of the attention kernel's QK^T and PV tile steps.",
+           "// Inline-assembly bodies of the attention kernel's tile steps.",
            ""]
     txt.append(emit("MLA_ASM_QK_TILE", qk()))
+    txt.append(emit("MLA_ASM_QK_TILE_DMA", qk(True)))
     txt.append(f"#define MLA_ASM_QK_CLOBBERS {clobbers(QK_TMP, 32)}\n")
     txt.append(emit("MLA_ASM_PV_TILE", pv()))
+    txt.append(emit("MLA_ASM_PV_SOFTMAX_TILE_DMA", pv_softmax(True)))
     txt.append(f"#define MLA_ASM_PV_CLOBBERS {clobbers(PV_TMP, 24)}\n")
+    txt.append(emit_plain("MLA_ASM_SOFTMAX_MAX", softmax_max()))
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))
