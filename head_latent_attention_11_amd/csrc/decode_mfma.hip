@@ -131,9 +131,19 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vb, const bf16x8 pf0, con
                : "memory", MLA_ASM_PV_CLOBBERS);
 }
 
+// LDS source offset mapping of a tile (rows at a pitch of 73 granules of 16
+// bytes): granule u of the slot holds granule u % 73 of token row u / 73,
+// or nothing (the row's padding granule, or past the tile's 32 rows), which
+// gets an offset past any valid range (the buffer load then writes zeros).
+// u / 73 = (449 u) >> 15 for u < 2368.
+__device__ inline uint32_t tile_src_offset(int u) {
+  const int tk = (u * 449) >> 15;
+  return (u - 73 * tk == NCH || tk >= TILE) ? kOOB : uint32_t(16 * (u - tk));
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_mfma_kernel(DecodeArgs a) {
+void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
   __shared__ float s_scale[NBUF][TILE];
   __shared__ int s_restart;
@@ -143,12 +153,26 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int h = lane >> 5, l32 = lane & 31, g = lane >> 4, j = lane & 15;
   const int gi = xcd_logical_index(blockIdx.x, gridDim.x);
   const int item = gi / a.row_blocks, rb = gi % a.row_blocks;
-  const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
-  if (loc.b < 0) return;
-  const int b = __builtin_amdgcn_readfirstlane(loc.b);
-  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+  // work item -> (sequence, split, length): from the host's table when the
+  // plan has few enough items, else located on the device
+  int b, s_idx, L;
+  if (tab.n > 0) {
+    const uint32_t e = tab.seq_split[item];
+    b = e & 0xFFFFF;
+    s_idx = e >> 20;
+    L = tab.len[item];
+  } else {
+    const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
+    if (loc.b < 0) return;
+    b = loc.b;
+    s_idx = loc.s;
+    L = a.seq_lens[loc.b];
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int ns = splits_of(L, a.num_splits, a.chunk);
   const int c = chunk_of(L, a.num_splits, a.chunk);
-  const int t0 = __builtin_amdgcn_readfirstlane(loc.s) * c;
+  const int t0 = __builtin_amdgcn_readfirstlane(s_idx) * c;
   const int t_end = min(L, t0 + c);                       // item end
   const int rows = a.n_h * a.T;
   const int row = rb * ROWS_WG + wave * 32 + l32;         // this lane's row
@@ -161,12 +185,34 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int nq = b * a.T + tau;
   const int ntiles = (t_stage > t0) ? (t_stage - t0 + TILE - 1) / TILE : 0;
 
-  // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims)
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
+
+  // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims).
+  // The wave's 32 rows are contiguous in memory (row = tau * n_h + head,
+  // query token b*T + tau): it copies them into ring slot `wave` at the tile
+  // row pitch with buffer loads that write LDS directly (each load 1 KB of
+  // contiguous memory), then reads its operands from there (the same
+  // conflict-free pattern as the K operand reads).
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q_abs + ((size_t)nq * a.n_h + head) * D;
+    const size_t r0 = (size_t)b * rows + rb * ROWS_WG + wave * 32;
+    const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs + r0 * (2 * D));
+    const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
+                       uint32_t(32 * 2 * D), 0x00020000u};
+    const uint32_t qlds = lds_ring + wave * TILE_BYTES;
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qrow + 16 * k + 8 * h);
+    for (int n = 0; n < NLOADS; ++n)
+      asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(qlds), "v"(tile_src_offset(64 * n + lane)), "s"(qrs), "i"(1024 * n)
+                   : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* qsrc = &s_kv[wave][0] + l32 * LROW + 16 * h;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qsrc + 32 * k);
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
+    __syncthreads();                    // every wave has its operands: the ring is free
   }
 
   const uint8_t* cache = (const uint8_t*)a.cache;
@@ -174,7 +220,6 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int seq_row0 = b * a.max_len;
   typedef __attribute__((address_space(4))) const int32_t* ConstI32;
   const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
-  const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
 
   // ---- staging.  bf16: LDS 16-byte chunk q of a tile holds token q / 73,
   // chunk q % 73 of its row (chunk 72 is the row padding, filled with zero
@@ -186,11 +231,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // (q/73 = (449 q) >> 15 for q < 2368); the padding chunk of each row and
   // chunks past the tile take an out-of-range offset.
   const int qbase = 64 * wave + lane;
-#define MLA_VOFF(n_)                                                                       \
-  ({                                                                                     \
-    const int q__ = qbase + 256 * (n_), tk__ = (q__ * 449) >> 15;                        \
-    (q__ - 73 * tk__ == NCH || tk__ >= TILE) ? kOOB : uint32_t(16 * (q__ - tk__));      \
-  })
+#define MLA_VOFF(n_) tile_src_offset(qbase + 256 * (n_))
   u32x2 stg8[FP8 ? NSTG8 : 1];
   float stg_scale = 0.f;
 
@@ -292,12 +333,6 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   if (tid == 0) s_restart = 0;
   MLA_PROLOGUE();
-  // The query loads were issued before the first tiles, so their latency
-  // overlaps; let them land here.  (The compiler waits for them with vmcnt
-  // counts that do not know of the tile loads; issued later, those can
-  // only make such a wait longer, never shorter.)
-#pragma unroll
-  for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
 
   for (;;) {                          // attempts (a restart is rare)
 #pragma unroll
@@ -475,7 +510,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   static_assert(4 * 32 * EROW <= NBUF * TILE_BYTES, "output staging must fit the ring");
   uint8_t* stg = &s_kv[0][0] + wave * (32 * EROW);
   const int row0 = rb * ROWS_WG + wave * 32;         // first row of this wave
-  if (loc.ns == 1) {
+  if (ns == 1) {
     const size_t g0 = (size_t)b * rows + row0;
     uint8_t* dst = (uint8_t*)(a.out_latent + g0 * DC);
 #pragma unroll
@@ -516,13 +551,13 @@ void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, const ItemTable& tab, hipStream_t st) {
   // a.row_blocks counts blocks of ROWS_WG query rows
   const int grid = a.n_items * a.row_blocks;
   if (a.kv_dtype == MLA_FP8_E4M3)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(256), 0, st, a, tab);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(256), 0, st, a, tab);
   return hipGetLastError();
 }
 

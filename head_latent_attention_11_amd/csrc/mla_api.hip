@@ -18,7 +18,7 @@ hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int3
 hipError_t launch_combine(const DecodeArgs&, hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
-hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_mfma(const DecodeArgs&, const ItemTable&, hipStream_t);
 hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
 }  // namespace mla
 
@@ -262,8 +262,25 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   a.kv_dtype = dims->kv_dtype;
   a.scale_log2 = softmax_scale_of(dims) * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = fast_decode(dims, q_tokens) ? launch_decode_mfma(a, s)
-                                             : launch_decode_general(a, s);
+  hipError_t e;
+  if (fast_decode(dims, q_tokens)) {
+    ItemTable tab;
+    tab.n = 0;
+    if (p.n_items <= kItemTable && batch < (1 << 20)) {
+      int n = 0;
+      for (int b = 0; b < batch; ++b) {
+        const int ns = splits_of(seq_lens_host[b], p.num_splits, p.chunk);
+        for (int sp = 0; sp < ns && sp < 4096; ++sp, ++n) {
+          tab.seq_split[n] = uint32_t(b) | (uint32_t(sp) << 20);
+          tab.len[n] = seq_lens_host[b];
+        }
+      }
+      tab.n = (n == p.n_items) ? n : 0;
+    }
+    e = launch_decode_mfma(a, tab, s);
+  } else {
+    e = launch_decode_general(a, s);
+  }
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   if (p.any_split) {
     e = launch_combine(a, s);

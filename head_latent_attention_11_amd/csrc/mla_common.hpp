@@ -125,4 +125,13 @@ struct DecodeArgs {
   float scale_log2;           // softmax scale * log2(e)
 };
 
+// Work items of a plan, listed by the host when there are at most
+// kItemTable of them (passed by value; n = 0: the kernel locates items).
+constexpr int kItemTable = 256;
+struct ItemTable {
+  int32_t n;
+  uint32_t seq_split[kItemTable];   // sequence | split << 20
+  int32_t len[kItemTable];          // the sequence's length
+};
+
 }  // namespace mla
