@@ -16,14 +16,19 @@ namespace mla {
 // ============================================================ RoPE helper
 // Interleaved pairs (2k, 2k+1) rotated by pos * base^(-2k/d); angle and
 // rotation in double precision.
-__device__ inline void rope_pair(float x0, float x1, int pos, int k, int d,
-                                 float base, float* y0, float* y1) {
-  double theta = pow((double)base, -2.0 * (double)k / (double)d);
+__device__ inline double rope_theta(int k, int d, float base) {
+  return pow((double)base, -2.0 * (double)k / (double)d);
+}
+__device__ inline void rope_rot(float x0, float x1, int pos, double theta, float* y0, float* y1) {
   double ang = (double)pos * theta;
   double s, c;
   sincos(ang, &s, &c);
   *y0 = (float)((double)x0 * c - (double)x1 * s);
   *y1 = (float)((double)x0 * s + (double)x1 * c);
+}
+__device__ inline void rope_pair(float x0, float x1, int pos, int k, int d,
+                                 float base, float* y0, float* y1) {
+  rope_rot(x0, x1, pos, rope_theta(k, d, base), y0, y1);
 }
 
 template <typename T> __device__ inline float load_f(const T* p, size_t i);
@@ -40,13 +45,18 @@ template <> __device__ inline void store_f<uint16_t>(uint16_t* p, size_t i, floa
 // ====================================================== absorb: MFMA path
 // q_abs[n, i, 0:512] = W^UK_i^T q_nope[n, i, :], d_h = 128.  One workgroup
 // per (head i, block of 128 latent columns); wave w owns 32 columns and
-// computes D^T[cols x tokens] = W^T q^T.  The 128 x 128 W^UK_i block is
-// staged row-major in LDS with 16-byte writes and read back column-wise
-// with the gfx950 transposing LDS read: within each group of 16 lanes,
-// ds_read_b64_tr_b16 hands lane i element i%4 of the 8-byte chunks
-// addressed by lanes 4k + i/4 (k = 0..3), so four rows of 16 elements come
-// back as 16 columns of 4.
+// computes D^T[cols x tokens] = W^T q^T for blocks of 32 tokens.  Every
+// global access is coalesced (16-byte chunks, consecutive lanes on
+// consecutive addresses): a lane-per-row pattern would cost the address
+// unit one cycle per lane.  The 128 x 128 W^UK_i block and each query block
+// are staged row-major in LDS; W^UK is read back column-wise with the gfx950
+// transposing LDS read (within each group of 16 lanes, ds_read_b64_tr_b16
+// hands lane i element i%4 of the 8-byte chunks addressed by lanes 4k + i/4,
+// k = 0..3, so four rows of 16 elements come back as 16 columns of 4), and
+// the results go back through LDS so that each token's 128 columns are
+// written as one contiguous run.
 constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsCols + 8;
+constexpr int kAbsOutRow = 528;       // bytes per token row of the output staging
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -67,20 +77,47 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     OutT* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
   __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kAbsLdsRow];
+  __shared__ __attribute__((aligned(16))) unsigned char os[32 * kAbsOutRow];
   const int head = blockIdx.x >> 2, cb = blockIdx.x & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, j = lane & 15;
 
-  // first token block's query operands, issued before the W^UK staging
-  bf16x8 bq0[kAbsDh / 16];
-#pragma unroll
-  for (int k = 0; k < kAbsDh / 16; ++k) {
-    bq0[k] = bf16x8{};
-    if (l32 < n_tok)
-      bq0[k] = *(const bf16x8*)(q_nope + ((size_t)l32 * n_h + head) * kAbsDh + 16 * k + 8 * h);
+  // The RoPE part q_abs[..., 512:576] is shared out over the head's four
+  // workgroups: pair p = 256 cb + tid + 1024 u (token p / 32, pair k = p % 32
+  // = tid % 32 for every u).  The first pair's inputs are loaded before the
+  // W^UK block (loads complete in order) and rotated while it is in flight.
+  const int n_pairs = n_tok * (DR / 2), rk = tid & 31;
+  const int p_first = cb * 256 + tid;
+  float rx0 = 0.f, rx1 = 0.f;
+  int rpos = 0;
+  if (p_first < n_pairs) {
+    const uint16_t* src = q_rope + ((size_t)(p_first >> 5) * n_h + head) * DR + 2 * rk;
+    rx0 = bf16_bits_to_f32(src[0]);
+    rx1 = bf16_bits_to_f32(src[1]);
+    if (q_pos) rpos = q_pos[p_first >> 5];
   }
-  // stage W^UK[head][r][cb*128 : cb*128 + 128] row-major (16-byte chunks)
+
+  // query block loader: 32 tokens x 128 d_h = 512 chunks of 16 bytes
+  auto load_q = [&](int t0, u32x4* qv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + 256 * i, t = ch >> 4, c8 = (ch & 15) * 8;
+      qv[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + t < n_tok) qv[i] = *(const u32x4*)(q_nope + ((size_t)(t0 + t) * n_h + head) * kAbsDh + c8);
+    }
+  };
+  auto store_q = [&](const u32x4* qv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + 256 * i, t = ch >> 4, c8 = (ch & 15) * 8;
+      *(u32x4*)(qs + t * kAbsLdsRow + c8) = qv[i];
+    }
+  };
+  u32x4 qv[2];
+  load_q(0, qv);
+  // W^UK[head][r][cb*128 : cb*128 + 128], row-major 16-byte chunks
   const uint16_t* wsrc = w_uk + (size_t)head * kAbsDh * DC + cb * kAbsCols;
   u32x4 stg[8];
 #pragma unroll
@@ -88,11 +125,31 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const int ch = tid + 256 * i, r = ch >> 4, c8 = (ch & 15) * 8;
     stg[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
+  const double theta = q_pos ? rope_theta(rk, DR, rope_base) : 0.0;
+  for (int p = p_first; p < n_pairs; p += 1024) {
+    const int tok = p >> 5;
+    float x0 = rx0, x1 = rx1;
+    int pos = rpos;
+    if (p != p_first) {
+      const uint16_t* src = q_rope + ((size_t)tok * n_h + head) * DR + 2 * rk;
+      x0 = bf16_bits_to_f32(src[0]);
+      x1 = bf16_bits_to_f32(src[1]);
+      if (q_pos) pos = q_pos[tok];
+    }
+    if (q_pos) rope_rot(x0, x1, pos, theta, &x0, &x1);
+    OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * rk;
+    if constexpr (sizeof(OutT) == 4) {
+      *(float2*)dst = float2{x0, x1};
+    } else {
+      *(uint32_t*)dst = pack_bf16x2(x0, x1);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int ch = tid + 256 * i, r = ch >> 4, c8 = (ch & 15) * 8;
     *(u32x4*)(ws + r * kAbsLdsRow + c8) = stg[i];
   }
+  store_q(qv);
   __syncthreads();
 
   // A operand (W^T, lane: column 32*wave + l32, d_h values 16k + 8h + e)
@@ -107,51 +164,38 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   }
 
   for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    const int tok = t0 + l32;         // B-operand column
-    bf16x8 bq[kAbsDh / 16];
-#pragma unroll
-    for (int k = 0; k < kAbsDh / 16; ++k) {
-      bq[k] = bq0[k];
-      if (t0 > 0) {
-        bq[k] = bf16x8{};
-        if (tok < n_tok)
-          bq[k] = *(const bf16x8*)(q_nope + ((size_t)tok * n_h + head) * kAbsDh + 16 * k + 8 * h);
-      }
+    if (t0 > 0) {                      // next query block (previous one consumed)
+      load_q(t0, qv);
+      __syncthreads();
+      store_q(qv);
+      __syncthreads();
     }
     floatx16 acc = {};
 #pragma unroll
-    for (int k = 0; k < kAbsDh / 16; ++k)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bq[k], acc, 0, 0, 0);
-    // acc[r]: column-in-block 8(r/4) + 4h + r%4 of wave's 32, token l32
-    if (tok < n_tok) {
-      OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + cb * kAbsCols + wave * 32;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if constexpr (sizeof(OutT) == 4)
-          *(floatx4*)(dst + 8 * jj + 4 * h) =
-              floatx4{acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
-        else
-          *(u32x2*)(dst + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
-                                                 pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
-      }
+    for (int k = 0; k < kAbsDh / 16; ++k) {
+      const bf16x8 bq = *(const bf16x8*)(qs + l32 * kAbsLdsRow + 16 * k + 8 * h);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bq, acc, 0, 0, 0);
     }
-  }
-
-  // the RoPE part q_abs[..., 512:576] is written by the cb == 0 workgroups
-  if (cb == 0) {
-    for (int idx = tid; idx < n_tok * (DR / 2); idx += 256) {
-      const int tok = idx / (DR / 2), k = idx % (DR / 2);
-      const uint16_t* src = q_rope + ((size_t)tok * n_h + head) * DR + 2 * k;
-      float x0 = bf16_bits_to_f32(src[0]), x1 = bf16_bits_to_f32(src[1]);
-      if (q_pos) rope_pair(x0, x1, q_pos[tok], k, DR, rope_base, &x0, &x1);
-      OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * k;
-      if constexpr (sizeof(OutT) == 4) {
-        dst[0] = x0;
-        dst[1] = x1;
-      } else {
-        dst[0] = f32_to_bf16_bits(x0);
-        dst[1] = f32_to_bf16_bits(x1);
-      }
+    // acc[r]: column-in-block 8(r/4) + 4h + r%4 of wave's 32, token l32
+    OutT* orow = (OutT*)(os + l32 * kAbsOutRow) + wave * 32;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if constexpr (sizeof(OutT) == 4)
+        *(floatx4*)(orow + 8 * jj + 4 * h) =
+            floatx4{acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
+      else
+        *(u32x2*)(orow + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
+                                                pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
+    }
+    __syncthreads();
+    // 32 tokens x 128 columns, 16-byte chunks, each token's run contiguous
+    constexpr int per_row = kAbsCols * (int)sizeof(OutT) / 16;
+#pragma unroll
+    for (int i = 0; i < 32 * per_row / 256; ++i) {
+      const int ch = tid + 256 * i, t = ch / per_row, c = ch % per_row;
+      if (t0 + t < n_tok)
+        *(u32x4*)((unsigned char*)(q_abs + ((size_t)(t0 + t) * n_h + head) * D + cb * kAbsCols) + 16 * c) =
+            *(const u32x4*)(os + t * kAbsOutRow + 16 * c);
     }
   }
 }
@@ -300,11 +344,47 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   }
   first = wave_sum_i(first);
   const float* lse_p = a.part_lse + (size_t)first * rows + row;
+  float* out = a.out_latent + (size_t)R * a.d_c;
+  const int d0 = 8 * lane;                                // this lane's 8 dims
+  const size_t pstride = (size_t)rows * a.d_c;            // elements between splits
+  if (a.part_bf16 && ns <= 16) {
+    // Few splits: every load (LSEs and partials) is issued before any of
+    // them is used, so the row costs one memory latency.
+    const float lse_l = (lane < ns) ? lse_p[(size_t)lane * rows] : -INFINITY;
+    const uint16_t* src = (const uint16_t*)a.part_o + ((size_t)first * rows + row) * a.d_c + d0;
+    u32x4 v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < ns) v[s] = *(const u32x4*)(src + (size_t)s * pstride);
+    const float mx = wave_max(lse_l);
+    if (mx == -INFINITY) {                                // no visible token at all
+      *(floatx4*)(out + d0) = floatx4{0.f, 0.f, 0.f, 0.f};
+      *(floatx4*)(out + d0 + 4) = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0) a.out_lse[R] = -INFINITY;
+      return;
+    }
+    const float e_l = (lane < ns) ? expf(lse_l - mx) : 0.f;
+    const float wsum = wave_sum(e_l);
+    const float w_l = e_l * (1.0f / wsum);
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      if (s < ns) {
+        const float w = __shfl(w_l, s, 64);
+        acc0 += w * floatx4{__builtin_bit_cast(float, v[s][0] << 16), __builtin_bit_cast(float, v[s][0] & 0xFFFF0000u),
+                            __builtin_bit_cast(float, v[s][1] << 16), __builtin_bit_cast(float, v[s][1] & 0xFFFF0000u)};
+        acc1 += w * floatx4{__builtin_bit_cast(float, v[s][2] << 16), __builtin_bit_cast(float, v[s][2] & 0xFFFF0000u),
+                            __builtin_bit_cast(float, v[s][3] << 16), __builtin_bit_cast(float, v[s][3] & 0xFFFF0000u)};
+      }
+    }
+    *(floatx4*)(out + d0) = acc0;
+    *(floatx4*)(out + d0 + 4) = acc1;
+    if (lane == 0) a.out_lse[R] = mx + logf(wsum);
+    return;
+  }
   float mx = -INFINITY;
   for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse_p[(size_t)s * rows]);
   mx = wave_max(mx);
-  float* out = a.out_latent + (size_t)R * a.d_c;
-  const int d0 = 8 * lane;                                // this lane's 8 dims
   if (mx == -INFINITY) {                                  // no visible token at all
     for (int d = d0; d < min(d0 + 8, a.d_c); d += 4) *(floatx4*)(out + d) = floatx4{0.f, 0.f, 0.f, 0.f};
     if (lane == 0) a.out_lse[R] = -INFINITY;
@@ -315,7 +395,6 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const size_t pstride = (size_t)rows * a.d_c;            // elements between splits
   if (a.part_bf16) {                                      // fast path: d_c = 512
     const uint16_t* src = (const uint16_t*)a.part_o + ((size_t)first * rows + row) * a.d_c + d0;
     for (int s0 = 0; s0 < ns; s0 += 64) {
@@ -367,74 +446,96 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 // ===================================================== up-projection: MFMA
 // out[n, i, :] = W^UV_i latent[n, i, :], d_h = 128, d_c = 512.  One
-// workgroup of 4 waves per (head i, block of 32 tokens); wave w owns d_h
-// rows 32w .. 32w+31.  All global loads are issued first: each lane's 32
-// W^UV operands (the workgroup streams W^UV_i once) and its share of the
-// latent block (32 tokens x 512 fp32), which is then staged in LDS as bf16
-// hi + lo parts (x = hi + lo + O(2^-17 x)), so the bf16 MFMA keeps nearly
-// fp32 accuracy with W^UV exact in bf16.
-constexpr int kUpLds = 512 + 8;       // padded bf16 row of the latent block
+// workgroup of 8 waves per (head i, half of the d_h rows): 2 n_h
+// workgroups, grouped so that both halves of a head run on one XCD and share
+// its L2 copy of the head's latent rows.  All global loads are coalesced
+// (16-byte chunks on consecutive lanes): the 64 x 512 W^UV block is staged
+// in LDS as is, and each block of 32 latent rows (fp32) is staged as bf16
+// hi + lo parts (x = hi + lo + O(2^-17 x)), so the bf16 products keep nearly
+// fp32 accuracy with W^UV exact in bf16.  Wave (mi, ni) computes the 16 x 16
+// output block d_h rows 16 mi .. of the half, tokens 16 ni .. of the block
+// with v_mfma_f32_16x16x32_bf16.
+__device__ inline int xcd_grouped(int i, int n) {
+  // workgroups are dispatched round-robin over the 8 XCDs
+  return (n & 7) ? i : (i & 7) * (n >> 3) + (i >> 3);
+}
+
+constexpr int kUpRow = 520;           // bf16 elements per LDS row (1040 bytes)
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void up_proj_mfma_kernel(
+__global__ __launch_bounds__(512) void up_proj_mfma_kernel(
     const float* __restrict__ latent, const uint16_t* __restrict__ w_uv,
     OutT* __restrict__ out, int n_tok, int n_h) {
   constexpr int DC = 512, DH = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t s_hi[32 * kUpLds];
-  __shared__ __attribute__((aligned(16))) uint16_t s_lo[32 * kUpLds];
-  const int head = blockIdx.x, t0 = blockIdx.y * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t sw[64 * kUpRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sh[32 * kUpRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sl[32 * kUpRow];
+  const int L = xcd_grouped(blockIdx.x, gridDim.x);
+  const int head = L >> 1, half = L & 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int m = wave * 32 + l32;                    // d_h row (A-operand row)
-  const uint16_t* wrow = w_uv + ((size_t)head * DH + m) * DC;
+  const int mi = wave & 3, ni = wave >> 2;
+  const int r16 = lane & 15, g = lane >> 4;
 
-  bf16x8 wa[DC / 16];
+  const uint16_t* wsrc = w_uv + ((size_t)head * DH + 64 * half) * DC;
+  u32x4 wv[8];                         // 64 rows x 64 chunks
 #pragma unroll
-  for (int k = 0; k < DC / 16; ++k) wa[k] = *(const bf16x8*)(wrow + 16 * k + 8 * h);
-  // latent block: 4096 chunks of 4 floats, 16 per thread
-  floatx4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int ch = tid + 256 * i, t = ch >> 7, c4 = (ch & 127) * 4;
-    v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
+  for (int i = 0; i < 8; ++i) {
+    const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
+    wv[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
+  for (int t0 = 0; t0 < n_tok; t0 += 32) {
+    floatx4 v[8];                      // 32 rows x 128 chunks of 4 floats
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int ch = tid + 256 * i, t = ch >> 7, c4 = (ch & 127) * 4;
-    u32x2 hi, lo;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float x0 = v[i][2 * e], x1 = v[i][2 * e + 1];
-      const bf16x2 hb = bf16x2{(__bf16)x0, (__bf16)x1};
-      hi[e] = __builtin_bit_cast(uint32_t, hb);
-      lo[e] = pack_bf16x2(x0 - (float)hb[0], x1 - (float)hb[1]);
+    for (int i = 0; i < 8; ++i) {
+      const int ch = tid + 512 * i, t = ch >> 7, c4 = (ch & 127) * 4;
+      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
     }
-    *(u32x2*)(s_hi + t * kUpLds + c4) = hi;
-    *(u32x2*)(s_lo + t * kUpLds + c4) = lo;
-  }
-  __syncthreads();
-
-  floatx16 acc_hi = {}, acc_lo = {};
+    if (t0 == 0) {
 #pragma unroll
-  for (int k = 0; k < DC / 16; ++k) {
-    const bf16x8 bh = *(const bf16x8*)(s_hi + l32 * kUpLds + 16 * k + 8 * h);
-    const bf16x8 bl = *(const bf16x8*)(s_lo + l32 * kUpLds + 16 * k + 8 * h);
-    acc_hi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bh, acc_hi, 0, 0, 0);
-    acc_lo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[k], bl, acc_lo, 0, 0, 0);
-  }
-  const int tok = t0 + l32;
-  if (tok < n_tok) {
-    OutT* dst = out + ((size_t)tok * n_h + head) * DH + wave * 32;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const floatx4 r = {acc_hi[4 * j] + acc_lo[4 * j], acc_hi[4 * j + 1] + acc_lo[4 * j + 1],
-                         acc_hi[4 * j + 2] + acc_lo[4 * j + 2], acc_hi[4 * j + 3] + acc_lo[4 * j + 3]};
-      if constexpr (sizeof(OutT) == 4) {
-        *(floatx4*)(dst + 8 * j + 4 * h) = r;
-      } else {
-        *(u32x2*)(dst + 8 * j + 4 * h) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      for (int i = 0; i < 8; ++i) {
+        const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
+        *(u32x4*)(sw + r * kUpRow + c8) = wv[i];
       }
+    } else {
+      __syncthreads();                 // the previous block's reads are done
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ch = tid + 512 * i, t = ch >> 7, c4 = (ch & 127) * 4;
+      u32x2 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x0 = v[i][2 * e], x1 = v[i][2 * e + 1];
+        const bf16x2 hb = bf16x2{(__bf16)x0, (__bf16)x1};
+        hi[e] = __builtin_bit_cast(uint32_t, hb);
+        lo[e] = pack_bf16x2(x0 - (float)hb[0], x1 - (float)hb[1]);
+      }
+      *(u32x2*)(sh + t * kUpRow + c4) = hi;
+      *(u32x2*)(sl + t * kUpRow + c4) = lo;
+    }
+    __syncthreads();
+
+    floatx4 acc_hi = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* pa = sw + (16 * mi + r16) * kUpRow + 8 * g;
+    const int bo = (16 * ni + r16) * kUpRow + 8 * g;
+#pragma unroll
+    for (int s = 0; s < DC / 32; ++s) {
+      const bf16x8 a = *(const bf16x8*)(pa + 32 * s);
+      const bf16x8 bh = *(const bf16x8*)(sh + bo + 32 * s);
+      const bf16x8 bl = *(const bf16x8*)(sl + bo + 32 * s);
+      acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc_hi, 0, 0, 0);
+      acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc_lo, 0, 0, 0);
+    }
+    // acc[e]: d_h row 64 half + 16 mi + 4 g + e, token t0 + 16 ni + r16
+    const int tok = t0 + 16 * ni + r16;
+    if (tok < n_tok) {
+      const floatx4 r = acc_hi + acc_lo;
+      OutT* dst = out + ((size_t)tok * n_h + head) * DH + 64 * half + 16 * mi + 4 * g;
+      if constexpr (sizeof(OutT) == 4)
+        *(floatx4*)dst = r;
+      else
+        *(u32x2*)dst = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
     }
   }
 }
@@ -531,12 +632,12 @@ hipError_t launch_up_proj(const mla_dims_t& d, bool fast, const float* latent,
                           const void* w_uv, void* out, bool out_f32, int n_tok,
                           hipStream_t st) {
   if (fast) {
-    const dim3 grid(d.n_heads, (n_tok + 31) / 32);
+    const dim3 grid(d.n_heads * 2);
     if (out_f32)
-      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(512), 0, st,
                          latent, (const uint16_t*)w_uv, (float*)out, n_tok, d.n_heads);
     else
-      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(up_proj_mfma_kernel<uint16_t>, grid, dim3(512), 0, st,
                          latent, (const uint16_t*)w_uv, (uint16_t*)out, n_tok, d.n_heads);
   } else {
     const size_t total = (size_t)n_tok * d.n_heads * d.d_head;
