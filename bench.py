@@ -29,6 +29,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 DEFAULT_WORKLOAD = "v2_b32_l4k_bf16"
 ATTN_PER_GRAPH = 20                     # attention calls captured per graph
+STEPS_PER_GRAPH = 10                    # decode steps captured per graph
 COPY_PROBE_BYTES = 512 * 2 ** 20        # calibration copy of the traffic probe
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 _CSRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc")
@@ -126,8 +127,8 @@ def cpu_baseline(w, gen, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
@@ -170,7 +171,32 @@ def main():
             fn()
         return g
 
-    step_graphs = [capture(lambda r=r: buf.step(replica=r)) for r in range(replicas)]
+    # A serving loop captures many launches per graph (a decode step of the
+    # whole model runs this layer once per layer), so the host-side cost of a
+    # graph launch is shared: STEPS_PER_GRAPH steps per graph, cache replicas
+    # round-robin.  n_steps(k) replays graphs for exactly k steps.
+    def steps_fn(first, n):
+        def fn():
+            for i in range(n):
+                buf.step(replica=(first + i) % replicas)
+        return fn
+
+    step_graphs = [capture(steps_fn(j * STEPS_PER_GRAPH, STEPS_PER_GRAPH))
+                   for j in range(replicas)]
+    tail_graphs = {}
+
+    def n_steps(k):
+        for j in range(k // STEPS_PER_GRAPH):
+            step_graphs[j % replicas].replay()
+        rem = k % STEPS_PER_GRAPH
+        if rem:
+            if rem not in tail_graphs:
+                tail_graphs[rem] = capture(steps_fn(0, rem))
+            tail_graphs[rem].replay()
+
+    if args.steps % STEPS_PER_GRAPH:
+        n_steps(args.steps % STEPS_PER_GRAPH)    # capture the tail graph now
+    torch.cuda.synchronize()
     # the attention call alone: ATTN_PER_GRAPH calls (replicas round-robin) per
     # graph, so the gap between graph launches is amortised and the per-call
     # time is the kernels' own (decode + combine)
@@ -196,8 +222,7 @@ def main():
                           "bytes_alg_per_launch": cache_b + io_b}), flush=True)
         return
 
-    for i in range(args.warmup):
-        step_graphs[i % replicas].replay()
+    n_steps(args.warmup)
     torch.cuda.synchronize()
 
     # ---- timed region: K whole steps
@@ -205,8 +230,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(args.steps):
-        step_graphs[i % replicas].replay()
+    n_steps(args.steps)
     e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -261,7 +285,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens,
                    "kv_len": w.kv_len or None, "n_heads": w.n_heads, "d_head": w.d_head,
                    "d_latent": w.d_latent, "d_rope": w.d_rope, "kv_dtype": w.kv_dtype,
-                   "layout": w.layout, "cache_replicas": replicas},
+                   "layout": w.layout, "cache_replicas": replicas,
+                   "steps_per_graph": STEPS_PER_GRAPH},
         "latent_cache_GBps": round(cache_b / attn_s / 1e9, 1),
         "attn_us": round(attn_ms * 1e3, 2),
         "step_us_events": round(ms_step_events * 1e3, 2),
