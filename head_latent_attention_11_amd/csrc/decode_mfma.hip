@@ -120,15 +120,42 @@ __device__ __forceinline__ floatx16 qk_tile(const uint8_t* kb, const bf16x8 (&q)
   return s;
 }
 
-__device__ __forceinline__ void pv_tile(const uint8_t* vb, const bf16x8 pf0, const bf16x8 pf1,
-                                        floatx16 (&o)[DC / 32]) {
-  const uint32_t ad = (uint32_t)(uintptr_t)vb;
-  asm volatile(MLA_ASM_PV_TILE
+// O^T[the wave's 128 dims, all 128 rows] += C^T P^T for one tile (vb: this
+// lane's transposed-read address in the tile's slot, including the wave's
+// dim offset; pb: this lane's address in the P^T fragment buffer).
+__device__ __forceinline__ void pvd_tile(const uint8_t* vb, const uint8_t* pb,
+                                         floatx16 (&o)[DC / 32]) {
+  const uint32_t ad = (uint32_t)(uintptr_t)vb, pa = (uint32_t)(uintptr_t)pb;
+  asm volatile(MLA_ASM_PVD_TILE
                : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
                  "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
                  "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
-               : "v"(ad), "v"(pf0), "v"(pf1)
-               : "memory", MLA_ASM_PV_CLOBBERS);
+               : "v"(ad), "v"(pa)
+               : "memory", MLA_ASM_PVD_CLOBBERS);
+}
+
+// The wave's P^T fragments of one tile (token halves 0 and 1, the B operands
+// of the PV product for its 32 rows) into the P buffer: fragment (row block
+// w, half k) at 1024 (2 w + k), 16 bytes per lane.
+__device__ __forceinline__ void put_p(uint8_t* s_p, int wave, int lane, const uint32_t (&pk)[8]) {
+  uint8_t* d = s_p + 2048 * wave + 16 * lane;
+  *(u32x4*)d = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  *(u32x4*)(d + 1024) = u32x4{pk[4], pk[5], pk[6], pk[7]};
+}
+
+// Score-row order inside a tile.  MFMA row m of the scores (the K operand
+// row read by lane m % 32) is tile row tile_row(m) = 16 (m/16) + (m/4)%4 +
+// 4 (m%4).  The transposed PV reads of a half-wave then cover four tile rows
+// p, p+4, p+8, p+12 (64 bytes each), which at the 1168-byte row pitch fall
+// in four disjoint quarters of the 64 LDS banks; the score-operand reads of
+// 16 lanes still cover 16 rows of distinct residues mod 16 (distinct bank
+// groups).  Score register r of a lane in half h (row m = 8(r/4) + 4h +
+// r%4) holds token tile_row(m).
+__device__ __forceinline__ int tile_row(int m) {
+  return 16 * (m >> 4) + ((m >> 2) & 3) + 4 * (m & 3);
+}
+__device__ __forceinline__ int reg_token(int r, int h) {
+  return tile_row(8 * (r >> 2) + 4 * h + (r & 3));
 }
 
 // LDS source offset mapping of a tile (rows at a pitch of 73 granules of 16
@@ -147,6 +174,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
   __shared__ float s_scale[NBUF][TILE];
   __shared__ int s_restart;
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[4 * 2 * 1024];   // P^T fragments
+  __shared__ float s_inv[ROWS_WG];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -156,7 +185,12 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   // work item -> (sequence, split, length): from the host's table when the
   // plan has few enough items, else located on the device
   int b, s_idx, L;
-  if (tab.n > 0) {
+  if (tab.uniform_len > 0) {           // every sequence has the same length
+    L = tab.uniform_len;
+    const int nsu = splits_of(L, a.num_splits, a.chunk);
+    b = item / nsu;
+    s_idx = item - b * nsu;
+  } else if (tab.n > 0) {
     const uint32_t e = tab.seq_split[item];
     b = e & 0xFFFFF;
     s_idx = e >> 20;
@@ -186,34 +220,6 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const int ntiles = (t_stage > t0) ? (t_stage - t0 + TILE - 1) / TILE : 0;
 
   const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
-
-  // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims).
-  // The wave's 32 rows are contiguous in memory (row = tau * n_h + head,
-  // query token b*T + tau): it copies them into ring slot `wave` at the tile
-  // row pitch with buffer loads that write LDS directly (each load 1 KB of
-  // contiguous memory), then reads its operands from there (the same
-  // conflict-free pattern as the K operand reads).
-  bf16x8 qf[D / 16];
-  {
-    const size_t r0 = (size_t)b * rows + rb * ROWS_WG + wave * 32;
-    const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs + r0 * (2 * D));
-    const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
-                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
-                       uint32_t(32 * 2 * D), 0x00020000u};
-    const uint32_t qlds = lds_ring + wave * TILE_BYTES;
-#pragma unroll
-    for (int n = 0; n < NLOADS; ++n)
-      asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(qlds), "v"(tile_src_offset(64 * n + lane)), "s"(qrs), "i"(1024 * n)
-                   : "memory");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint8_t* qsrc = &s_kv[wave][0] + l32 * LROW + 16 * h;
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qsrc + 32 * k);
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
-    __syncthreads();                    // every wave has its operands: the ring is free
-  }
 
   const uint8_t* cache = (const uint8_t*)a.cache;
   constexpr int ROWB = FP8 ? D : 2 * D;                   // bytes per cache row
@@ -307,12 +313,42 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   }
 
   // ---- per-lane LDS offsets of the MFMA operands
-  const int qk_off = l32 * LROW + 16 * h;                                  // + 32 k
-  const int pv_off = ((j >> 2) + 4 * h) * LROW + (16 * (g & 1) + 4 * (j & 3)) * 2;
+  const int qk_off = tile_row(l32) * LROW + 16 * h;                        // + 32 k
+  // transposed reads: + 256 w selects the wave's 128 latent dims
+  const int pv_off = (h + 4 * (j >> 2)) * LROW + (16 * (g & 1) + 4 * (j & 3)) * 2 + 256 * wave;
   // lane offsets of this wave's tile loads (the same for every tile)
   uint32_t voff[NLD];
 #pragma unroll
   for (int n = 0; n < NLD; ++n) voff[n] = MLA_VOFF(n);
+
+  // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims).
+  // The wave's 32 rows are contiguous in memory (row = tau * n_h + head,
+  // query token b*T + tau): it copies them into ring slot `wave` at the tile
+  // row pitch with buffer loads that write LDS directly (each load 1 KB of
+  // contiguous memory), then reads its operands from there (the same
+  // conflict-free pattern as the K operand reads).
+  bf16x8 qf[D / 16];
+  {
+    const size_t r0 = (size_t)b * rows + rb * ROWS_WG + wave * 32;
+    const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs + r0 * (2 * D));
+    const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
+                       uint32_t(32 * 2 * D), 0x00020000u};
+    const uint32_t qlds = lds_ring + wave * TILE_BYTES;
+#pragma unroll
+    for (int n = 0; n < NLOADS; ++n)
+      asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(qlds), "v"(tile_src_offset(64 * n + lane)), "s"(qrs), "i"(1024 * n)
+                   : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint8_t* qsrc = &s_kv[wave][0] + l32 * LROW + 16 * h;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qsrc + 32 * k);
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
+    __syncthreads();                    // every wave has its operands: the ring is free
+  }
+
 
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
@@ -352,11 +388,12 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
         if (ntiles > 1) MLA_WAIT_ONE_TILE_IN_FLIGHT();   // tile 0 landed
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        bf16x8 pf_prev = {}, pf_prev1 = {};
+        uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         for (int it = 0; it < ntiles; ++it) {
           const int ts = t0 + it * TILE;
           MLA_TILE_RSRC(ts + 2 * TILE, rs_n);
           const uint32_t lb_n = lds_ring + ((it + 2) & 3) * TILE_BYTES + 1024 * wave;
+          put_p(s_p, wave, lane, pk_prev);   // weights of tile it-1 (zero at step 0)
           floatx16 s_cur;
           {
             const uint32_t ad = (uint32_t)(uintptr_t)(s_kv[it & 3] + qk_off);
@@ -373,7 +410,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
                            "v"(voff[2]), "v"(voff[3]), "v"(voff[4])
                          : "memory", MLA_ASM_QK_CLOBBERS);
           }
-          // register r holds token 8*(r/4) + 4h + r%4.  The 32 rows of a
+          __syncthreads();                   // every wave's weights of tile it-1 are in
+          // register r holds token reg_token(r, h).  The 32 rows of a
           // wave share one query token, so the visibility limit is
           // wave-uniform and only a tile that crosses it is masked.
           float sv[16];
@@ -382,7 +420,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           if (ts + TILE - 1 > lim) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
+              if (ts + reg_token(r, h) > lim) sv[r] = kNegInf;
           }
           float mt;
           if (m_ref == kNegInf) {
@@ -398,9 +436,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           }
           const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
           const uint32_t vb = (uint32_t)(uintptr_t)(s_kv[(it > 0 ? it - 1 : 0) & 3] + pv_off);
+          const uint32_t pb = (uint32_t)(uintptr_t)(s_p + 16 * lane);
           uint32_t pk[8];
           float tmp;
-          asm volatile(MLA_ASM_PV_SOFTMAX_TILE_DMA
+          asm volatile(MLA_ASM_PVD_SOFTMAX_TILE_DMA
                        : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
                          "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
                          "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
@@ -410,24 +449,28 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
                          "+v"(sv[14]), "+v"(sv[15]), "=&v"(pk[0]), "=&v"(pk[1]), "=&v"(pk[2]),
                          "=&v"(pk[3]), "=&v"(pk[4]), "=&v"(pk[5]), "=&v"(pk[6]), "=&v"(pk[7]),
                          "=&v"(mt), "=&v"(tmp), "+v"(l_run)
-                       : "v"(vb), "v"(pf_prev), "v"(pf_prev1), "v"(neg_m), "v"(a.scale_log2),
+                       : "v"(vb), "v"(pb), "v"(neg_m), "v"(a.scale_log2),
                          "s"(rs_n), "s"(lb_n), "v"(voff[5]), "v"(voff[6]), "v"(voff[7]),
                          "v"(voff[8])
-                       : "memory", MLA_ASM_PV_CLOBBERS);
+                       : "memory", MLA_ASM_PVD_CLOBBERS);
           if (wave == 0)                         // the tile's 37th load
             asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :: "s"(lds_ring + ((it + 2) & 3) * TILE_BYTES), "v"(voff[NLD - 1]),
                             "s"(rs_n), "i"(1024 * 36) : "memory");
-          pf_prev = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-          pf_prev1 = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pk_prev[i] = pk[i];
           m_seen = fmaxf(m_seen, mt);
           if (mt > m_ref + 64.0f) s_restart = 1;
           MLA_WAIT_ONE_TILE_IN_FLIGHT();     // tile it+1 landed (it+2 may fly)
           __syncthreads();
-          restart = s_restart;               // uniform: read after the barrier
+          restart = __builtin_amdgcn_readfirstlane(s_restart);   // uniform: read after the barrier
           if (restart) break;
         }
-        if (!restart) pv_tile(s_kv[(ntiles - 1) & 3] + pv_off, pf_prev, pf_prev1, o);
+        if (!restart) {
+          put_p(s_p, wave, lane, pk_prev);
+          __syncthreads();
+          pvd_tile(s_kv[(ntiles - 1) & 3] + pv_off, s_p + 16 * lane, o);
+        }
       }
     } else {
       // Step it works on tile it in ring slot it & 3 while tile it+2 is
@@ -439,17 +482,17 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           const uint8_t* tile = s_kv[it & 3];
           MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
           const floatx16 s_cur = qk_tile(tile + qk_off, qf);
-          // softmax of tile it: register r holds token 8*(r/4) + 4h + r%4.
+          // softmax of tile it: register r holds token reg_token(r, h).
           // The 32 rows of a wave share one query token, so the visibility
           // limit is wave-uniform and only a tile that crosses it is masked.
           float sv[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            sv[r] = s_cur[r] * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)];
+            sv[r] = s_cur[r] * s_scale[it & 3][reg_token(r, h)];
           if (ts + TILE - 1 > lim) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (ts + 8 * (r >> 2) + 4 * h + (r & 3) > lim) sv[r] = kNegInf;
+              if (ts + reg_token(r, h) > lim) sv[r] = kNegInf;
           }
           // max of the raw scores over the row's 32 tokens (lane pair l, l^32)
           float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
@@ -471,10 +514,16 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #pragma clang fp contract(off)
             const float p = __builtin_amdgcn_exp2f(sv[r] * a.scale_log2 - m_use);
             l_run += p;
-            const __bf16 pb = (__bf16)(p * s_scale[it & 3][8 * (r >> 2) + 4 * h + (r & 3)]);
+            const __bf16 pb = (__bf16)(p * s_scale[it & 3][reg_token(r, h)]);
             if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
           }
-          pv_tile(tile + pv_off, pf0, pf1, o);
+          {
+            const u32x4 p0 = __builtin_bit_cast(u32x4, pf0), p1 = __builtin_bit_cast(u32x4, pf1);
+            const uint32_t pk[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            put_p(s_p, wave, lane, pk);
+          }
+          __syncthreads();                   // every wave's weights of tile it are in
+          pvd_tile(tile + pv_off, s_p + 16 * lane, o);
           MLA_STORE_FP8_TILE((it + 2) & 3);
           __syncthreads();
           restart = s_restart;               // uniform: read after the barrier
@@ -497,57 +546,82 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #undef MLA_VOFF
 
   // ---- normalise and write (the final output, or this split's partial).
-  // O^T sits in the MFMA layout (lane: one row, 4-dim pieces); each wave
-  // stages its 32 rows in LDS and writes them back as whole rows, so every
-  // store instruction covers 1 KB of contiguous memory.  The wave's rows are
-  // consecutive in the output (row = tau * n_h + head).
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile loads past the end still write LDS
-  __syncthreads();                                   // every wave is done with the ring
+  // Wave w holds O^T for its 128 latent dims and all 128 rows (block
+  // 4 db + rb: dims 128 w + 32 db + 8 (r/4) + 4h + r%4 in register r, row
+  // 32 rb + l32); each row's normaliser is with the wave that owns the row.
+  // Each wave stages its part of the rows in LDS and writes it back with
+  // 16-byte stores over runs of 256 (bf16) or 512 (fp32) contiguous bytes.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const float lse = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
-  constexpr int EROW = 1040;                         // staged row: 1 KB + 16 B padding
-  static_assert(4 * 32 * EROW <= NBUF * TILE_BYTES, "output staging must fit the ring");
-  uint8_t* stg = &s_kv[0][0] + wave * (32 * EROW);
-  const int row0 = rb * ROWS_WG + wave * 32;         // first row of this wave
+  if (h == 0) s_inv[32 * wave + l32] = inv;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile loads past the end still write LDS
+  __syncthreads();                                   // the ring is free; s_inv is in
+  float inv_rb[4];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) inv_rb[r4] = s_inv[32 * r4 + l32];
+  const int row0 = rb * ROWS_WG;                     // first row of the workgroup
+  const int own0 = row0 + 32 * wave;                 // first row this wave owns
   if (ns == 1) {
+    // fp32 rows: 512 bytes per row from this wave, two passes of 64 rows
+    constexpr int SROW = 528;
+    uint8_t* stg = &s_kv[0][0] + wave * (64 * SROW);
     const size_t g0 = (size_t)b * rows + row0;
-    uint8_t* dst = (uint8_t*)(a.out_latent + g0 * DC);
+    uint8_t* dst = (uint8_t*)(a.out_latent + g0 * DC) + 512 * wave;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {                    // fp32 rows: two halves of 256 dims
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const int r4 = 2 * p + r2;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const floatx16& ob = o[8 * p + db];
-          const floatx4 v = {ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]};
-          *(floatx4*)(stg + l32 * EROW + 4 * (32 * db + 8 * jj + 4 * h)) = v * inv;
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const floatx16& ob = o[4 * db + r4];
+            const floatx4 v = {ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]};
+            *(floatx4*)(stg + (32 * r2 + l32) * SROW + 4 * (32 * db + 8 * jj + 4 * h)) = v * inv_rb[r4];
+          }
         }
       }
+      // 64 rows x 512 bytes: one store covers two rows
 #pragma unroll
-      for (int r = 0; r < 32; ++r)
-        *(floatx4*)(dst + (size_t)r * (4 * DC) + 1024 * p + 16 * lane) =
-            *(const floatx4*)(stg + r * EROW + 16 * lane);
-    }
-    if (h == 0) a.out_lse[g0 + l32] = lse;
-  } else {
-    // split partial, normalised, stored as bf16 (combined in fp32)
-    const size_t g0 = (size_t)item * rows + row0;
-    uint8_t* dst = (uint8_t*)a.part_o + g0 * (2 * DC);
-#pragma unroll
-    for (int db = 0; db < DC / 32; ++db) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bf16x2 p01 = {(__bf16)(o[db][4 * jj] * inv), (__bf16)(o[db][4 * jj + 1] * inv)};
-        const bf16x2 p23 = {(__bf16)(o[db][4 * jj + 2] * inv), (__bf16)(o[db][4 * jj + 3] * inv)};
-        *(u32x2*)(stg + l32 * EROW + 2 * (32 * db + 8 * jj + 4 * h)) =
-            u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+      for (int n = 0; n < 32; ++n) {
+        const int r = 2 * n + (lane >> 5);
+        *(floatx4*)(dst + (size_t)(64 * p + r) * (4 * DC) + 16 * (lane & 31)) =
+            *(const floatx4*)(stg + r * SROW + 16 * (lane & 31));
       }
     }
+    if (h == 0) a.out_lse[(size_t)b * rows + own0 + l32] = lse;
+  } else {
+    // split partial, normalised, stored as bf16 (combined in fp32): 256
+    // bytes per row from this wave, all 128 rows at once
+    constexpr int SROW = 272;
+    uint8_t* stg = &s_kv[0][0] + wave * (128 * SROW);
+    const size_t g0 = (size_t)item * rows + row0;
+    uint8_t* dst = (uint8_t*)a.part_o + g0 * (2 * DC) + 256 * wave;
 #pragma unroll
-    for (int r = 0; r < 32; ++r)
-      *(u32x4*)(dst + (size_t)r * (2 * DC) + 16 * lane) = *(const u32x4*)(stg + r * EROW + 16 * lane);
-    if (h == 0) a.part_lse[g0 + l32] = lse;
+    for (int r4 = 0; r4 < 4; ++r4) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const floatx16& ob = o[4 * db + r4];
+          const float w = inv_rb[r4];
+          const bf16x2 p01 = {(__bf16)(ob[4 * jj] * w), (__bf16)(ob[4 * jj + 1] * w)};
+          const bf16x2 p23 = {(__bf16)(ob[4 * jj + 2] * w), (__bf16)(ob[4 * jj + 3] * w)};
+          *(u32x2*)(stg + (32 * r4 + l32) * SROW + 2 * (32 * db + 8 * jj + 4 * h)) =
+              u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+        }
+      }
+    }
+    // 128 rows x 256 bytes: one store covers four rows
+#pragma unroll
+    for (int n = 0; n < 32; ++n) {
+      const int r = 4 * n + (lane >> 4);
+      *(u32x4*)(dst + (size_t)r * (2 * DC) + 16 * (lane & 15)) =
+          *(const u32x4*)(stg + r * SROW + 16 * (lane & 15));
+    }
+    if (h == 0) a.part_lse[(size_t)item * rows + own0 + l32] = lse;
   }
 }
 

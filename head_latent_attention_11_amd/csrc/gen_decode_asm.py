@@ -21,16 +21,16 @@ LROW = 1168          # LDS bytes per token row
 QK_STEPS = 36        # 576 / 16 dims per v_mfma_f32_32x32x16_bf16
 QK_AHEAD = 6         # reads in flight ahead of the current MFMA
 QK_BUFS = 8
-PV_STEPS = 32        # 16 latent blocks x 2 token halves
-PV_AHEAD = 4
-PV_BUFS = 6
+PVD_AHEAD = 2        # C^T fragments read ahead (each feeds 4 MFMAs)
+PVD_NVBUF = 4        # C^T fragment buffers
+PVD_LEAD = 8         # softmax instructions before the first PV MFMA
 QK_DMA = 5           # tile loads interleaved with the QK sequence
 PV_DMA = 4           # ... and with the PV + softmax sequence (9 per wave)
 NOPS = "s_nop 7\\n\\ts_nop 7\\n\\t"   # 16 wait states: XDL result -> VALU read
 
 
 QK_TMP = 224         # first VGPR of the QK operand buffers (8 x 4)
-PV_TMP = 232         # first VGPR of the PV operand buffers (6 x 4)
+PVD_VBUF = 224 - 4 * PVD_NVBUF   # first VGPR of the C^T fragment buffers
 
 
 def quad(base, i, nbuf):
@@ -67,35 +67,6 @@ def qk(with_dma=False):
         if with_dma and k % 4 == 3 and k // 4 < QK_DMA:
             n = k // 4
             out += dma(n, "%38", "%39", f"%{40 + n}")
-    return out
-
-
-def pv_reads(m, base):
-    """The two transposed reads of PV step m (32-dim block m // 2, token
-    half m % 2) relative to the base address operand."""
-    db, ks = m // 2, m % 2
-    r = quad(PV_TMP, m, PV_BUFS)
-    lo = (16 * ks) * LROW + 64 * db
-    hi = (16 * ks + 8) * LROW + 64 * db
-    return [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], {base} offset:{lo}",
-            f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], {base} offset:{hi}"]
-
-
-def pv():
-    # operands: %0..%15 O blocks (accumulators), %16 base address, %17 / %18
-    # probabilities of token halves 0 / 1; operand buffers are the fixed
-    # VGPRs v[232:255]
-    out = []
-    for m in range(PV_AHEAD):
-        out += pv_reads(m, "%16")
-    for m in range(PV_STEPS):
-        n = m + PV_AHEAD
-        if n < PV_STEPS:
-            out += pv_reads(n, "%16")
-        out.append(f"s_waitcnt lgkmcnt({2 * min(PV_AHEAD, PV_STEPS - 1 - m)})")
-        db, ks = m // 2, m % 2
-        r = quad(PV_TMP, m, PV_BUFS)
-        out.append(f"v_mfma_f32_32x32x16_bf16 %{db}, v[{r}:{r + 3}], %{17 + ks}, %{db}")
     return out
 
 
@@ -145,37 +116,86 @@ def softmax_valu(S, PK, MT, TMP, LRUN, NEGM, SCALE):
     return max_valu(S, MT, TMP, SCALE) + weights_valu(S, PK, LRUN, NEGM, SCALE)
 
 
-def pv_softmax(with_dma=False):
-    """PV of the previous tile interleaved with the softmax of the current.
+def pvd(with_softmax=False, with_dma=False):
+    """PV product of one tile for this wave's 128 latent dims and all 128
+    query rows of the workgroup: O^T[dims, rows] += C^T[dims, tok] P^T[tok,
+    rows], 32 MFMAs (4 dim blocks x 4 row blocks x 2 token halves).  The
+    weights of every row block come from the LDS P buffer (written there by
+    the waves that own the rows); each weight fragment is read once and used
+    for 4 MFMAs, each transposed C^T fragment read once and used for 4.
+    with_softmax: the softmax of the current tile is interleaved (two vector
+    instructions per MFMA).
 
-    operands: %0..%15 O blocks (accumulators), %16..%31 the current tile's
-    scores s_0..s_15 (in; overwritten), %32..%39 the current tile's packed
-    bf16 weight pairs (out), %40 its scaled max (out), %41 a temporary,
-    %42 the running normaliser (in/out), %43 base address of the previous
-    tile's transposed reads, %44 / %45 the previous tile's weights (token
-    halves 0 / 1), %46 -m_ref, %47 the scale (log2 domain).  with_dma:
-    %48 buffer descriptor, %49 LDS base of this wave's loads, %50..%53 lane
-    offsets of loads 5..8 (one load after every eighth MFMA).  Operand
-    buffers: v[232:255].
+    operands: %0..%15 O blocks (block 4 db + rb: dims 32 db of the wave's
+    128, rows 32 rb), %16..%31 the current tile's scores s_0..s_15 (in;
+    overwritten), %32..%39 its packed bf16 weight pairs (out), %40 its
+    scaled max (out), %41 a temporary, %42 the running normaliser (in/out),
+    %43 base address of this lane's transposed reads (slot of the previous
+    tile + the wave's dim offset), %44 this lane's P fragment address, %45
+    -m_ref, %46 the scale (log2 domain).  with_dma: %47 buffer descriptor,
+    %48 LDS base of this wave's loads, %49..%52 lane offsets of loads 5..8.
+    Without the softmax only %0..%15, %16 (= transposed-read base) and %17
+    (= P fragment address) are used.
+    Fixed registers: P fragments v[224:255], C^T fragment buffers
+    v[PVD_VBUF:223].
     """
-    valu = softmax_valu(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
-                        "%40", "%41", "%42", "%46", "%47")
-    out = []
-    for m in range(PV_AHEAD):
-        out += pv_reads(m, "%43")
+    vbase, pbase = ("%43", "%44") if with_softmax else ("%16", "%17")
+    valu = []
+    if with_softmax:
+        valu = softmax_valu(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
+                            "%40", "%41", "%42", "%45", "%46")
+    out, issued = [], []
+
+    def read(name, instrs):
+        for x in instrs:
+            out.append(x)
+            issued.append(name)
+
+    def wait_for(names):
+        last = max(i for i, n in enumerate(issued) if n in names)
+        out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
+
+    def pfrag(rb, ks):
+        return 224 + 4 * (4 * ks + rb)
+
+    def vbuf(g):
+        return PVD_VBUF + 4 * (g % PVD_NVBUF)
+
+    def vread(g):
+        ks, db = g // 4, g % 4
+        r = vbuf(g)
+        lo = (16 * ks) * LROW + 64 * db
+        hi = (16 * ks + 2) * LROW + 64 * db
+        read(("V", g), [f"ds_read_b64_tr_b16 v[{r}:{r + 1}], {vbase} offset:{lo}",
+                        f"ds_read_b64_tr_b16 v[{r + 2}:{r + 3}], {vbase} offset:{hi}"])
+
+    def pread(rb, ks):
+        r = pfrag(rb, ks)
+        read(("P", rb, ks), [f"ds_read_b128 v[{r}:{r + 3}], {pbase} offset:{1024 * (2 * rb + ks)}"])
+
+    for rb in range(4):
+        pread(rb, 0)
+    for g in range(PVD_AHEAD):
+        vread(g)
+    for rb in range(4):
+        pread(rb, 1)
     vi = 0
-    for m in range(PV_STEPS):
-        n = m + PV_AHEAD
-        if n < PV_STEPS:
-            out += pv_reads(n, "%43")
-        out.append(f"s_waitcnt lgkmcnt({2 * min(PV_AHEAD, PV_STEPS - 1 - m)})")
-        db, ks = m // 2, m % 2
-        r = quad(PV_TMP, m, PV_BUFS)
-        out.append(f"v_mfma_f32_32x32x16_bf16 %{db}, v[{r}:{r + 3}], %{44 + ks}, %{db}")
-        if with_dma and m % 8 == 3 and m // 8 < PV_DMA:
-            k = m // 8
-            out += dma(QK_DMA + k, "%48", "%49", f"%{50 + k}")
-        take = 2 if m < PV_STEPS - 1 else len(valu) - vi
+    for _ in range(PVD_LEAD):                 # independent softmax work first
+        if vi < len(valu):
+            out.append(valu[vi])
+            vi += 1
+    for i in range(32):
+        ks, db, rb = i // 16, (i // 4) % 4, i % 4
+        g = i // 4
+        if i % 4 == 0 and g + PVD_AHEAD < 8:
+            vread(g + PVD_AHEAD)
+        wait_for({("V", g), ("P", rb, ks)})
+        out.append(f"v_mfma_f32_32x32x16_bf16 %{4 * db + rb}, v[{vbuf(g)}:{vbuf(g) + 3}], "
+                   f"v[{pfrag(rb, ks)}:{pfrag(rb, ks) + 3}], %{4 * db + rb}")
+        if with_dma and i % 8 == 3 and i // 8 < PV_DMA:
+            k = i // 8
+            out += dma(QK_DMA + k, "%47", "%48", f"%{49 + k}")
+        take = 2 if i < 31 else len(valu) - vi
         for _ in range(take):
             if vi < len(valu):
                 out.append(valu[vi])
@@ -204,8 +224,8 @@ if __name__ == "__main__":
     txt.append(emit("MLA_ASM_QK_TILE", qk()))
     txt.append(emit("MLA_ASM_QK_TILE_DMA", qk(True)))
     txt.append(f"#define MLA_ASM_QK_CLOBBERS {clobbers(QK_TMP, 32)}\n")
-    txt.append(emit("MLA_ASM_PV_TILE", pv()))
-    txt.append(emit("MLA_ASM_PV_SOFTMAX_TILE_DMA", pv_softmax(True)))
-    txt.append(f"#define MLA_ASM_PV_CLOBBERS {clobbers(PV_TMP, 24)}\n")
+    txt.append(emit("MLA_ASM_PVD_TILE", pvd()))
+    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_DMA", pvd(True, True)))
+    txt.append(f"#define MLA_ASM_PVD_CLOBBERS {clobbers(PVD_VBUF, 256 - PVD_VBUF)}\n")
     txt.append(emit_plain("MLA_ASM_SOFTMAX_MAX", softmax_max()))
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))

@@ -266,7 +266,13 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   if (fast_decode(dims, q_tokens)) {
     ItemTable tab;
     tab.n = 0;
-    if (p.n_items <= kItemTable && batch < (1 << 20)) {
+    tab.uniform_len = 0;
+    bool uniform = seq_lens_host[0] > 0;
+    for (int b = 1; b < batch && uniform; ++b) uniform = seq_lens_host[b] == seq_lens_host[0];
+    if (uniform &&
+        (int64_t)batch * splits_of(seq_lens_host[0], p.num_splits, p.chunk) == p.n_items) {
+      tab.uniform_len = seq_lens_host[0];
+    } else if (p.n_items <= kItemTable && batch < (1 << 20)) {
       int n = 0;
       for (int b = 0; b < batch; ++b) {
         const int ns = splits_of(seq_lens_host[b], p.num_splits, p.chunk);

@@ -125,10 +125,12 @@ struct DecodeArgs {
   float scale_log2;           // softmax scale * log2(e)
 };
 
-// Work items of a plan, listed by the host when there are at most
-// kItemTable of them (passed by value; n = 0: the kernel locates items).
+// Work items of a plan (passed by value).  uniform_len > 0: every sequence
+// has this length and item = b * splits + s.  Else the host lists the items
+// when there are at most kItemTable of them; n = 0: the kernel locates them.
 constexpr int kItemTable = 256;
 struct ItemTable {
+  int32_t uniform_len;
   int32_t n;
   uint32_t seq_split[kItemTable];   // sequence | split << 20
   int32_t len[kItemTable];          // the sequence's length
