@@ -14,15 +14,17 @@
 //     of 4 waves handles 128 query rows (row = tau * n_h + head) of an item.
 //     Row blocks of the same item are placed on the same XCD so that the
 //     chunk is fetched from HBM once and re-read from that XCD's L2.
-//   * Wave w owns 32 rows.  Its absorbed queries live in VGPRs for the whole
-//     item (36 MFMA operands of 8 bf16 = 144 VGPRs) and its output
-//     accumulator O^T (512 x 32 fp32 = 256 registers) stays in the matrix
-//     accumulators.
-//   * KV tiles of 32 tokens go through a 3-buffer LDS ring (rows padded to
-//     1168 bytes so the 16-byte operand reads of 16 consecutive tokens hit
-//     distinct banks).  While tile i+2 streams in, a wave takes the softmax
-//     of tile i, the scores of tile i+1 and the PV product of tile i, so the
-//     matrix pipe has independent work while the softmax runs.
+//   * For the scores, wave w owns rows 32w .. 32w+31: its absorbed queries
+//     live in VGPRs for the whole item (36 MFMA operands of 8 bf16 = 144
+//     VGPRs).  For the PV product, wave w owns latent dims 128w .. 128w+127
+//     of all 128 rows: its accumulator O^T (128 x 128 fp32 = 256 registers)
+//     stays in the matrix accumulators, and the softmax weights of every row
+//     block reach it through an 8 KB LDS buffer.
+//   * KV tiles of 32 tokens go through a 4-slot LDS ring (rows padded to
+//     1168 bytes so the 16-byte operand reads of 16 token rows of distinct
+//     residues mod 16 hit distinct banks).  Step i takes the scores of tile
+//     i, then the PV product of tile i-1 interleaved with the softmax of
+//     tile i, while tiles i+1 and i+2 stream in.
 //     bf16 tiles move HBM -> LDS with buffer loads that write LDS directly
 //     (no VGPR staging); a load range that ends at the last valid token makes
 //     the hardware write zeros for masked tokens, so they enter the PV
@@ -30,15 +32,15 @@
 //     through VGPRs; the per-token scale multiplies the score and is folded
 //     into P for the PV product, so the fp8 values enter the bf16 MFMA
 //     exactly.
-//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one head's 16 token scores
-//     in each lane: the per-head max and sum need no cross-lane reduction
-//     except with the partner lane (lane ^ 32).  The probability registers
-//     are then already in the B-operand layout of O^T += C^T P^T (the token
-//     order inside the K dimension is chosen to match the score layout), and
-//     the A operand C^T comes from the transposing LDS read
-//     (ds_read_b64_tr_b16: in each 16-lane group, lane i receives element
-//     i%4 of the 8-byte chunks addressed by lanes 4k + i/4, k = 0..3, i.e.
-//     four token rows of 16 latent dims come back as 16 dims of 4 tokens).
+//   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one row's 16 token scores
+//     in each lane: the per-row max and sum need no cross-lane reduction
+//     except with the partner lane (lane ^ 32).  The packed weights are then
+//     already in the B-operand layout of O^T += C^T P^T (the token order
+//     inside the K dimension is chosen to match the score layout), and the A
+//     operand C^T comes from the transposing LDS read (ds_read_b64_tr_b16: in
+//     each 16-lane group, lane i receives element i%4 of the 8-byte chunks
+//     addressed by lanes 4k + i/4, k = 0..3, i.e. four token rows of 16
+//     latent dims come back as 16 dims of 4 tokens).
 //   * Softmax in the log2 domain against a per-row reference m_ref instead
 //     of a running max: m_ref is the max of the first tile in which the row
 //     sees a token, and p = 2^(s - m_ref) is accumulated without rescaling
