@@ -66,7 +66,10 @@ constexpr int NLOADS = 37;               // direct loads of 64 x 16 B per tile
 constexpr int TILE_BYTES = NLOADS * 1024;
 constexpr int NLD = 10;                  // loads per wave per tile (wave 0: 10, others: 9)
 constexpr int NCH = 72;                  // 16-byte chunks per bf16 row
-constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte staging chunks per thread (9)
+constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte chunks per thread (9)
+constexpr int RAW8 = 18944;              // fp8: raw tile (18 KB) at this offset of its slot
+constexpr int SCL8 = 37376;              // fp8: the tile's 32 token scales, end of the slot
+constexpr int NLD8 = TILE * D / 1024;    // fp8: 1 KB loads per raw tile (18)
 constexpr uint32_t kOOB = 0x40000000u;   // buffer offset past any valid range
 constexpr float kNegInf = -INFINITY;
 }  // namespace
@@ -174,7 +177,7 @@ template <bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
-  __shared__ float s_scale[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) float s_scale[NBUF][TILE];
   __shared__ int s_restart;
   __shared__ __attribute__((aligned(16))) uint8_t s_p[4 * 2 * 1024];   // P^T fragments
   __shared__ float s_inv[ROWS_WG];
@@ -241,7 +244,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const int qbase = 64 * wave + lane;
 #define MLA_VOFF(n_) tile_src_offset(qbase + 256 * (n_))
   u32x2 stg8[FP8 ? NSTG8 : 1];
-  float stg_scale = 0.f;
+  const uint32_t lane16 = 16 * lane;                      // fp8: lane offset of raw loads
 
   // Issue the loads of the tile starting at token ts into ring slot buf.  A
   // tile never crosses a page (ts is a multiple of 32, pages hold 64 tokens).
@@ -275,21 +278,44 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
                      :: "s"(lds_ring + (buf_) * TILE_BYTES + 1024 * 36),                 \
                         "v"(MLA_VOFF(NLD - 1)), "s"(rs__) : "memory");                   \
     } else {                                                                             \
-      const __amdgpu_buffer_rsrc_t rb__ = __builtin_amdgcn_make_buffer_rsrc(             \
-          (void*)(cache + (size_t)r0__ * ROWB), (short)0, nv__ * ROWB, 0x00020000);      \
-      _Pragma("unroll") for (int i = 0; i < NSTG8; ++i)                                  \
-        stg8[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rb__, 8 * tid, 2048 * i, 0)); \
-      if (tid < TILE) stg_scale = (tid < nv__) ? a.kv_scale[r0__ + tid] : 0.f;           \
+      /* raw fp8 rows (contiguous) into the slot's upper part; wave w issues */          \
+      /* loads w, w+4, ...; wave 3 also the 32 token scales (128 bytes) */                \
+      const uint32_t lb__ = lds_ring + (buf_) * TILE_BYTES + RAW8 + 1024 * wave;         \
+      _Pragma("unroll") for (int k = 0; k < (NLD8 + 3) / 4; ++k)                         \
+        if (wave + 4 * k < NLD8)                                                         \
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"     \
+                       :: "s"(lb__ + 4096 * k), "v"(lane16), "s"(rs__),                  \
+                          "s"(__builtin_amdgcn_readfirstlane(1024 * (wave + 4 * k))) : "memory"); \
+      if (wave == 3) {                                                                   \
+        const uint64_t sa__ = (uint64_t)(a.kv_scale + r0__);                             \
+        const u32x4 ss__ = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa__),    \
+                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa__ >> 32)) & 0xFFFFu, \
+                            (uint32_t)__builtin_amdgcn_readfirstlane(nv__ * 4), 0x00020000u}; \
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"          \
+                     :: "s"(lds_ring + (buf_) * TILE_BYTES + SCL8),                      \
+                        "v"(uint32_t(lane < TILE ? 4 * lane : kOOB)), "s"(ss__) : "memory"); \
+      }                                                                                  \
     }                                                                                    \
   } while (0)
-  // fp8: decode the staged registers into ring slot buf
-#define MLA_STORE_FP8_TILE(buf_)                                                           \
+  // fp8: this thread's raw chunks of the tile in slot buf (8 bytes each)
+#define MLA_READ_RAW8(buf_)                                                                \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NSTG8; ++i)                                    \
+      stg8[i] = *(const u32x2*)(&s_kv[(buf_)][RAW8 + 8 * (tid + 256 * i)]);              \
+  } while (0)
+  // fp8: decode them into the slot's bf16 rows (every wave's raw reads are
+  // done: a barrier separates the two) and put the token scales in
+  // score-register order (a masked token's zero scale becomes 1)
+#define MLA_DECODE8(buf_)                                                                  \
   do {                                                                                   \
     _Pragma("unroll") for (int i = 0; i < NSTG8; ++i) {                                  \
       const int ci = tid + 256 * i;                                                      \
       *(u32x4*)(&s_kv[(buf_)][16 * ci + 16 * (ci / NCH)]) = fp8x8_to_bf16x8(stg8[i]);    \
     }                                                                                    \
-    if (tid < TILE) s_scale[(buf_)][tid] = stg_scale;                                    \
+    if (tid < TILE) {                                                                    \
+      const float sc = *(const float*)(&s_kv[(buf_)][SCL8 + 4 * reg_token(tid & 15, tid >> 4)]); \
+      s_scale[(buf_)][tid] = (sc == 0.f) ? 1.f : sc;                                     \
+    }                                                                                    \
   } while (0)
   // bf16: wait until at most one tile's loads of this wave are in flight
 #define MLA_WAIT_ONE_TILE_IN_FLIGHT()                                                      \
@@ -361,10 +387,13 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   do {                                                                                   \
     if (ntiles > 0) {                                                                    \
       MLA_ISSUE_TILE(t0, 0);                                                             \
-      if constexpr (FP8) MLA_STORE_FP8_TILE(0);                                          \
-      if (ntiles > 1) {                                                                  \
-        MLA_ISSUE_TILE(t0 + TILE, 1);                                                    \
-        if constexpr (FP8) MLA_STORE_FP8_TILE(1);                                        \
+      if (ntiles > 1) MLA_ISSUE_TILE(t0 + TILE, 1);                                      \
+      if constexpr (FP8) {            /* tile 0 decoded now, tile 1 in step 0 */         \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                 \
+        __syncthreads();                                                                 \
+        MLA_READ_RAW8(0);                                                                \
+        __syncthreads();                                                                 \
+        MLA_DECODE8(0);                                                                  \
       }                                                                                  \
     }                                                                                    \
   } while (0)
@@ -475,61 +504,77 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
         }
       }
     } else {
-      // Step it works on tile it in ring slot it & 3 while tile it+2 is
-      // staged through VGPRs.
+      // The same step as for bf16.  Raw fp8 tiles are copied into the upper
+      // part of their ring slot; tile it+1 (copied during step it-1) is read
+      // at the start of step it and decoded in place after its first barrier,
+      // while tile it+2 is copied.  The token scales are applied in the
+      // softmax: the scores are multiplied by them first, the PV weights
+      // after it.  s_scale holds a tile's 32 scales in score-register order
+      // (16 per lane half).
       if (ntiles > 0) {
         __syncthreads();
+        uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         for (int it = 0; it < ntiles; ++it) {
           const int ts = t0 + it * TILE;
-          const uint8_t* tile = s_kv[it & 3];
+          MLA_READ_RAW8((it + 1) & 3);
           MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
-          const floatx16 s_cur = qk_tile(tile + qk_off, qf);
-          // softmax of tile it: register r holds token reg_token(r, h).
-          // The 32 rows of a wave share one query token, so the visibility
-          // limit is wave-uniform and only a tile that crosses it is masked.
-          float sv[16];
+          put_p(s_p, wave, lane, pk_prev);   // weights of tile it-1 (zero at step 0)
+          const floatx16 s_cur = qk_tile(s_kv[it & 3] + qk_off, qf);
+          __syncthreads();                   // weights of tile it-1 in; raw tile it+1 read
+          MLA_DECODE8((it + 1) & 3);
+          const float* kvp = &s_scale[it & 3][16 * h];   // this lane's token scales
+          float sv[16];                      // raw scores (scaled in the sequence)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sv[r] = s_cur[r] * s_scale[it & 3][reg_token(r, h)];
+          for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
           if (ts + TILE - 1 > lim) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (ts + reg_token(r, h) > lim) sv[r] = kNegInf;
           }
-          // max of the raw scores over the row's 32 tokens (lane pair l, l^32)
-          float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                               fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-          mx = pair_max32(mx);
-          const float mt = mx * a.scale_log2;            // log2 domain (scale > 0)
-          m_seen = fmaxf(m_seen, mt);
-          if (m_ref == kNegInf) m_ref = mt;          // O and l are still zero here
-          if (mt > m_ref + 64.0f) s_restart = 1;
-          const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-          bf16x8 pf0, pf1;
+          float mt;
+          if (m_ref == kNegInf) {
+            float tmp0, sc[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // product rounded before the subtraction (no contraction), as
-            // in m_ref: the maximum score gives exactly 2^0, so an L = 1 row
-            // returns its value exactly
-#pragma clang fp contract(off)
-            const float p = __builtin_amdgcn_exp2f(sv[r] * a.scale_log2 - m_use);
-            l_run += p;
-            const __bf16 pb = (__bf16)(p * s_scale[it & 3][reg_token(r, h)]);
-            if (r < 8) pf0[r] = pb; else pf1[r - 8] = pb;
+            for (int r = 0; r < 16; ++r) sc[r] = sv[r] * kvp[r];   // as in the sequence
+            asm volatile(MLA_ASM_SOFTMAX_MAX
+                         : "=&v"(mt), "=&v"(tmp0)
+                         : "v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]), "v"(sc[4]),
+                           "v"(sc[5]), "v"(sc[6]), "v"(sc[7]), "v"(sc[8]), "v"(sc[9]),
+                           "v"(sc[10]), "v"(sc[11]), "v"(sc[12]), "v"(sc[13]), "v"(sc[14]),
+                           "v"(sc[15]), "v"(a.scale_log2));
+            m_ref = mt;                          // O and l are still zero here
           }
-          {
-            const u32x4 p0 = __builtin_bit_cast(u32x4, pf0), p1 = __builtin_bit_cast(u32x4, pf1);
-            const uint32_t pk[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            put_p(s_p, wave, lane, pk);
-          }
-          __syncthreads();                   // every wave's weights of tile it are in
-          pvd_tile(tile + pv_off, s_p + 16 * lane, o);
-          MLA_STORE_FP8_TILE((it + 2) & 3);
+          const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+          const uint32_t vb = (uint32_t)(uintptr_t)(s_kv[(it > 0 ? it - 1 : 0) & 3] + pv_off);
+          const uint32_t pb = (uint32_t)(uintptr_t)(s_p + 16 * lane);
+          const uint32_t kb = (uint32_t)(uintptr_t)kvp;
+          uint32_t pk[8];
+          float tmp;
+          asm volatile(MLA_ASM_PVD_SOFTMAX_TILE_FP8
+                       : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
+                         "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
+                         "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
+                         "+a"(o[15]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3]),
+                         "+v"(sv[4]), "+v"(sv[5]), "+v"(sv[6]), "+v"(sv[7]), "+v"(sv[8]),
+                         "+v"(sv[9]), "+v"(sv[10]), "+v"(sv[11]), "+v"(sv[12]), "+v"(sv[13]),
+                         "+v"(sv[14]), "+v"(sv[15]), "=&v"(pk[0]), "=&v"(pk[1]), "=&v"(pk[2]),
+                         "=&v"(pk[3]), "=&v"(pk[4]), "=&v"(pk[5]), "=&v"(pk[6]), "=&v"(pk[7]),
+                         "=&v"(mt), "=&v"(tmp), "+v"(l_run)
+                       : "v"(vb), "v"(pb), "v"(neg_m), "v"(a.scale_log2), "v"(kb)
+                       : "memory", MLA_ASM_PVD_FP8_CLOBBERS);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pk_prev[i] = pk[i];
+          m_seen = fmaxf(m_seen, mt);
+          if (mt > m_ref + 64.0f) s_restart = 1;
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // raw tile it+2 landed
           __syncthreads();
-          restart = s_restart;               // uniform: read after the barrier
+          restart = __builtin_amdgcn_readfirstlane(s_restart);   // uniform: read after the barrier
           if (restart) break;
+        }
+        if (!restart) {
+          put_p(s_p, wave, lane, pk_prev);
+          __syncthreads();
+          pvd_tile(s_kv[(ntiles - 1) & 3] + pv_off, s_p + 16 * lane, o);
         }
       }
     }
@@ -542,7 +587,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   }
 #undef MLA_ISSUE_TILE
 #undef MLA_PROLOGUE
-#undef MLA_STORE_FP8_TILE
+#undef MLA_READ_RAW8
+#undef MLA_DECODE8
 #undef MLA_WAIT_ONE_TILE_IN_FLIGHT
 #undef MLA_TILE_RSRC
 #undef MLA_VOFF

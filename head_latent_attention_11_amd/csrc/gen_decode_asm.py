@@ -104,6 +104,18 @@ def weights_valu(S, PK, LRUN, NEGM, SCALE):
     return seq
 
 
+def weights_valu_fp8(S, PK, LRUN, NEGM, SCALE, KV):
+    """fp8 cache: the scores arrive multiplied by their token's scale.  p_r
+    as for bf16; the normaliser sums the rounded unscaled weights, and the PV
+    weights are p_r times the token scale (the cache values enter the MFMA
+    unscaled), packed to bf16."""
+    seq = weights_valu(S, PK, LRUN, NEGM, SCALE)
+    seq += [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
+    seq.append("s_nop 1")
+    seq += [f"v_cvt_pk_bf16_f32 {PK(i)}, {S(2 * i)}, {S(2 * i + 1)}" for i in range(8)]
+    return seq
+
+
 def softmax_max():
     """operands: %0 scaled max (out), %1 a temporary, %2..%17 scores, %18 scale."""
     return max_valu(lambda r: f"%{2 + r}", "%0", "%1", "%18") + ["s_nop 1"]
@@ -116,7 +128,7 @@ def softmax_valu(S, PK, MT, TMP, LRUN, NEGM, SCALE):
     return max_valu(S, MT, TMP, SCALE) + weights_valu(S, PK, LRUN, NEGM, SCALE)
 
 
-def pvd(with_softmax=False, with_dma=False):
+def pvd(with_softmax=False, with_dma=False, fp8=False):
     """PV product of one tile for this wave's 128 latent dims and all 128
     query rows of the workgroup: O^T[dims, rows] += C^T[dims, tok] P^T[tok,
     rows], 32 MFMAs (4 dim blocks x 4 row blocks x 2 token halves).  The
@@ -134,14 +146,26 @@ def pvd(with_softmax=False, with_dma=False):
     tile + the wave's dim offset), %44 this lane's P fragment address, %45
     -m_ref, %46 the scale (log2 domain).  with_dma: %47 buffer descriptor,
     %48 LDS base of this wave's loads, %49..%52 lane offsets of loads 5..8.
+    fp8 (no loads): %16..%31 are the raw scores; %47 is the address of this
+    lane's 16 token scales in LDS (read into v[212:227]); the sequence
+    multiplies the scores by them first.
     Without the softmax only %0..%15, %16 (= transposed-read base) and %17
     (= P fragment address) are used.
     Fixed registers: P fragments v[224:255], C^T fragment buffers
-    v[PVD_VBUF:223].
+    v[PVD_VBUF:223].  fp8 (which also holds the staged next tile): P
+    fragments v[240:255], the second token half's fragments read into them 4
+    MFMAs after the first half's last use, 3 C^T buffers v[228:239], token
+    scales v[212:227].
     """
     vbase, pbase = ("%43", "%44") if with_softmax else ("%16", "%17")
     valu = []
-    if with_softmax:
+    if with_softmax and fp8:
+        kv = lambda r: f"v{212 + r}"
+        valu = ([f"v_mul_f32 %{16 + r}, %{16 + r}, {kv(r)}" for r in range(16)]
+                + max_valu(lambda r: f"%{16 + r}", "%40", "%41", "%46")
+                + weights_valu_fp8(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
+                                   "%42", "%45", "%46", kv))
+    elif with_softmax:
         valu = softmax_valu(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
                             "%40", "%41", "%42", "%45", "%46")
     out, issued = [], []
@@ -156,10 +180,10 @@ def pvd(with_softmax=False, with_dma=False):
         out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
 
     def pfrag(rb, ks):
-        return 224 + 4 * (4 * ks + rb)
+        return 240 + 4 * rb if fp8 else 224 + 4 * (4 * ks + rb)
 
     def vbuf(g):
-        return PVD_VBUF + 4 * (g % PVD_NVBUF)
+        return (228 + 4 * (g % 3)) if fp8 else PVD_VBUF + 4 * (g % PVD_NVBUF)
 
     def vread(g):
         ks, db = g // 4, g % 4
@@ -173,12 +197,18 @@ def pvd(with_softmax=False, with_dma=False):
         r = pfrag(rb, ks)
         read(("P", rb, ks), [f"ds_read_b128 v[{r}:{r + 3}], {pbase} offset:{1024 * (2 * rb + ks)}"])
 
+    if fp8 and with_softmax:
+        for q in range(4):
+            read("K", [f"ds_read_b128 v[{212 + 4 * q}:{215 + 4 * q}], %47 offset:{16 * q}"])
     for rb in range(4):
         pread(rb, 0)
     for g in range(PVD_AHEAD):
         vread(g)
-    for rb in range(4):
-        pread(rb, 1)
+    if not fp8:
+        for rb in range(4):
+            pread(rb, 1)
+    if fp8 and with_softmax:
+        wait_for({"K"})                       # the scales, before the first scaling
     vi = 0
     for _ in range(PVD_LEAD):                 # independent softmax work first
         if vi < len(valu):
@@ -192,6 +222,8 @@ def pvd(with_softmax=False, with_dma=False):
         wait_for({("V", g), ("P", rb, ks)})
         out.append(f"v_mfma_f32_32x32x16_bf16 %{4 * db + rb}, v[{vbuf(g)}:{vbuf(g) + 3}], "
                    f"v[{pfrag(rb, ks)}:{pfrag(rb, ks) + 3}], %{4 * db + rb}")
+        if fp8 and 12 <= i < 16:
+            pread(i - 12, 1)                  # after the last use of P(rb, 0)
         if with_dma and i % 8 == 3 and i // 8 < PV_DMA:
             k = i // 8
             out += dma(QK_DMA + k, "%47", "%48", f"%{49 + k}")
@@ -226,6 +258,8 @@ if __name__ == "__main__":
     txt.append(f"#define MLA_ASM_QK_CLOBBERS {clobbers(QK_TMP, 32)}\n")
     txt.append(emit("MLA_ASM_PVD_TILE", pvd()))
     txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_DMA", pvd(True, True)))
+    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_FP8", pvd(True, False, True)))
     txt.append(f"#define MLA_ASM_PVD_CLOBBERS {clobbers(PVD_VBUF, 256 - PVD_VBUF)}\n")
+    txt.append(f"#define MLA_ASM_PVD_FP8_CLOBBERS {clobbers(212, 44)}\n")
     txt.append(emit_plain("MLA_ASM_SOFTMAX_MAX", softmax_max()))
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))

@@ -333,16 +333,21 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int rows = a.n_h * a.T;
   if (R >= a.B * rows) return;
   const int b = R / rows, row = R % rows;
-  const int L = a.seq_lens[b];
-  const int ns = splits_of(L, a.num_splits, a.chunk);
-  if (ns <= 1) return;                                    // written by the attention kernel
-  // first work item of sequence b: splits of the sequences before it
-  int first = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) {
-    const int bb = b0 + lane;
-    first += (bb < b) ? splits_of(a.seq_lens[bb], a.num_splits, a.chunk) : 0;
+  int ns, first;
+  if (a.uniform_len > 0) {                                // same length everywhere
+    ns = splits_of(a.uniform_len, a.num_splits, a.chunk);
+    first = b * ns;
+  } else {
+    ns = splits_of(a.seq_lens[b], a.num_splits, a.chunk);
+    // first work item of sequence b: splits of the sequences before it
+    first = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+      const int bb = b0 + lane;
+      first += (bb < b) ? splits_of(a.seq_lens[bb], a.num_splits, a.chunk) : 0;
+    }
+    first = wave_sum_i(first);
   }
-  first = wave_sum_i(first);
+  if (ns <= 1) return;                                    // written by the attention kernel
   const float* lse_p = a.part_lse + (size_t)first * rows + row;
   float* out = a.out_latent + (size_t)R * a.d_c;
   const int d0 = 8 * lane;                                // this lane's 8 dims

@@ -261,17 +261,20 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   a.q_dtype = qabs_dtype(dims);
   a.kv_dtype = dims->kv_dtype;
   a.scale_log2 = softmax_scale_of(dims) * 1.4426950408889634f;
+  {
+    bool uniform = seq_lens_host[0] > 0;
+    for (int b = 1; b < batch && uniform; ++b) uniform = seq_lens_host[b] == seq_lens_host[0];
+    if (uniform &&
+        (int64_t)batch * splits_of(seq_lens_host[0], p.num_splits, p.chunk) == p.n_items)
+      a.uniform_len = seq_lens_host[0];
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (fast_decode(dims, q_tokens)) {
     ItemTable tab;
     tab.n = 0;
-    tab.uniform_len = 0;
-    bool uniform = seq_lens_host[0] > 0;
-    for (int b = 1; b < batch && uniform; ++b) uniform = seq_lens_host[b] == seq_lens_host[0];
-    if (uniform &&
-        (int64_t)batch * splits_of(seq_lens_host[0], p.num_splits, p.chunk) == p.n_items) {
-      tab.uniform_len = seq_lens_host[0];
+    tab.uniform_len = a.uniform_len;
+    if (a.uniform_len > 0) {
     } else if (p.n_items <= kItemTable && batch < (1 << 20)) {
       int n = 0;
       for (int b = 0; b < batch; ++b) {

@@ -123,6 +123,7 @@ struct DecodeArgs {
   int32_t num_splits, chunk, n_items, row_blocks;
   int32_t q_dtype, kv_dtype;
   float scale_log2;           // softmax scale * log2(e)
+  int32_t uniform_len;        // > 0: every sequence has this length
 };
 
 // Work items of a plan (passed by value).  uniform_len > 0: every sequence
