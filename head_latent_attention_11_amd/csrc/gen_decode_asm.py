@@ -136,7 +136,7 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
     the waves that own the rows); each weight fragment is read once and used
     for 4 MFMAs, each transposed C^T fragment read once and used for 4.
     with_softmax: the softmax of the current tile is interleaved (two vector
-    instructions per MFMA).
+    instructions per MFMA, four for the longer fp8 softmax).
 
     operands: %0..%15 O blocks (block 4 db + rb: dims 32 db of the wave's
     128, rows 32 rb), %16..%31 the current tile's scores s_0..s_15 (in;
@@ -227,7 +227,7 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
         if with_dma and i % 8 == 3 and i // 8 < PV_DMA:
             k = i // 8
             out += dma(QK_DMA + k, "%47", "%48", f"%{49 + k}")
-        take = 2 if i < 31 else len(valu) - vi
+        take = (4 if fp8 else 2) if i < 31 else len(valu) - vi
         for _ in range(take):
             if vi < len(valu):
                 out.append(valu[vi])
