@@ -31,6 +31,7 @@ DEFAULT_WORKLOAD = "v2_b32_l4k_bf16"
 ATTN_PER_GRAPH = 20                     # attention calls captured per graph
 STEPS_PER_GRAPH = 10                    # decode steps captured per graph
 COPY_PROBE_BYTES = 512 * 2 ** 20        # calibration copy of the traffic probe
+COPY_CEILING_BYTES = 2 ** 30            # plain device copy reported as the practical ceiling
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 _CSRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
@@ -269,6 +270,22 @@ def main():
     roof["bytes_alg_per_launch"] = bytes_alg
     roof["flops_alg_per_launch"] = flops
 
+    # Practical HBM ceiling on this GPU, for context: a plain 1 GiB device
+    # copy (read + write bytes over its time).  Not part of any step.
+    cp_src = torch.empty(COPY_CEILING_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    cp_dst = torch.empty_like(cp_src)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * COPY_CEILING_BYTES / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e9
+    del cp_src, cp_dst
+
     out = {
         "metric": "MLA decode tokens/s and latent-cache GB/s (% of HBM/MFMA roofline)",
         "value": round(w.batch * w.q_tokens / (ms_step * 1e-3), 1),
@@ -288,6 +305,7 @@ def main():
                    "layout": w.layout, "cache_replicas": replicas,
                    "steps_per_graph": STEPS_PER_GRAPH},
         "latent_cache_GBps": round(cache_b / attn_s / 1e9, 1),
+        "hbm_copy_GBps": round(copy_gbps, 1),
         "attn_us": round(attn_ms * 1e3, 2),
         "step_us_events": round(ms_step_events * 1e3, 2),
         "roofline": roof,

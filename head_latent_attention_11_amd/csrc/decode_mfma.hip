@@ -189,7 +189,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const int item = gi / a.row_blocks, rb = gi % a.row_blocks;
   // work item -> (sequence, split, length): from the host's table when the
   // plan has few enough items, else located on the device
-  int b, s_idx, L;
+  int b, s_idx, L, item_id = item;      // item_id: where the partial goes
   if (tab.uniform_len > 0) {           // every sequence has the same length
     L = tab.uniform_len;
     const int nsu = splits_of(L, a.num_splits, a.chunk);
@@ -199,7 +199,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     const uint32_t e = tab.seq_split[item];
     b = e & 0xFFFFF;
     s_idx = e >> 20;
-    L = tab.len[item];
+    item_id = tab.item_id[item];
+    L = a.seq_lens[b];
   } else {
     const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
     if (loc.b < 0) return;
@@ -231,6 +232,24 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const int seq_row0 = b * a.max_len;
   typedef __attribute__((address_space(4))) const int32_t* ConstI32;
   const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
+  // Paged cache: the item's page ids are loaded once, one per lane (up to
+  // 128 pages), and each tile takes its page from a lane with v_readlane, so
+  // no tile waits for a page-table load.  Items are page-aligned (the chunk
+  // is a multiple of the page size).  Longer items read the table per tile.
+  const int pg_first = t0 / kPage;
+  const int pg_n = (t_stage > t0) ? (t_stage - t0 + kPage - 1) / kPage : 0;
+  const bool pg_regs = ptab && pg_n <= 128;
+  int pg_lo = 0, pg_hi = 0;
+  if (pg_regs) {
+    if (lane < pg_n) pg_lo = a.page_table[(size_t)b * a.max_pages + pg_first + lane];
+    if (64 + lane < pg_n) pg_hi = a.page_table[(size_t)b * a.max_pages + pg_first + 64 + lane];
+  }
+
+  // page id of the tile starting at token ts (ts inside the item)
+#define MLA_PAGE(ts_)                                                                      \
+  (pg_regs ? __builtin_amdgcn_readlane(((ts_) / kPage - pg_first) < 64 ? pg_lo : pg_hi,   \
+                                       ((ts_) / kPage - pg_first) & 63)                  \
+           : ptab[(ts_) / kPage])
 
   // ---- staging.  bf16: LDS 16-byte chunk q of a tile holds token q / 73,
   // chunk q % 73 of its row (chunk 72 is the row padding, filled with zero
@@ -261,7 +280,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     const int nv__ = max(0, min(TILE, t_stage - ts__));                                  \
     int r0__ = 0;                                                                        \
     if (nv__ > 0)                                                                        \
-      r0__ = ptab ? ptab[ts__ / kPage] * kPage + (ts__ % kPage) : seq_row0 + ts__;      \
+      r0__ = ptab ? MLA_PAGE(ts__) * kPage + (ts__ % kPage) : seq_row0 + ts__;          \
     r0__ = __builtin_amdgcn_readfirstlane(r0__);                                         \
     const uint64_t ad__ = (uint64_t)(cache + (size_t)r0__ * ROWB);                       \
     const u32x4 rs__ = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad__),        \
@@ -332,7 +351,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     const int nv__ = max(0, min(TILE, t_stage - ts__));                                  \
     int r0__ = 0;                                                                        \
     if (nv__ > 0)                                                                        \
-      r0__ = ptab ? ptab[ts__ / kPage] * kPage + (ts__ % kPage) : seq_row0 + ts__;      \
+      r0__ = ptab ? MLA_PAGE(ts__) * kPage + (ts__ % kPage) : seq_row0 + ts__;          \
     r0__ = __builtin_amdgcn_readfirstlane(r0__);                                         \
     const uint64_t ad__ = (uint64_t)(cache + (size_t)r0__ * ROWB);                       \
     rs_ = u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad__),                \
@@ -592,6 +611,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #undef MLA_WAIT_ONE_TILE_IN_FLIGHT
 #undef MLA_TILE_RSRC
 #undef MLA_VOFF
+#undef MLA_PAGE
 
   // ---- normalise and write (the final output, or this split's partial).
   // Wave w holds O^T for its 128 latent dims and all 128 rows (block
@@ -645,7 +665,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     // bytes per row from this wave, all 128 rows at once
     constexpr int SROW = 272;
     uint8_t* stg = &s_kv[0][0] + wave * (128 * SROW);
-    const size_t g0 = (size_t)item * rows + row0;
+    const size_t g0 = (size_t)item_id * rows + row0;
     uint8_t* dst = (uint8_t*)a.part_o + g0 * (2 * DC) + 256 * wave;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -669,7 +689,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
       *(u32x4*)(dst + (size_t)r * (2 * DC) + 16 * (lane & 15)) =
           *(const u32x4*)(stg + r * SROW + 16 * (lane & 15));
     }
-    if (h == 0) a.part_lse[(size_t)item * rows + own0 + l32] = lse;
+    if (h == 0) a.part_lse[(size_t)item_id * rows + own0 + l32] = lse;
   }
 }
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "mla_common.hpp"
 
@@ -19,6 +20,8 @@ hipError_t launch_combine(const DecodeArgs&, hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
 hipError_t launch_decode_mfma(const DecodeArgs&, const ItemTable&, hipStream_t);
+static_assert(sizeof(DecodeArgs) + sizeof(ItemTable) <= 4096,
+              "the attention kernel's arguments must stay within 4 KB");
 hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
 }  // namespace mla
 
@@ -276,15 +279,37 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
     tab.uniform_len = a.uniform_len;
     if (a.uniform_len > 0) {
     } else if (p.n_items <= kItemTable && batch < (1 << 20)) {
-      int n = 0;
+      // items in sequence order with their token counts, then largest first
+      struct It { uint32_t key; int32_t id; int32_t size; };
+      std::vector<It> its;
+      its.reserve(p.n_items);
       for (int b = 0; b < batch; ++b) {
-        const int ns = splits_of(seq_lens_host[b], p.num_splits, p.chunk);
-        for (int sp = 0; sp < ns && sp < 4096; ++sp, ++n) {
-          tab.seq_split[n] = uint32_t(b) | (uint32_t(sp) << 20);
-          tab.len[n] = seq_lens_host[b];
-        }
+        const int L = seq_lens_host[b];
+        const int c = chunk_of(L, p.num_splits, p.chunk);
+        const int ns = splits_of(L, p.num_splits, p.chunk);
+        for (int sp = 0; sp < ns && sp < 4096; ++sp)
+          its.push_back({uint32_t(b) | (uint32_t(sp) << 20), (int32_t)its.size(),
+                         std::min(c, L - sp * c)});
       }
-      tab.n = (n == p.n_items) ? n : 0;
+      if ((int64_t)its.size() == p.n_items) {
+        std::stable_sort(its.begin(), its.end(),
+                         [](const It& x, const It& y) { return x.size > y.size; });
+        // Workgroup g runs table entry xcd_logical_index(g, G) / row_blocks:
+        // the entries are filled with the largest items in the order in
+        // which workgroups first reach them.
+        const int n = (int)its.size(), G = n * p.row_blocks;
+        std::vector<char> done(n, 0);
+        int next = 0;
+        for (int g = 0; g < G && next < n; ++g) {
+          const int i = xcd_logical_index(g, G) / p.row_blocks;
+          if (done[i]) continue;
+          done[i] = 1;
+          tab.seq_split[i] = its[next].key;
+          tab.item_id[i] = its[next].id;
+          ++next;
+        }
+        tab.n = (next == n) ? n : 0;
+      }
     }
     e = launch_decode_mfma(a, tab, s);
   } else {

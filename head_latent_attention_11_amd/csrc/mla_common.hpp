@@ -99,7 +99,7 @@ __host__ __device__ inline int splits_of(int L, int num_splits, int chunk) {
 
 // Logical work index of a workgroup so that consecutive logical indices run
 // on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
-__device__ inline int xcd_logical_index(int g, int G) {
+__host__ __device__ inline int xcd_logical_index(int g, int G) {
   int q = G / kNumXCD, r = G % kNumXCD;
   int x = g % kNumXCD;
   return x * q + (x < r ? x : r) + g / kNumXCD;
@@ -128,13 +128,17 @@ struct DecodeArgs {
 
 // Work items of a plan (passed by value).  uniform_len > 0: every sequence
 // has this length and item = b * splits + s.  Else the host lists the items
-// when there are at most kItemTable of them; n = 0: the kernel locates them.
-constexpr int kItemTable = 256;
+// when there are at most kItemTable of them, largest first in the order the
+// workgroups are dealt out (round-robin over the XCDs, each item's row blocks
+// on one XCD), so the long items start first and spread over all XCDs; n = 0: the
+// kernel locates them in sequence order.  Partials are stored at the item's
+// index in sequence order (item_id), where the combine looks for them.
+constexpr int kItemTable = 448;     // keeps the kernel arguments under 4 KB
 struct ItemTable {
   int32_t uniform_len;
   int32_t n;
   uint32_t seq_split[kItemTable];   // sequence | split << 20
-  int32_t len[kItemTable];          // the sequence's length
+  int32_t item_id[kItemTable];      // index in sequence order
 };
 
 }  // namespace mla
