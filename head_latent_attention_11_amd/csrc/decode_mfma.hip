@@ -70,6 +70,8 @@ constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte chunks per thread (9)
 constexpr int RAW8 = 18944;              // fp8: raw tile (18 KB) at this offset of its slot
 constexpr int SCL8 = 37376;              // fp8: the tile's 32 token scales, end of the slot
 constexpr int NLD8 = TILE * D / 1024;    // fp8: 1 KB loads per raw tile (18)
+constexpr int QROW = 592;                // LDS bytes per staged half query row (576 + 16 pad)
+constexpr int QLOADS = ROWS_WG * (QROW / 16) / 64;   // 1 KB loads per staged half (74)
 constexpr uint32_t kOOB = 0x40000000u;   // buffer offset past any valid range
 constexpr float kNegInf = -INFINITY;
 }  // namespace
@@ -171,6 +173,16 @@ __device__ __forceinline__ int reg_token(int r, int h) {
 __device__ inline uint32_t tile_src_offset(int u) {
   const int tk = (u * 449) >> 15;
   return (u - 73 * tk == NCH || tk >= TILE) ? kOOB : uint32_t(16 * (u - tk));
+}
+
+static_assert(QLOADS * 1024 == 2 * TILE_BYTES, "query halves fill ring slots 2 and 3");
+static_assert(QLOADS * 64 == ROWS_WG * (QROW / 16), "whole staged rows");
+
+// Staged query halves: 16-byte unit u holds row u / 37, unit u % 37 of the
+// half (unit 36 is the row padding: an out-of-range offset, zero-filled).
+__device__ inline uint32_t q_src_offset(int u, int half) {
+  const int r = u / (QROW / 16), c = u - (QROW / 16) * r;
+  return c == QROW / 16 - 1 ? kOOB : uint32_t(r * (2 * D) + half * D + 16 * c);
 }
 
 template <bool FP8>
@@ -369,56 +381,99 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   for (int n = 0; n < NLD; ++n) voff[n] = MLA_VOFF(n);
 
   // ---- absorbed query rows -> MFMA B operands (lane: head l32, 8 dims).
-  // The wave's 32 rows are contiguous in memory (row = tau * n_h + head,
-  // query token b*T + tau): it copies them into ring slot `wave` at the tile
-  // row pitch with buffer loads that write LDS directly (each load 1 KB of
-  // contiguous memory), then reads its operands from there (the same
-  // conflict-free pattern as the K operand reads).
+  // The workgroup's 128 rows are contiguous in memory (row = tau * n_h +
+  // head, query token b*T + tau).  They are staged in two halves of 288
+  // dims through ring slots 2 and 3, with buffer loads that write LDS
+  // directly (each load 1 KB of LDS), at a row pitch of QROW bytes so that
+  // the operand reads of 16 rows fall on distinct banks.  The loads of tiles
+  // 0 and 1 (slots 0 and 1) go out between the first half's loads and its
+  // wait, so their HBM latency overlaps the query staging.
   bf16x8 qf[D / 16];
-  {
-    const size_t r0 = (size_t)b * rows + rb * ROWS_WG + wave * 32;
-    const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs + r0 * (2 * D));
-    const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
-                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
-                       uint32_t(32 * 2 * D), 0x00020000u};
-    const uint32_t qlds = lds_ring + wave * TILE_BYTES;
-#pragma unroll
-    for (int n = 0; n < NLOADS; ++n)
-      asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(qlds), "v"(tile_src_offset(64 * n + lane)), "s"(qrs), "i"(1024 * n)
-                   : "memory");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    const uint8_t* qsrc = &s_kv[wave][0] + l32 * LROW + 16 * h;
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) qf[k] = *(const bf16x8*)(qsrc + 32 * k);
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
-    __syncthreads();                    // every wave has its operands: the ring is free
-  }
-
+  const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs +
+                                 ((size_t)b * rows + rb * ROWS_WG) * (2 * D));
+  const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
+                     uint32_t(ROWS_WG * 2 * D), 0x00020000u};
+  const uint32_t qlds = lds_ring + 2 * TILE_BYTES;
+  // half p_: load n = wave + 4k (n < QLOADS) fills staging units 64n .. 64n+63
+#define MLA_Q_ISSUE(p_)                                                                    \
+  do {                                                                                   \
+    _Pragma("unroll") for (int k = 0; k < (QLOADS + 3) / 4; ++k)                         \
+      if (wave + 4 * k < QLOADS)                                                         \
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
+                     :: "s"(qlds + 1024 * (wave + 4 * k)),                               \
+                        "v"(q_src_offset(64 * (wave + 4 * k) + lane, (p_))), "s"(qrs)    \
+                     : "memory");                                                        \
+  } while (0)
+  // half p_ -> qf[18 p_ .. 18 p_ + 17]
+#define MLA_Q_READ(p_)                                                                     \
+  do {                                                                                   \
+    const uint8_t* qsrc__ = &s_kv[2][0] + (32 * wave + l32) * QROW + 16 * h;             \
+    _Pragma("unroll") for (int k = 0; k < D / 32; ++k)                                   \
+      qf[(D / 32) * (p_) + k] = *(const bf16x8*)(qsrc__ + 32 * k);                       \
+  } while (0)
 
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
 
-  // Prologue of an attempt: issue tiles 0 and 1 (fp8: decoded into the ring
-  // right away).
-#define MLA_PROLOGUE()                                                                     \
+  // Prologue of an attempt: issue tiles 0 and 1; fp8: once they have
+  // landed (vmcnt(0) and a barrier), tile 0 is decoded right away, tile 1
+  // in step 0.
+#define MLA_ISSUE_FIRST_TILES()                                                            \
   do {                                                                                   \
-    if (ntiles > 0) {                                                                    \
-      MLA_ISSUE_TILE(t0, 0);                                                             \
-      if (ntiles > 1) MLA_ISSUE_TILE(t0 + TILE, 1);                                      \
-      if constexpr (FP8) {            /* tile 0 decoded now, tile 1 in step 0 */         \
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                 \
-        __syncthreads();                                                                 \
+    if (ntiles > 0) MLA_ISSUE_TILE(t0, 0);                                               \
+    if (ntiles > 1) MLA_ISSUE_TILE(t0 + TILE, 1);                                        \
+  } while (0)
+#define MLA_DECODE_FIRST_TILE()                                                            \
+  do {                                                                                   \
+    if constexpr (FP8) {                                                                 \
+      if (ntiles > 0) {                                                                  \
         MLA_READ_RAW8(0);                                                                \
         __syncthreads();                                                                 \
         MLA_DECODE8(0);                                                                  \
       }                                                                                  \
     }                                                                                    \
   } while (0)
+#define MLA_PROLOGUE()                                                                     \
+  do {                                                                                   \
+    MLA_ISSUE_FIRST_TILES();                                                             \
+    if constexpr (FP8) {                                                                 \
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                   \
+      __syncthreads();                                                                   \
+    }                                                                                    \
+    MLA_DECODE_FIRST_TILE();                                                             \
+  } while (0)
 
   if (tid == 0) s_restart = 0;
-  MLA_PROLOGUE();
+  // first attempt: query half 0, tiles 0 and 1, query half 1
+  MLA_Q_ISSUE(0);
+  MLA_ISSUE_FIRST_TILES();
+  {
+    // wait for query half 0 only: at most the loads of the tiles issued
+    // after it (the fewest any wave issues per tile) stay in flight
+    const int nt = min(ntiles, 2);
+    if (nt == 2) {
+      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    } else if (nt == 1) {
+      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  }
+  __syncthreads();                    // every wave's share of half 0 landed
+  MLA_Q_READ(0);
+  __syncthreads();                    // every wave has read half 0: the slots are free
+  MLA_Q_ISSUE(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                    // half 1 and tiles 0 and 1 landed
+  MLA_Q_READ(1);
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) asm volatile("" ::"v"(qf[k]));
+  MLA_DECODE_FIRST_TILE();
+#undef MLA_Q_ISSUE
+#undef MLA_Q_READ
 
   for (;;) {                          // attempts (a restart is rare)
 #pragma unroll
@@ -606,6 +661,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   }
 #undef MLA_ISSUE_TILE
 #undef MLA_PROLOGUE
+#undef MLA_ISSUE_FIRST_TILES
+#undef MLA_DECODE_FIRST_TILE
 #undef MLA_READ_RAW8
 #undef MLA_DECODE8
 #undef MLA_WAIT_ONE_TILE_IN_FLIGHT
