@@ -28,10 +28,11 @@
 //     bf16 tiles move HBM -> LDS with buffer loads that write LDS directly
 //     (no VGPR staging); a load range that ends at the last valid token makes
 //     the hardware write zeros for masked tokens, so they enter the PV
-//     product as exact zeros.  fp8 tiles are decoded to bf16 while staged
-//     through VGPRs; the per-token scale multiplies the score and is folded
-//     into P for the PV product, so the fp8 values enter the bf16 MFMA
-//     exactly.
+//     product as exact zeros.  Raw fp8 tiles are copied the same way into
+//     the upper half of their slot and decoded in place to bf16 (exact: every
+//     E4M3 value is a bf16 value) one step before they are used; the
+//     per-token scale multiplies the score and the PV weight, so the fp8
+//     values enter the bf16 MFMA exactly.
 //   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one row's 16 token scores
 //     in each lane: the per-row max and sum need no cross-lane reduction
 //     except with the partner lane (lane ^ 32).  The packed weights are then
