@@ -333,3 +333,49 @@ def test_up_proj_parity(w):
     got = to_np(out)
     check("o", got, ref, 1e-6 if kind == "f32" else 4e-3)
     check("o (fp32 out)", to_np(out32), ref, 1e-5)
+
+
+# ------------------------------------------ the benchmark's launch configuration
+@pytest.mark.parametrize("w", [V2,
+                               small_variant(WORKLOADS["v2_fp8_t4_b64_l8k"], name="fp8_t4_graph",
+                                             batch=5, kv_len=0, lengths=(700, 64, 4, 333, 1200)),
+                               small_variant(WORKLOADS["v2_paged_b128_bf16"], name="paged_graph",
+                                             batch=6, kv_len=0,
+                                             lengths=(513, 64, 2000, 1, 65, 900))],
+                         ids=["v2_b32_l4k_bf16", "fp8_t4_ragged", "paged_ragged"])
+def test_graph_replays_match_eager(w):
+    """Steps captured as one HIP graph over two cache replicas (as the
+    benchmark runs them) give, on every replay, the eager step's outputs bit
+    for bit; the outputs are poisoned with NaN by eager work between replays.
+    The eager step itself is checked against the oracle on sampled rows."""
+    say(f"case graph {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout}")
+    gen = generate(w)
+    buf = _buffers(w, gen, cache_replicas=2)
+    buf.step(replica=0)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (buf.o, buf.latent, buf.lse)]
+    seqs = sorted({0, w.batch - 1})
+    ref = omla.decode_workload(gen, w, seqs=seqs, heads=[0, w.n_heads - 1])
+    mask = sample_mask((w.batch * w.q_tokens, w.n_heads), seqs, [0, w.n_heads - 1], w.q_tokens)
+    rel, mabs = _gates(w)
+    check("o (eager)", to_np(eager[0])[mask], ref["o"][mask], rel, mabs)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        buf.step(replica=1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for r in (1, 0, 1, 0):                 # the last step reads replica 0
+            buf.step(replica=r)
+    for rep in range(3):
+        for t in (buf.o, buf.latent, buf.lse):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("o", "latent", "lse"), (buf.o, buf.latent, buf.lse), eager):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
+    say(f"  3 replays bit-identical to the eager step")
