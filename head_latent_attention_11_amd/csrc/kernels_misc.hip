@@ -164,12 +164,12 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   }
 
   for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    if (t0 > 0) {                      // next query block (previous one consumed)
-      load_q(t0, qv);
-      __syncthreads();
+    if (t0 > 0) {                      // next query block (loaded during the last one)
+      __syncthreads();                 // the last block's operand reads and copy-out are done
       store_q(qv);
       __syncthreads();
     }
+    if (t0 + 32 < n_tok) load_q(t0 + 32, qv);   // in flight during this block
     floatx16 acc = {};
 #pragma unroll
     for (int k = 0; k < kAbsDh / 16; ++k) {
@@ -488,14 +488,17 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
     const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
     wv[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
-  for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    floatx4 v[8];                      // 32 rows x 128 chunks of 4 floats
+  floatx4 v[8];                        // 32 rows x 128 chunks of 4 floats
+  auto load_latent = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ch = tid + 512 * i, t = ch >> 7, c4 = (ch & 127) * 4;
       v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
     }
+  };
+  load_latent(0);
+  for (int t0 = 0; t0 < n_tok; t0 += 32) {
     if (t0 == 0) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -519,6 +522,7 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
       *(u32x2*)(sh + t * kUpRow + c4) = hi;
       *(u32x2*)(sl + t * kUpRow + c4) = lo;
     }
+    if (t0 + 32 < n_tok) load_latent(t0 + 32);   // in flight during this block
     __syncthreads();
 
     floatx4 acc_hi = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
