@@ -88,6 +88,10 @@ SMALL = [
                   layout="paged"),
     small_variant(V2, name="v2_outliers_split7", batch=2, kv_len=0, lengths=(3000, 2900),
                   num_splits=7, outlier_frac=0.01, outlier_scale=8.0),
+    # more than 16 splits in one sequence (the one-workgroup-per-row combine),
+    # uneven split counts across sequences, an unsplit sequence
+    small_variant(V2, name="v2_ragged_split40", batch=3, kv_len=0, lengths=(2600, 64, 1300),
+                  num_splits=40),
     small_variant(V2, name="bf16_t4", batch=2, q_tokens=4, kv_len=0, lengths=(129, 64)),
     small_variant(V2, name="fp8_t4", batch=4, q_tokens=4, kv_len=0, lengths=(300, 77, 4, 130),
                   kv_dtype="fp8"),
