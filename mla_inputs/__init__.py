@@ -72,6 +72,7 @@ class Workload:
     outlier_scale: float = 1.0
     seed: int = 0
     description: str = ""
+    d_model: int = 5120        # hidden size d (rows of W^O)
 
     @property
     def d_qk(self) -> int:
@@ -83,7 +84,7 @@ WORKLOADS: Dict[str, Workload] = {
         Workload(
             name="tiny_fp32", batch=1, q_tokens=1, n_heads=4, d_head=16,
             d_latent=32, d_rope=16, kv_len=64, kv_dtype="f32", q_dtype="f32",
-            rope=True,
+            rope=True, d_model=48,
             description="Tiny MLA decode, fp32: B=1, T=1, n_h=4, d_h=16, "
                         "d_c=32, d_h^R=16, L=64, RoPE base 1e4 at positions "
                         "0..63"),
@@ -226,6 +227,17 @@ def generate(w: Workload, seed: Optional[int] = None,
         out["page_table"] = table
         out["num_pages"] = np.int64(n_pages.sum())
     return out
+
+
+def output_weights(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """W^O [d_model, n_h * d_h] (the attention output projection), drawn
+    from its own stream (child len(FIELDS) of the workload's seed, so that
+    no other field changes): N(0, 1/(n_h d_h)), rounded like W^UK / W^UV."""
+    seed = w.seed if seed is None else seed
+    ss = np.random.SeedSequence(seed).spawn(len(FIELDS) + 1)[len(FIELDS)]
+    K = w.n_heads * w.d_head
+    wdt = "f32" if w.q_dtype == "f32" else "bf16"
+    return _gauss(np.random.default_rng(ss), (w.d_model, K), 1.0 / math.sqrt(K), wdt)
 
 
 def small_variant(w: Workload, **changes) -> Workload:

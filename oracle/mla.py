@@ -130,6 +130,22 @@ def up_project(latent: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     return out
 
 
+def output_project(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """u_n = W^O [o_{n,1}; o_{n,2}; ...; o_{n,n_h}]: the attention output
+    projection of the [V3] notes, MLA section (the equation after the
+    attention-output equation), W^O in R^{d x d_h n_h}.  Written per head
+    block: column block i of W^O (columns [i d_h, (i+1) d_h)) multiplies
+    o_{n,i}, and the blocks are summed.
+
+    o [N, n_h, d_h], w_o [d, n_h d_h] -> u [N, d] (float64).
+    """
+    n_tok, H, d_h = o.shape
+    u = np.zeros((n_tok, w_o.shape[0]))
+    for i in range(H):
+        u += o[:, i, :] @ w_o[:, i * d_h:(i + 1) * d_h].T
+    return u
+
+
 def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)

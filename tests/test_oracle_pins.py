@@ -435,3 +435,42 @@ def test_up_project_matches_literal_values():
     w_uk, w_uv, C, KR, qn, qr = _golden_operands(g)
     lat = np.array(g["expected_T1"]["latent"])[None]
     np.testing.assert_allclose(mla.up_project(lat, w_uv)[0], g["expected_T1"]["o"], atol=1e-13)
+
+
+# ------------------------------------------------ output projection (W^O)
+def test_output_projection_absorbs_w_uv():
+    """[V2] section 2.1.2: W^UV can be absorbed into W^O.  Projecting the
+    up-projected heads, W^O [W^UV_1 lat_1; ...], equals applying the merged
+    per-head matrices (W^O_i W^UV_i) to the latent rows directly."""
+    rng = np.random.default_rng(41)
+    n_tok, H, d_h, d_c, d = 3, 4, 5, 7, 6
+    lat = rng.standard_normal((n_tok, H, d_c))
+    w_uv = rng.standard_normal((H, d_h, d_c))
+    w_o = rng.standard_normal((d, H * d_h))
+    u = mla.output_project(mla.up_project(lat, w_uv), w_o)
+    merged = [w_o[:, i * d_h:(i + 1) * d_h] @ w_uv[i] for i in range(H)]   # [d, d_c] each
+    u2 = sum(lat[:, i, :] @ merged[i].T for i in range(H))
+    np.testing.assert_allclose(u, u2, rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_special_cases():
+    """Identity W^O returns the concatenated heads in head order; a W^O with
+    one nonzero column block reads only that head; a permutation of the
+    output rows permutes u; the map is linear."""
+    rng = np.random.default_rng(42)
+    n_tok, H, d_h = 2, 3, 4
+    o = rng.standard_normal((n_tok, H, d_h))
+    u = mla.output_project(o, np.eye(H * d_h))
+    np.testing.assert_array_equal(u, o.reshape(n_tok, H * d_h))
+    blk = np.zeros((5, H * d_h))
+    E = rng.standard_normal((5, d_h))
+    blk[:, 2 * d_h:3 * d_h] = E
+    np.testing.assert_allclose(mla.output_project(o, blk), o[:, 2, :] @ E.T, rtol=1e-13)
+    w_o = rng.standard_normal((7, H * d_h))
+    perm = rng.permutation(7)
+    np.testing.assert_allclose(mla.output_project(o, w_o[perm]), mla.output_project(o, w_o)[:, perm],
+                               rtol=1e-13)
+    o2 = rng.standard_normal(o.shape)
+    np.testing.assert_allclose(mla.output_project(2.0 * o - 3.0 * o2, w_o),
+                               2.0 * mla.output_project(o, w_o) - 3.0 * mla.output_project(o2, w_o),
+                               rtol=1e-12, atol=1e-12)
