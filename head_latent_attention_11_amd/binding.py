@@ -21,7 +21,8 @@ PREC_BF16, PREC_FP32 = 0, 1
 PRECISION_CODES = {"bf16": PREC_BF16, "fp32": PREC_FP32}
 
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
-            "mla_decode_attn", "mla_up_proj_v", "mla_status_string", "mla_version")
+            "mla_decode_attn", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
+            "mla_status_string", "mla_version")
 
 
 class MLAError(RuntimeError):
@@ -81,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_attn.argtypes = [pdims, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
                                     i32, vp, sz, vp, vp, vp]
     lib.mla_up_proj_v.argtypes = [pdims, vp, vp, vp, i32, i32, vp]
+    lib.mla_out_proj_workspace_size.argtypes = [pdims, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.mla_out_proj.argtypes = [pdims, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp]
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
@@ -184,3 +187,28 @@ def up_proj_v(dims: MLADims, latent, w_uv, out, n_tokens: int, stream=None,
     _check(lib.mla_up_proj_v(ctypes.byref(dims), _ptr(latent), _ptr(w_uv), _ptr(out),
                              int(out_dtype), int(n_tokens), _stream(stream)),
            "mla_up_proj_v")
+
+
+def out_proj_workspace_size(dims: MLADims, d_model: int, n_tokens: int, o_dtype: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.mla_out_proj_workspace_size(ctypes.byref(dims), int(d_model), int(n_tokens),
+                                           int(o_dtype), ctypes.byref(out)),
+           "mla_out_proj_workspace_size")
+    return int(out.value)
+
+
+def out_proj(dims: MLADims, o, w_o, d_model: int, u, n_tokens: int, workspace, ws_bytes: int,
+             stream=None, o_dtype: Optional[int] = None, u_dtype: Optional[int] = None):
+    """u = W^O [o_1; ...; o_{n_h}].  The dtypes default to those of the tensors
+    (float32 -> F32, else BF16)."""
+    lib = load_library()
+    import torch
+
+    def code(t):
+        return F32 if (not isinstance(t, int) and t.dtype == torch.float32) else BF16
+    o_dtype = code(o) if o_dtype is None else o_dtype
+    u_dtype = code(u) if u_dtype is None else u_dtype
+    _check(lib.mla_out_proj(ctypes.byref(dims), _ptr(o), int(o_dtype), _ptr(w_o), int(d_model),
+                            _ptr(u), int(u_dtype), int(n_tokens), _ptr(workspace), int(ws_bytes),
+                            _stream(stream)), "mla_out_proj")

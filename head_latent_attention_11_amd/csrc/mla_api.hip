@@ -17,6 +17,10 @@ hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int3
                          const int32_t*, const int32_t*, int, int, int, long long, int,
                          void*, float*, int, float, hipStream_t);
 hipError_t launch_combine(const DecodeArgs&, hipStream_t);
+bool out_proj_fast(int, int, int, int);
+size_t out_proj_workspace(int, int, int, int, int);
+hipError_t launch_out_proj(const void*, int, const void*, int, void*, bool, int, int, int, void*,
+                           hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
 hipError_t launch_decode_mfma(const DecodeArgs&, const ItemTable&, hipStream_t);
@@ -321,6 +325,36 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;
+}
+
+int32_t mla_out_proj_workspace_size(const mla_dims_t* dims, int32_t d_model, int32_t n_tokens,
+                                    int32_t o_dtype, size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL;
+  if (o_dtype != MLA_F32 && o_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d_model < 1 || n_tokens < 1) return MLA_ERR_ARG;
+  *bytes = out_proj_workspace(d_model, dims->n_heads * dims->d_head, n_tokens, o_dtype,
+                              dims->q_dtype);
+  return MLA_OK;
+}
+
+int32_t mla_out_proj(const mla_dims_t* dims, const void* o, int32_t o_dtype, const void* w_o,
+                     int32_t d_model, void* u, int32_t u_dtype, int32_t n_tokens,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!o || !w_o || !u) return MLA_ERR_NULL;
+  if (o_dtype != MLA_F32 && o_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (u_dtype != MLA_F32 && u_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d_model < 1 || n_tokens < 1) return MLA_ERR_ARG;
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(u) || (workspace && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  const int K = dims->n_heads * dims->d_head;
+  const size_t need = out_proj_workspace(d_model, K, n_tokens, o_dtype, dims->q_dtype);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  return status_of(launch_out_proj(o, o_dtype, w_o, dims->q_dtype, u, u_dtype == MLA_F32,
+                                   n_tokens, d_model, K, workspace, (hipStream_t)stream));
 }
 
 int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent, const void* w_uv,

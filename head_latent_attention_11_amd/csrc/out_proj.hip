@@ -1,0 +1,298 @@
+// Attention output projection ("DeepSeek-V3 Technical Report" notes, MLA
+// section, the equation after the attention-output equation):
+//
+//   u_t = W^O [o_{t,1}; o_{t,2}; ...; o_{t,n_h}],   W^O in R^{d x d_h n_h}
+//
+// With K = n_h d_h (16384 for DeepSeek-V2) and the few query tokens of a
+// decode step, this is a skinny GEMM that streams W^O (d x K bf16, 168 MB
+// for d = 5120) from HBM once per group of up to 128 tokens; the tokens'
+// concatenated heads (M x K bf16) are re-read from L2 by every feature block.
+//
+// Matrix-core path (bf16 W^O and o, d % 128 == 0, K % 2048 == 0):
+//   * Workgroup (feature block of 32 NW rows of W^O, K block of 2048, group
+//     of up to MT token tiles of 32): NW waves, wave w owns features
+//     32w..32w+31 of the block.  Stages of 64 K pass through an LDS ring:
+//     each wave copies its own W^O rows (32 x 128 B), waves 0..3 the token
+//     rows (32 x 128 B per token tile), HBM/L2 -> LDS by buffer loads that
+//     write LDS directly, NBUF - 1 stages ahead.  For DeepSeek-V2 (d = 5120,
+//     K = 16384) and up to 32 tokens: NW = 5, 6 slots, 32 x 8 = 256
+//     workgroups, one per CU.  Inside a row, 16-byte unit c of the 8 sits at position
+//     c ^ ((row >> 1) & 7), so the MFMA operand reads of 16 consecutive rows
+//     fall on 16 distinct 4-bank groups.
+//   * D[feature, token] += W^O[feature, k16] x[token, k16]^T with
+//     v_mfma_f32_32x32x16_bf16 (fp32 accumulators, 16 per token tile).
+//   * Each K block writes an fp32 partial [M, d]; out_proj_reduce_kernel sums
+//     the K blocks into u (fp32 or bf16 round-to-nearest-even).
+// General path: any dims and dtypes, one thread per output element (slow;
+// for small shapes and fp32 operands).
+#include <algorithm>
+
+#include "mla_common.hpp"
+
+namespace mla {
+
+namespace {
+constexpr int OP_KB = 2048;            // K per workgroup (one partial per K block)
+constexpr uint32_t kOpOOB = 0x40000000u;
+#ifndef OP_V1_U
+#define OP_V1_U 8                      // one token tile: 16-byte units per row and stage
+#define OP_V1_NBUF 6                   // ... and ring slots
+#endif
+}  // namespace
+
+// A stage's tile holds U 16-byte units (8 K each) of every row, rows at a
+// pitch of 16 U bytes.  Unit c of row r sits at position c ^ g(r), g(r) =
+// (r >> 1) & 7 for U = 8 (128-byte rows: two rows share the 64 banks) and
+// r & 15 for U = 16, so that the operand reads of 16 consecutive rows (same
+// c) fall on 16 distinct 4-bank groups.
+template <int U>
+__device__ inline int op_swz(int r, int c) {
+  return r * (16 * U) + ((c ^ (U == 8 ? ((r >> 1) & 7) : (r & 15))) << 4);
+}
+
+// Source offset (bytes, from the tile's first row) of what lane `lane` of
+// copy n brings to LDS: copy n fills LDS bytes 1024 n .. +1023, i.e. rows
+// (64/U) n .. +64/U-1, unit position lane % U of row (64/U) n + lane / U.
+template <int U>
+__device__ inline uint32_t op_src(int n, int lane, size_t row_bytes) {
+  const int r = (64 / U) * n + lane / U, pos = lane % U;
+  const int c = pos ^ (U == 8 ? ((r >> 1) & 7) : (r & 15));
+  return uint32_t(r * row_bytes + 16 * c);
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 40
+__device__ inline void op_wait_vm(int n) {
+  switch (n) {
+#define MLA_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    MLA_W(0) MLA_W(1) MLA_W(2) MLA_W(3) MLA_W(4) MLA_W(5) MLA_W(6) MLA_W(7) MLA_W(8)
+    MLA_W(9) MLA_W(10) MLA_W(11) MLA_W(12) MLA_W(13) MLA_W(14) MLA_W(15) MLA_W(16)
+    MLA_W(17) MLA_W(18) MLA_W(19) MLA_W(20) MLA_W(21) MLA_W(22) MLA_W(23) MLA_W(24)
+    MLA_W(25) MLA_W(26) MLA_W(27) MLA_W(28) MLA_W(29) MLA_W(30) MLA_W(31) MLA_W(32)
+    MLA_W(33) MLA_W(34) MLA_W(35) MLA_W(36) MLA_W(37) MLA_W(38) MLA_W(39) MLA_W(40)
+#undef MLA_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// NW waves (feature block of 32 NW rows of W^O), up to MT token tiles of 32,
+// NBUF ring slots (NBUF - 1 stages copied ahead of the one computed), stages
+// of 8 U values of K (U 16-byte units per row).
+template <int NW, int MT, int NBUF, int U>
+__global__ __launch_bounds__(64 * NW) void out_proj_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_o,
+    float* __restrict__ part, int n_tok, int d_model, int K) {
+  constexpr int OP_KS = 8 * U;                   // K per stage
+  constexpr int OP_NST = OP_KB / OP_KS;          // stages per workgroup
+  constexpr int CPR = U / 2;                     // 1 KB copies per 32 rows
+  constexpr int WBYTES = 32 * NW * OP_KS * 2;    // W^O rows of a stage
+  constexpr int XBYTES = 32 * OP_KS * 2;         // per token tile
+  constexpr int SLOT = WBYTES + MT * XBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF][SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int fb = blockIdx.x, kb = blockIdx.y, tg = blockIdx.z;
+  const int f0 = fb * 32 * NW, k0 = kb * OP_KB, t0 = tg * (32 * MT);
+  const int mt = min(MT, (n_tok - t0 + 31) / 32);           // token tiles in this group
+  const size_t row_bytes = (size_t)K * 2;
+
+  // buffer descriptors: W^O rows f0 .. f0+32NW-1, token rows t0 .. n_tok-1
+  // (rows past n_tok are out of range: the hardware writes zeros)
+  const uint64_t wa = (uint64_t)(w_o + (size_t)f0 * K + k0);
+  const u32x4 wrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)wa),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(wa >> 32)) & 0xFFFFu,
+                     0xFFFFFFFFu, 0x00020000u};
+  const uint64_t xa = (uint64_t)(x + (size_t)t0 * K + k0);
+  const u32x4 xrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xa),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(xa >> 32)) & 0xFFFFu,
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(
+                         (size_t)(n_tok - t0) * row_bytes - (size_t)k0 * 2)),
+                     0x00020000u};
+  // wave w copies its own 32 W^O rows (copies CPR w .. CPR w + CPR-1 of the
+  // stage) and, for w < 4, copies CPR/4 w .. of every token tile; the
+  // stage's K offset goes in the scalar offset
+  constexpr int XPW = CPR / 4;                   // token-tile copies per copying wave
+  uint32_t wsrc[CPR];
+#pragma unroll
+  for (int j = 0; j < CPR; ++j) wsrc[j] = op_src<U>(CPR * wave + j, lane, row_bytes);
+  uint32_t xsrc[MT][XPW];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      const int n = XPW * (wave & 3) + j;
+      const uint32_t o = op_src<U>(n, lane, row_bytes) + uint32_t(32 * t) * uint32_t(row_bytes);
+      xsrc[t][j] = (32 * t + (64 / U) * n + lane / U < n_tok - t0) ? o : kOpOOB;
+    }
+  const bool x_copier = wave < 4;
+  const int per_stage = CPR + (x_copier ? XPW * mt : 0);    // this wave's copies per stage
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&ring[0][0];
+
+  auto issue = [&](int st) {           // copies of stage st into slot st % NBUF
+    const uint32_t slot = lds0 + (st % NBUF) * SLOT;
+    const uint32_t koff = __builtin_amdgcn_readfirstlane(st * OP_KS * 2);
+#pragma unroll
+    for (int j = 0; j < CPR; ++j)
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :: "s"(slot + 1024 * (CPR * wave + j)), "v"(wsrc[j]), "s"(wrs), "s"(koff)
+                   : "memory");
+    if (x_copier) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if (t < mt)
+#pragma unroll
+          for (int j = 0; j < XPW; ++j)
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                         :: "s"(slot + WBYTES + XBYTES * t + 1024 * (XPW * wave + j)),
+                            "v"(xsrc[t][j]), "s"(xrs), "s"(koff)
+                         : "memory");
+    }
+  };
+
+  floatx16 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = floatx16{};
+  // operand reads: row l % 32 of the wave's 32 features / of a token tile,
+  // 16-byte unit 2 s + l / 32 for k16 step s of the stage
+  const int r32 = lane & 31, hh = lane >> 5;
+
+  constexpr int AHEAD = NBUF - 1;
+  for (int st = 0; st < AHEAD && st < OP_NST; ++st) issue(st);
+  for (int st = 0; st < OP_NST; ++st) {
+    // stage st landed: the later stages' copies may still fly
+    op_wait_vm(min(AHEAD - 1, OP_NST - 1 - st) * per_stage);
+    __syncthreads();                   // every wave's copies landed; stage st-1 was read
+    if (st + AHEAD < OP_NST) issue(st + AHEAD);
+    const uint8_t* slot = &ring[st % NBUF][0];
+#pragma unroll
+    for (int s = 0; s < U / 2; ++s) {
+      const int c = 2 * s + hh;
+      const bf16x8 a = *(const bf16x8*)(slot + op_swz<U>(32 * wave + r32, c));
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (t < mt) {
+          const bf16x8 b = *(const bf16x8*)(slot + WBYTES + XBYTES * t + op_swz<U>(r32, c));
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // acc[t][r]: feature f0 + 32 wave + 8 (r/4) + 4 hh + r%4, token t0 + 32 t + r32
+  float* pk = part + (size_t)kb * n_tok * d_model;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int tok = t0 + 32 * t + r32;
+    if (t < mt && tok < n_tok) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(floatx4*)(pk + (size_t)tok * d_model + f0 + 32 * wave + 8 * q + 4 * hh) =
+            floatx4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+    }
+  }
+}
+
+// u = sum over the K blocks of the partials; four consecutive outputs per thread.
+template <typename OutT>
+__global__ __launch_bounds__(256) void out_proj_reduce_kernel(
+    const float* __restrict__ part, OutT* __restrict__ u, size_t n4, int nkb) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  // every K block's partial is loaded before any is added (at most 16 in
+  // flight), then summed in K-block order
+  floatx4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < nkb; k0 += 16) {
+    floatx4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < nkb) v[k] = *(const floatx4*)(part + (size_t)(k0 + k) * 4 * n4 + 4 * i);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < nkb) s += v[k];
+  }
+  if constexpr (sizeof(OutT) == 4) {
+    *(floatx4*)(u + 4 * i) = s;
+  } else {
+    *(u32x2*)(u + 4 * i) = u32x2{uint32_t(f32_to_bf16_bits(s[0])) | (uint32_t(f32_to_bf16_bits(s[1])) << 16),
+                                 uint32_t(f32_to_bf16_bits(s[2])) | (uint32_t(f32_to_bf16_bits(s[3])) << 16)};
+  }
+}
+
+template <typename T>
+__device__ inline float op_load(const T* p, size_t i) {
+  if constexpr (sizeof(T) == 4) return p[i];
+  else return bf16_bits_to_f32(p[i]);
+}
+
+// General path: u[n, f] = sum_k x[n, k] W^O[f, k], one thread per output.
+template <typename XT, typename WT, typename OutT>
+__global__ __launch_bounds__(256) void out_proj_general_kernel(
+    const XT* __restrict__ x, const WT* __restrict__ w_o, OutT* __restrict__ u, int n_tok,
+    int d_model, int K) {
+  const size_t total = (size_t)n_tok * d_model;
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * 256) {
+    const size_t n = idx / d_model, f = idx % d_model;
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) acc = fmaf(op_load(x, n * K + k), op_load(w_o, f * K + k), acc);
+    if constexpr (sizeof(OutT) == 4) u[idx] = acc;
+    else u[idx] = f32_to_bf16_bits(acc);
+  }
+}
+
+bool out_proj_fast(int d_model, int K, int x_dtype, int w_dtype) {
+  return x_dtype == MLA_BF16 && w_dtype == MLA_BF16 && d_model % 128 == 0 &&
+         K % OP_KB == 0 && d_model > 0;
+}
+
+size_t out_proj_workspace(int d_model, int K, int n_tok, int x_dtype, int w_dtype) {
+  if (!out_proj_fast(d_model, K, x_dtype, w_dtype)) return 0;
+  return (size_t)(K / OP_KB) * n_tok * d_model * sizeof(float);
+}
+
+hipError_t launch_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype,
+                           void* u, bool u_f32, int n_tok, int d_model, int K,
+                           void* workspace, hipStream_t st) {
+  if (out_proj_fast(d_model, K, x_dtype, w_dtype)) {
+    // feature blocks of 160 rows (5 waves) when they divide d_model, else
+    // 128; one token tile with a 6-slot ring for at most 32 tokens, else
+    // groups of 4 token tiles with a 4-slot ring
+    const int nw = (d_model % 160 == 0) ? 5 : 4;
+    const int mt = (n_tok <= 32) ? 1 : 4;
+    const dim3 grid(d_model / (32 * nw), K / OP_KB, (n_tok + 32 * mt - 1) / (32 * mt));
+    const uint16_t* xp = (const uint16_t*)x;
+    const uint16_t* wp = (const uint16_t*)w_o;
+    float* pp = (float*)workspace;
+    if (nw == 5 && mt == 1)
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+    else if (nw == 5)
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+    else if (mt == 1)
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+    else
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+    const size_t n4 = (size_t)n_tok * d_model / 4;
+    const dim3 rgrid((unsigned)((n4 + 255) / 256));
+    if (u_f32)
+      hipLaunchKernelGGL(out_proj_reduce_kernel<float>, rgrid, dim3(256), 0, st,
+                         (const float*)workspace, (float*)u, n4, K / OP_KB);
+    else
+      hipLaunchKernelGGL(out_proj_reduce_kernel<uint16_t>, rgrid, dim3(256), 0, st,
+                         (const float*)workspace, (uint16_t*)u, n4, K / OP_KB);
+    return hipGetLastError();
+  }
+  const size_t total = (size_t)n_tok * d_model;
+  const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
+#define MLA_OP(XT, WT, OT)                                                               \
+  hipLaunchKernelGGL((out_proj_general_kernel<XT, WT, OT>), dim3(grid), dim3(256), 0, st, \
+                     (const XT*)x, (const WT*)w_o, (OT*)u, n_tok, d_model, K)
+  if (x_dtype == MLA_F32) {
+    if (w_dtype == MLA_F32) { if (u_f32) MLA_OP(float, float, float); else MLA_OP(float, float, uint16_t); }
+    else { if (u_f32) MLA_OP(float, uint16_t, float); else MLA_OP(float, uint16_t, uint16_t); }
+  } else {
+    if (w_dtype == MLA_F32) { if (u_f32) MLA_OP(uint16_t, float, float); else MLA_OP(uint16_t, float, uint16_t); }
+    else { if (u_f32) MLA_OP(uint16_t, uint16_t, float); else MLA_OP(uint16_t, uint16_t, uint16_t); }
+  }
+#undef MLA_OP
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -211,6 +211,28 @@ int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent,
                       const void* w_uv, void* out, int32_t out_dtype,
                       int32_t n_tokens, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Attention output projection ("DeepSeek-V3 Technical Report" notes, MLA
+ * section, the equation after the attention-output equation):
+ *
+ *   u[n, :] = W^O [o[n, 0, :]; o[n, 1, :]; ...; o[n, n_h-1, :]]  (fp32 accumulate)
+ *
+ * o [n_tokens, n_h, d_h] in o_dtype (MLA_F32 or MLA_BF16), e.g. written by
+ * mla_up_proj_v; w_o [d_model, n_h*d_h] row-major in q_dtype; u [n_tokens,
+ * d_model] in u_dtype (MLA_F32, or MLA_BF16 rounded to nearest even).
+ * workspace/ws_bytes: at least mla_out_proj_workspace_size() bytes (fp32
+ * partial sums; the size is 0, and workspace may be NULL, when the shapes do
+ * not take the matrix-core path).  Errors: MLA_ERR_NULL, MLA_ERR_DTYPE,
+ * MLA_ERR_ARG (d_model or n_tokens < 1), MLA_ERR_ALIGN (any pointer not
+ * 16-byte aligned), MLA_ERR_WORKSPACE; nothing is enqueued on an error.   */
+int32_t mla_out_proj_workspace_size(const mla_dims_t* dims, int32_t d_model,
+                                    int32_t n_tokens, int32_t o_dtype,
+                                    size_t* bytes);
+int32_t mla_out_proj(const mla_dims_t* dims, const void* o, int32_t o_dtype,
+                     const void* w_o, int32_t d_model, void* u, int32_t u_dtype,
+                     int32_t n_tokens, void* workspace, size_t ws_bytes,
+                     void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

@@ -95,6 +95,28 @@ def test_decode_validation(mla):
                                None, 0, FAKE, FAKE, None) == NULL
 
 
+def test_out_proj_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    sz = ctypes.c_size_t(0)
+    assert lib.mla_out_proj_workspace_size(ctypes.byref(d), 5120, 32, 1, ctypes.byref(sz)) == OK
+    assert sz.value == 8 * 32 * 5120 * 4          # 8 K blocks of fp32 partials
+    assert lib.mla_out_proj_workspace_size(ctypes.byref(d), 5120, 32, 0, ctypes.byref(sz)) == OK
+    assert sz.value == 0                          # fp32 o: no matrix-core path, no workspace
+    assert lib.mla_out_proj_workspace_size(ctypes.byref(d), 0, 32, 1, ctypes.byref(sz)) == ARG
+    assert lib.mla_out_proj_workspace_size(ctypes.byref(d), 5120, 32, 2, ctypes.byref(sz)) == DTYPE
+    op = lib.mla_out_proj
+    assert op(ctypes.byref(d), None, 1, FAKE, 5120, FAKE, 0, 32, FAKE, 1 << 30, None) == NULL
+    assert op(ctypes.byref(d), FAKE, 1, None, 5120, FAKE, 0, 32, FAKE, 1 << 30, None) == NULL
+    assert op(ctypes.byref(d), FAKE, 2, FAKE, 5120, FAKE, 0, 32, FAKE, 1 << 30, None) == DTYPE
+    assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 2, 32, FAKE, 1 << 30, None) == DTYPE
+    assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 0, 0, FAKE, 1 << 30, None) == ARG
+    assert op(ctypes.byref(d), FAKE, 1, FAKE, -1, FAKE, 0, 32, FAKE, 1 << 30, None) == ARG
+    assert op(ctypes.byref(d), FAKE, 1, MIS, 5120, FAKE, 0, 32, FAKE, 1 << 30, None) == ALIGN
+    assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 0, 32, None, 0, None) == WS
+    assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 0, 32, FAKE, 1024, None) == WS
+
+
 def test_absorb_append_upproj_validation(mla):
     lib, b = mla
     d = _v2(b)

@@ -383,3 +383,52 @@ def test_graph_replays_match_eager(w):
         for name, got, want in zip(("o", "latent", "lse"), (buf.o, buf.latent, buf.lse), eager):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
     say(f"  3 replays bit-identical to the eager step")
+
+
+
+# ------------------------------------------- output projection u = W^O [o_1; ...]
+OUT_PROJ = [
+    (V2, 32, "f32"),            # the benchmark's 32 tokens, one token tile
+    (V2, 45, "bf16"),           # a ragged second token tile, bf16 output
+    (V2, 200, "f32"),           # two token groups (128 + 72)
+    (small_variant(V2, name="v2_d256", d_model=256), 7, "f32"),
+    (WORKLOADS["tiny_fp32"], 5, "f32"),                           # general path (fp32)
+    (small_variant(V2, name="v2_d200", d_model=200), 9, "bf16"),  # general path (d % 128 != 0)
+]
+
+
+@pytest.mark.parametrize("w,n_tok,u_kind", OUT_PROJ,
+                         ids=[f"{c[0].name}-{c[1]}-{c[2]}" for c in OUT_PROJ])
+def test_out_proj_parity(w, n_tok, u_kind):
+    """u = W^O [o_1; ...; o_{n_h}] through the C ABI against the oracle, on all
+    outputs; o is drawn here (seeded) in the query format, W^O by the input
+    generator; u in fp32 or bf16."""
+    from head_latent_attention_11_amd import binding as B
+    from head_latent_attention_11_amd.runner import to_device
+    from mla_inputs import output_weights
+    say(f"case out_proj {w.name}: n_tok={n_tok} d_model={w.d_model} K={w.n_heads * w.d_head} "
+        f"u={u_kind}")
+    kind = "f32" if w.q_dtype == "f32" else "bf16"
+    rng = np.random.default_rng(91)
+    o32 = rng.standard_normal((n_tok, w.n_heads, w.d_head)).astype(np.float32)
+    from mla_inputs import bf16_bits_from_f32
+    o_st = o32 if kind == "f32" else bf16_bits_from_f32(o32)
+    w_o = output_weights(w)
+    dims = B.MLADims.from_workload(w)
+    o_d = to_device(o_st, kind, "cuda")
+    w_d = to_device(w_o, kind, "cuda")
+    udt = torch.float32 if u_kind == "f32" else torch.bfloat16
+    u = torch.full((n_tok, w.d_model), float("nan"), dtype=udt, device="cuda")
+    o_code = B.F32 if kind == "f32" else B.BF16
+    wsb = B.out_proj_workspace_size(dims, w.d_model, n_tok, o_code)
+    ws = (torch.full(((wsb + 15) // 16 * 4,), float("nan"), dtype=torch.float32, device="cuda")
+          if wsb else None)
+    B.out_proj(dims, o_d, w_d, w.d_model, u, n_tok, ws, wsb)
+    torch.cuda.synchronize()
+    got = to_np(u)
+    assert np.all(np.isfinite(got))
+    o64 = o_st.astype(np.float64) if kind == "f32" else formats.bf16_to_f64(o_st)
+    w64 = w_o.astype(np.float64) if kind == "f32" else formats.bf16_to_f64(w_o)
+    ref = omla.output_project(o64, w64)
+    # exact bf16 products, fp32 sums over K = n_h d_h; bf16 output adds 2^-9
+    check("u", got, ref, 1e-5 if u_kind == "f32" else 4e-3)
