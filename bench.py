@@ -125,6 +125,56 @@ def cpu_baseline(w, gen, budget_s: float):
     }
 
 
+def time_out_proj(w, buf, stream):
+    """The attention output projection u = W^O [o_1; ...; o_{n_h}] that follows
+    the step (not part of it): its own HIP-event time over graph replays of 20
+    calls on the step's o (as bf16), W^O [d_model, n_h d_h] bf16 drawn by the
+    input generator and replicated so that the memory-side cache cannot hold
+    it.  Bound: streaming W^O from HBM."""
+    import numpy as np
+    import torch
+    from head_latent_attention_11_amd import binding as B
+    from mla_inputs import output_weights
+    K = w.n_heads * w.d_head
+    w_bytes = w.d_model * K * 2
+    reps = max(2, -(-512 * 2 ** 20 // w_bytes))
+    w0 = torch.from_numpy(output_weights(w).view(np.int16)).to("cuda").view(torch.bfloat16)
+    w_o = [w0] + [w0.clone() for _ in range(reps - 1)]
+    o = buf.o.to(torch.bfloat16).contiguous()
+    u = torch.empty((buf.n_tok, w.d_model), dtype=torch.float32, device="cuda")
+    wsb = B.out_proj_workspace_size(buf.dims, w.d_model, buf.n_tok, B.BF16)
+    ws = torch.empty(((wsb + 15) // 16 * 4,), dtype=torch.float32, device="cuda") if wsb else None
+    calls = 20
+
+    def fn():
+        for i in range(calls):
+            B.out_proj(buf.dims, o, w_o[i % reps], w.d_model, u, buf.n_tok, ws, wsb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (5 * calls)
+    byts = w_bytes + buf.n_tok * K * 2 + buf.n_tok * w.d_model * 4
+    res = {"us": round(t * 1e6, 2), "d_model": w.d_model, "n_tokens": buf.n_tok,
+           "bytes_alg": byts, "achieved_GBps": round(byts / t / 1e9, 1),
+           "frac_hbm": round(byts / t / 1e9 / HBM_PEAK_GBPS, 4)}
+    del w_o, g
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +183,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
+    ap.add_argument("--no-out-proj", action="store_true",
+                    help="skip the timing of the output projection that follows the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a calibration copy and a few attention calls for "
@@ -310,6 +362,8 @@ def main():
         "step_us_events": round(ms_step_events * 1e3, 2),
         "roofline": roof,
     }
+    if w.q_dtype == "bf16" and not args.no_out_proj:
+        out["out_proj"] = time_out_proj(w, buf, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, gen, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -5,7 +5,7 @@
 //
 // With K = n_h d_h (16384 for DeepSeek-V2) and the few query tokens of a
 // decode step, this is a skinny GEMM that streams W^O (d x K bf16, 168 MB
-// for d = 5120) from HBM once per group of up to 128 tokens; the tokens'
+// for d = 5120) from HBM once per group of up to 256 tokens; the tokens'
 // concatenated heads (M x K bf16) are re-read from L2 by every feature block.
 //
 // Matrix-core path (bf16 W^O and o, d % 128 == 0, K % 2048 == 0):
@@ -253,22 +253,27 @@ hipError_t launch_out_proj(const void* x, int x_dtype, const void* w_o, int w_dt
                            void* workspace, hipStream_t st) {
   if (out_proj_fast(d_model, K, x_dtype, w_dtype)) {
     // feature blocks of 160 rows (5 waves) when they divide d_model, else
-    // 128; one token tile with a 6-slot ring for at most 32 tokens, else
-    // groups of 4 token tiles with a 4-slot ring
+    // 128; one token tile with a 6-slot ring for at most 32 tokens, groups
+    // of 4 token tiles with a 4-slot ring up to 128 tokens, else groups of 8
+    // token tiles (W^O streamed once per 256 tokens) with a 3-slot ring
     const int nw = (d_model % 160 == 0) ? 5 : 4;
-    const int mt = (n_tok <= 32) ? 1 : 4;
+    const int mt = (n_tok <= 32) ? 1 : (n_tok <= 128) ? 4 : 8;
     const dim3 grid(d_model / (32 * nw), K / OP_KB, (n_tok + 32 * mt - 1) / (32 * mt));
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w_o;
     float* pp = (float*)workspace;
     if (nw == 5 && mt == 1)
       hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
-    else if (nw == 5)
+    else if (nw == 5 && mt == 4)
       hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+    else if (nw == 5)
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 8, 3, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
     else if (mt == 1)
       hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
-    else
+    else if (mt == 4)
       hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+    else
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 8, 3, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
     const size_t n4 = (size_t)n_tok * d_model / 4;
     const dim3 rgrid((unsigned)((n4 + 255) / 256));
     if (u_f32)

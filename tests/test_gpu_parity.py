@@ -392,6 +392,7 @@ OUT_PROJ = [
     (V2, 45, "bf16"),           # a ragged second token tile, bf16 output
     (V2, 200, "f32"),           # two token groups (128 + 72)
     (small_variant(V2, name="v2_d256", d_model=256), 7, "f32"),
+    (small_variant(V2, name="v2_d640", d_model=640), 300, "bf16"),   # groups of 256 + 44 tokens
     (WORKLOADS["tiny_fp32"], 5, "f32"),                           # general path (fp32)
     (small_variant(V2, name="v2_d200", d_model=200), 9, "bf16"),  # general path (d % 128 != 0)
 ]
