@@ -240,6 +240,24 @@ def output_weights(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     return _gauss(np.random.default_rng(ss), (w.d_model, K), 1.0 / math.sqrt(K), wdt)
 
 
+def producer_inputs(w: Workload, n_rows: int, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Inputs of the cache producer, from their own stream (child
+    len(FIELDS) + 1 of the workload's seed): hidden states h [n_rows, d_model]
+    ~ N(0, 1); [W^DKV; W^KR] [d_c + d_h^R, d_model] ~ N(0, 1/d_model) (unit-
+    variance outputs), both rounded like the queries / weights; an RMS-norm
+    gain [d_c] ~ N(1, 0.1^2) in fp32."""
+    seed = w.seed if seed is None else seed
+    ss = np.random.SeedSequence(seed).spawn(len(FIELDS) + 2)[len(FIELDS) + 1]
+    rng = np.random.default_rng(ss)
+    wdt = "f32" if w.q_dtype == "f32" else "bf16"
+    D = w.d_latent + w.d_rope
+    return {
+        "h": _gauss(rng, (n_rows, w.d_model), 1.0, w.q_dtype),
+        "w_dkv_kr": _gauss(rng, (D, w.d_model), 1.0 / math.sqrt(w.d_model), wdt),
+        "gain": (1.0 + 0.1 * rng.standard_normal(w.d_latent)).astype(np.float32),
+    }
+
+
 def small_variant(w: Workload, **changes) -> Workload:
     """A copy of ``w`` with some fields changed (used for scaled-down tests)."""
     return dataclasses.replace(w, **changes)

@@ -130,6 +130,28 @@ def up_project(latent: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     return out
 
 
+def produce_rows(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, gain, eps: float,
+                 pos=None, rope_base: float = 10000.0) -> np.ndarray:
+    """The cache row of each token, from its hidden state h_t ([V3] notes, MLA
+    section: c^KV_t = W^DKV h_t and k^R_t = RoPE(W^KR h_t); [V2] section 3.2.1:
+    an RMS norm follows the compressed latent vector):
+        c = W^DKV h,  c <- c * gain / sqrt(mean(c^2) + eps)  (gain None: no norm),
+        k = W^KR h, rotated at position pos (pos None: not rotated),
+        row = [c ; k].
+
+    h [N, d], w_dkv [d_c, d], w_kr [d_h^R, d], gain [d_c] or None, pos [N]
+    -> [N, d_c + d_h^R] (float64).
+    """
+    c = h @ w_dkv.T
+    if gain is not None:
+        rms = np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
+        c = c / rms * np.asarray(gain, dtype=np.float64)[None, :]
+    k = h @ w_kr.T
+    if pos is not None:
+        k = _rope(k, np.asarray(pos), rope_base)
+    return np.concatenate([c, k], axis=1)
+
+
 def output_project(o: np.ndarray, w_o: np.ndarray) -> np.ndarray:
     """u_n = W^O [o_{n,1}; o_{n,2}; ...; o_{n,n_h}]: the attention output
     projection of the [V3] notes, MLA section (the equation after the

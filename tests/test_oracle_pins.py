@@ -474,3 +474,49 @@ def test_output_projection_special_cases():
     np.testing.assert_allclose(mla.output_project(2.0 * o - 3.0 * o2, w_o),
                                2.0 * mla.output_project(o, w_o) - 3.0 * mla.output_project(o2, w_o),
                                rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ cache producer (W^DKV, W^KR)
+def test_producer_rms_norm_closed_forms():
+    """With unit gain and eps = 0 every c part has RMS exactly 1; scaling h by
+    a > 0 leaves the normalised c unchanged and scales k by a; the gain
+    multiplies elementwise; without a gain c is the plain projection."""
+    rng = np.random.default_rng(51)
+    n, d, d_c, d_r = 4, 9, 6, 4
+    h = rng.standard_normal((n, d))
+    w_dkv, w_kr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    rows = mla.produce_rows(h, w_dkv, w_kr, np.ones(d_c), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(rows[:, :d_c] ** 2, axis=1)), 1.0, rtol=1e-13)
+    rows3 = mla.produce_rows(3.0 * h, w_dkv, w_kr, np.ones(d_c), 0.0)
+    np.testing.assert_allclose(rows3[:, :d_c], rows[:, :d_c], rtol=1e-12)
+    np.testing.assert_allclose(rows3[:, d_c:], 3.0 * rows[:, d_c:], rtol=1e-12)
+    g = rng.standard_normal(d_c)
+    np.testing.assert_allclose(mla.produce_rows(h, w_dkv, w_kr, g, 0.0)[:, :d_c],
+                               rows[:, :d_c] * g[None, :], rtol=1e-12)
+    plain = mla.produce_rows(h, w_dkv, w_kr, None, 0.0)
+    np.testing.assert_allclose(plain[:, :d_c], h @ w_dkv.T, rtol=1e-13)
+    # eps: c / sqrt(mean c^2 + eps) for a row of equal entries 2: 2 / sqrt(4 + 5) = 2/3
+    one = mla.produce_rows(np.ones((1, 1)), np.full((d_c, 1), 2.0), np.zeros((d_r, 1)),
+                           np.ones(d_c), 5.0)
+    np.testing.assert_allclose(one[0, :d_c], 2.0 / 3.0, rtol=1e-14)
+
+
+def test_producer_selection_weights_and_rope():
+    """Unit-vector rows of W^DKV / W^KR pick entries of h (catches a
+    transposed operand); the k part is rotated at its token's position, and
+    position 0 leaves it unrotated (R_0 = I)."""
+    rng = np.random.default_rng(52)
+    n, d, d_c, d_r = 3, 8, 3, 4
+    h = rng.standard_normal((n, d))
+    w_dkv = np.eye(d)[[5, 0, 2]]
+    w_kr = np.eye(d)[[1, 3, 4, 7]]
+    rows = mla.produce_rows(h, w_dkv, w_kr, None, 0.0, pos=np.zeros(n, dtype=int))
+    np.testing.assert_array_equal(rows[:, :d_c], h[:, [5, 0, 2]])
+    np.testing.assert_allclose(rows[:, d_c:], h[:, [1, 3, 4, 7]], rtol=0, atol=1e-15)
+    pos = np.array([0, 7, 1000])
+    rot = mla.produce_rows(h, w_dkv, w_kr, None, 0.0, pos=pos)
+    np.testing.assert_allclose(rot[:, d_c:], rope(h[:, [1, 3, 4, 7]], pos), rtol=1e-13)
+    # a rotation keeps the norm of each pair
+    a = rot[:, d_c:].reshape(n, -1, 2)
+    b = h[:, [1, 3, 4, 7]].reshape(n, -1, 2)
+    np.testing.assert_allclose(np.linalg.norm(a, axis=2), np.linalg.norm(b, axis=2), rtol=1e-13)
