@@ -175,6 +175,62 @@ def time_out_proj(w, buf, stream):
     return res
 
 
+def time_kv_produce(w, buf, stream):
+    """The cache producer that precedes the step (not part of it): the rows
+    [RMSNorm(W^DKV h) ; RoPE(W^KR h)] of the step's B*T new tokens appended
+    into a cache of the step's format (a scratch one, so the step's cache is
+    left as it is); HIP-event time over graph replays of 20 calls."""
+    import torch
+    from head_latent_attention_11_amd import binding as B
+    from head_latent_attention_11_amd.runner import to_device
+    from mla_inputs import producer_inputs
+    n = buf.n_tok
+    inp = producer_inputs(w, n)
+    D = w.d_latent + w.d_rope
+    h = to_device(inp["h"], "bf16", "cuda")
+    wk = to_device(inp["w_dkv_kr"], "bf16", "cuda")
+    gain = torch.from_numpy(inp["gain"]).cuda()
+    seq = torch.arange(n, dtype=torch.int32, device="cuda") // w.q_tokens
+    pos = (torch.arange(n, dtype=torch.int32, device="cuda") % w.q_tokens)
+    B_, ml = w.batch, w.q_tokens
+    if w.kv_dtype == "fp8":
+        cache = torch.zeros((B_ * ml, D), dtype=torch.uint8, device="cuda")
+        scale = torch.zeros((B_ * ml,), dtype=torch.float32, device="cuda")
+    else:
+        cache = torch.zeros((B_ * ml, D), dtype=torch.bfloat16, device="cuda")
+        scale = None
+    wsb = B.kv_produce_workspace_size(buf.dims, w.d_model, n)
+    ws = torch.empty(((wsb + 15) // 16 * 4,), dtype=torch.float32, device="cuda")
+    calls = 20
+
+    def fn():
+        for _ in range(calls):
+            B.kv_produce(buf.dims, h, w.d_model, wk, gain, 1e-6, seq, pos, None, B_, 0, ml,
+                         B_ * ml, True, cache, scale, n, ws, wsb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (5 * calls)
+    byts = D * w.d_model * 2 + n * w.d_model * 2 + n * (D * (1 if w.kv_dtype == "fp8" else 2))
+    return {"us": round(t * 1e6, 2), "d_model": w.d_model, "n_rows": n, "bytes_alg": byts,
+            "achieved_GBps": round(byts / t / 1e9, 1),
+            "frac_hbm": round(byts / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +240,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
     ap.add_argument("--no-out-proj", action="store_true",
-                    help="skip the timing of the output projection that follows the step")
+                    help="skip the timings of the cache producer and of the output "
+                         "projection around the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a calibration copy and a few attention calls for "
@@ -364,6 +421,7 @@ def main():
     }
     if w.q_dtype == "bf16" and not args.no_out_proj:
         out["out_proj"] = time_out_proj(w, buf, stream)
+        out["kv_produce"] = time_kv_produce(w, buf, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, gen, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -22,6 +22,7 @@ PRECISION_CODES = {"bf16": PREC_BF16, "fp32": PREC_FP32}
 
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
+            "mla_kv_produce_workspace_size", "mla_kv_produce",
             "mla_status_string", "mla_version")
 
 
@@ -84,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_up_proj_v.argtypes = [pdims, vp, vp, vp, i32, i32, vp]
     lib.mla_out_proj_workspace_size.argtypes = [pdims, i32, i32, i32, ctypes.POINTER(sz)]
     lib.mla_out_proj.argtypes = [pdims, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp]
+    lib.mla_kv_produce_workspace_size.argtypes = [pdims, i32, i32, ctypes.POINTER(sz)]
+    lib.mla_kv_produce.argtypes = [pdims, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, i32, i32,
+                                   i32, i64, i32, vp, vp, i32, vp, sz, vp]
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_version.argtypes = []
@@ -212,3 +216,25 @@ def out_proj(dims: MLADims, o, w_o, d_model: int, u, n_tokens: int, workspace, w
     _check(lib.mla_out_proj(ctypes.byref(dims), _ptr(o), int(o_dtype), _ptr(w_o), int(d_model),
                             _ptr(u), int(u_dtype), int(n_tokens), _ptr(workspace), int(ws_bytes),
                             _stream(stream)), "mla_out_proj")
+
+
+def kv_produce_workspace_size(dims: MLADims, d_model: int, n_rows: int) -> int:
+    lib = load_library()
+    out = ctypes.c_size_t(0)
+    _check(lib.mla_kv_produce_workspace_size(ctypes.byref(dims), int(d_model), int(n_rows),
+                                             ctypes.byref(out)), "mla_kv_produce_workspace_size")
+    return int(out.value)
+
+
+def kv_produce(dims: MLADims, h, d_model: int, w_dkv_kr, norm_gain, norm_eps: float, seq_idx,
+               pos, page_table, batch: int, max_pages: int, max_len: int, cache_rows: int,
+               apply_rope: bool, cache, kv_scale, n_rows: int, workspace, ws_bytes: int,
+               stream=None):
+    """Cache rows [RMSNorm(W^DKV h) | RoPE(W^KR h)] appended at (seq_idx, pos)."""
+    lib = load_library()
+    _check(lib.mla_kv_produce(ctypes.byref(dims), _ptr(h), int(d_model), _ptr(w_dkv_kr),
+                              _ptr(norm_gain), float(norm_eps), _ptr(seq_idx), _ptr(pos),
+                              _ptr(page_table), int(batch), int(max_pages), int(max_len),
+                              int(cache_rows), int(bool(apply_rope)), _ptr(cache), _ptr(kv_scale),
+                              int(n_rows), _ptr(workspace), int(ws_bytes), _stream(stream)),
+           "mla_kv_produce")

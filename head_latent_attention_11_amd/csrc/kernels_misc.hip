@@ -233,14 +233,17 @@ __global__ __launch_bounds__(256) void absorb_general_kernel(
 }
 
 // ================================================================ append
-// One wave per new row.  Source rows are F32 (F32 cache) or BF16.
+// One wave per new row.  Source rows are F32 or BF16, row r of new_c at
+// r * c_stride (elements), of new_kr at r * kr_stride.  With norm_gain, the
+// c^KV part is RMS-normalised first: c_i * g_i / sqrt(mean(c^2) + eps).
 template <typename SrcT, int KV>
 __global__ __launch_bounds__(256) void append_kernel(
     const SrcT* __restrict__ new_c, const SrcT* __restrict__ new_kr,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
     long long cache_rows, int apply_rope, void* __restrict__ cache,
-    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, float rope_base) {
+    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, float rope_base,
+    int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps) {
   const int lane = threadIdx.x & 63;
   const int D = d_c + d_r;
   for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += gridDim.x * 4) {
@@ -266,23 +269,36 @@ __global__ __launch_bounds__(256) void append_kernel(
       const int e = lane + 64 * k;
       float x = 0.f;
       if (e < d_c) {
-        x = load_f(new_c, (size_t)r * d_c + e);
+        x = load_f(new_c, (size_t)r * c_stride + e);
       } else if (e < D) {
         const int q = e - d_c;
         if (apply_rope) {
           const int kp = q >> 1;
-          float x0 = load_f(new_kr, (size_t)r * d_r + 2 * kp);
-          float x1 = load_f(new_kr, (size_t)r * d_r + 2 * kp + 1);
+          float x0 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp);
+          float x1 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp + 1);
           float y0, y1;
           rope_pair(x0, x1, p, kp, d_r, rope_base, &y0, &y1);
           x = (q & 1) ? y1 : y0;
         } else {
-          x = load_f(new_kr, (size_t)r * d_r + q);
+          x = load_f(new_kr, (size_t)r * kr_stride + q);
         }
       }
       v[k] = x;
-      amax = fmaxf(amax, fabsf(x));
     }
+    if (norm_gain) {
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 10; ++k)
+        if (lane + 64 * k < d_c) ss = fmaf(v[k], v[k], ss);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      const float inv = 1.0f / sqrtf(ss / float(d_c) + norm_eps);
+#pragma unroll
+      for (int k = 0; k < 10; ++k)
+        if (lane + 64 * k < d_c) v[k] = v[k] * inv * norm_gain[lane + 64 * k];
+    }
+#pragma unroll
+    for (int k = 0; k < 10; ++k) amax = fmaxf(amax, fabsf(v[k]));
     if (KV == MLA_F32) {
       float* dst = (float*)cache + row * D;
 #pragma unroll
@@ -612,23 +628,20 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
                          const int32_t* page_table, int B, int max_pages,
                          int max_len, long long cache_rows, int apply_rope,
                          void* cache, float* kv_scale, int n_rows,
-                         float rope_base, hipStream_t st) {
+                         float rope_base, hipStream_t st, bool src_f32, int c_stride,
+                         int kr_stride, const float* norm_gain, float norm_eps) {
   const int grid = std::min((n_rows + 3) / 4, 16384);
-  if (d.kv_dtype == MLA_F32)
-    hipLaunchKernelGGL((append_kernel<float, MLA_F32>), dim3(grid), dim3(256), 0, st,
-                       (const float*)new_c, (const float*)new_kr, seq_idx, pos,
-                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
-                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
-  else if (d.kv_dtype == MLA_BF16)
-    hipLaunchKernelGGL((append_kernel<uint16_t, MLA_BF16>), dim3(grid), dim3(256), 0, st,
-                       (const uint16_t*)new_c, (const uint16_t*)new_kr, seq_idx, pos,
-                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
-                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
-  else
-    hipLaunchKernelGGL((append_kernel<uint16_t, MLA_FP8_E4M3>), dim3(grid), dim3(256), 0, st,
-                       (const uint16_t*)new_c, (const uint16_t*)new_kr, seq_idx, pos,
-                       page_table, B, max_pages, max_len, cache_rows, apply_rope,
-                       cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope_base);
+#define MLA_APPEND(ST, KV)                                                                   \
+  hipLaunchKernelGGL((append_kernel<ST, KV>), dim3(grid), dim3(256), 0, st,                  \
+                     (const ST*)new_c, (const ST*)new_kr, seq_idx, pos, page_table, B,       \
+                     max_pages, max_len, cache_rows, apply_rope, cache, kv_scale, n_rows,    \
+                     d.d_latent, d.d_rope, rope_base, c_stride, kr_stride, norm_gain, norm_eps)
+  if (d.kv_dtype == MLA_F32) MLA_APPEND(float, MLA_F32);
+  else if (d.kv_dtype == MLA_BF16 && !src_f32) MLA_APPEND(uint16_t, MLA_BF16);
+  else if (d.kv_dtype == MLA_BF16) MLA_APPEND(float, MLA_BF16);
+  else if (!src_f32) MLA_APPEND(uint16_t, MLA_FP8_E4M3);
+  else MLA_APPEND(float, MLA_FP8_E4M3);
+#undef MLA_APPEND
   return hipGetLastError();
 }
 

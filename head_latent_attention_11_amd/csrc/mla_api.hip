@@ -15,11 +15,11 @@ hipError_t launch_absorb(const mla_dims_t&, bool, const void*, const void*, cons
                          const int32_t*, void*, int, float, hipStream_t);
 hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int32_t*,
                          const int32_t*, const int32_t*, int, int, int, long long, int,
-                         void*, float*, int, float, hipStream_t);
+                         void*, float*, int, float, hipStream_t, bool, int, int, const float*,
+                         float);
 hipError_t launch_combine(const DecodeArgs&, hipStream_t);
-bool out_proj_fast(int, int, int, int);
-size_t out_proj_workspace(int, int, int, int, int);
-hipError_t launch_out_proj(const void*, int, const void*, int, void*, bool, int, int, int, void*,
+size_t gemm_xwt_workspace(int, int, int, int, int);
+hipError_t launch_gemm_xwt(const void*, int, const void*, int, void*, bool, int, int, int, void*,
                            hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
@@ -202,7 +202,82 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* 
     return MLA_ERR_ALIGN;
   return status_of(launch_append(*dims, new_c, new_kr, seq_idx, pos, page_table, batch,
                                  max_pages, max_len, cache_rows, apply_rope, cache,
-                                 kv_scale, n_rows, rope_base_of(dims), (hipStream_t)stream));
+                                 kv_scale, n_rows, rope_base_of(dims), (hipStream_t)stream,
+                                 dims->kv_dtype == MLA_F32, dims->d_latent, dims->d_rope,
+                                 nullptr, 0.f));
+}
+
+// Checks shared by the cache writers (mla_cache_append, mla_kv_produce).
+static int32_t check_append(const mla_dims_t* dims, const int32_t* seq_idx, const int32_t* pos,
+                            const int32_t* page_table, int32_t batch, int32_t max_pages,
+                            int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                            const void* cache, const float* kv_scale, int32_t n_rows) {
+  if (!seq_idx || !pos || !cache) return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_FP8_E4M3) {
+    if (!kv_scale) return MLA_ERR_NULL;
+  } else if (kv_scale) {
+    return MLA_ERR_ARG;
+  }
+  if (n_rows < 1 || batch < 1 || cache_rows < 1) return MLA_ERR_ARG;
+  if (apply_rope != 0 && apply_rope != 1) return MLA_ERR_ARG;
+  if (page_table) {
+    if (max_pages < 1) return MLA_ERR_ARG;
+  } else {
+    if (max_len < 1) return MLA_ERR_ARG;
+    if ((int64_t)batch * max_len > cache_rows) return MLA_ERR_ARG;
+  }
+  if (dims->d_latent + dims->d_rope > 640) return MLA_ERR_DIMS;
+  if (!aligned16(cache)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+static size_t produce_rows_bytes(const mla_dims_t* d, int32_t n_rows) {
+  return ((size_t)n_rows * (d->d_latent + d->d_rope) * sizeof(float) + 255) / 256 * 256;
+}
+
+int32_t mla_kv_produce_workspace_size(const mla_dims_t* dims, int32_t d_model, int32_t n_rows,
+                                      size_t* bytes) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL;
+  if (d_model < 1 || n_rows < 1) return MLA_ERR_ARG;
+  const int D = dims->d_latent + dims->d_rope;
+  *bytes = produce_rows_bytes(dims, n_rows) +
+           gemm_xwt_workspace(D, d_model, n_rows, dims->q_dtype, dims->q_dtype);
+  return MLA_OK;
+}
+
+int32_t mla_kv_produce(const mla_dims_t* dims, const void* h, int32_t d_model,
+                       const void* w_dkv_kr, const float* norm_gain, float norm_eps,
+                       const int32_t* seq_idx, const int32_t* pos, const int32_t* page_table,
+                       int32_t batch, int32_t max_pages, int32_t max_len, int64_t cache_rows,
+                       int32_t apply_rope, void* cache, float* kv_scale, int32_t n_rows,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!h || !w_dkv_kr) return MLA_ERR_NULL;
+  st = check_append(dims, seq_idx, pos, page_table, batch, max_pages, max_len, cache_rows,
+                    apply_rope, cache, kv_scale, n_rows);
+  if (st != MLA_OK) return st;
+  if (d_model < 1) return MLA_ERR_ARG;
+  if (!(norm_eps >= 0.f) || !isfinite(norm_eps)) return MLA_ERR_ARG;
+  if (!aligned16(h) || !aligned16(w_dkv_kr) || (norm_gain && !aligned16(norm_gain)) ||
+      (workspace && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  const int D = dims->d_latent + dims->d_rope;
+  const size_t rows_b = produce_rows_bytes(dims, n_rows);
+  const size_t need = rows_b + gemm_xwt_workspace(D, d_model, n_rows, dims->q_dtype,
+                                                  dims->q_dtype);
+  if (!workspace || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float* rows = (float*)workspace;
+  hipError_t e = launch_gemm_xwt(h, dims->q_dtype, w_dkv_kr, dims->q_dtype, rows, true, n_rows,
+                                 D, d_model, (char*)workspace + rows_b, s);
+  if (e != hipSuccess) return MLA_ERR_LAUNCH;
+  return status_of(launch_append(*dims, rows, rows + dims->d_latent, seq_idx, pos, page_table,
+                                 batch, max_pages, max_len, cache_rows, apply_rope, cache,
+                                 kv_scale, n_rows, rope_base_of(dims), s, true, D, D, norm_gain,
+                                 norm_eps));
 }
 
 int32_t mla_decode_workspace_size(const mla_dims_t* dims, const int32_t* seq_lens_host,
@@ -334,7 +409,7 @@ int32_t mla_out_proj_workspace_size(const mla_dims_t* dims, int32_t d_model, int
   if (!bytes) return MLA_ERR_NULL;
   if (o_dtype != MLA_F32 && o_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (d_model < 1 || n_tokens < 1) return MLA_ERR_ARG;
-  *bytes = out_proj_workspace(d_model, dims->n_heads * dims->d_head, n_tokens, o_dtype,
+  *bytes = gemm_xwt_workspace(d_model, dims->n_heads * dims->d_head, n_tokens, o_dtype,
                               dims->q_dtype);
   return MLA_OK;
 }
@@ -351,9 +426,9 @@ int32_t mla_out_proj(const mla_dims_t* dims, const void* o, int32_t o_dtype, con
   if (!aligned16(o) || !aligned16(w_o) || !aligned16(u) || (workspace && !aligned16(workspace)))
     return MLA_ERR_ALIGN;
   const int K = dims->n_heads * dims->d_head;
-  const size_t need = out_proj_workspace(d_model, K, n_tokens, o_dtype, dims->q_dtype);
+  const size_t need = gemm_xwt_workspace(d_model, K, n_tokens, o_dtype, dims->q_dtype);
   if (need > 0 && (!workspace || ws_bytes < need)) return MLA_ERR_WORKSPACE;
-  return status_of(launch_out_proj(o, o_dtype, w_o, dims->q_dtype, u, u_dtype == MLA_F32,
+  return status_of(launch_gemm_xwt(o, o_dtype, w_o, dims->q_dtype, u, u_dtype == MLA_F32,
                                    n_tokens, d_model, K, workspace, (hipStream_t)stream));
 }
 

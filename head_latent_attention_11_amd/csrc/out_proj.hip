@@ -32,7 +32,6 @@
 namespace mla {
 
 namespace {
-constexpr int OP_KB = 2048;            // K per workgroup (one partial per K block)
 constexpr uint32_t kOpOOB = 0x40000000u;
 #ifndef OP_V1_U
 #define OP_V1_U 8                      // one token tile: 16-byte units per row and stage
@@ -80,9 +79,9 @@ __device__ inline void op_wait_vm(int n) {
 template <int NW, int MT, int NBUF, int U>
 __global__ __launch_bounds__(64 * NW) void out_proj_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_o,
-    float* __restrict__ part, int n_tok, int d_model, int K) {
+    float* __restrict__ part, int n_tok, int d_model, int K, int kb_size) {
   constexpr int OP_KS = 8 * U;                   // K per stage
-  constexpr int OP_NST = OP_KB / OP_KS;          // stages per workgroup
+  const int OP_NST = kb_size / OP_KS;            // stages per workgroup
   constexpr int CPR = U / 2;                     // 1 KB copies per 32 rows
   constexpr int WBYTES = 32 * NW * OP_KS * 2;    // W^O rows of a stage
   constexpr int XBYTES = 32 * OP_KS * 2;         // per token tile
@@ -91,16 +90,19 @@ __global__ __launch_bounds__(64 * NW) void out_proj_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fb = blockIdx.x, kb = blockIdx.y, tg = blockIdx.z;
-  const int f0 = fb * 32 * NW, k0 = kb * OP_KB, t0 = tg * (32 * MT);
+  const int f0 = fb * 32 * NW, k0 = kb * kb_size, t0 = tg * (32 * MT);
   const int mt = min(MT, (n_tok - t0 + 31) / 32);           // token tiles in this group
   const size_t row_bytes = (size_t)K * 2;
 
   // buffer descriptors: W^O rows f0 .. f0+32NW-1, token rows t0 .. n_tok-1
   // (rows past n_tok are out of range: the hardware writes zeros)
   const uint64_t wa = (uint64_t)(w_o + (size_t)f0 * K + k0);
+  // rows past d_model (a partial last feature block) are out of range
   const u32x4 wrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)wa),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(wa >> 32)) & 0xFFFFu,
-                     0xFFFFFFFFu, 0x00020000u};
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(
+                         (size_t)(d_model - f0) * row_bytes - (size_t)k0 * 2)),
+                     0x00020000u};
   const uint64_t xa = (uint64_t)(x + (size_t)t0 * K + k0);
   const u32x4 xrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)xa),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(xa >> 32)) & 0xFFFFu,
@@ -113,7 +115,10 @@ __global__ __launch_bounds__(64 * NW) void out_proj_mfma_kernel(
   constexpr int XPW = CPR / 4;                   // token-tile copies per copying wave
   uint32_t wsrc[CPR];
 #pragma unroll
-  for (int j = 0; j < CPR; ++j) wsrc[j] = op_src<U>(CPR * wave + j, lane, row_bytes);
+  for (int j = 0; j < CPR; ++j) {
+    const int n = CPR * wave + j;
+    wsrc[j] = (f0 + (64 / U) * n + lane / U < d_model) ? op_src<U>(n, lane, row_bytes) : kOpOOB;
+  }
   uint32_t xsrc[MT][XPW];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -183,9 +188,12 @@ __global__ __launch_bounds__(64 * NW) void out_proj_mfma_kernel(
     const int tok = t0 + 32 * t + r32;
     if (t < mt && tok < n_tok) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(floatx4*)(pk + (size_t)tok * d_model + f0 + 32 * wave + 8 * q + 4 * hh) =
-            floatx4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+      for (int q = 0; q < 4; ++q) {
+        const int f = f0 + 32 * wave + 8 * q + 4 * hh;      // 4 features; d_model % 4 == 0
+        if (f < d_model)
+          *(floatx4*)(pk + (size_t)tok * d_model + f) =
+              floatx4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
+      }
     }
   }
 }
@@ -238,50 +246,72 @@ __global__ __launch_bounds__(256) void out_proj_general_kernel(
   }
 }
 
-bool out_proj_fast(int d_model, int K, int x_dtype, int w_dtype) {
-  return x_dtype == MLA_BF16 && w_dtype == MLA_BF16 && d_model % 128 == 0 &&
-         K % OP_KB == 0 && d_model > 0;
+// out [n_tok, d_out] = x [n_tok, K] W [d_out, K]^T.  Matrix-core path: bf16
+// x and W, d_out % 4 == 0, K % 256 == 0.
+bool gemm_xwt_fast(int d_out, int K, int x_dtype, int w_dtype) {
+  return x_dtype == MLA_BF16 && w_dtype == MLA_BF16 && d_out > 0 && d_out % 4 == 0 &&
+         K % 256 == 0;
 }
 
-size_t out_proj_workspace(int d_model, int K, int n_tok, int x_dtype, int w_dtype) {
-  if (!out_proj_fast(d_model, K, x_dtype, w_dtype)) return 0;
-  return (size_t)(K / OP_KB) * n_tok * d_model * sizeof(float);
+namespace {
+// feature blocks of 160 rows (5 waves) when they divide d_out, else 128 (the
+// last block may be partial); K blocks of 2048 or less, halved (while they
+// divide K and hold at least 4 stages) until there are 256 workgroups
+struct GemmPlan { int nw, nfb, kb, nkb; };
+GemmPlan gemm_plan(int d_out, int K) {
+  GemmPlan p;
+  p.nw = (d_out % 160 == 0) ? 5 : 4;
+  p.nfb = (d_out + 32 * p.nw - 1) / (32 * p.nw);
+  p.kb = 2048;
+  while (p.kb > 256 && (K % p.kb != 0 || (int64_t)p.nfb * (K / p.kb) < kNumCU)) p.kb /= 2;
+  p.nkb = K / p.kb;
+  return p;
+}
+}  // namespace
+
+size_t gemm_xwt_workspace(int d_out, int K, int n_tok, int x_dtype, int w_dtype) {
+  if (!gemm_xwt_fast(d_out, K, x_dtype, w_dtype)) return 0;
+  return (size_t)gemm_plan(d_out, K).nkb * n_tok * d_out * sizeof(float);
 }
 
-hipError_t launch_out_proj(const void* x, int x_dtype, const void* w_o, int w_dtype,
-                           void* u, bool u_f32, int n_tok, int d_model, int K,
+hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtype,
+                           void* out, bool out_f32, int n_tok, int d_out, int K,
                            void* workspace, hipStream_t st) {
-  if (out_proj_fast(d_model, K, x_dtype, w_dtype)) {
-    // feature blocks of 160 rows (5 waves) when they divide d_model, else
-    // 128; one token tile with a 6-slot ring for at most 32 tokens, groups
-    // of 4 token tiles with a 4-slot ring up to 128 tokens, else groups of 8
-    // token tiles (W^O streamed once per 256 tokens) with a 3-slot ring
-    const int nw = (d_model % 160 == 0) ? 5 : 4;
+  const int d_model = d_out;
+  const void* w_o = w;
+  void* u = out;
+  const bool u_f32 = out_f32;
+  if (gemm_xwt_fast(d_out, K, x_dtype, w_dtype)) {
+    // one token tile with a 6-slot ring for at most 32 tokens, groups of 4
+    // token tiles with a 4-slot ring up to 128 tokens, else groups of 8
+    // token tiles (W streamed once per 256 tokens) with a 3-slot ring
+    const GemmPlan p = gemm_plan(d_out, K);
+    const int nw = p.nw, kb = p.kb;
     const int mt = (n_tok <= 32) ? 1 : (n_tok <= 128) ? 4 : 8;
-    const dim3 grid(d_model / (32 * nw), K / OP_KB, (n_tok + 32 * mt - 1) / (32 * mt));
+    const dim3 grid(p.nfb, p.nkb, (n_tok + 32 * mt - 1) / (32 * mt));
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)w_o;
     float* pp = (float*)workspace;
     if (nw == 5 && mt == 1)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     else if (nw == 5 && mt == 4)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     else if (nw == 5)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 8, 3, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 8, 3, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     else if (mt == 1)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     else if (mt == 4)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     else
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 8, 3, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 8, 3, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
     const size_t n4 = (size_t)n_tok * d_model / 4;
     const dim3 rgrid((unsigned)((n4 + 255) / 256));
     if (u_f32)
       hipLaunchKernelGGL(out_proj_reduce_kernel<float>, rgrid, dim3(256), 0, st,
-                         (const float*)workspace, (float*)u, n4, K / OP_KB);
+                         (const float*)workspace, (float*)u, n4, p.nkb);
     else
       hipLaunchKernelGGL(out_proj_reduce_kernel<uint16_t>, rgrid, dim3(256), 0, st,
-                         (const float*)workspace, (uint16_t*)u, n4, K / OP_KB);
+                         (const float*)workspace, (uint16_t*)u, n4, p.nkb);
     return hipGetLastError();
   }
   const size_t total = (size_t)n_tok * d_model;

@@ -212,6 +212,38 @@ int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent,
                       int32_t n_tokens, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Latent-cache producer, fused with the append: the cached vectors of the
+ * "DeepSeek-V3 Technical Report" notes, MLA section (c^KV_t = W^DKV h_t,
+ * k^R_t = RoPE(W^KR h_t)), with the RMS norm that the "DeepSeek-V2" page
+ * (section 3.2.1) places after the compressed latent vector:
+ *
+ *   c   = W^DKV h_t                       (fp32 accumulate)
+ *   c_i = c_i g_i / sqrt(mean_j c_j^2 + norm_eps)     (when norm_gain != NULL)
+ *   k   = W^KR h_t, rotated at position pos[t] when apply_rope
+ *   cache row of (seq_idx[t], pos[t]) = [c | k], stored as mla_cache_append
+ *   stores it (bf16 rounding, or a per-row fp8 scale and E4M3 codes).
+ *
+ * h [n_rows, d_model] in q_dtype; w_dkv_kr [d_c + d_h^R, d_model] in q_dtype,
+ * rows 0..d_c-1 = W^DKV and rows d_c.. = W^KR (the order of the cache row);
+ * norm_gain [d_c] fp32 or NULL; norm_eps >= 0.  seq_idx, pos, page_table,
+ * batch, max_pages, max_len, cache_rows, apply_rope, cache, kv_scale, n_rows:
+ * as mla_cache_append (rows whose slot falls outside the cache are skipped).
+ * workspace/ws_bytes: at least mla_kv_produce_workspace_size() bytes (the
+ * projected rows in fp32, and the projection's partial sums).  Errors: those
+ * of mla_cache_append, MLA_ERR_ARG for d_model < 1 or a negative or
+ * non-finite norm_eps, MLA_ERR_WORKSPACE; nothing is enqueued on an error.  */
+int32_t mla_kv_produce_workspace_size(const mla_dims_t* dims, int32_t d_model,
+                                      int32_t n_rows, size_t* bytes);
+int32_t mla_kv_produce(const mla_dims_t* dims, const void* h, int32_t d_model,
+                       const void* w_dkv_kr, const float* norm_gain,
+                       float norm_eps, const int32_t* seq_idx,
+                       const int32_t* pos, const int32_t* page_table,
+                       int32_t batch, int32_t max_pages, int32_t max_len,
+                       int64_t cache_rows, int32_t apply_rope, void* cache,
+                       float* kv_scale, int32_t n_rows, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Attention output projection ("DeepSeek-V3 Technical Report" notes, MLA
  * section, the equation after the attention-output equation):
  *

@@ -117,6 +117,38 @@ def test_out_proj_validation(mla):
     assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 0, 32, FAKE, 1024, None) == WS
 
 
+def test_kv_produce_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    sz = ctypes.c_size_t(0)
+    assert lib.mla_kv_produce_workspace_size(ctypes.byref(d), 5120, 32, ctypes.byref(sz)) == OK
+    assert sz.value >= 32 * 576 * 4                # the projected rows in fp32
+    assert lib.mla_kv_produce_workspace_size(ctypes.byref(d), 0, 32, ctypes.byref(sz)) == ARG
+    kp = lib.mla_kv_produce
+
+    def call(h=FAKE, w=FAKE, gain=None, eps=1e-6, seq=FAKE, pos=FAKE, pt=None, batch=4,
+             max_pages=0, max_len=128, rows=512, rope=1, cache=FAKE, scale=None, n=8,
+             d_model=5120, ws=FAKE, wsb=1 << 30, dims=d):
+        return kp(ctypes.byref(dims), h, d_model, w, gain, eps, seq, pos, pt, batch, max_pages,
+                  max_len, rows, rope, cache, scale, n, ws, wsb, None)
+    assert call(h=None) == NULL
+    assert call(w=None) == NULL
+    assert call(seq=None) == NULL
+    assert call(cache=None) == NULL
+    assert call(dims=_v2(b, kv_dtype="fp8")) == NULL          # fp8 needs kv_scale
+    assert call(scale=FAKE) == ARG                             # a scale without fp8
+    assert call(n=0) == ARG
+    assert call(rope=2) == ARG
+    assert call(d_model=0) == ARG
+    assert call(eps=-1.0) == ARG
+    assert call(eps=float("inf")) == ARG
+    assert call(max_len=200) == ARG                            # batch * max_len > cache rows
+    assert call(h=MIS) == ALIGN
+    assert call(gain=MIS) == ALIGN
+    assert call(ws=None, wsb=0) == WS
+    assert call(wsb=64) == WS
+
+
 def test_absorb_append_upproj_validation(mla):
     lib, b = mla
     d = _v2(b)

@@ -433,3 +433,89 @@ def test_out_proj_parity(w, n_tok, u_kind):
     ref = omla.output_project(o64, w64)
     # exact bf16 products, fp32 sums over K = n_h d_h; bf16 output adds 2^-9
     check("u", got, ref, 1e-5 if u_kind == "f32" else 4e-3)
+
+
+
+# ------------------------------ cache producer: [RMSNorm(W^DKV h) ; RoPE(W^KR h)]
+PRODUCE = [
+    (V2, "contiguous", True),
+    (small_variant(V2, name="v2_fp8", kv_dtype="fp8"), "paged", True),
+    (V2, "paged", False),                                          # no RMS norm
+    (WORKLOADS["tiny_fp32"], "contiguous", True),                  # fp32: general projection
+]
+
+
+@pytest.mark.parametrize("w,layout,norm", PRODUCE,
+                         ids=[f"{c[0].name}-{c[1]}-{'norm' if c[2] else 'nonorm'}" for c in PRODUCE])
+def test_kv_produce_parity(w, layout, norm):
+    """mla_kv_produce through the C ABI: the rows it writes into a NaN-poisoned
+    cache against the oracle's rows of the same hidden states (stored in the
+    cache's format: bf16 rounding, fp8 codes times the row scale, fp32);
+    every other slot stays untouched."""
+    from head_latent_attention_11_amd import binding as B
+    from head_latent_attention_11_amd.runner import to_device
+    from mla_inputs import producer_inputs
+    say(f"case kv_produce {w.name}: layout={layout} kv={w.kv_dtype} norm={norm}")
+    n_seq, max_len = 5, 192
+    rng = np.random.default_rng(61)
+    n_rows = 45
+    seq = rng.integers(0, n_seq, size=n_rows).astype(np.int32)
+    pos = np.empty(n_rows, dtype=np.int32)
+    for s_ in range(n_seq):                                   # distinct positions per sequence
+        idx = np.nonzero(seq == s_)[0]
+        pos[idx] = rng.choice(max_len, size=len(idx), replace=False)
+    inp = producer_inputs(w, n_rows)
+    D = w.d_latent + w.d_rope
+    kind = "f32" if w.q_dtype == "f32" else "bf16"
+    dims = B.MLADims.from_workload(w)
+    if layout == "paged":
+        pages_per_seq = max_len // 64
+        table = rng.permutation(n_seq * pages_per_seq).astype(np.int32).reshape(n_seq, -1)
+        pt, max_pages, ml = torch.from_numpy(table).cuda(), pages_per_seq, 0
+        slot = table[seq, pos // 64].astype(np.int64) * 64 + pos % 64
+    else:
+        pt, max_pages, ml = None, 0, max_len
+        slot = seq.astype(np.int64) * max_len + pos
+    n_slots = n_seq * max_len
+    if w.kv_dtype == "fp8":
+        cache = torch.full((n_slots, D), 0x7F, dtype=torch.uint8, device="cuda")
+        scale = torch.full((n_slots,), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        cache = torch.full((n_slots, D), float("nan"),
+                           dtype=torch.float32 if w.kv_dtype == "f32" else torch.bfloat16,
+                           device="cuda")
+        scale = None
+    gain = torch.from_numpy(inp["gain"]).cuda() if norm else None
+    eps = 1e-6
+    wsb = B.kv_produce_workspace_size(dims, w.d_model, n_rows)
+    ws = torch.full(((wsb + 15) // 16 * 4,), float("nan"), dtype=torch.float32, device="cuda")
+    B.kv_produce(dims, to_device(inp["h"], kind, "cuda"), w.d_model,
+                 to_device(inp["w_dkv_kr"], kind, "cuda"), gain, eps,
+                 torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), pt, n_seq, max_pages,
+                 ml, n_slots, True, cache, scale, n_rows, ws, wsb)
+    torch.cuda.synchronize()
+    h64 = inp["h"].astype(np.float64) if kind == "f32" else formats.bf16_to_f64(inp["h"])
+    w64 = (inp["w_dkv_kr"].astype(np.float64) if kind == "f32"
+           else formats.bf16_to_f64(inp["w_dkv_kr"]))
+    ref = omla.produce_rows(h64, w64[:w.d_latent], w64[w.d_latent:],
+                            inp["gain"].astype(np.float64) if norm else None, eps, pos=pos,
+                            rope_base=w.rope_base)
+    if w.kv_dtype == "fp8":
+        codes = cache.cpu().numpy()
+        sc = scale.cpu().numpy()
+        got = formats.e4m3_to_f64(codes[slot]) * sc[slot][:, None]
+        written = np.zeros(n_slots, dtype=bool)
+        written[slot] = True
+        assert np.all(np.isnan(sc[~written])), "a slot outside the new rows was written"
+        check("rows (fp8)", got, ref, REL_L2_FP8)
+        # against the oracle's rows stored the same way (per-row scale, E4M3
+        # codes): the fp32 projection moves only codes at a rounding boundary
+        qc, qs = formats.quantize_rows_e4m3(ref.astype(np.float32))
+        check("rows (fp8, both quantised)", got, formats.dequantize_rows_e4m3(qc, qs), 5e-3)
+    else:
+        c = to_np(cache)
+        got = c[slot]
+        written = np.zeros(n_slots, dtype=bool)
+        written[slot] = True
+        assert np.all(np.isnan(c[~written])), "a slot outside the new rows was written"
+        check("rows", got, ref, 1e-5 if w.kv_dtype == "f32" else 4e-3)
