@@ -277,10 +277,6 @@ size_t gemm_xwt_workspace(int d_out, int K, int n_tok, int x_dtype, int w_dtype)
 hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtype,
                            void* out, bool out_f32, int n_tok, int d_out, int K,
                            void* workspace, hipStream_t st) {
-  const int d_model = d_out;
-  const void* w_o = w;
-  void* u = out;
-  const bool u_f32 = out_f32;
   if (gemm_xwt_fast(d_out, K, x_dtype, w_dtype)) {
     // one token tile with a 6-slot ring for at most 32 tokens, groups of 4
     // token tiles with a 4-slot ring up to 128 tokens, else groups of 8
@@ -290,41 +286,41 @@ hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtyp
     const int mt = (n_tok <= 32) ? 1 : (n_tok <= 128) ? 4 : 8;
     const dim3 grid(p.nfb, p.nkb, (n_tok + 32 * mt - 1) / (32 * mt));
     const uint16_t* xp = (const uint16_t*)x;
-    const uint16_t* wp = (const uint16_t*)w_o;
+    const uint16_t* wp = (const uint16_t*)w;
     float* pp = (float*)workspace;
     if (nw == 5 && mt == 1)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
     else if (nw == 5 && mt == 4)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 4, 4, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
     else if (nw == 5)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 8, 3, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<5, 8, 3, 8>), grid, dim3(320), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
     else if (mt == 1)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 1, OP_V1_NBUF, OP_V1_U>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
     else if (mt == 4)
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 4, 4, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
     else
-      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 8, 3, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_model, K, kb);
-    const size_t n4 = (size_t)n_tok * d_model / 4;
+      hipLaunchKernelGGL((out_proj_mfma_kernel<4, 8, 3, 8>), grid, dim3(256), 0, st, xp, wp, pp, n_tok, d_out, K, kb);
+    const size_t n4 = (size_t)n_tok * d_out / 4;
     const dim3 rgrid((unsigned)((n4 + 255) / 256));
-    if (u_f32)
+    if (out_f32)
       hipLaunchKernelGGL(out_proj_reduce_kernel<float>, rgrid, dim3(256), 0, st,
-                         (const float*)workspace, (float*)u, n4, p.nkb);
+                         (const float*)workspace, (float*)out, n4, p.nkb);
     else
       hipLaunchKernelGGL(out_proj_reduce_kernel<uint16_t>, rgrid, dim3(256), 0, st,
-                         (const float*)workspace, (uint16_t*)u, n4, p.nkb);
+                         (const float*)workspace, (uint16_t*)out, n4, p.nkb);
     return hipGetLastError();
   }
-  const size_t total = (size_t)n_tok * d_model;
+  const size_t total = (size_t)n_tok * d_out;
   const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
 #define MLA_OP(XT, WT, OT)                                                               \
   hipLaunchKernelGGL((out_proj_general_kernel<XT, WT, OT>), dim3(grid), dim3(256), 0, st, \
-                     (const XT*)x, (const WT*)w_o, (OT*)u, n_tok, d_model, K)
+                     (const XT*)x, (const WT*)w, (OT*)out, n_tok, d_out, K)
   if (x_dtype == MLA_F32) {
-    if (w_dtype == MLA_F32) { if (u_f32) MLA_OP(float, float, float); else MLA_OP(float, float, uint16_t); }
-    else { if (u_f32) MLA_OP(float, uint16_t, float); else MLA_OP(float, uint16_t, uint16_t); }
+    if (w_dtype == MLA_F32) { if (out_f32) MLA_OP(float, float, float); else MLA_OP(float, float, uint16_t); }
+    else { if (out_f32) MLA_OP(float, uint16_t, float); else MLA_OP(float, uint16_t, uint16_t); }
   } else {
-    if (w_dtype == MLA_F32) { if (u_f32) MLA_OP(uint16_t, float, float); else MLA_OP(uint16_t, float, uint16_t); }
-    else { if (u_f32) MLA_OP(uint16_t, uint16_t, float); else MLA_OP(uint16_t, uint16_t, uint16_t); }
+    if (w_dtype == MLA_F32) { if (out_f32) MLA_OP(uint16_t, float, float); else MLA_OP(uint16_t, float, uint16_t); }
+    else { if (out_f32) MLA_OP(uint16_t, uint16_t, float); else MLA_OP(uint16_t, uint16_t, uint16_t); }
   }
 #undef MLA_OP
   return hipGetLastError();
