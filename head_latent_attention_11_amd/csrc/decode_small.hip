@@ -1,0 +1,395 @@
+// Attention over the latent cache on gfx950 matrix cores for small blocks of
+// query rows: 16, 32 or 64 rows per workgroup.  This covers head counts that
+// are a multiple of 16 but give no multiple of 128 rows per sequence, e.g.
+// the 16 heads of DeepSeek-V2-Lite ("DeepSeek-V2: Strong, Economical,
+// Efficient", Appendix B) with one to four query tokens.
+//
+// Same contractions as the 128-row kernel (absorbed MLA decode, section
+// 2.1.2 and Appendix C of the DeepSeek-V2 paper): per sequence
+//   S^T = K Q_abs^T   (tokens x rows, K-dim 576)
+//   O^T = C^T P^T     (512 x rows,    K-dim tokens)
+// With 16 rows a cache row of 1152 bytes carries only ~35 kFLOP of work, so
+// the kernel is bound by streaming the cache, not by the matrix cores; the
+// design keeps three tiles in flight per workgroup and splits the matrix
+// work of a tile over the four waves without duplicating any of it.
+//
+// Work decomposition
+//   * A work item is (sequence b, KV chunk) x one block of RB = 16 NR query
+//     rows (row = tau * n_h + head); a workgroup of 4 waves handles it.  Row
+//     blocks of one item run on the same XCD (they share its L2 copy).
+//   * KV tiles of 32 tokens move HBM -> LDS with buffer loads that write LDS
+//     directly, through a 4-slot ring (rows padded to 1168 bytes); three
+//     tiles stream in while one is used.  A load range that ends at the last
+//     staged token writes zeros for the rest of the tile.  The query block
+//     is staged the same way (into the last one or two slots) before the
+//     loop and kept in VGPRs.
+//   * Scores (v_mfma_f32_16x16x32_bf16; A = 16 tokens x 32 dims of K, B =
+//     32 dims x 16 rows of Q^T): wave w takes token block tb = w % 2 and
+//       NR = 1: the 16 rows over dims 288 (w / 2) .. +287 (the two halves
+//               are added when the pieces are gathered),
+//       NR = 2: row sub-block w / 2 over all 576 dims,
+//       NR = 4: row sub-blocks 2 (w / 2) and 2 (w / 2) + 1.
+//     The 16 x 16 pieces go through a small LDS buffer so that every wave
+//     then holds all scores of the tile: lane (g, j) = (lane / 16, lane %
+//     16) holds row j's scores of tokens tok_row(tb, 4 g + i), i = 0..3,
+//     for both token blocks.
+//   * Softmax per row with a running max (log2 domain); when the max grows
+//     the row's accumulators and sum are rescaled.  Every wave computes the
+//     same weights.
+//   * PV: wave w owns latent dims 128 w .. 128 w + 127 of all rows:
+//     O^T[dim, row] += C^T[dim, tok] P^T[tok, row] (v_mfma_f32_16x16x32_bf16).
+//     The B operand is the lane's own 8 weights (row j, the 8 tokens above:
+//     the token order inside the K dimension is chosen to match), the A
+//     operand comes from two transposing LDS reads (ds_read_b64_tr_b16:
+//     within 16 lanes, lane i gets dim i of the four token rows addressed by
+//     lanes 4k + i/4).  The accumulator lane (g, j) holds dims 4 g .. 4 g + 3
+//     of row j, so each row's rescaling factor is the lane's own.
+//   * Token order of a tile: MFMA row m of token block tb reads tile row
+//     tok_row(tb, m) = 16 tb + 2 (m % 8) + m / 8.  The score-operand reads
+//     of 16 lanes (16 rows 16 tb .. 16 tb + 15) and the transposing reads of
+//     a half wave (eight rows of one parity, 32 bytes each) then fall on
+//     distinct LDS banks at the 1168-byte pitch.
+#include <math.h>
+
+#include "mla_common.hpp"
+#include "plan_device.hpp"
+
+namespace mla {
+
+namespace {
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+
+constexpr int kDim = 576;                  // cache row: 512 latent + 64 rope dims
+constexpr int kLatent = 512;
+constexpr int kRowBytes = 2 * kDim;        // bf16 cache row
+constexpr int kTile = 32;                  // tokens per tile
+constexpr int kPitch = 1168;               // LDS bytes per staged row (73 chunks of 16)
+constexpr int kSlots = 4;                  // LDS ring
+constexpr int kLoads = 37;                 // 1 KB direct loads per tile
+constexpr int kSlotBytes = kLoads * 1024;
+constexpr int kChunks = kRowBytes / 16;    // 72 chunks of 16 bytes per row
+constexpr uint32_t kPastEnd = 0x40000000u; // buffer offset past any valid range
+
+// LDS chunk u of a slot holds chunk u % 73 of staged row u / 73, or nothing
+// (the row's padding chunk, or past the 32 rows): then the source offset
+// lies past the buffer's range and the load writes zeros.
+// u / 73 = (449 u) >> 15 for u < 2368.
+__device__ inline uint32_t staged_src_offset(int u) {
+  const int r = (u * 449) >> 15;
+  return (u - 73 * r == kChunks || r >= kTile) ? kPastEnd : uint32_t(16 * (u - r));
+}
+
+__device__ __forceinline__ int tok_row(int tb, int m) { return 16 * tb + 2 * (m & 7) + (m >> 3); }
+
+// One 1 KB load (64 lanes x 16 bytes) from the buffer rs into LDS at lds.
+__device__ __forceinline__ void dma_1k(uint32_t lds, uint32_t voff, u32x4 rs) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
+// Wait until at most n of this wave's loads are in flight (n wave-uniform;
+// counts that do not occur wait for all).
+__device__ __forceinline__ void wait_loads(int n) {
+  switch (n) {
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t ad = (uint64_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ad),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad >> 32)) & 0xFFFFu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+__device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((shortx4 __attribute__((address_space(3)))*)(p));
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace
+
+template <int NR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_small_kernel(DecodeArgs a, ItemTable tab) {
+  constexpr int RB = 16 * NR;                    // query rows per workgroup
+  constexpr int NQ = NR == 1 ? 1 : NR / 2;       // row sub-blocks of a wave's scores
+  constexpr int KS = NR == 1 ? 9 : 18;           // 32-dim steps of a wave's scores
+  constexpr int NPIECE = NR == 1 ? 4 : 2 * NR;   // 1 KB score pieces per tile
+  constexpr int QSLOTS = NR == 4 ? 2 : 1;        // ring slots that stage the queries
+  static_assert(NR == 1 || NR == 2 || NR == 4, "16, 32 or 64 rows");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSlots][kSlotBytes];
+  __shared__ __attribute__((aligned(16))) floatx4 s_x[NPIECE][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int gi = xcd_logical_index(blockIdx.x, gridDim.x);
+  const int item = gi / a.row_blocks, rb = gi % a.row_blocks;
+  // work item -> (sequence, split, length), as for the 128-row kernel
+  int b, s_idx, L, item_id = item;
+  if (tab.uniform_len > 0) {
+    L = tab.uniform_len;
+    const int nsu = splits_of(L, a.num_splits, a.chunk);
+    b = item / nsu;
+    s_idx = item - b * nsu;
+  } else if (tab.n > 0) {
+    const uint32_t e = tab.seq_split[item];
+    b = e & 0xFFFFF;
+    s_idx = e >> 20;
+    item_id = tab.item_id[item];
+    L = a.seq_lens[b];
+  } else {
+    const ItemLoc loc = locate_item(a.seq_lens, a.B, a.num_splits, a.chunk, item);
+    if (loc.b < 0) return;
+    b = loc.b;
+    s_idx = loc.s;
+    L = a.seq_lens[loc.b];
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int ns = splits_of(L, a.num_splits, a.chunk);
+  const int c = chunk_of(L, a.num_splits, a.chunk);
+  const int t0 = __builtin_amdgcn_readfirstlane(s_idx) * c;
+  const int t_end = min(L, t0 + c);
+  const int rows = a.n_h * a.T;
+  const int row0 = rb * RB;
+  // last visible token of each 16-row sub-block (its rows share one query
+  // token: n_h is a multiple of 16)
+  int lim[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr)
+    lim[nr] = __builtin_amdgcn_readfirstlane(min(t_end - 1, L - a.T + (row0 + 16 * nr) / a.n_h));
+  const int tau_max = (row0 + RB - 1) / a.n_h;
+  const int t_stage = __builtin_amdgcn_readfirstlane(min(t_end, L - a.T + tau_max + 1));
+  const int ntiles = (t_stage > t0) ? (t_stage - t0 + kTile - 1) / kTile : 0;
+
+  const uint8_t* cache = (const uint8_t*)a.cache;
+  const int seq_row0 = b * a.max_len;
+  typedef __attribute__((address_space(4))) const int32_t* ConstI32;
+  const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
+  // Paged cache: the item's page ids (up to 128) are loaded once, one per
+  // lane, and each tile takes its page from a lane with v_readlane; longer
+  // items read the table per tile.  Items start on a page boundary.
+  const int pg_first = t0 / kPage;
+  const int pg_n = (ntiles > 0) ? (t_stage - t0 + kPage - 1) / kPage : 0;
+  const bool pg_regs = ptab && pg_n <= 128;
+  int pg_lo = 0, pg_hi = 0;
+  if (pg_regs) {
+    if (lane < pg_n) pg_lo = a.page_table[(size_t)b * a.max_pages + pg_first + lane];
+    if (64 + lane < pg_n) pg_hi = a.page_table[(size_t)b * a.max_pages + pg_first + 64 + lane];
+  }
+  // buffer of the tile starting at token ts (a tile never crosses a page)
+  auto tile_rsrc = [&](int ts) -> u32x4 {
+    const int nv = max(0, min(kTile, t_stage - ts));
+    int r0 = 0;
+    if (nv > 0) {
+      if (ptab) {
+        const int k = ts / kPage - pg_first;
+        const int pg = pg_regs ? __builtin_amdgcn_readlane(k < 64 ? pg_lo : pg_hi, k & 63)
+                               : ptab[ts / kPage];
+        r0 = pg * kPage + (ts % kPage);
+      } else {
+        r0 = seq_row0 + ts;
+      }
+    }
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+    return buffer_rsrc(cache + (size_t)r0 * kRowBytes, nv * kRowBytes);
+  };
+  // Wave w issues loads n = w + 4k of a tile (wave 0: 10 loads, others 9).
+  const int nld = wave == 0 ? 10 : 9;
+  uint32_t voff[10];
+#pragma unroll
+  for (int n = 0; n < 10; ++n) voff[n] = staged_src_offset(64 * (wave + 4 * n) + lane);
+  const uint32_t ring = (uint32_t)(uintptr_t)&s_ring[0][0];
+  auto issue = [&](const u32x4 rs, int slot) {
+    const uint32_t lb = ring + slot * kSlotBytes + 1024 * wave;
+#pragma unroll
+    for (int n = 0; n < 9; ++n) dma_1k(lb + 4096 * n, voff[n], rs);
+    if (wave == 0) dma_1k(lb + 4096 * 9, voff[9], rs);
+  };
+
+  // ---- query block -> VGPRs (B operands of the scores: lane (g, j) holds
+  // row 16 nr + j, dims 32 ks + 8 g .. + 7).  Rows 32 q .. 32 q + 31 of the
+  // block are staged in slot kSlots - 1 - q; tiles 0 .. kSlots - 1 - QSLOTS
+  // go out right behind them.
+  const uint8_t* qblk = (const uint8_t*)a.q_abs + ((size_t)b * rows + row0) * kRowBytes;
+#pragma unroll
+  for (int q = 0; q < QSLOTS; ++q)
+    issue(buffer_rsrc(qblk + (size_t)q * kTile * kRowBytes, min(RB, kTile) * kRowBytes),
+          kSlots - 1 - q);
+  constexpr int kFirst = kSlots - QSLOTS;        // tiles issued with the queries
+#pragma unroll
+  for (int t = 0; t < kFirst; ++t)
+    if (t < ntiles) issue(tile_rsrc(t0 + t * kTile), t);
+  wait_loads(min(ntiles, kFirst) * nld);         // the query loads have landed
+  __syncthreads();
+  const int tb = wave & 1;
+  const int ks0 = NR == 1 ? 9 * (wave >> 1) : 0;
+  int nr_of[NQ];
+#pragma unroll
+  for (int iq = 0; iq < NQ; ++iq) nr_of[iq] = NR == 1 ? 0 : (NR == 2 ? wave >> 1 : 2 * (wave >> 1) + iq);
+  bf16x8 qf[NQ][KS];
+#pragma unroll
+  for (int iq = 0; iq < NQ; ++iq) {
+    const int qr = 16 * nr_of[iq] + j;
+    const uint8_t* src = s_ring[kSlots - 1 - qr / kTile] + (qr % kTile) * kPitch + 64 * ks0 + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[iq][ks] = *(const bf16x8*)(src + 64 * ks);
+  }
+  if constexpr (QSLOTS == 2) {
+    __syncthreads();                             // slot 2 is free again
+    if (2 < ntiles) issue(tile_rsrc(t0 + 2 * kTile), 2);
+  }
+
+  // ---- per-lane LDS offsets of the operands
+  const int k_off = tok_row(tb, j) * kPitch + 64 * ks0 + 16 * g;               // + 64 ks
+  const int kq = (lane >> 2) & 3, m4 = lane & 3;
+  const int v_off0 = tok_row(0, 4 * g + kq) * kPitch + 256 * wave + 8 * m4;     // + 32 cb
+  const int v_off1 = tok_row(1, 4 * g + kq) * kPitch + 256 * wave + 8 * m4;
+
+  floatx4 o[NR][8];
+  float m_run[NR], l_run[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    m_run[nr] = -INFINITY;
+    l_run[nr] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) o[nr][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    // tile it has landed (tiles it+1, it+2 may still be in flight), and
+    // every wave is done with tile it-1 and with the score pieces
+    wait_loads((min(ntiles, it + kSlots - 1) - it - 1) * nld);
+    __syncthreads();
+    if (it + kSlots - 1 < ntiles) issue(tile_rsrc(t0 + (it + kSlots - 1) * kTile), (it + kSlots - 1) & 3);
+    const uint8_t* kt = s_ring[it & 3];
+
+    // scores: this wave's pieces
+    floatx4 sp[NQ];
+#pragma unroll
+    for (int iq = 0; iq < NQ; ++iq) sp[iq] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 kv = *(const bf16x8*)(kt + k_off + 64 * ks);
+#pragma unroll
+      for (int iq = 0; iq < NQ; ++iq)
+        sp[iq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[iq][ks], sp[iq], 0, 0, 0);
+    }
+#pragma unroll
+    for (int iq = 0; iq < NQ; ++iq) s_x[NR == 1 ? wave : tb + 2 * nr_of[iq]][lane] = sp[iq];
+    __syncthreads();
+
+    const int ts = t0 + it * kTile;
+    bf16x8 pk[NR];
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const floatx4 v = NR == 1 ? s_x[t][lane] + s_x[t + 2][lane] : s_x[t + 2 * nr][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = ts + tok_row(t, 4 * g + i);
+          x[4 * t + i] = (tok > lim[nr]) ? -INFINITY : v[i] * a.scale_log2;
+        }
+      }
+      float mt = x[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[nr], mt);
+      const float base = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_hw(m_run[nr] - base);   // 0 while the row has seen nothing
+      m_run[nr] = m_new;
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_hw(x[e] - base);
+        ps += p[e];
+      }
+      l_run[nr] = l_run[nr] * alpha + ps;
+      if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) o[nr][cb] *= alpha;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[nr][e] = (__bf16)p[e];
+    }
+
+    // PV: this wave's 128 latent dims of every row
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const shortx4 v0 = lds_tr16(kt + v_off0 + 32 * cb);
+      const shortx4 v1 = lds_tr16(kt + v_off1 + 32 * cb);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nr = 0; nr < NR; ++nr)
+        o[nr][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pk[nr], o[nr][cb], 0, 0, 0);
+    }
+  }
+
+  // ---- normalise and write: lane (g, j) holds dims 128 w + 16 cb + 4 g ..
+  // + 3 of row 16 nr + j.  The final output in fp32, or this split's
+  // partial in bf16 (combined in fp32).
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    float l_tot = l_run[nr] + __shfl_xor(l_run[nr], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+    const float lse = (l_tot > 0.f) ? (m_run[nr] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    const int row = row0 + 16 * nr + j;
+    if (ns == 1) {
+      const size_t gr = (size_t)b * rows + row;
+      float* dst = a.out_latent + gr * kLatent + 128 * wave + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) *(floatx4*)(dst + 16 * cb) = o[nr][cb] * inv;
+      if (wave == 0 && g == 0) a.out_lse[gr] = lse;
+    } else {
+      const size_t pr = (size_t)item_id * rows + row;
+      uint8_t* dst = (uint8_t*)a.part_o + (pr * kLatent + 128 * wave + 4 * g) * 2;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) {
+        const floatx4 v = o[nr][cb] * inv;
+        const bf16x2 p01 = {(__bf16)v[0], (__bf16)v[1]};
+        const bf16x2 p23 = {(__bf16)v[2], (__bf16)v[3]};
+        *(u32x2*)(dst + 32 * cb) = u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
+      }
+      if (wave == 0 && g == 0) a.part_lse[pr] = lse;
+    }
+  }
+}
+
+// rows_wg: query rows per workgroup (16, 32 or 64); a.row_blocks counts
+// blocks of that many rows.
+hipError_t launch_decode_small(const DecodeArgs& a, const ItemTable& tab, int rows_wg,
+                               hipStream_t st) {
+  const int grid = a.n_items * a.row_blocks;
+  switch (rows_wg) {
+    case 16:
+      hipLaunchKernelGGL(decode_small_kernel<1>, dim3(grid), dim3(256), 0, st, a, tab);
+      break;
+    case 32:
+      hipLaunchKernelGGL(decode_small_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
+      break;
+    case 64:
+      hipLaunchKernelGGL(decode_small_kernel<4>, dim3(grid), dim3(256), 0, st, a, tab);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -27,6 +27,7 @@ hipError_t launch_decode_mfma(const DecodeArgs&, const ItemTable&, hipStream_t);
 static_assert(sizeof(DecodeArgs) + sizeof(ItemTable) <= 4096,
               "the attention kernel's arguments must stay within 4 KB");
 hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_small(const DecodeArgs&, const ItemTable&, int rows_wg, hipStream_t);
 }  // namespace mla
 
 using namespace mla;
@@ -55,16 +56,28 @@ int32_t check_dims(const mla_dims_t* d) {
   return MLA_OK;
 }
 
-// The matrix-core path: DeepSeek-V2 / V3 MLA shapes with bf16 operands.
+// The matrix-core path: DeepSeek-V2 / V3 / V2-Lite MLA shapes with bf16
+// operands (absorption and up-projection run one head per workgroup).
 bool fast_shape(const mla_dims_t* d) {
-  return d->d_head == 128 && d->d_latent == 512 && d->d_rope == 64 &&
-         d->n_heads % 32 == 0 && d->q_dtype == MLA_BF16;
+  return d->d_head == 128 && d->d_latent == 512 && d->d_rope == 64 && d->q_dtype == MLA_BF16;
 }
 
+// Attention in blocks of 128 rows: 32 heads of one query token per wave.
 bool fast_decode(const mla_dims_t* d, int T) {
   return fast_shape(d) && d->precision == MLA_PREC_BF16 &&
-         (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) &&
+         (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) && d->n_heads % 32 == 0 &&
          ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
+}
+
+// Attention in blocks of 16, 32 or 64 rows (16 heads of one query token per
+// row sub-block) for the other head counts that are multiples of 16, bf16
+// cache.  Returns the rows per block, or 0.
+int small_decode_rows(const mla_dims_t* d, int T) {
+  if (!fast_shape(d) || d->precision != MLA_PREC_BF16 || d->kv_dtype != MLA_BF16 ||
+      d->n_heads % 16 != 0 || fast_decode(d, T))
+    return 0;
+  const int64_t rows = (int64_t)d->n_heads * T;
+  return rows % 64 == 0 ? 64 : rows % 32 == 0 ? 32 : 16;
 }
 
 // Format of the absorbed query.
@@ -100,9 +113,10 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
                   int num_splits, Plan* p) {
   if (B < 1 || T < 1 || T > 1024) return MLA_ERR_ARG;
   if (num_splits < 0 || num_splits > 4096) return MLA_ERR_ARG;
-  const bool fast = fast_decode(d, T);
+  const int small = small_decode_rows(d, T);
+  const bool fast = fast_decode(d, T) || small > 0;   // matrix-core kernels
   const int64_t rows = (int64_t)d->n_heads * T;
-  const int64_t rb = fast ? rows / kRowsPerWorkgroup : rows;
+  const int64_t rb = small > 0 ? rows / small : fast ? rows / kRowsPerWorkgroup : rows;
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     if (lens[b] < 1 || lens[b] < T) return MLA_ERR_SEQLEN;
@@ -352,7 +366,8 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
   }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (fast_decode(dims, q_tokens)) {
+  const int small_rows = small_decode_rows(dims, q_tokens);
+  if (fast_decode(dims, q_tokens) || small_rows > 0) {
     ItemTable tab;
     tab.n = 0;
     tab.uniform_len = a.uniform_len;
@@ -390,7 +405,7 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
         tab.n = (next == n) ? n : 0;
       }
     }
-    e = launch_decode_mfma(a, tab, s);
+    e = small_rows > 0 ? launch_decode_small(a, tab, small_rows, s) : launch_decode_mfma(a, tab, s);
   } else {
     e = launch_decode_general(a, s);
   }

@@ -100,10 +100,13 @@ typedef enum mla_precision {
 } mla_precision_t;
 
 /* Supported combinations:
- *   fast path (MFMA): n_h % 32 == 0, (n_h*T) % 128 == 0, d_h = 128,
- *       d_c = 512, d_h^R = 64, q_dtype = BF16, kv_dtype = BF16 or FP8_E4M3,
- *       precision = MLA_PREC_BF16 (the query absorption also uses matrix
- *       cores with MLA_PREC_FP32);
+ *   matrix-core path: d_h = 128, d_c = 512, d_h^R = 64, q_dtype = BF16
+ *       (absorption and up-projection: any n_h; the absorption also with
+ *       MLA_PREC_FP32); attention with precision = MLA_PREC_BF16 and
+ *         n_h % 32 == 0, (n_h*T) % 128 == 0, kv_dtype = BF16 or FP8_E4M3
+ *           (blocks of 128 query rows: DeepSeek-V2 / V3, 128 heads), or
+ *         n_h % 16 == 0 otherwise, kv_dtype = BF16 (blocks of 16, 32 or 64
+ *           rows: e.g. DeepSeek-V2-Lite, 16 heads, T = 1..4);
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
  *       d_h^R <= 128 (even),
  *       every q_dtype / kv_dtype combination (e.g. the all-fp32 problems).

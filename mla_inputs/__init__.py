@@ -116,6 +116,11 @@ WORKLOADS: Dict[str, Workload] = {
             d_head=128, d_latent=512, d_rope=64, kv_len=8192,
             description="bf16 companion of the fp8 workload: B=64, T=1, "
                         "L=8192, contiguous"),
+        Workload(
+            name="v2lite_b64_l8k_bf16", batch=64, q_tokens=1, n_heads=16,
+            d_head=128, d_latent=512, d_rope=64, kv_len=8192, d_model=2048,
+            description="DeepSeek-V2-Lite attention shapes (16 heads, hidden "
+                        "size 2048), bf16: B=64, T=1, L=8192, contiguous"),
     ]
 }
 

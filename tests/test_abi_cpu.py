@@ -49,8 +49,8 @@ def test_status_strings_and_version(mla):
     assert b.version() >= 10000
 
 
-def _v2(b, **kw):
-    return b.MLADims.make(128, 128, 512, 64, **kw)
+def _v2(b, n_heads=128, **kw):
+    return b.MLADims.make(n_heads, 128, 512, 64, **kw)
 
 
 def _decode(lib, b, dims, lens, T=1, q=FAKE, cache=FAKE, scale=None, pt=None, max_pages=0,
@@ -198,6 +198,12 @@ def test_split_planner_sizes(mla):
     # explicit 64 splits of 131072 tokens: 4 * 64 items
     st, n = _ws(lib, d, [131072] * 4, splits=64)
     assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 2
+    # 16 heads (one block of 16 rows): 32 x 4096 tokens fill 256 items of 512
+    st, n = _ws(lib, _v2(b, n_heads=16), [4096] * 32)
+    assert st == OK and n == 256 * 16 * 4 + 256 * 16 * dc * 2
+    # 48 heads: three blocks of 16 rows, 86 items wanted -> chunk 1536, 3 splits
+    st, n = _ws(lib, _v2(b, n_heads=48), [4096] * 32)
+    assert st == OK and n == 96 * 48 * 4 + 96 * 48 * dc * 2
     # fp32 precision mode: same items, fp32 partials
     st, n = _ws(lib, _v2(b, precision=1), [131072] * 4, splits=64)
     assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4

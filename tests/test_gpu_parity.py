@@ -99,7 +99,27 @@ SMALL = [
                   lengths=(300, 77, 4, 130), kv_dtype="fp8", num_splits=3),
     small_variant(V2, name="fp8_t1_paged", batch=2, kv_len=0, lengths=(100, 520),
                   kv_dtype="fp8", layout="paged"),
-    small_variant(V2, name="general_n16_bf16", batch=2, n_heads=16, kv_len=0,
+    # head counts with no multiple of 128 rows: the 16/32/64-row kernel
+    small_variant(V2, name="lite_n16_ragged", batch=4, n_heads=16, kv_len=0,
+                  lengths=(1, 33, 700, 64)),
+    small_variant(V2, name="lite_n16_split5", batch=4, n_heads=16, kv_len=0,
+                  lengths=(1, 33, 700, 64), num_splits=5),
+    small_variant(V2, name="lite_n16_paged", batch=5, n_heads=16, kv_len=0,
+                  lengths=(40, 900, 64, 65, 333), layout="paged"),
+    small_variant(V2, name="lite_n16_t2", batch=3, n_heads=16, q_tokens=2, kv_len=0,
+                  lengths=(129, 64, 3)),
+    small_variant(V2, name="lite_n16_t4_split3", batch=4, n_heads=16, q_tokens=4, kv_len=0,
+                  lengths=(300, 77, 4, 130), num_splits=3),
+    small_variant(V2, name="lite_n16_t4_paged", batch=2, n_heads=16, q_tokens=4, kv_len=0,
+                  lengths=(520, 100), layout="paged"),
+    small_variant(V2, name="n48_t1", batch=3, n_heads=48, kv_len=0, lengths=(700, 64, 1)),
+    small_variant(V2, name="n64_t1_split40", batch=3, n_heads=64, kv_len=0,
+                  lengths=(2600, 64, 1300), num_splits=40),
+    small_variant(V2, name="n96_t2", batch=2, n_heads=96, q_tokens=2, kv_len=0,
+                  lengths=(333, 65)),
+    small_variant(V2, name="lite_n16_rope", batch=2, n_heads=16, kv_len=0,
+                  lengths=(70, 129), rope=True),
+    small_variant(V2, name="general_n8_bf16", batch=2, n_heads=8, kv_len=0,
                   lengths=(50, 300)),
     small_variant(V2, name="general_n16_fp8_rope", batch=2, n_heads=16, kv_len=0,
                   lengths=(70, 129), kv_dtype="fp8", rope=True),
@@ -132,6 +152,7 @@ FULL = [
     (WORKLOADS["v2_b64_l8k_bf16"], [5, 63], [3, 100]),
     (WORKLOADS["v2_fp8_t4_b64_l8k"], [0, 63], [0, 64, 127]),
     (WORKLOADS["v2_long_b4_l128k_bf16"], [0, 3], [0, 77]),
+    (WORKLOADS["v2lite_b64_l8k_bf16"], [0, 31, 63], [0, 5, 15]),
 ]
 
 
