@@ -25,6 +25,14 @@ HIPCC_FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-file additions.  The small-row attention kernel rescales its matrix
+# accumulators with vector instructions: keeping them in ordinary VGPRs
+# (rather than the accumulation registers) avoids copying them back and
+# forth on every tile.
+FILE_FLAGS = {
+    "decode_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -50,7 +58,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(args):
         src, obj = args
-        _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+              "-o", obj], verbose)
 
     jobs = min(len(srcs), max(1, (os.cpu_count() or 4)), 16)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:

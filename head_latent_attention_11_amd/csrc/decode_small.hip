@@ -1,5 +1,5 @@
 // Attention over the latent cache on gfx950 matrix cores for small blocks of
-// query rows: 16, 32 or 64 rows per workgroup.  This covers head counts that
+// query rows: 16 or 32 rows per workgroup.  This covers head counts that
 // are a multiple of 16 but give no multiple of 128 rows per sequence, e.g.
 // the 16 heads of DeepSeek-V2-Lite ("DeepSeek-V2: Strong, Economical,
 // Efficient", Appendix B) with one to four query tokens.
@@ -27,15 +27,17 @@
 //     32 dims x 16 rows of Q^T): wave w takes token block tb = w % 2 and
 //       NR = 1: the 16 rows over dims 288 (w / 2) .. +287 (the two halves
 //               are added when the pieces are gathered),
-//       NR = 2: row sub-block w / 2 over all 576 dims,
-//       NR = 4: row sub-blocks 2 (w / 2) and 2 (w / 2) + 1.
+//       NR = 2: row sub-block w / 2 over all 576 dims.
+//     (64 rows run as two blocks of 32: holding four sub-blocks' queries
+//     leaves too few registers to keep the operand reads ahead.)
 //     The 16 x 16 pieces go through a small LDS buffer so that every wave
 //     then holds all scores of the tile: lane (g, j) = (lane / 16, lane %
 //     16) holds row j's scores of tokens tok_row(tb, 4 g + i), i = 0..3,
 //     for both token blocks.
-//   * Softmax per row with a running max (log2 domain); when the max grows
-//     the row's accumulators and sum are rescaled.  Every wave computes the
-//     same weights.
+//   * Softmax per row in the log2 domain against a reference m_ref (the
+//     first max the row sees, raised only when a later max exceeds it by
+//     more than 8, with an exact rescaling of the row's accumulators and
+//     sum).  Every wave computes the same weights.
 //   * PV: wave w owns latent dims 128 w .. 128 w + 127 of all rows:
 //     O^T[dim, row] += C^T[dim, tok] P^T[tok, row] (v_mfma_f32_16x16x32_bf16).
 //     The B operand is the lane's own 8 weights (row j, the 8 tokens above:
@@ -116,19 +118,48 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x[l ^ 16] and x[l ^ 32] in lane l, without LDS.  v_permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second (v_permlane32_swap: the upper half with the lower half); with x
+// in both, one operand comes back holding x[l] and the other x[l ^ 16] (or
+// x[l ^ 32]), in an order that depends on the lane.  Written as assembly:
+// the compiler's builtins take the two results as equal when the two inputs
+// are, which they are not.
+__device__ __forceinline__ void swap16(float& lo, float& hi) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+}
+__device__ __forceinline__ void swap32(float& lo, float& hi) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+}
+// max / sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups
+// that hold one row's tokens)
+__device__ __forceinline__ float group_max4(float x) {
+  float lo = x, hi = x;
+  swap16(lo, hi);
+  x = fmaxf(lo, hi);
+  lo = x; hi = x;
+  swap32(lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float group_sum4(float x) {
+  float lo = x, hi = x;
+  swap16(lo, hi);
+  x = lo + hi;
+  lo = x; hi = x;
+  swap32(lo, hi);
+  return lo + hi;
+}
+
 }  // namespace
 
 template <int NR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   constexpr int RB = 16 * NR;                    // query rows per workgroup
-  constexpr int NQ = NR == 1 ? 1 : NR / 2;       // row sub-blocks of a wave's scores
   constexpr int KS = NR == 1 ? 9 : 18;           // 32-dim steps of a wave's scores
-  constexpr int NPIECE = NR == 1 ? 4 : 2 * NR;   // 1 KB score pieces per tile
-  constexpr int QSLOTS = NR == 4 ? 2 : 1;        // ring slots that stage the queries
-  static_assert(NR == 1 || NR == 2 || NR == 4, "16, 32 or 64 rows");
+  static_assert(NR == 1 || NR == 2, "16 or 32 rows");
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kSlots][kSlotBytes];
-  __shared__ __attribute__((aligned(16))) floatx4 s_x[NPIECE][64];
+  __shared__ __attribute__((aligned(16))) floatx4 s_x[4][64];   // score pieces
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -219,36 +250,23 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   };
 
   // ---- query block -> VGPRs (B operands of the scores: lane (g, j) holds
-  // row 16 nr + j, dims 32 ks + 8 g .. + 7).  Rows 32 q .. 32 q + 31 of the
-  // block are staged in slot kSlots - 1 - q; tiles 0 .. kSlots - 1 - QSLOTS
-  // go out right behind them.
+  // row 16 nq + j, dims 32 ks + 8 g .. + 7).  The block's rows are staged
+  // in the last ring slot; tiles 0, 1 and 2 go out right behind them.
   const uint8_t* qblk = (const uint8_t*)a.q_abs + ((size_t)b * rows + row0) * kRowBytes;
+  issue(buffer_rsrc(qblk, RB * kRowBytes), kSlots - 1);
 #pragma unroll
-  for (int q = 0; q < QSLOTS; ++q)
-    issue(buffer_rsrc(qblk + (size_t)q * kTile * kRowBytes, min(RB, kTile) * kRowBytes),
-          kSlots - 1 - q);
-  constexpr int kFirst = kSlots - QSLOTS;        // tiles issued with the queries
-#pragma unroll
-  for (int t = 0; t < kFirst; ++t)
+  for (int t = 0; t < kSlots - 1; ++t)
     if (t < ntiles) issue(tile_rsrc(t0 + t * kTile), t);
-  wait_loads(min(ntiles, kFirst) * nld);         // the query loads have landed
+  wait_loads(min(ntiles, kSlots - 1) * nld);     // the query loads have landed
   __syncthreads();
-  const int tb = wave & 1;
-  const int ks0 = NR == 1 ? 9 * (wave >> 1) : 0;
-  int nr_of[NQ];
+  const int tb = wave & 1;                       // token block of this wave's scores
+  const int ks0 = NR == 1 ? 9 * (wave >> 1) : 0; // first 32-dim step
+  const int nq = NR == 1 ? 0 : wave >> 1;        // row sub-block
+  bf16x8 qf[KS];
+  {
+    const uint8_t* src = s_ring[kSlots - 1] + (16 * nq + j) * kPitch + 64 * ks0 + 16 * g;
 #pragma unroll
-  for (int iq = 0; iq < NQ; ++iq) nr_of[iq] = NR == 1 ? 0 : (NR == 2 ? wave >> 1 : 2 * (wave >> 1) + iq);
-  bf16x8 qf[NQ][KS];
-#pragma unroll
-  for (int iq = 0; iq < NQ; ++iq) {
-    const int qr = 16 * nr_of[iq] + j;
-    const uint8_t* src = s_ring[kSlots - 1 - qr / kTile] + (qr % kTile) * kPitch + 64 * ks0 + 16 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[iq][ks] = *(const bf16x8*)(src + 64 * ks);
-  }
-  if constexpr (QSLOTS == 2) {
-    __syncthreads();                             // slot 2 is free again
-    if (2 < ntiles) issue(tile_rsrc(t0 + 2 * kTile), 2);
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8*)(src + 64 * ks);
   }
 
   // ---- per-lane LDS offsets of the operands
@@ -258,10 +276,10 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   const int v_off1 = tok_row(1, 4 * g + kq) * kPitch + 256 * wave + 8 * m4;
 
   floatx4 o[NR][8];
-  float m_run[NR], l_run[NR];
+  float m_ref[NR], l_run[NR];
 #pragma unroll
   for (int nr = 0; nr < NR; ++nr) {
-    m_run[nr] = -INFINITY;
+    m_ref[nr] = -INFINITY;
     l_run[nr] = 0.f;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) o[nr][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -275,68 +293,79 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
     if (it + kSlots - 1 < ntiles) issue(tile_rsrc(t0 + (it + kSlots - 1) * kTile), (it + kSlots - 1) & 3);
     const uint8_t* kt = s_ring[it & 3];
 
-    // scores: this wave's pieces
-    floatx4 sp[NQ];
+    // scores: this wave's piece.  All operand reads go out first (one LDS
+    // latency per tile), then the products, in two chains.
+    {
+      bf16x8 kv[KS];
 #pragma unroll
-    for (int iq = 0; iq < NQ; ++iq) sp[iq] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) kv[ks] = *(const bf16x8*)(kt + k_off + 64 * ks);
+      floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 kv = *(const bf16x8*)(kt + k_off + 64 * ks);
-#pragma unroll
-      for (int iq = 0; iq < NQ; ++iq)
-        sp[iq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qf[iq][ks], sp[iq], 0, 0, 0);
+      for (int ks = 0; ks < KS; ks += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[ks], qf[ks], s0, 0, 0, 0);
+        if (ks + 1 < KS) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[ks + 1], qf[ks + 1], s1, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);   // the LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, KS, 0);   // then the products
+      s_x[wave][lane] = s0 + s1;
     }
-#pragma unroll
-    for (int iq = 0; iq < NQ; ++iq) s_x[NR == 1 ? wave : tb + 2 * nr_of[iq]][lane] = sp[iq];
     __syncthreads();
 
     const int ts = t0 + it * kTile;
     bf16x8 pk[NR];
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr) {
-      float x[8];
+      float x[8];                                // raw scores of row j
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const floatx4 v = NR == 1 ? s_x[t][lane] + s_x[t + 2][lane] : s_x[t + 2 * nr][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = ts + tok_row(t, 4 * g + i);
-          x[4 * t + i] = (tok > lim[nr]) ? -INFINITY : v[i] * a.scale_log2;
-        }
+        for (int i = 0; i < 4; ++i) x[4 * t + i] = v[i];
       }
-      float mt = x[0];
+      if (ts + kTile - 1 > lim[nr]) {            // the tile crosses the visibility limit
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[nr], mt);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run[nr] - base);   // 0 while the row has seen nothing
-      m_run[nr] = m_new;
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = exp2_hw(x[e] - base);
-        ps += p[e];
+        for (int e = 0; e < 8; ++e)
+          if (ts + tok_row(e >> 2, 4 * g + (e & 3)) > lim[nr]) x[e] = -INFINITY;
       }
-      l_run[nr] = l_run[nr] * alpha + ps;
-      if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      float mt = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mt = group_max4(mt) * a.scale_log2;                        // the row's max over the tile (log2 domain)
+      // The weights are taken against a reference m_ref that only moves
+      // when the max exceeds it by more than 8 (weights up to 2^8): the
+      // accumulators are rescaled rarely, and exactly.
+      const bool raise = m_ref[nr] != -INFINITY && mt > m_ref[nr] + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float alpha = raise ? exp2_hw(m_ref[nr] - mt) : 1.0f;
+        l_run[nr] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) o[nr][cb] *= alpha;
       }
+      if (raise || m_ref[nr] == -INFINITY) m_ref[nr] = mt;
+      const float neg = (m_ref[nr] == -INFINITY) ? 0.f : -m_ref[nr];
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = exp2_hw(fmaf(x[e], a.scale_log2, neg));
+      l_run[nr] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 #pragma unroll
       for (int e = 0; e < 8; ++e) pk[nr][e] = (__bf16)p[e];
     }
 
-    // PV: this wave's 128 latent dims of every row
+    // PV: this wave's 128 latent dims of every row (reads first, then the
+    // products)
+    {
+      shortx4 v0[8], v1[8];
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const shortx4 v0 = lds_tr16(kt + v_off0 + 32 * cb);
-      const shortx4 v1 = lds_tr16(kt + v_off1 + 32 * cb);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int cb = 0; cb < 8; ++cb) {
+        v0[cb] = lds_tr16(kt + v_off0 + 32 * cb);
+        v1[cb] = lds_tr16(kt + v_off1 + 32 * cb);
+      }
 #pragma unroll
-      for (int nr = 0; nr < NR; ++nr)
-        o[nr][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pk[nr], o[nr][cb], 0, 0, 0);
+      for (int cb = 0; cb < 8; ++cb) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0[cb], v1[cb], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr)
+          o[nr][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pk[nr], o[nr][cb], 0, 0, 0);
+      }
     }
   }
 
@@ -345,10 +374,9 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   // partial in bf16 (combined in fp32).
 #pragma unroll
   for (int nr = 0; nr < NR; ++nr) {
-    float l_tot = l_run[nr] + __shfl_xor(l_run[nr], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = group_sum4(l_run[nr]);
     const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-    const float lse = (l_tot > 0.f) ? (m_run[nr] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    const float lse = (l_tot > 0.f) ? (m_ref[nr] + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     const int row = row0 + 16 * nr + j;
     if (ns == 1) {
       const size_t gr = (size_t)b * rows + row;
@@ -371,7 +399,7 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   }
 }
 
-// rows_wg: query rows per workgroup (16, 32 or 64); a.row_blocks counts
+// rows_wg: query rows per workgroup (16 or 32); a.row_blocks counts
 // blocks of that many rows.
 hipError_t launch_decode_small(const DecodeArgs& a, const ItemTable& tab, int rows_wg,
                                hipStream_t st) {
@@ -382,9 +410,6 @@ hipError_t launch_decode_small(const DecodeArgs& a, const ItemTable& tab, int ro
       break;
     case 32:
       hipLaunchKernelGGL(decode_small_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
-      break;
-    case 64:
-      hipLaunchKernelGGL(decode_small_kernel<4>, dim3(grid), dim3(256), 0, st, a, tab);
       break;
     default:
       return hipErrorInvalidValue;

@@ -69,7 +69,7 @@ bool fast_decode(const mla_dims_t* d, int T) {
          ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
 }
 
-// Attention in blocks of 16, 32 or 64 rows (16 heads of one query token per
+// Attention in blocks of 16 or 32 rows (16 heads of one query token per
 // row sub-block) for the other head counts that are multiples of 16, bf16
 // cache.  Returns the rows per block, or 0.
 int small_decode_rows(const mla_dims_t* d, int T) {
@@ -77,7 +77,7 @@ int small_decode_rows(const mla_dims_t* d, int T) {
       d->n_heads % 16 != 0 || fast_decode(d, T))
     return 0;
   const int64_t rows = (int64_t)d->n_heads * T;
-  return rows % 64 == 0 ? 64 : rows % 32 == 0 ? 32 : 16;
+  return rows % 32 == 0 ? 32 : 16;
 }
 
 // Format of the absorbed query.
