@@ -73,6 +73,12 @@ class Workload:
     seed: int = 0
     description: str = ""
     d_model: int = 5120        # hidden size d (rows of W^O)
+    # context extension of the RoPE parts (YaRN); yarn_factor <= 1: off
+    yarn_factor: float = 0.0   # s
+    yarn_alpha: float = 1.0
+    yarn_beta: float = 32.0
+    yarn_orig_len: int = 4096  # original (training) context
+    yarn_coef: float = 0.0707  # sqrt(t) = coef * ln(s) + 1
 
     @property
     def d_qk(self) -> int:

@@ -34,6 +34,7 @@ import numpy as np
 
 from . import formats
 from .rope import rope as _rope
+from .rope import yarn_logit_factor, yarn_theta
 
 
 def attend_head(q_c: np.ndarray, q_r: np.ndarray, C: np.ndarray, KR: np.ndarray,
@@ -131,12 +132,13 @@ def up_project(latent: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
 
 
 def produce_rows(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, gain, eps: float,
-                 pos=None, rope_base: float = 10000.0) -> np.ndarray:
+                 pos=None, rope_base: float = 10000.0, theta=None) -> np.ndarray:
     """The cache row of each token, from its hidden state h_t ([V3] notes, MLA
     section: c^KV_t = W^DKV h_t and k^R_t = RoPE(W^KR h_t); [V2] section 3.2.1:
     an RMS norm follows the compressed latent vector):
         c = W^DKV h,  c <- c * gain / sqrt(mean(c^2) + eps)  (gain None: no norm),
-        k = W^KR h, rotated at position pos (pos None: not rotated),
+        k = W^KR h, rotated at position pos (pos None: not rotated) by the
+            frequencies theta (None: plain RoPE with rope_base),
         row = [c ; k].
 
     h [N, d], w_dkv [d_c, d], w_kr [d_h^R, d], gain [d_c] or None, pos [N]
@@ -148,7 +150,7 @@ def produce_rows(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray, gain, eps: 
         c = c / rms * np.asarray(gain, dtype=np.float64)[None, :]
     k = h @ w_kr.T
     if pos is not None:
-        k = _rope(k, np.asarray(pos), rope_base)
+        k = _rope(k, np.asarray(pos), rope_base, theta=theta)
     return np.concatenate([c, k], axis=1)
 
 
@@ -215,9 +217,11 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload, seqs=None) -> Dict[str,
     c = _to_f64(gen["c_kv"][idx], src_dt)
     kr = _to_f64(gen["k_r"][idx], src_dt)
     if w.rope:
-        kr = _rope(kr, row_pos, w.rope_base)
+        theta = yarn_theta(w.d_rope, w.rope_base, w.yarn_factor, w.yarn_alpha, w.yarn_beta,
+                           w.yarn_orig_len)
+        kr = _rope(kr, row_pos, theta=theta)
         qpos = np.repeat(gen["q_pos"], w.n_heads).reshape(-1, w.n_heads)
-        d["q_rope"] = _rope(d["q_rope"], qpos, w.rope_base)
+        d["q_rope"] = _rope(d["q_rope"], qpos, theta=theta)
     if w.kv_dtype == "fp8":
         rows = np.concatenate([c, kr], axis=1).astype(np.float32)
         codes, scales = formats.quantize_rows_e4m3(rows)
@@ -230,10 +234,12 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload, seqs=None) -> Dict[str,
 
 def decode_workload(gen: Dict[str, np.ndarray], workload, seqs=None, heads=None):
     """Oracle outputs for a generated workload (optionally a sample of it)."""
-    d = logical_inputs(gen, workload, seqs)
+    w = workload
+    d = logical_inputs(gen, w, seqs)
+    scale = yarn_logit_factor(w.yarn_factor, w.yarn_coef) / math.sqrt(w.d_head + w.d_rope)
     return decode(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_rows"],
                   d["kr_rows"], d["row_offsets"], d["seq_lens"],
-                  workload.q_tokens, seqs=seqs, heads=heads)
+                  w.q_tokens, softmax_scale=scale, seqs=seqs, heads=heads)
 
 
 def cache_row_index(seq: np.ndarray, pos: np.ndarray, page_table, page_size: int,

@@ -520,3 +520,80 @@ def test_producer_selection_weights_and_rope():
     a = rot[:, d_c:].reshape(n, -1, 2)
     b = h[:, [1, 3, 4, 7]].reshape(n, -1, 2)
     np.testing.assert_allclose(np.linalg.norm(a, axis=2), np.linalg.norm(b, axis=2), rtol=1e-13)
+
+
+# ------------------------------------------------- YaRN context extension
+# DeepSeek-V2's settings ("DeepSeek-V2", section 3, long context extension):
+# s = 40, alpha = 1, beta = 32 over a 4K training context, RoPE base 10^4,
+# d_h^R = 64.
+from oracle.rope import rope_theta, yarn_logit_factor, yarn_theta  # noqa: E402
+
+V2_YARN = dict(base=10000.0, factor=40.0, alpha=1.0, beta=32.0, orig_len=4096)
+
+
+def test_yarn_without_scaling_is_plain_rope():
+    for s in (0.0, 0.5, 1.0):
+        np.testing.assert_array_equal(yarn_theta(64, 10000.0, s, 1.0, 32.0, 4096),
+                                      rope_theta(64))
+    # and rope_theta is the frequency rope() uses by default
+    x = np.random.default_rng(3).standard_normal((4, 64))
+    p = np.array([0, 5, 999, 4095])
+    np.testing.assert_array_equal(rope(x, p, theta=rope_theta(64)), rope(x, p))
+
+
+def test_yarn_regimes_for_the_v2_settings():
+    # Pair k turns r_k = 4096 * 10^(-k/8) / (2 pi) times over the 4K context.
+    # r_k > beta = 32  <=>  k < 8 log10(4096 / (64 pi)) = 10.47: pairs 0..10 keep theta;
+    # r_k < alpha = 1  <=>  k > 8 log10(4096 / (2 pi)) = 22.51: pairs 23..31 get theta / 40.
+    th, t0 = yarn_theta(64, **V2_YARN), rope_theta(64)
+    assert list(np.nonzero(th == t0)[0]) == list(range(0, 11))
+    assert list(np.nonzero(np.abs(th * 40 / t0 - 1) < 1e-15)[0]) == list(range(23, 32))
+    mid = np.arange(11, 23)
+    assert np.all(th[mid] < t0[mid]) and np.all(th[mid] > t0[mid] / 40)
+
+
+def test_yarn_ramp_is_monotone():
+    ratio = yarn_theta(64, **V2_YARN) / rope_theta(64)
+    assert np.all(np.diff(ratio) <= 1e-15)      # fewer turns -> closer to 1/s (up to rounding)
+    assert ratio[0] == 1.0 and abs(ratio[-1] * 40 - 1) < 1e-15
+
+
+def test_yarn_interpolates_low_and_keeps_high_frequencies():
+    # Low-frequency pairs rotate at position s*p as plain RoPE does at p
+    # (position interpolation); high-frequency pairs rotate exactly as
+    # plain RoPE at the same position.
+    th = yarn_theta(64, **V2_YARN)
+    x = np.random.default_rng(4).standard_normal((5, 64))
+    p = np.array([3, 77, 1000, 4095, 100])
+    np.testing.assert_allclose(rope(x, 40 * p, theta=th)[:, 46:], rope(x, p)[:, 46:],
+                               rtol=0, atol=1e-9)
+    np.testing.assert_array_equal(rope(x, p, theta=th)[:, :22], rope(x, p)[:, :22])
+
+
+def test_yarn_relative_position_property():
+    th = yarn_theta(64, **V2_YARN)
+    rng = np.random.default_rng(5)
+    x, y = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n, k in ((100000, 99000, 98000), (160000, 5, 5), (7, 3, 2)):
+        a = rope(x[None], np.array([m]), theta=th)[0] @ rope(y[None], np.array([n]), theta=th)[0]
+        b = rope(x[None], np.array([m - k]), theta=th)[0] @ rope(y[None], np.array([n - k]), theta=th)[0]
+        assert abs(a - b) <= 1e-9 * (abs(a) + 1)
+
+
+def test_yarn_logit_factor_and_how_it_enters():
+    assert yarn_logit_factor(1.0, 0.0707) == 1.0 and yarn_logit_factor(0.0, 0.1) == 1.0
+    # sqrt(t) = 0.0707 ln 40 + 1 with ln 40 = 3.6888794541139363
+    m = 0.0707 * 3.6888794541139363 + 1.0
+    assert abs(yarn_logit_factor(40.0, 0.0707) - m * m) < 1e-14
+    assert yarn_logit_factor(40.0, 0.1) > yarn_logit_factor(40.0, 0.0707) > 1.0
+    # a factor t on the logits is the same as scaling the whole query by t
+    rng = np.random.default_rng(6)
+    H, dh, dc, dr, L = 2, 8, 16, 4, 9
+    qn, qr = rng.standard_normal((1, H, dh)), rng.standard_normal((1, H, dr))
+    wuk, wuv = rng.standard_normal((H, dh, dc)), rng.standard_normal((H, dh, dc))
+    C, KR = rng.standard_normal((L, dc)), rng.standard_normal((L, dr))
+    t = yarn_logit_factor(40.0, 0.0707)
+    a = mla.decode(qn, qr, wuk, wuv, C, KR, [0], [L], 1, softmax_scale=t / math.sqrt(dh + dr))
+    b = mla.decode(t * qn, t * qr, wuk, wuv, C, KR, [0], [L], 1)
+    for k in ("o", "latent", "lse"):
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-12)
