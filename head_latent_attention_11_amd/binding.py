@@ -40,22 +40,29 @@ class MLADims(ctypes.Structure):
         ("page_size", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("rope_base", ctypes.c_float), ("precision", ctypes.c_int32),
+        ("yarn_factor", ctypes.c_float), ("yarn_alpha", ctypes.c_float),
+        ("yarn_beta", ctypes.c_float), ("yarn_orig_len", ctypes.c_int32),
+        ("yarn_coef", ctypes.c_float),
     ]
 
     @classmethod
     def make(cls, n_heads, d_head, d_latent, d_rope, kv_dtype="bf16",
              q_dtype="bf16", softmax_scale=0.0, rope_base=0.0, page_size=64,
-             precision="bf16"):
+             precision="bf16", yarn_factor=0.0, yarn_alpha=1.0, yarn_beta=32.0,
+             yarn_orig_len=4096, yarn_coef=0.0707):
         kv = DTYPE_CODES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
         qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else q_dtype
         pr = PRECISION_CODES[precision] if isinstance(precision, str) else precision
         return cls(n_heads, d_head, d_latent, d_rope, page_size, kv, qd,
-                   softmax_scale, rope_base, pr)
+                   softmax_scale, rope_base, pr, yarn_factor, yarn_alpha, yarn_beta,
+                   yarn_orig_len, yarn_coef)
 
     @classmethod
     def from_workload(cls, w, precision="bf16"):
         return cls.make(w.n_heads, w.d_head, w.d_latent, w.d_rope, w.kv_dtype,
-                        w.q_dtype, 0.0, w.rope_base, w.page_size, precision)
+                        w.q_dtype, 0.0, w.rope_base, w.page_size, precision,
+                        w.yarn_factor, w.yarn_alpha, w.yarn_beta, w.yarn_orig_len,
+                        w.yarn_coef)
 
     def qabs_is_f32(self) -> bool:
         return self.q_dtype == F32 or self.precision == PREC_FP32

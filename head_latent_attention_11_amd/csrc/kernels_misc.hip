@@ -14,11 +14,8 @@
 namespace mla {
 
 // ============================================================ RoPE helper
-// Interleaved pairs (2k, 2k+1) rotated by pos * base^(-2k/d); angle and
-// rotation in double precision.
-__device__ inline double rope_theta(int k, int d, float base) {
-  return pow((double)base, -2.0 * (double)k / (double)d);
-}
+// Interleaved pairs (2k, 2k+1) rotated by pos * theta_k (rope_theta, with
+// or without context extension); angle and rotation in double precision.
 __device__ inline void rope_rot(float x0, float x1, int pos, double theta, float* y0, float* y1) {
   double ang = (double)pos * theta;
   double s, c;
@@ -27,8 +24,8 @@ __device__ inline void rope_rot(float x0, float x1, int pos, double theta, float
   *y1 = (float)((double)x0 * s + (double)x1 * c);
 }
 __device__ inline void rope_pair(float x0, float x1, int pos, int k, int d,
-                                 float base, float* y0, float* y1) {
-  rope_rot(x0, x1, pos, rope_theta(k, d, base), y0, y1);
+                                 const RopeFreq& rf, float* y0, float* y1) {
+  rope_rot(x0, x1, pos, rope_theta(k, d, rf), y0, y1);
 }
 
 template <typename T> __device__ inline float load_f(const T* p, size_t i);
@@ -74,7 +71,7 @@ template <typename OutT>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
-    OutT* __restrict__ q_abs, int n_tok, int n_h, float rope_base) {
+    OutT* __restrict__ q_abs, int n_tok, int n_h, RopeFreq rope) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
   __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kAbsLdsRow];
@@ -125,7 +122,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const int ch = tid + 256 * i, r = ch >> 4, c8 = (ch & 15) * 8;
     stg[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
-  const double theta = q_pos ? rope_theta(rk, DR, rope_base) : 0.0;
+  const double theta = q_pos ? rope_theta(rk, DR, rope) : 0.0;
   for (int p = p_first; p < n_pairs; p += 1024) {
     const int tok = p >> 5;
     float x0 = rx0, x1 = rx1;
@@ -206,7 +203,7 @@ __global__ __launch_bounds__(256) void absorb_general_kernel(
     const T* __restrict__ q_nope, const T* __restrict__ q_rope,
     const T* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
     OutT* __restrict__ q_abs, int n_tok, int n_h, int d_h, int d_c, int d_r,
-    float rope_base) {
+    RopeFreq rope) {
   const int D = d_c + d_r;
   const size_t total = (size_t)n_tok * n_h * D;
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(256) void absorb_general_kernel(
       const int k = (e - d_c) >> 1;
       const T* q = q_rope + row * d_r;
       float x0 = load_f(q, 2 * k), x1 = load_f(q, 2 * k + 1);
-      if (q_pos) rope_pair(x0, x1, q_pos[tok], k, d_r, rope_base, &x0, &x1);
+      if (q_pos) rope_pair(x0, x1, q_pos[tok], k, d_r, rope, &x0, &x1);
       v = ((e - d_c) & 1) ? x1 : x0;
     }
     store_f(q_abs, idx, v);
@@ -242,7 +239,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
     long long cache_rows, int apply_rope, void* __restrict__ cache,
-    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, float rope_base,
+    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, RopeFreq rope,
     int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps) {
   const int lane = threadIdx.x & 63;
   const int D = d_c + d_r;
@@ -277,7 +274,7 @@ __global__ __launch_bounds__(256) void append_kernel(
           float x0 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp);
           float x1 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp + 1);
           float y0, y1;
-          rope_pair(x0, x1, p, kp, d_r, rope_base, &y0, &y1);
+          rope_pair(x0, x1, p, kp, d_r, rope, &y0, &y1);
           x = (q & 1) ? y1 : y0;
         } else {
           x = load_f(new_kr, (size_t)r * kr_stride + q);
@@ -588,19 +585,19 @@ __global__ __launch_bounds__(256) void up_proj_general_kernel(
 hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
                          const void* q_rope, const void* w_uk,
                          const int32_t* q_pos, void* q_abs, int n_tok,
-                         float rope_base, hipStream_t st) {
+                         RopeFreq rope, hipStream_t st) {
   const bool out_f32 = d.q_dtype == MLA_F32 || d.precision == MLA_PREC_FP32;
   if (fast) {
     if (out_f32)
       hipLaunchKernelGGL(absorb_mfma_kernel<float>, dim3(d.n_heads * 4), dim3(256), 0, st,
                          (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok,
-                         d.n_heads, rope_base);
+                         d.n_heads, rope);
     else
       hipLaunchKernelGGL(absorb_mfma_kernel<uint16_t>, dim3(d.n_heads * 4), dim3(256), 0, st,
                          (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
-                         d.n_heads, rope_base);
+                         d.n_heads, rope);
   } else {
     const size_t total = (size_t)n_tok * d.n_heads * (d.d_latent + d.d_rope);
     const int grid = (int)std::min<size_t>((total + 255) / 256, 65535);
@@ -608,17 +605,17 @@ hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
       hipLaunchKernelGGL((absorb_general_kernel<float, float>), dim3(grid), dim3(256), 0, st,
                          (const float*)q_nope, (const float*)q_rope, (const float*)w_uk,
                          q_pos, (float*)q_abs, n_tok, d.n_heads, d.d_head,
-                         d.d_latent, d.d_rope, rope_base);
+                         d.d_latent, d.d_rope, rope);
     else if (out_f32)
       hipLaunchKernelGGL((absorb_general_kernel<uint16_t, float>), dim3(grid), dim3(256), 0,
                          st, (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok, d.n_heads,
-                         d.d_head, d.d_latent, d.d_rope, rope_base);
+                         d.d_head, d.d_latent, d.d_rope, rope);
     else
       hipLaunchKernelGGL((absorb_general_kernel<uint16_t, uint16_t>), dim3(grid), dim3(256),
                          0, st, (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok, d.n_heads,
-                         d.d_head, d.d_latent, d.d_rope, rope_base);
+                         d.d_head, d.d_latent, d.d_rope, rope);
   }
   return hipGetLastError();
 }
@@ -628,14 +625,14 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
                          const int32_t* page_table, int B, int max_pages,
                          int max_len, long long cache_rows, int apply_rope,
                          void* cache, float* kv_scale, int n_rows,
-                         float rope_base, hipStream_t st, bool src_f32, int c_stride,
+                         RopeFreq rope, hipStream_t st, bool src_f32, int c_stride,
                          int kr_stride, const float* norm_gain, float norm_eps) {
   const int grid = std::min((n_rows + 3) / 4, 16384);
 #define MLA_APPEND(ST, KV)                                                                   \
   hipLaunchKernelGGL((append_kernel<ST, KV>), dim3(grid), dim3(256), 0, st,                  \
                      (const ST*)new_c, (const ST*)new_kr, seq_idx, pos, page_table, B,       \
                      max_pages, max_len, cache_rows, apply_rope, cache, kv_scale, n_rows,    \
-                     d.d_latent, d.d_rope, rope_base, c_stride, kr_stride, norm_gain, norm_eps)
+                     d.d_latent, d.d_rope, rope, c_stride, kr_stride, norm_gain, norm_eps)
   if (d.kv_dtype == MLA_F32) MLA_APPEND(float, MLA_F32);
   else if (d.kv_dtype == MLA_BF16 && !src_f32) MLA_APPEND(uint16_t, MLA_BF16);
   else if (d.kv_dtype == MLA_BF16) MLA_APPEND(float, MLA_BF16);

@@ -12,10 +12,10 @@
 
 namespace mla {
 hipError_t launch_absorb(const mla_dims_t&, bool, const void*, const void*, const void*,
-                         const int32_t*, void*, int, float, hipStream_t);
+                         const int32_t*, void*, int, RopeFreq, hipStream_t);
 hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int32_t*,
                          const int32_t*, const int32_t*, int, int, int, long long, int,
-                         void*, float*, int, float, hipStream_t, bool, int, int, const float*,
+                         void*, float*, int, RopeFreq, hipStream_t, bool, int, int, const float*,
                          float);
 hipError_t launch_combine(const DecodeArgs&, hipStream_t);
 size_t gemm_xwt_workspace(int, int, int, int, int);
@@ -53,6 +53,13 @@ int32_t check_dims(const mla_dims_t* d) {
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return MLA_ERR_ARG;
   if (d->precision != MLA_PREC_BF16 && d->precision != MLA_PREC_FP32) return MLA_ERR_ARG;
+  if (!isfinite(d->yarn_factor) || d->yarn_factor < 0.f) return MLA_ERR_ARG;
+  if (d->yarn_factor > 1.f) {                        // context extension in use
+    if (!(d->yarn_alpha > 0.f) || !(d->yarn_beta > d->yarn_alpha) || !isfinite(d->yarn_beta))
+      return MLA_ERR_ARG;
+    if (d->yarn_orig_len < 1) return MLA_ERR_ARG;
+    if (!(d->yarn_coef >= 0.f) || !isfinite(d->yarn_coef)) return MLA_ERR_ARG;
+  }
   return MLA_OK;
 }
 
@@ -85,11 +92,26 @@ int32_t qabs_dtype(const mla_dims_t* d) {
   return d->precision == MLA_PREC_FP32 ? MLA_F32 : d->q_dtype;
 }
 
-float rope_base_of(const mla_dims_t* d) { return d->rope_base > 0.f ? d->rope_base : 10000.f; }
+RopeFreq rope_of(const mla_dims_t* d) {
+  RopeFreq r;
+  r.base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  r.factor = d->yarn_factor > 1.f ? d->yarn_factor : 1.f;
+  r.alpha = d->yarn_alpha;
+  r.beta = d->yarn_beta;
+  r.orig_len = (float)d->yarn_orig_len;
+  return r;
+}
 
+// 1/sqrt(d_h + d_h^R), times the YaRN logit factor (c ln s + 1)^2 when
+// context extension is on; an explicit softmax_scale replaces both.
 float softmax_scale_of(const mla_dims_t* d) {
-  return d->softmax_scale > 0.f ? d->softmax_scale
-                                : 1.0f / sqrtf((float)(d->d_head + d->d_rope));
+  if (d->softmax_scale > 0.f) return d->softmax_scale;
+  double sc = 1.0 / sqrt((double)(d->d_head + d->d_rope));
+  if (d->yarn_factor > 1.f) {
+    const double m = (double)d->yarn_coef * log((double)d->yarn_factor) + 1.0;
+    sc *= m * m;
+  }
+  return (float)sc;
 }
 
 int32_t status_of(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
@@ -186,7 +208,7 @@ int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_r
     return MLA_ERR_ALIGN;
   const bool fast = fast_shape(dims);
   return status_of(launch_absorb(*dims, fast, q_nope, q_rope, w_uk, q_pos, q_abs, n_tokens,
-                                 rope_base_of(dims), (hipStream_t)stream));
+                                 rope_of(dims), (hipStream_t)stream));
 }
 
 int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* new_kr,
@@ -216,7 +238,7 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* 
     return MLA_ERR_ALIGN;
   return status_of(launch_append(*dims, new_c, new_kr, seq_idx, pos, page_table, batch,
                                  max_pages, max_len, cache_rows, apply_rope, cache,
-                                 kv_scale, n_rows, rope_base_of(dims), (hipStream_t)stream,
+                                 kv_scale, n_rows, rope_of(dims), (hipStream_t)stream,
                                  dims->kv_dtype == MLA_F32, dims->d_latent, dims->d_rope,
                                  nullptr, 0.f));
 }
@@ -290,7 +312,7 @@ int32_t mla_kv_produce(const mla_dims_t* dims, const void* h, int32_t d_model,
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   return status_of(launch_append(*dims, rows, rows + dims->d_latent, seq_idx, pos, page_table,
                                  batch, max_pages, max_len, cache_rows, apply_rope, cache,
-                                 kv_scale, n_rows, rope_base_of(dims), s, true, D, D, norm_gain,
+                                 kv_scale, n_rows, rope_of(dims), s, true, D, D, norm_gain,
                                  norm_eps));
 }
 

@@ -80,6 +80,28 @@ __host__ __device__ inline uint32_t f32_to_e4m3(float x) {
   return code | sign;
 }
 
+// ------------------------------------------------------------------ RoPE
+// Frequencies of the interleaved pairs (2k, 2k+1): theta_k = base^(-2k/d),
+// and with context extension (factor > 1, YaRN's NTK-by-parts rule) pair k,
+// which turns r_k = orig_len theta_k / (2 pi) times over the original
+// context, takes (1 - g) theta_k / factor + g theta_k with g = clamp((r_k -
+// alpha) / (beta - alpha), 0, 1).  Computed in double precision.
+struct RopeFreq {
+  float base;
+  float factor;     // <= 1: no extension
+  float alpha, beta;
+  float orig_len;
+};
+
+__host__ __device__ inline double rope_theta(int k, int d, const RopeFreq& rf) {
+  const double theta = pow((double)rf.base, -2.0 * (double)k / (double)d);
+  if (!(rf.factor > 1.0f)) return theta;
+  const double turns = (double)rf.orig_len * theta / 6.283185307179586;
+  double g = (turns - (double)rf.alpha) / ((double)rf.beta - (double)rf.alpha);
+  g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+  return (1.0 - g) * theta / (double)rf.factor + g * theta;
+}
+
 // ------------------------------------------------------------ split planner
 // Tokens per KV chunk of sequence b.  num_splits > 0: each sequence is cut
 // into at most num_splits chunks of equal size rounded up to the page size;

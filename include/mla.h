@@ -81,6 +81,25 @@ typedef struct mla_dims {
   float softmax_scale; /* 0 -> 1/sqrt(d_head + d_rope) */
   float rope_base;     /* RoPE base; 0 -> 10000 */
   int32_t precision;   /* MLA_PREC_BF16 or MLA_PREC_FP32, see below */
+  /* Context extension of the RoPE parts (YaRN, which "DeepSeek-V2",
+   * section 3, long context extension, applies to the decoupled key and
+   * query only: s = 40, alpha = 1, beta = 32, 4K training context).
+   * yarn_factor <= 1 (or 0): plain RoPE.  Otherwise pair k's frequency
+   * theta_k = base^(-2k/d_h^R) becomes
+   *   (1 - g) theta_k / s + g theta_k,
+   *   g = clamp((r_k - alpha) / (beta - alpha), 0, 1),
+   *   r_k = yarn_orig_len * theta_k / (2 pi)   (turns over the old context),
+   * in every rotation the library applies (mla_absorb_q, mla_cache_append,
+   * mla_kv_produce), and when softmax_scale is 0 the attention scale is
+   * (yarn_coef * ln s + 1)^2 / sqrt(d_h + d_h^R) (the pages' length scaling
+   * factor sqrt(t) = c ln s + 1, taken as a factor t on every logit;
+   * c = 0.0707 for DeepSeek-V2, 0.1 in the DeepSeek-V3 notes).  Zeroed
+   * fields keep the plain behaviour.                                       */
+  float yarn_factor;   /* s */
+  float yarn_alpha;    /* alpha > 0 */
+  float yarn_beta;     /* beta > alpha */
+  int32_t yarn_orig_len; /* original context length L (tokens), >= 1 */
+  float yarn_coef;     /* c >= 0 */
 } mla_dims_t;
 
 /* Arithmetic of the absorbed query and the attention (inputs and weights are
@@ -110,7 +129,8 @@ typedef enum mla_precision {
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
  *       d_h^R <= 128 (even),
  *       every q_dtype / kv_dtype combination (e.g. the all-fp32 problems).
- * RoPE uses interleaved pairs (2k, 2k+1) rotated by pos * base^(-2k/d_h^R).
+ * RoPE uses interleaved pairs (2k, 2k+1) rotated by pos * theta_k, theta_k =
+ * base^(-2k/d_h^R) (or its YaRN form, above).
  */
 
 /* ------------------------------------------------------------------------ */

@@ -177,6 +177,19 @@ def test_absorb_append_upproj_validation(mla):
               8, None) == ALIGN
 
 
+def test_yarn_settings_validation(mla):
+    lib, b = mla
+    assert _ws(lib, _v2(b, yarn_factor=40.0), [4096])[0] == OK
+    assert _ws(lib, _v2(b, yarn_factor=1.0, yarn_alpha=0.0), [4096])[0] == OK   # off: unchecked
+    for bad in (dict(yarn_factor=-1.0), dict(yarn_factor=float("nan")),
+                dict(yarn_factor=40.0, yarn_alpha=0.0),
+                dict(yarn_factor=40.0, yarn_beta=0.5),                  # beta <= alpha
+                dict(yarn_factor=40.0, yarn_orig_len=0),
+                dict(yarn_factor=40.0, yarn_coef=-0.1),
+                dict(yarn_factor=40.0, yarn_beta=float("inf"))):
+        assert _ws(lib, _v2(b, **bad), [4096])[0] == ARG, bad
+
+
 def _ws(lib, dims, lens, T=1, splits=0):
     arr = (ctypes.c_int32 * len(lens))(*lens)
     out = ctypes.c_size_t(0)

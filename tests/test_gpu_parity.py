@@ -18,6 +18,7 @@ from gpu_support import (LSE_ABS, MAX_ABS_BF16, REL_L2_BF16, REL_L2_FP8, REL_L2_
 from mla_inputs import WORKLOADS, generate, small_variant
 from oracle import formats
 from oracle import mla as omla
+from oracle.rope import yarn_theta
 
 pytestmark = pytest.mark.gpu
 
@@ -125,12 +126,31 @@ SMALL = [
                   lengths=(70, 129), kv_dtype="fp8", rope=True),
     small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_bf16cache", kv_dtype="bf16",
                   batch=2, kv_len=0, lengths=(64, 300), num_splits=2),
+    small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_yarn", yarn_factor=8.0,
+                  yarn_orig_len=16, yarn_beta=8.0),
 ]
 
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_decode_parity_small(w):
     _run_compare(w, precision=PRECISION.get(w.name, "bf16"))
+
+
+# Context extension (YaRN) of the RoPE parts, rotated by the library (query
+# absorption and cache append) at positions past the 4K context, and the
+# logit factor (c ln s + 1)^2 in the attention; sampled heads.
+YARN = [
+    (small_variant(V2, name="v2_yarn_rope", batch=3, kv_len=0, lengths=(5000, 700, 4500),
+                   rope=True, yarn_factor=40.0), [0, 77, 127]),
+    (small_variant(V2, name="lite_yarn_rope", batch=3, n_heads=16, kv_len=0,
+                   lengths=(5000, 700, 4500), rope=True, yarn_factor=40.0, yarn_coef=0.1),
+     [0, 9, 15]),
+]
+
+
+@pytest.mark.parametrize("w,heads", YARN, ids=[c[0].name for c in YARN])
+def test_decode_parity_yarn(w, heads):
+    _run_compare(w, heads=heads)
 
 
 FP32_MODE = [
@@ -278,8 +298,12 @@ def test_cache_append_bit_exact(layout, kv):
         assert np.all(np.isnan(rest))
 
 
-def test_cache_append_rope_matches_oracle():
-    w = WORKLOADS["tiny_fp32"]
+@pytest.mark.parametrize("w", [WORKLOADS["tiny_fp32"],
+                               small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_yarn",
+                                             yarn_factor=8.0, yarn_orig_len=16,
+                                             yarn_beta=8.0)],
+                         ids=["plain", "yarn"])
+def test_cache_append_rope_matches_oracle(w):
     gen = generate(w)
     buf = _buffers(w, gen)
     torch.cuda.synchronize()
@@ -463,6 +487,7 @@ PRODUCE = [
     (small_variant(V2, name="v2_fp8", kv_dtype="fp8"), "paged", True),
     (V2, "paged", False),                                          # no RMS norm
     (WORKLOADS["tiny_fp32"], "contiguous", True),                  # fp32: general projection
+    (small_variant(V2, name="v2_yarn", yarn_factor=40.0, yarn_orig_len=64), "paged", True),
 ]
 
 
@@ -520,7 +545,8 @@ def test_kv_produce_parity(w, layout, norm):
            else formats.bf16_to_f64(inp["w_dkv_kr"]))
     ref = omla.produce_rows(h64, w64[:w.d_latent], w64[w.d_latent:],
                             inp["gain"].astype(np.float64) if norm else None, eps, pos=pos,
-                            rope_base=w.rope_base)
+                            theta=yarn_theta(w.d_rope, w.rope_base, w.yarn_factor,
+                                             w.yarn_alpha, w.yarn_beta, w.yarn_orig_len))
     if w.kv_dtype == "fp8":
         codes = cache.cpu().numpy()
         sc = scale.cpu().numpy()
