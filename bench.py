@@ -35,8 +35,9 @@ COPY_CEILING_BYTES = 2 ** 30            # plain device copy reported as the prac
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 _CSRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
-                  ("decode_mfma.hip", "decode_mfma_asm.inc", "kernels_misc.hip",
-                   "mla_common.hpp", "plan_device.hpp", "mla_api.hip")]
+                  ("decode_mfma.hip", "decode_mfma_asm.inc", "decode_small.hip",
+                   "kernels_misc.hip", "mla_common.hpp", "plan_device.hpp", "mla_api.hip")]
+LITE_WORKLOAD = "v2lite_b64_l8k_bf16"   # DeepSeek-V2-Lite shapes (16 heads)
 
 
 def algorithmic(w, seq_lens):
@@ -231,6 +232,61 @@ def time_kv_produce(w, buf, stream):
             "frac_hbm": round(byts / t / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def time_lite(stream, steps: int):
+    """DeepSeek-V2-Lite attention shapes (16 heads: the 16-row attention
+    kernel), reported next to the main line: the whole step (absorb ->
+    attention -> up-projection) and the attention call alone, HIP-event
+    timed over graph replays with the cache replicated past the memory-side
+    cache."""
+    import torch
+    from head_latent_attention_11_amd.runner import DecodeBuffers
+    from mla_inputs import WORKLOADS, generate
+    w = WORKLOADS[LITE_WORKLOAD]
+    gen = generate(w)
+    seq_lens = [int(x) for x in gen["seq_lens"]]
+    cache_b, io_b, flops = algorithmic(w, seq_lens)
+    reps = max(2, -(-768 * 2 ** 20 // cache_b))
+    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=reps)
+    per = 10
+
+    def timed(call):
+        def fn():
+            for i in range(per):
+                call(i % reps)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(2):
+            g.replay()
+        n = max(2, steps // per)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / (n * per)
+
+    t_step = timed(lambda r: buf.step(replica=r))
+    t_attn = timed(lambda r: buf.attend(replica=r))
+    del buf
+    byts = cache_b + io_b
+    return {"workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "n_heads": w.n_heads,
+            "step_us": round(t_step * 1e6, 2),
+            "tokens_per_s": round(w.batch * w.q_tokens / t_step, 1),
+            "attn_us": round(t_attn * 1e6, 2),
+            "latent_cache_GBps": round(cache_b / t_attn / 1e9, 1),
+            "bytes_alg_per_launch": byts,
+            "frac_hbm": round(byts / t_attn / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +299,8 @@ def main():
                     help="skip the timings of the cache producer and of the output "
                          "projection around the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lite", action="store_true",
+                    help="skip the DeepSeek-V2-Lite (16-head) attention line")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a calibration copy and a few attention calls for "
                          "rocprofv3 counter runs (see bench_traffic.py), then exit")
@@ -374,8 +432,9 @@ def main():
                 "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4)}
     tr = traffic_for_current_kernel(w.name)
     roof["traffic"] = tr["hbm_bytes_per_launch"] if tr else None
-    roof["kernel"] = ("mla_decode_attn (decode_mfma_kernel + combine_kernel when split), "
-                      "per call, HIP-event timed over back-to-back graph replays")
+    roof["kernel"] = ("mla_decode_attn (decode_mfma_kernel, or decode_small_kernel for "
+                      "query-row counts that are no multiple of 128, + combine_kernel when "
+                      "split), per call, HIP-event timed over back-to-back graph replays")
     roof["bytes_alg_per_launch"] = bytes_alg
     roof["flops_alg_per_launch"] = flops
 
@@ -422,6 +481,8 @@ def main():
     if w.q_dtype == "bf16" and not args.no_out_proj:
         out["out_proj"] = time_out_proj(w, buf, stream)
         out["kv_produce"] = time_kv_produce(w, buf, stream)
+    if not args.no_lite and w.name != LITE_WORKLOAD:
+        out["v2lite"] = time_lite(stream, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, gen, args.cpu_budget)
     print(json.dumps(out), flush=True)
