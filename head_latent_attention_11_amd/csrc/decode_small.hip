@@ -20,9 +20,13 @@
 //   * KV tiles of 32 tokens move HBM -> LDS with buffer loads that write LDS
 //     directly, through a 4-slot ring (rows padded to 1168 bytes); three
 //     tiles stream in while one is used.  A load range that ends at the last
-//     staged token writes zeros for the rest of the tile.  The query block
-//     is staged the same way (into the last one or two slots) before the
-//     loop and kept in VGPRs.
+//     staged token writes zeros for the rest of the tile.  An fp8 tile's raw
+//     rows land in the upper part of the slot with the 32 token scales
+//     behind them, and are decoded in place to bf16 rows (exact: every E4M3
+//     value is a bf16 value) once the tile is there; the scales multiply the
+//     scores and the PV weights.  The query block
+//     is staged the same way (into the last slot) before the loop and kept
+//     in VGPRs.
 //   * Scores (v_mfma_f32_16x16x32_bf16; A = 16 tokens x 32 dims of K, B =
 //     32 dims x 16 rows of Q^T): wave w takes token block tb = w % 2 and
 //       NR = 1: the 16 rows over dims 288 (w / 2) .. +287 (the two halves
@@ -73,6 +77,14 @@ constexpr int kLoads = 37;                 // 1 KB direct loads per tile
 constexpr int kSlotBytes = kLoads * 1024;
 constexpr int kChunks = kRowBytes / 16;    // 72 chunks of 16 bytes per row
 constexpr uint32_t kPastEnd = 0x40000000u; // buffer offset past any valid range
+// fp8 cache: a tile's raw rows (32 x 576 codes, contiguous) land at kRawOff
+// of its slot and are decoded in place into the bf16 row layout; its 32
+// token scales land at kScaleOff, past the decoded rows.
+constexpr int kRawOff = 18944;
+constexpr int kScaleOff = kTile * kPitch;  // 37376
+constexpr int kRawLoads = kTile * kDim / 1024;   // 18 loads of 1 KB
+static_assert(kRawOff + kTile * kDim == kScaleOff, "raw rows end where the scales start");
+static_assert(kScaleOff + 256 <= kSlotBytes, "the scale load writes 64 x 4 bytes");
 
 // LDS chunk u of a slot holds chunk u % 73 of staged row u / 73, or nothing
 // (the row's padding chunk, or past the 32 rows): then the source offset
@@ -95,6 +107,11 @@ __device__ __forceinline__ void dma_1k(uint32_t lds, uint32_t voff, u32x4 rs) {
 // counts that do not occur wait for all).
 __device__ __forceinline__ void wait_loads(int n) {
   switch (n) {
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
     case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
     case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
     case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
@@ -117,6 +134,16 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+  return r;
+}
 
 // x[l ^ 16] and x[l ^ 32] in lane l, without LDS.  v_permlane16_swap
 // exchanges the odd 16-lane rows of its first operand with the even rows of
@@ -152,7 +179,7 @@ __device__ __forceinline__ float group_sum4(float x) {
 
 }  // namespace
 
-template <int NR>
+template <int NR, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   constexpr int RB = 16 * NR;                    // query rows per workgroup
@@ -220,8 +247,10 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
     if (64 + lane < pg_n) pg_hi = a.page_table[(size_t)b * a.max_pages + pg_first + 64 + lane];
   }
   // buffer of the tile starting at token ts (a tile never crosses a page)
-  auto tile_rsrc = [&](int ts) -> u32x4 {
-    const int nv = max(0, min(kTile, t_stage - ts));
+  constexpr int ROWB = FP8 ? kDim : kRowBytes;    // bytes per cache row
+  // first cache row of the tile starting at token ts, and its valid rows
+  auto tile_row0 = [&](int ts, int& nv) -> int {
+    nv = max(0, min(kTile, t_stage - ts));
     int r0 = 0;
     if (nv > 0) {
       if (ptab) {
@@ -233,11 +262,14 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
         r0 = seq_row0 + ts;
       }
     }
-    r0 = __builtin_amdgcn_readfirstlane(r0);
-    return buffer_rsrc(cache + (size_t)r0 * kRowBytes, nv * kRowBytes);
+    return __builtin_amdgcn_readfirstlane(r0);
   };
-  // Wave w issues loads n = w + 4k of a tile (wave 0: 10 loads, others 9).
-  const int nld = wave == 0 ? 10 : 9;
+  // bf16 rows (and the query block): wave w issues loads n = w + 4k of the
+  // 37 that fill a slot (wave 0: 10 loads, others 9).  fp8: wave w issues
+  // raw loads n = w + 4k of 18, wave 3 also the scales (waves 0, 1 and 3:
+  // 5 loads, wave 2: 4).
+  const int nld_q = wave == 0 ? 10 : 9;
+  const int nld = FP8 ? (wave == 2 ? 4 : 5) : nld_q;
   uint32_t voff[10];
 #pragma unroll
   for (int n = 0; n < 10; ++n) voff[n] = staged_src_offset(64 * (wave + 4 * n) + lane);
@@ -248,6 +280,26 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
     for (int n = 0; n < 9; ++n) dma_1k(lb + 4096 * n, voff[n], rs);
     if (wave == 0) dma_1k(lb + 4096 * 9, voff[9], rs);
   };
+  auto issue_tile = [&](int ts, int slot) {
+    int nv;
+    const int r0 = tile_row0(ts, nv);
+    if constexpr (!FP8) {
+      issue(buffer_rsrc(cache + (size_t)r0 * kRowBytes, nv * kRowBytes), slot);
+    } else {
+      const u32x4 rs = buffer_rsrc(cache + (size_t)r0 * kDim, nv * kDim);
+      const uint32_t lb = ring + slot * kSlotBytes + kRawOff;
+#pragma unroll
+      for (int k = 0; k < (kRawLoads + 3) / 4; ++k)
+        if (wave + 4 * k < kRawLoads)
+          dma_1k(lb + 1024 * (wave + 4 * k), uint32_t(1024 * (wave + 4 * k) + 16 * lane), rs);
+      if (wave == 3) {
+        const u32x4 ss = buffer_rsrc(a.kv_scale + r0, nv * 4);
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :: "s"(ring + slot * kSlotBytes + kScaleOff),
+                        "v"(uint32_t(lane < kTile ? 4 * lane : kPastEnd)), "s"(ss) : "memory");
+      }
+    }
+  };
 
   // ---- query block -> VGPRs (B operands of the scores: lane (g, j) holds
   // row 16 nq + j, dims 32 ks + 8 g .. + 7).  The block's rows are staged
@@ -256,7 +308,7 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   issue(buffer_rsrc(qblk, RB * kRowBytes), kSlots - 1);
 #pragma unroll
   for (int t = 0; t < kSlots - 1; ++t)
-    if (t < ntiles) issue(tile_rsrc(t0 + t * kTile), t);
+    if (t < ntiles) issue_tile(t0 + t * kTile, t);
   wait_loads(min(ntiles, kSlots - 1) * nld);     // the query loads have landed
   __syncthreads();
   const int tb = wave & 1;                       // token block of this wave's scores
@@ -290,8 +342,23 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
     // every wave is done with tile it-1 and with the score pieces
     wait_loads((min(ntiles, it + kSlots - 1) - it - 1) * nld);
     __syncthreads();
-    if (it + kSlots - 1 < ntiles) issue(tile_rsrc(t0 + (it + kSlots - 1) * kTile), (it + kSlots - 1) & 3);
+    if (it + kSlots - 1 < ntiles) issue_tile(t0 + (it + kSlots - 1) * kTile, (it + kSlots - 1) & 3);
     const uint8_t* kt = s_ring[it & 3];
+    if constexpr (FP8) {
+      // decode the raw tile in place: every thread reads its 9 chunks of 8
+      // codes, then (after a barrier) writes them as bf16 rows
+      u32x2 raw[kTile * kDim / 8 / 256];
+#pragma unroll
+      for (int i = 0; i < kTile * kDim / 8 / 256; ++i)
+        raw[i] = *(const u32x2*)(kt + kRawOff + 8 * (tid + 256 * i));
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kTile * kDim / 8 / 256; ++i) {
+        const int ci = tid + 256 * i;             // row ci / 72, codes 8 (ci % 72) ..
+        *(u32x4*)(s_ring[it & 3] + 16 * ci + 16 * (ci / kChunks)) = e4m3x8_to_bf16x8(raw[i]);
+      }
+      __syncthreads();
+    }
 
     // scores: this wave's piece.  All operand reads go out first (one LDS
     // latency per tile), then the products, in two chains.
@@ -312,6 +379,14 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
     __syncthreads();
 
     const int ts = t0 + it * kTile;
+    // fp8: this lane's 8 token scales (scores and weights are multiplied by
+    // them, so the codes enter the matrix products exactly)
+    float sc[8];
+    if constexpr (FP8) {
+      const float* sp = (const float*)(kt + kScaleOff);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[e] = sp[tok_row(e >> 2, 4 * g + (e & 3))];
+    }
     bf16x8 pk[NR];
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr) {
@@ -321,6 +396,10 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
         const floatx4 v = NR == 1 ? s_x[t][lane] + s_x[t + 2][lane] : s_x[t + 2 * nr][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[4 * t + i] = v[i];
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= sc[e];
       }
       if (ts + kTile - 1 > lim[nr]) {            // the tile crosses the visibility limit
 #pragma unroll
@@ -345,9 +424,14 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = exp2_hw(fmaf(x[e], a.scale_log2, neg));
-      l_run[nr] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // the normaliser sums the weights as rounded to bf16 (unscaled), the
+      // weights that enter the product (times the token scale for fp8)
+      float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pk[nr][e] = (__bf16)p[e];
+      for (int e = 0; e < 8; ++e) pr[e] = (float)(__bf16)p[e];
+      l_run[nr] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[nr][e] = (__bf16)(FP8 ? p[e] * sc[e] : pr[e]);
     }
 
     // PV: this wave's 128 latent dims of every row (reads first, then the
@@ -399,21 +483,22 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
   }
 }
 
-// rows_wg: query rows per workgroup (16 or 32); a.row_blocks counts
-// blocks of that many rows.
+// rows_wg: query rows per workgroup (16 or 32); a.row_blocks counts blocks
+// of that many rows.
 hipError_t launch_decode_small(const DecodeArgs& a, const ItemTable& tab, int rows_wg,
                                hipStream_t st) {
   const int grid = a.n_items * a.row_blocks;
-  switch (rows_wg) {
-    case 16:
-      hipLaunchKernelGGL(decode_small_kernel<1>, dim3(grid), dim3(256), 0, st, a, tab);
-      break;
-    case 32:
-      hipLaunchKernelGGL(decode_small_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
+  const bool fp8 = a.kv_dtype == MLA_FP8_E4M3;
+  if (rows_wg == 16 && !fp8)
+    hipLaunchKernelGGL((decode_small_kernel<1, false>), dim3(grid), dim3(256), 0, st, a, tab);
+  else if (rows_wg == 16)
+    hipLaunchKernelGGL((decode_small_kernel<1, true>), dim3(grid), dim3(256), 0, st, a, tab);
+  else if (rows_wg == 32 && !fp8)
+    hipLaunchKernelGGL((decode_small_kernel<2, false>), dim3(grid), dim3(256), 0, st, a, tab);
+  else if (rows_wg == 32)
+    hipLaunchKernelGGL((decode_small_kernel<2, true>), dim3(grid), dim3(256), 0, st, a, tab);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -78,10 +78,11 @@ bool fast_decode(const mla_dims_t* d, int T) {
 
 // Attention in blocks of 16 or 32 rows (16 heads of one query token per
 // row sub-block) for the other head counts that are multiples of 16, bf16
-// cache.  Returns the rows per block, or 0.
+// or fp8 cache.  Returns the rows per block, or 0.
 int small_decode_rows(const mla_dims_t* d, int T) {
-  if (!fast_shape(d) || d->precision != MLA_PREC_BF16 || d->kv_dtype != MLA_BF16 ||
-      d->n_heads % 16 != 0 || fast_decode(d, T))
+  if (!fast_shape(d) || d->precision != MLA_PREC_BF16 ||
+      (d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3) || d->n_heads % 16 != 0 ||
+      fast_decode(d, T))
     return 0;
   const int64_t rows = (int64_t)d->n_heads * T;
   return rows % 32 == 0 ? 32 : 16;

@@ -124,7 +124,7 @@ typedef enum mla_precision {
  *       MLA_PREC_FP32); attention with precision = MLA_PREC_BF16 and
  *         n_h % 32 == 0, (n_h*T) % 128 == 0, kv_dtype = BF16 or FP8_E4M3
  *           (blocks of 128 query rows: DeepSeek-V2 / V3, 128 heads), or
- *         n_h % 16 == 0 otherwise, kv_dtype = BF16 (blocks of 16 or 32
+ *         n_h % 16 == 0 otherwise, kv_dtype = BF16 or FP8_E4M3 (blocks of 16 or 32
  *           rows: e.g. DeepSeek-V2-Lite, 16 heads, T = 1..4);
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
  *       d_h^R <= 128 (even),

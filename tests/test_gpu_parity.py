@@ -122,8 +122,16 @@ SMALL = [
                   lengths=(70, 129), rope=True),
     small_variant(V2, name="general_n8_bf16", batch=2, n_heads=8, kv_len=0,
                   lengths=(50, 300)),
-    small_variant(V2, name="general_n16_fp8_rope", batch=2, n_heads=16, kv_len=0,
+    small_variant(V2, name="lite_n16_fp8_rope", batch=2, n_heads=16, kv_len=0,
                   lengths=(70, 129), kv_dtype="fp8", rope=True),
+    small_variant(V2, name="lite_n16_fp8_split5", batch=4, n_heads=16, kv_len=0,
+                  lengths=(1, 33, 700, 64), kv_dtype="fp8", num_splits=5),
+    small_variant(V2, name="lite_n16_fp8_t4_paged", batch=3, n_heads=16, q_tokens=4,
+                  kv_len=0, lengths=(520, 100, 4), kv_dtype="fp8", layout="paged"),
+    small_variant(V2, name="n32_fp8_t1", batch=3, n_heads=32, kv_len=0, lengths=(333, 65, 1000),
+                  kv_dtype="fp8"),
+    small_variant(V2, name="general_n8_fp8", batch=2, n_heads=8, kv_len=0, lengths=(50, 300),
+                  kv_dtype="fp8"),
     small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_bf16cache", kv_dtype="bf16",
                   batch=2, kv_len=0, lengths=(64, 300), num_splits=2),
     small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_yarn", yarn_factor=8.0,
@@ -151,6 +159,17 @@ YARN = [
 @pytest.mark.parametrize("w,heads", YARN, ids=[c[0].name for c in YARN])
 def test_decode_parity_yarn(w, heads):
     _run_compare(w, heads=heads)
+
+
+def test_small_rows_items_located_on_device():
+    """More work items than the host's item table holds, lengths not all
+    equal: the 16-row kernel locates each item from the lengths itself."""
+    lengths = tuple(200 + (37 * i) % 1500 for i in range(40))
+    w = small_variant(V2, name="lite_many_items", batch=40, n_heads=16, kv_len=0,
+                      lengths=lengths, num_splits=40, layout="paged")
+    n_items = sum(-(-L // (-(-(-(-L // 40)) // 64) * 64)) for L in lengths)
+    assert n_items > 448
+    _run_compare(w, seqs=[0, 13, 39], heads=[0, 7, 15])
 
 
 FP32_MODE = [
@@ -313,12 +332,14 @@ def test_cache_append_rope_matches_oracle(w):
     np.testing.assert_allclose(got[:, w.d_latent:], d["kr_rows"], rtol=1e-6, atol=1e-6)
 
 
-def test_fp8_every_code_decodes_exactly():
+@pytest.mark.parametrize("n_heads", [128, 16], ids=["rows128", "rows16"])
+def test_fp8_every_code_decodes_exactly(n_heads):
     """L = 1: the softmax weight is exactly 1, so the latent output is the
     stored row itself; rows built from all 254 finite E4M3 codes with scale 1
-    must come back as their exact values."""
+    must come back as their exact values (both attention kernels)."""
     from head_latent_attention_11_amd.runner import DecodeBuffers
-    w = small_variant(V2, name="codes", batch=2, kv_len=0, lengths=(1, 1), kv_dtype="fp8")
+    w = small_variant(V2, name="codes", batch=2, kv_len=0, lengths=(1, 1), kv_dtype="fp8",
+                      n_heads=n_heads)
     gen = generate(w)
     buf = DecodeBuffers(w, gen)
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
@@ -331,7 +352,7 @@ def test_fp8_every_code_decodes_exactly():
     buf.kv_scale[:2] = 1.0
     buf.step()
     torch.cuda.synchronize()
-    lat = to_np(buf.latent)                       # [2, 128, 512]
+    lat = to_np(buf.latent)                       # [2, n_h, 512]
     exp = formats.e4m3_to_f64(row[:, :512])
     for b in range(2):
         assert np.array_equal(lat[b], np.broadcast_to(exp[b], lat[b].shape)), b
