@@ -411,8 +411,16 @@ def test_up_proj_parity(w):
                                              batch=5, kv_len=0, lengths=(700, 64, 4, 333, 1200)),
                                small_variant(WORKLOADS["v2_paged_b128_bf16"], name="paged_graph",
                                              batch=6, kv_len=0,
-                                             lengths=(513, 64, 2000, 1, 65, 900))],
-                         ids=["v2_b32_l4k_bf16", "fp8_t4_ragged", "paged_ragged"])
+                                             lengths=(513, 64, 2000, 1, 65, 900)),
+                               small_variant(WORKLOADS["v2lite_b64_l8k_bf16"], name="lite_graph",
+                                             batch=6, kv_len=0,
+                                             lengths=(513, 64, 2000, 1, 65, 900),
+                                             layout="paged"),
+                               small_variant(WORKLOADS["v2lite_b64_l8k_bf16"], name="lite_fp8_graph",
+                                             batch=5, kv_len=0, q_tokens=2,
+                                             lengths=(700, 64, 4, 333, 1200), kv_dtype="fp8")],
+                         ids=["v2_b32_l4k_bf16", "fp8_t4_ragged", "paged_ragged", "lite_paged_ragged",
+                              "lite_fp8_t2_ragged"])
 def test_graph_replays_match_eager(w):
     """Steps captured as one HIP graph over two cache replicas (as the
     benchmark runs them) give, on every replay, the eager step's outputs bit
