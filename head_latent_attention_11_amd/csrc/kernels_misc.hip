@@ -81,12 +81,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, j = lane & 15;
 
-  // The RoPE part q_abs[..., 512:576] is shared out over the head's four
-  // workgroups: pair p = 256 cb + tid + 1024 u (token p / 32, pair k = p % 32
-  // = tid % 32 for every u).  The first pair's inputs are loaded before the
-  // W^UK block (loads complete in order) and rotated while it is in flight.
+  // blockIdx.y splits the tokens when there are few heads: group y takes
+  // the blocks of 32 tokens t0 = 32 (y + k gridDim.y).
+  // The RoPE part q_abs[..., 512:576] is shared out over the head's
+  // workgroups: pair p = 256 cb + tid + 1024 (y + u gridDim.y) (token p / 32,
+  // pair k = p % 32 = tid % 32 for every u).  The first pair's inputs are
+  // loaded before the W^UK block (loads complete in order) and rotated while
+  // it is in flight.
   const int n_pairs = n_tok * (DR / 2), rk = tid & 31;
-  const int p_first = cb * 256 + tid;
+  const int p_first = 1024 * blockIdx.y + cb * 256 + tid, p_step = 1024 * gridDim.y;
+  const int t_first = 32 * blockIdx.y, t_step = 32 * gridDim.y;
   float rx0 = 0.f, rx1 = 0.f;
   int rpos = 0;
   if (p_first < n_pairs) {
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     }
   };
   u32x4 qv[2];
-  load_q(0, qv);
+  load_q(t_first, qv);
   // W^UK[head][r][cb*128 : cb*128 + 128], row-major 16-byte chunks
   const uint16_t* wsrc = w_uk + (size_t)head * kAbsDh * DC + cb * kAbsCols;
   u32x4 stg[8];
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     stg[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
   const double theta = q_pos ? rope_theta(rk, DR, rope) : 0.0;
-  for (int p = p_first; p < n_pairs; p += 1024) {
+  for (int p = p_first; p < n_pairs; p += p_step) {
     const int tok = p >> 5;
     float x0 = rx0, x1 = rx1;
     int pos = rpos;
@@ -160,13 +164,13 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     af[k] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
   }
 
-  for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    if (t0 > 0) {                      // next query block (loaded during the last one)
+  for (int t0 = t_first; t0 < n_tok; t0 += t_step) {
+    if (t0 > t_first) {                // next query block (loaded during the last one)
       __syncthreads();                 // the last block's operand reads and copy-out are done
       store_q(qv);
       __syncthreads();
     }
-    if (t0 + 32 < n_tok) load_q(t0 + 32, qv);   // in flight during this block
+    if (t0 + t_step < n_tok) load_q(t0 + t_step, qv);   // in flight during this block
     floatx16 acc = {};
 #pragma unroll
     for (int k = 0; k < kAbsDh / 16; ++k) {
@@ -510,9 +514,12 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
       if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
     }
   };
-  load_latent(0);
-  for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    if (t0 == 0) {
+  // blockIdx.y splits the tokens when there are few heads: group y takes
+  // the blocks of 32 tokens t0 = 32 (y + k gridDim.y)
+  const int t_first = 32 * blockIdx.y, t_step = 32 * gridDim.y;
+  load_latent(t_first);
+  for (int t0 = t_first; t0 < n_tok; t0 += t_step) {
+    if (t0 == t_first) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
       *(u32x2*)(sh + t * kUpRow + c4) = hi;
       *(u32x2*)(sl + t * kUpRow + c4) = lo;
     }
-    if (t0 + 32 < n_tok) load_latent(t0 + 32);   // in flight during this block
+    if (t0 + t_step < n_tok) load_latent(t0 + t_step);   // in flight during this block
     __syncthreads();
 
     floatx4 acc_hi = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
@@ -588,13 +595,17 @@ hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
                          RopeFreq rope, hipStream_t st) {
   const bool out_f32 = d.q_dtype == MLA_F32 || d.precision == MLA_PREC_FP32;
   if (fast) {
+    // four workgroups per head; with few heads the tokens are split over up
+    // to 256 workgroups in all
+    const int groups = std::max(1, std::min((n_tok + 31) / 32, kNumCU / (4 * d.n_heads)));
+    const dim3 grid(d.n_heads * 4, groups);
     if (out_f32)
-      hipLaunchKernelGGL(absorb_mfma_kernel<float>, dim3(d.n_heads * 4), dim3(256), 0, st,
+      hipLaunchKernelGGL(absorb_mfma_kernel<float>, grid, dim3(256), 0, st,
                          (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok,
                          d.n_heads, rope);
     else
-      hipLaunchKernelGGL(absorb_mfma_kernel<uint16_t>, dim3(d.n_heads * 4), dim3(256), 0, st,
+      hipLaunchKernelGGL(absorb_mfma_kernel<uint16_t>, grid, dim3(256), 0, st,
                          (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
                          d.n_heads, rope);
@@ -651,7 +662,11 @@ hipError_t launch_up_proj(const mla_dims_t& d, bool fast, const float* latent,
                           const void* w_uv, void* out, bool out_f32, int n_tok,
                           hipStream_t st) {
   if (fast) {
-    const dim3 grid(d.n_heads * 2);
+    // two workgroups per head; with few heads the tokens are split over up
+    // to 256 workgroups in all
+    const int tok_blocks = (n_tok + 31) / 32;
+    const int groups = std::max(1, std::min(tok_blocks, kNumCU / (2 * d.n_heads)));
+    const dim3 grid(d.n_heads * 2, groups);
     if (out_f32)
       hipLaunchKernelGGL(up_proj_mfma_kernel<float>, grid, dim3(512), 0, st,
                          latent, (const uint16_t*)w_uv, (float*)out, n_tok, d.n_heads);

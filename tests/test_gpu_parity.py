@@ -360,8 +360,10 @@ def test_fp8_every_code_decodes_exactly(n_heads):
 
 # ------------------------------------------- absorb and up-projection
 @pytest.mark.parametrize("w", [V2, WORKLOADS["tiny_fp32"],
-                               small_variant(V2, name="n16", n_heads=16)],
-                         ids=["v2_mfma", "tiny_fp32_rope", "general_n16"])
+                               small_variant(V2, name="n16", n_heads=16),
+                               small_variant(V2, name="n16_t3", n_heads=16, q_tokens=3,
+                                             rope=True, yarn_factor=40.0)],
+                         ids=["v2_mfma", "tiny_fp32_rope", "n16_mfma", "n16_111_tokens_yarn"])
 def test_absorb_q_parity(w):
     w = small_variant(w, batch=min(w.batch, 37), kv_len=0, lengths=(64,) * min(w.batch, 37))
     gen = generate(w)
@@ -379,7 +381,7 @@ def test_absorb_q_parity(w):
 
 @pytest.mark.parametrize("w", [V2, WORKLOADS["tiny_fp32"],
                                small_variant(V2, name="n16", n_heads=16)],
-                         ids=["v2_mfma", "tiny_fp32", "general_n16"])
+                         ids=["v2_mfma", "tiny_fp32", "n16_mfma"])
 def test_up_proj_parity(w):
     """Latent inputs are drawn here (seeded), never taken from the HIP path."""
     n_tok = 45
