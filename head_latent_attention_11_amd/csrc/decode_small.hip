@@ -24,9 +24,8 @@
 //     rows land in the upper part of the slot with the 32 token scales
 //     behind them, and are decoded in place to bf16 rows (exact: every E4M3
 //     value is a bf16 value) once the tile is there; the scales multiply the
-//     scores and the PV weights.  The query block
-//     is staged the same way (into the last slot) before the loop and kept
-//     in VGPRs.
+//     scores and the PV weights.  The query block is staged the same way
+//     (into the last slot) before the loop and kept in VGPRs.
 //   * Scores (v_mfma_f32_16x16x32_bf16; A = 16 tokens x 32 dims of K, B =
 //     32 dims x 16 rows of Q^T): wave w takes token block tb = w % 2 and
 //       NR = 1: the 16 rows over dims 288 (w / 2) .. +287 (the two halves
@@ -65,7 +64,6 @@ namespace mla {
 namespace {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef short shortx8 __attribute__((ext_vector_type(8)));
 
 constexpr int kDim = 576;                  // cache row: 512 latent + 64 rope dims
 constexpr int kLatent = 512;
