@@ -217,6 +217,20 @@ def test_split_planner_sizes(mla):
     # 48 heads: three blocks of 16 rows, 86 items wanted -> chunk 1536, 3 splits
     st, n = _ws(lib, _v2(b, n_heads=48), [4096] * 32)
     assert st == OK and n == 96 * 48 * 4 + 96 * 48 * dc * 2
+    # 16 heads x T = 4 on an fp8 cache: two blocks of 32 rows, 128 items
+    # wanted -> chunk 4096, 2 splits each; 64 x 8192 with T = 1: chunk 2048,
+    # 4 splits each (the V2-Lite benchmark workload)
+    st, n = _ws(lib, _v2(b, n_heads=16, kv_dtype="fp8"), [8192] * 64, T=4)
+    assert st == OK and n == 128 * 64 * 4 + 128 * 64 * dc * 2
+    st, n = _ws(lib, _v2(b, n_heads=16), [8192] * 64)
+    assert st == OK and n == 256 * 16 * 4 + 256 * 16 * dc * 2
+    # head counts that are no multiple of 16 (general path, one workgroup per
+    # row): 8 rows want 32 items -> chunk 4096, no split; with 8 splits the
+    # partials are fp32
+    st, n = _ws(lib, _v2(b, n_heads=8), [4096] * 32)
+    assert st == OK and n == 0
+    st, n = _ws(lib, _v2(b, n_heads=8), [4096] * 32, splits=8)
+    assert st == OK and n == 256 * 8 * 4 + 256 * 8 * dc * 4
     # fp32 precision mode: same items, fp32 partials
     st, n = _ws(lib, _v2(b, precision=1), [131072] * 4, splits=64)
     assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4
