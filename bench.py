@@ -454,6 +454,22 @@ def main():
     copy_gbps = 2 * COPY_CEILING_BYTES / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e9
     del cp_src, cp_dst
 
+    # Achievable dense bf16 matrix throughput on this GPU, for context: a
+    # library GEMM (torch.mm -> hipBLASLt) of 8192^3 with contiguous
+    # operands.  Not part of any step.
+    n_g = 8192
+    ga = torch.randn(n_g, n_g, device="cuda").to(torch.bfloat16)
+    gb = torch.randn(n_g, n_g, device="cuda").to(torch.bfloat16)
+    gc = torch.mm(ga, gb)
+    torch.cuda.synchronize()
+    c0.record(stream)
+    for _ in range(10):
+        torch.mm(ga, gb, out=gc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * n_g ** 3 / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e12
+    del ga, gb, gc
+
     out = {
         "metric": "MLA decode tokens/s and latent-cache GB/s (% of HBM/MFMA roofline)",
         "value": round(w.batch * w.q_tokens / (ms_step * 1e-3), 1),
@@ -474,6 +490,7 @@ def main():
                    "steps_per_graph": STEPS_PER_GRAPH},
         "latent_cache_GBps": round(cache_b / attn_s / 1e9, 1),
         "hbm_copy_GBps": round(copy_gbps, 1),
+        "gemm_bf16_TFLOPs": round(gemm_tflops, 1),
         "attn_us": round(attn_ms * 1e3, 2),
         "step_us_events": round(ms_step_events * 1e3, 2),
         "roofline": roof,
