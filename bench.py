@@ -4,9 +4,10 @@
 A step is one pass of the whole hot path over one batch of synthetic inputs:
     mla_absorb_q -> mla_decode_attn (split-KV attention + LSE combine)
     -> mla_up_proj_v
-with every input already resident in HBM.  The latent cache is replicated
-(>= 768 MB in total) and the replicas are used round-robin, so each step
-reads its cache from HBM rather than from the 256 MB memory-side cache.
+with every input already resident in HBM.  The latent cache (>= 768 MB in
+total) and W^UK / W^UV are replicated and the replicas are used round-robin,
+so each step reads its cache and weights from HBM rather than from the
+256 MB memory-side cache.
 
 Prints ONE JSON line.  `value` is decode tokens/s (B*T query tokens per
 step / step time).  `roofline` describes the dominant kernel (the attention
@@ -246,7 +247,8 @@ def time_lite(stream, steps: int):
     seq_lens = [int(x) for x in gen["seq_lens"]]
     cache_b, io_b, flops = algorithmic(w, seq_lens)
     reps = max(2, -(-768 * 2 ** 20 // cache_b))
-    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=reps)
+    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=reps,
+                        weight_replicas=reps)
     per = 10
 
     def timed(call):
@@ -321,7 +323,8 @@ def main():
     cache_b, io_b, flops = algorithmic(w, seq_lens)
     replicas = max(1, -(-768 * 2 ** 20 // max(cache_b, 1)))
     torch.cuda.set_device(0)
-    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=replicas)
+    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=replicas,
+                        weight_replicas=replicas)
     torch.cuda.synchronize()
 
     # Each step is captured once per cache replica as a HIP graph and

@@ -36,7 +36,8 @@ def to_device(arr: np.ndarray, kind: str, device) -> torch.Tensor:
 class DecodeBuffers:
     def __init__(self, w, gen: Dict[str, np.ndarray], device="cuda",
                  num_splits: Optional[int] = None, poison: bool = True,
-                 cache_replicas: int = 1, precision: str = "bf16"):
+                 cache_replicas: int = 1, precision: str = "bf16",
+                 weight_replicas: int = 1):
         self.w = w
         self.device = torch.device(device)
         dev = self.device
@@ -45,6 +46,11 @@ class DecodeBuffers:
         qk = "f32" if w.q_dtype == "f32" else "bf16"
         self.w_uk = to_device(gen["w_uk"], qk, dev)
         self.w_uv = to_device(gen["w_uv"], qk, dev)
+        # copies of W^UK / W^UV used round-robin with the cache replicas, so
+        # that a step reads its weights from HBM as a layer of a whole model
+        # would, not from the memory-side cache
+        self.w_uks = [self.w_uk] + [self.w_uk.clone() for _ in range(max(1, weight_replicas) - 1)]
+        self.w_uvs = [self.w_uv] + [self.w_uv.clone() for _ in range(max(1, weight_replicas) - 1)]
         self.q_nope = to_device(gen["q_nope"], qk, dev)
         self.q_rope = to_device(gen["q_rope"], qk, dev)
         self.q_pos = to_device(gen["q_pos"], "i32", dev) if w.rope else None
@@ -117,9 +123,9 @@ class DecodeBuffers:
         self._lens_c = B._lens_host(self.seq_lens_host)
 
     # ----------------------------------------------------------- the step
-    def absorb(self, stream=None):
-        B.absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_pos, self.q_abs,
-                   self.n_tok, stream)
+    def absorb(self, stream=None, replica: int = 0):
+        B.absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uks[replica % len(self.w_uks)],
+                   self.q_pos, self.q_abs, self.n_tok, stream)
 
     def attend(self, replica: int = 0, stream=None, num_splits: Optional[int] = None):
         ns = self.num_splits if num_splits is None else num_splits
@@ -133,10 +139,11 @@ class DecodeBuffers:
                       self.seq_lens_host, self.T, ns, ws, wsb, self.latent, self.lse,
                       stream, _lens_cache=self._lens_c)
 
-    def up_proj(self, stream=None):
-        B.up_proj_v(self.dims, self.latent, self.w_uv, self.o, self.n_tok, stream)
+    def up_proj(self, stream=None, replica: int = 0):
+        B.up_proj_v(self.dims, self.latent, self.w_uvs[replica % len(self.w_uvs)], self.o,
+                    self.n_tok, stream)
 
     def step(self, replica: int = 0, stream=None):
-        self.absorb(stream)
+        self.absorb(stream, replica)
         self.attend(replica, stream)
-        self.up_proj(stream)
+        self.up_proj(stream, replica)
