@@ -239,3 +239,29 @@ def test_split_planner_sizes(mla):
     assert st == OK and n == 0
     st, _ = _ws(lib, d, [5], T=6)
     assert st == SEQLEN
+
+
+def test_dims_struct_layout_matches_header(tmp_path):
+    """The binding's mirror of mla_dims_t has the header's size and field
+    offsets: a C program built from include/mla.h prints them."""
+    import shutil
+    import subprocess
+    from head_latent_attention_11_amd import binding
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = [f[0] for f in binding.MLADims._fields_]
+    src = tmp_path / "dims.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "mla.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu\\n", sizeof(mla_dims_t));\n'
+        + "".join(f'  printf("%zu\\n", offsetof(mla_dims_t, {n}));\n' for n in names)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "dims"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(binding.MLADims)
+    assert out[1:] == [getattr(binding.MLADims, n).offset for n in names]
