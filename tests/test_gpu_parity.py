@@ -161,6 +161,15 @@ def test_decode_parity_yarn(w, heads):
     _run_compare(w, heads=heads)
 
 
+def test_small_rows_long_paged_item():
+    """One unsplit item of 9000 tokens in 64-token pages (141 pages: more
+    than the 128 page ids the 16-row kernel keeps in registers, so it reads
+    the page table per tile)."""
+    w = small_variant(V2, name="lite_long_item", batch=2, n_heads=16, kv_len=0,
+                      lengths=(9000, 300), layout="paged", num_splits=1)
+    _run_compare(w, heads=[0, 5, 15])
+
+
 def test_small_rows_items_located_on_device():
     """More work items than the host's item table holds, lengths not all
     equal: the 16-row kernel locates each item from the lengths itself."""
