@@ -153,6 +153,13 @@ YARN = [
     (small_variant(V2, name="lite_yarn_rope", batch=3, n_heads=16, kv_len=0,
                    lengths=(5000, 700, 4500), rope=True, yarn_factor=40.0, yarn_coef=0.1),
      [0, 9, 15]),
+    (small_variant(V2, name="v2_yarn_fp8_t4", batch=2, q_tokens=4, kv_len=0,
+                   lengths=(4600, 900), rope=True, yarn_factor=40.0, kv_dtype="fp8"),
+     [0, 64, 127]),
+    (small_variant(V2, name="lite_yarn_fp8_paged", batch=2, n_heads=16, kv_len=0,
+                   lengths=(4600, 900), rope=True, yarn_factor=40.0, kv_dtype="fp8",
+                   layout="paged"),
+     [0, 15]),
 ]
 
 
