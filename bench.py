@@ -2,8 +2,8 @@
 """Benchmark of one MLA decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic inputs:
-    mla_absorb_q -> mla_decode_attn (split-KV attention + LSE combine)
-    -> mla_up_proj_v
+    mla_absorb_q -> mla_cache_append (the B*T new rows) -> mla_decode_attn
+    (split-KV attention + LSE combine) -> mla_up_proj_v
 with every input already resident in HBM.  The latent cache (>= 768 MB in
 total) and W^UK / W^UV are replicated and the replicas are used round-robin,
 so each step reads its cache and weights from HBM rather than from the
@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
-DEFAULT_WORKLOAD = "v2_b32_l4k_bf16"
+DEFAULT_WORKLOAD = "v2_fp8_t4_b64_l8k"       # B=64, T=4, L=8192, fp8 cache
+COMPANION_WORKLOAD = "v2_b64_l8k_bf16"      # B=64, T=1, L=8192, bf16 cache
 ATTN_PER_GRAPH = 20                     # attention calls captured per graph
 STEPS_PER_GRAPH = 10                    # decode steps captured per graph
 COPY_PROBE_BYTES = 512 * 2 ** 20        # calibration copy of the traffic probe
@@ -87,43 +88,49 @@ def traffic_for_current_kernel(workload: str):
 
 def cpu_baseline(w, gen, budget_s: float):
     """Time the CPU oracle (as it is) on a bounded sample: whole-length
-    (sequence, head) evaluations, scaled to the full step."""
-    from threadpoolctl import threadpool_info
+    (sequence, head) evaluations, scaled to the full step.  BLAS runs one
+    thread per core of this process's affinity set."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import mla as omla
-    t0 = time.perf_counter()
-    n_eval = 0
-    seqs = list(range(w.batch))
-    h = 0
-    b_i = 0
-    d = None
-    cur_b = None
-    while True:
-        b = seqs[b_i % len(seqs)]
-        if b != cur_b:
-            d = omla.logical_inputs(gen, w, seqs=[b])
-            cur_b = b
-        omla.decode(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_rows"], d["kr_rows"],
-                    d["row_offsets"], d["seq_lens"], w.q_tokens, seqs=[b], heads=[h])
-        n_eval += 1
-        h += 1
-        if h == w.n_heads:
-            h = 0
-            b_i += 1
-        if time.perf_counter() - t0 >= budget_s and n_eval >= 2:
-            break
-    elapsed = time.perf_counter() - t0
+    cores, model = host_info()
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        n_eval = 0
+        seqs = list(range(w.batch))
+        h = 0
+        b_i = 0
+        d = None
+        cur_b = None
+        while True:
+            b = seqs[b_i % len(seqs)]
+            if b != cur_b:
+                d = omla.logical_inputs(gen, w, seqs=[b])
+                cur_b = b
+            omla.decode(d["q_nope"], d["q_rope"], d["w_uk"], d["w_uv"], d["c_rows"],
+                        d["kr_rows"], d["row_offsets"], d["seq_lens"], w.q_tokens, seqs=[b],
+                        heads=[h])
+            n_eval += 1
+            h += 1
+            if h == w.n_heads:
+                h = 0
+                b_i += 1
+            if time.perf_counter() - t0 >= budget_s and n_eval >= 2:
+                break
+        elapsed = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     per_eval = elapsed / n_eval                       # one (sequence, head) incl. all T
     full_step = per_eval * w.batch * w.n_heads
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": w.batch * w.q_tokens / full_step,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"{n_eval} whole-length (sequence, head) evaluations of the literal "
-                   f"fp64 oracle in {elapsed:.1f} s, scaled to B*n_h = "
-                   f"{w.batch * w.n_heads} evaluations per step"),
+                   f"fp64 oracle (all T={w.q_tokens} query tokens each) in {elapsed:.1f} s, "
+                   f"scaled to B*n_h = {w.batch * w.n_heads} evaluations per step"),
+        "host_cores_affinity": cores,
+        "cpu_model": model,
     }
 
 
@@ -233,60 +240,180 @@ def time_kv_produce(w, buf, stream):
             "frac_hbm": round(byts / t / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def time_lite(stream, steps: int):
-    """DeepSeek-V2-Lite attention shapes (16 heads: the 16-row attention
-    kernel), reported next to the main line: the whole step (absorb ->
-    attention -> up-projection) and the attention call alone, HIP-event
-    timed over graph replays with the cache replicated past the memory-side
-    cache."""
-    import torch
-    from head_latent_attention_11_amd.runner import DecodeBuffers
-    from mla_inputs import WORKLOADS, generate
-    w = WORKLOADS[LITE_WORKLOAD]
-    gen = generate(w)
-    seq_lens = [int(x) for x in gen["seq_lens"]]
-    cache_b, io_b, flops = algorithmic(w, seq_lens)
-    reps = max(2, -(-768 * 2 ** 20 // cache_b))
-    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=reps,
-                        weight_replicas=reps)
-    per = 10
+def host_info():
+    """Host CPU context of the oracle timing: the cores this process may run
+    on (its affinity set) and the CPU model."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
 
-    def timed(call):
-        def fn():
-            for i in range(per):
-                call(i % reps)
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def roofline(bytes_alg, flops, attn_s):
+    """Fraction of the binding roofline for one attention call: HBM bytes
+    against 8 TB/s, or flops against the dense peak of the matrix precision
+    the kernels issue (bf16: fp8 caches are decoded to bf16 before the
+    products); the fp8 dense peak is given next to it."""
+    achieved_gbps = bytes_alg / attn_s / 1e9
+    tflops = flops / attn_s / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    t_hbm = bytes_alg / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (peak * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                "frac_fp8_peak": round(tflops / MFMA_PEAK_TFLOPS["fp8"], 4)}
+    roof["achieved_GBps"] = round(achieved_gbps, 1)
+    roof["achieved_TFLOPs"] = round(tflops, 1)
+    return roof
+
+
+class Timer:
+    """A workload resident on the GPU, its decode step and attention call
+    captured in HIP graphs (cache and weights replicated to >= 768 MB and
+    used round-robin, so each step reads them from HBM), timed with HIP
+    events on the stream the graphs are launched on."""
+
+    def __init__(self, name):
+        import torch
+        from head_latent_attention_11_amd.runner import DecodeBuffers
+        from mla_inputs import WORKLOADS, generate
+        self.w = w = WORKLOADS[name]
+        self.gen = generate(w)
+        self.seq_lens = [int(x) for x in self.gen["seq_lens"]]
+        self.cache_b, self.io_b, self.flops = algorithmic(w, self.seq_lens)
+        self.replicas = reps = max(2, -(-768 * 2 ** 20 // max(self.cache_b, 1)))
+        self.buf = DecodeBuffers(w, self.gen, device="cuda", poison=False, cache_replicas=reps,
+                                 weight_replicas=reps)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.current_stream()
+        buf = self.buf
+
+        # A serving loop captures many launches per graph (a decode step of
+        # the whole model runs this layer once per layer), so the host-side
+        # cost of a graph launch is shared: STEPS_PER_GRAPH steps per graph,
+        # cache replicas round-robin.
+        def steps_fn(first, n):
+            def fn():
+                for i in range(n):
+                    buf.step(replica=(first + i) % reps)
+            return fn
+        self.step_graphs = [self.capture(steps_fn(j * STEPS_PER_GRAPH, STEPS_PER_GRAPH))
+                            for j in range(reps)]
+        self.tail_graphs = {}
+
+        def attn_calls():
+            for i in range(ATTN_PER_GRAPH):
+                buf.attend(replica=i % reps)
+        self.attn_graph = self.capture(attn_calls)
+        self.steps_fn = steps_fn
+
+    @staticmethod
+    def capture(fn):
+        import torch
+        g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            fn()
+            fn()                      # warm up outside the graph
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
-        for _ in range(2):
-            g.replay()
-        n = max(2, steps // per)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / (n * per)
+        return g
 
-    t_step = timed(lambda r: buf.step(replica=r))
-    t_attn = timed(lambda r: buf.attend(replica=r))
-    del buf
-    byts = cache_b + io_b
-    return {"workload": w.name, "batch": w.batch, "kv_len": w.kv_len, "n_heads": w.n_heads,
-            "step_us": round(t_step * 1e6, 2),
-            "tokens_per_s": round(w.batch * w.q_tokens / t_step, 1),
-            "attn_us": round(t_attn * 1e6, 2),
-            "latent_cache_GBps": round(cache_b / t_attn / 1e9, 1),
-            "bytes_alg_per_launch": byts,
-            "frac_hbm": round(byts / t_attn / 1e9 / HBM_PEAK_GBPS, 4)}
+    def graphs_for(self, k):
+        """The graph replays that run exactly k steps, with their step counts."""
+        out = [(self.step_graphs[j % self.replicas], STEPS_PER_GRAPH)
+               for j in range(k // STEPS_PER_GRAPH)]
+        rem = k % STEPS_PER_GRAPH
+        if rem:
+            if rem not in self.tail_graphs:
+                self.tail_graphs[rem] = self.capture(self.steps_fn(0, rem))
+            out.append((self.tail_graphs[rem], rem))
+        return out
+
+    def time_steps(self, k, warmup):
+        """K steps: one HIP event before and after each graph replay (per-step
+        percentiles), the whole region bracketed by device synchronisations."""
+        import torch
+        for g, _ in self.graphs_for(warmup):
+            g.replay()
+        plan = self.graphs_for(k)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(self.stream)
+        for i, (g, _) in enumerate(plan):
+            g.replay()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per_step = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / n for i, (_, n) in enumerate(plan)]
+        total_ev = ev[0].elapsed_time(ev[-1]) * 1e-3
+        return {"wall_s": t1 - t0, "events_s": total_ev, "per_step_s": per_step}
+
+    def time_attention(self, n_graphs, warmup_graphs=3):
+        import torch
+        for _ in range(warmup_graphs):
+            self.attn_graph.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_graphs + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(self.stream)
+        for i in range(n_graphs):
+            self.attn_graph.replay()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        per_call = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / ATTN_PER_GRAPH for i in range(n_graphs)]
+        return {"mean_s": ev[0].elapsed_time(ev[-1]) * 1e-3 / (n_graphs * ATTN_PER_GRAPH),
+                "per_call_s": per_call}
+
+    def release(self):
+        import torch
+        del self.buf, self.step_graphs, self.tail_graphs, self.attn_graph
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def side_line(name, steps):
+    """Step and attention-call numbers of another workload (same method as
+    the main line), reported as a field next to it."""
+    t = Timer(name)
+    w = t.w
+    st = t.time_steps(max(steps, 2 * STEPS_PER_GRAPH), 2 * STEPS_PER_GRAPH)
+    at = t.time_attention(max(3, steps // ATTN_PER_GRAPH))
+    step_s = st["events_s"] / max(steps, 2 * STEPS_PER_GRAPH)
+    attn_s = at["mean_s"]
+    ps, pa = percentiles(st["per_step_s"]), percentiles(at["per_call_s"])
+    out = {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens, "kv_len": w.kv_len,
+           "n_heads": w.n_heads, "kv_dtype": w.kv_dtype,
+           "step_us": round(step_s * 1e6, 2),
+           "step_us_p10_p90": [round(ps["p10"] * 1e6, 2), round(ps["p90"] * 1e6, 2)],
+           "tokens_per_s": round(w.batch * w.q_tokens / step_s, 1),
+           "attn_us": round(attn_s * 1e6, 2),
+           "attn_us_p10_p90": [round(pa["p10"] * 1e6, 2), round(pa["p90"] * 1e6, 2)],
+           "latent_cache_GBps": round(t.cache_b / attn_s / 1e9, 1),
+           "bytes_alg_per_launch": t.cache_b + t.io_b, "flops_alg_per_launch": t.flops,
+           "roofline": roofline(t.cache_b + t.io_b, t.flops, attn_s)}
+    t.release()
+    return out
 
 
 def main():
@@ -301,81 +428,22 @@ def main():
                     help="skip the timings of the cache producer and of the output "
                          "projection around the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-lite", action="store_true",
-                    help="skip the DeepSeek-V2-Lite (16-head) attention line")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the companion (bf16, T=1) and DeepSeek-V2-Lite lines")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a calibration copy and a few attention calls for "
                          "rocprofv3 counter runs (see bench_traffic.py), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
-
-    from head_latent_attention_11_amd.runner import DecodeBuffers
-    from mla_inputs import WORKLOADS, generate
-
-    w = WORKLOADS[args.workload]
-    gen = generate(w)
-    seq_lens = [int(x) for x in gen["seq_lens"]]
-    cache_b, io_b, flops = algorithmic(w, seq_lens)
-    replicas = max(1, -(-768 * 2 ** 20 // max(cache_b, 1)))
     torch.cuda.set_device(0)
-    buf = DecodeBuffers(w, gen, device="cuda", poison=False, cache_replicas=replicas,
-                        weight_replicas=replicas)
-    torch.cuda.synchronize()
-
-    # Each step is captured once per cache replica as a HIP graph and
-    # replayed: the library calls are asynchronous launches on the current
-    # stream, and replay removes the per-call host overhead of the binding.
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()                      # warm up outside the graph
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            fn()
-        return g
-
-    # A serving loop captures many launches per graph (a decode step of the
-    # whole model runs this layer once per layer), so the host-side cost of a
-    # graph launch is shared: STEPS_PER_GRAPH steps per graph, cache replicas
-    # round-robin.  n_steps(k) replays graphs for exactly k steps.
-    def steps_fn(first, n):
-        def fn():
-            for i in range(n):
-                buf.step(replica=(first + i) % replicas)
-        return fn
-
-    step_graphs = [capture(steps_fn(j * STEPS_PER_GRAPH, STEPS_PER_GRAPH))
-                   for j in range(replicas)]
-    tail_graphs = {}
-
-    def n_steps(k):
-        for j in range(k // STEPS_PER_GRAPH):
-            step_graphs[j % replicas].replay()
-        rem = k % STEPS_PER_GRAPH
-        if rem:
-            if rem not in tail_graphs:
-                tail_graphs[rem] = capture(steps_fn(0, rem))
-            tail_graphs[rem].replay()
-
-    if args.steps % STEPS_PER_GRAPH:
-        n_steps(args.steps % STEPS_PER_GRAPH)    # capture the tail graph now
-    torch.cuda.synchronize()
-    # the attention call alone: ATTN_PER_GRAPH calls (replicas round-robin) per
-    # graph, so the gap between graph launches is amortised and the per-call
-    # time is the kernels' own (decode + combine)
-    def attn_calls():
-        for i in range(ATTN_PER_GRAPH):
-            buf.attend(replica=i % replicas)
-    attn_graph = capture(attn_calls)
-    stream = torch.cuda.current_stream()
+    t = Timer(args.workload)
+    w, buf, stream = t.w, t.buf, t.stream
+    cache_b, io_b, flops = t.cache_b, t.io_b, t.flops
 
     if args.traffic_probe:
         # For rocprofv3 counter runs: a plain copy of known size (the
@@ -386,53 +454,26 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         for i in range(3):
-            buf.attend(replica=i % replicas)
+            buf.attend(replica=i % t.replicas)
         torch.cuda.synchronize()
         print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_PROBE_BYTES,
                           "workload": w.name, "sources_sha256": kernel_sources_sha256(),
                           "bytes_alg_per_launch": cache_b + io_b}), flush=True)
         return
 
-    n_steps(args.warmup)
-    torch.cuda.synchronize()
-
-    # ---- timed region: K whole steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    n_steps(args.steps)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    ms_step_events = e0.elapsed_time(e1) / args.steps
+    # ---- timed region: K whole steps (absorb, append, attention, up-projection)
+    st = t.time_steps(args.steps, args.warmup)
+    ms_step = st["wall_s"] * 1e3 / args.steps
+    ms_step_events = st["events_s"] * 1e3 / args.steps
+    ps = percentiles(st["per_step_s"])
 
     # ---- the attention launches alone, back to back (same stream)
-    n_rep = max(1, -(-args.steps // ATTN_PER_GRAPH))
-    for i in range(max(1, args.warmup // ATTN_PER_GRAPH)):
-        attn_graph.replay()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a0.record(stream)
-    for i in range(n_rep):
-        attn_graph.replay()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    attn_ms = a0.elapsed_time(a1) / (n_rep * ATTN_PER_GRAPH)
-    attn_s = attn_ms * 1e-3
+    at = t.time_attention(max(3, -(-args.steps // ATTN_PER_GRAPH)),
+                          max(1, args.warmup // ATTN_PER_GRAPH))
+    attn_s = at["mean_s"]
+    pa = percentiles(at["per_call_s"])
     bytes_alg = cache_b + io_b
-    achieved_gbps = bytes_alg / attn_s / 1e9
-    tflops = flops / attn_s / 1e12
-    mfma_peak = MFMA_PEAK_TFLOPS["bf16"]          # the MFMA precision issued
-    t_hbm = bytes_alg / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = flops / (mfma_peak * 1e12)
-    if t_hbm >= t_mfma:
-        roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4)}
+    roof = roofline(bytes_alg, flops, attn_s)
     tr = traffic_for_current_kernel(w.name)
     roof["traffic"] = tr["hbm_bytes_per_launch"] if tr else None
     roof["kernel"] = ("mla_decode_attn (decode_mfma_kernel, or decode_small_kernel for "
@@ -484,27 +525,36 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.kv_dtype if w.kv_dtype != "f32" else "f32",
+        "dtype": "bf16" if w.kv_dtype in ("bf16", "fp8") else "f32",
         "data": "synthetic (seeded N(0,1) latent cache and queries, N(0,1/d_c) weights)",
         "config": {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens,
                    "kv_len": w.kv_len or None, "n_heads": w.n_heads, "d_head": w.d_head,
                    "d_latent": w.d_latent, "d_rope": w.d_rope, "kv_dtype": w.kv_dtype,
-                   "layout": w.layout, "cache_replicas": replicas,
-                   "steps_per_graph": STEPS_PER_GRAPH},
+                   "layout": w.layout, "cache_replicas": t.replicas,
+                   "steps_per_graph": STEPS_PER_GRAPH,
+                   "step": "absorb_q + cache_append(B*T rows) + decode_attn + up_proj_v"},
+        "step_us_events": round(ms_step_events * 1e3, 2),
+        "step_us_median_p10_p90": [round(ps["median"] * 1e6, 2), round(ps["p10"] * 1e6, 2),
+                                   round(ps["p90"] * 1e6, 2)],
+        "attn_us": round(attn_s * 1e6, 2),
+        "attn_us_median_p10_p90": [round(pa["median"] * 1e6, 2), round(pa["p10"] * 1e6, 2),
+                                   round(pa["p90"] * 1e6, 2)],
         "latent_cache_GBps": round(cache_b / attn_s / 1e9, 1),
         "hbm_copy_GBps": round(copy_gbps, 1),
         "gemm_bf16_TFLOPs": round(gemm_tflops, 1),
-        "attn_us": round(attn_ms * 1e3, 2),
-        "step_us_events": round(ms_step_events * 1e3, 2),
         "roofline": roof,
     }
     if w.q_dtype == "bf16" and not args.no_out_proj:
         out["out_proj"] = time_out_proj(w, buf, stream)
         out["kv_produce"] = time_kv_produce(w, buf, stream)
-    if not args.no_lite and w.name != LITE_WORKLOAD:
-        out["v2lite"] = time_lite(stream, args.steps)
+    t.release()
+    if not args.no_side:
+        if w.name != COMPANION_WORKLOAD:
+            out["companion"] = side_line(COMPANION_WORKLOAD, args.steps)
+        if w.name != LITE_WORKLOAD:
+            out["v2lite"] = side_line(LITE_WORKLOAD, args.steps)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, gen, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(t.w, t.gen, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

@@ -5,9 +5,12 @@
 cache with ``mla_cache_append`` (so the cache bytes are written by the
 library's own append kernel), and runs the decode step
 
-    mla_absorb_q -> mla_decode_attn (split-KV + combine) -> mla_up_proj_v
+    mla_absorb_q -> mla_cache_append -> mla_decode_attn (split-KV + combine)
+    -> mla_up_proj_v
 
-on the current torch stream.  No arithmetic of the method happens here.
+on the current torch stream (the step also appends its B*T new rows with
+``mla_cache_append`` before the attention call).  No arithmetic of the
+method happens here.
 """
 from __future__ import annotations
 
@@ -101,6 +104,18 @@ class DecodeBuffers:
             B.cache_append(self.dims, new_c, new_kr, seq_idx, pos, self.page_table,
                            w.batch, self.max_pages, self.max_len, self.cache_rows,
                            w.rope, cache, scale, new_c.shape[0])
+        # ---- the step's own B*T new rows (positions L_b - T .. L_b - 1 of each
+        # sequence), appended again by every step: the append of a decode
+        # step.  Writing the same row twice stores the same bytes, so a step
+        # leaves the prefilled cache as it is.
+        offs = np.asarray(gen["row_offsets"], dtype=np.int64)
+        lens = np.asarray(gen["seq_lens"], dtype=np.int64)
+        rows = np.concatenate([offs[b] + np.arange(lens[b] - self.T, lens[b])
+                               for b in range(w.batch)])
+        self.new_c = new_c[torch.from_numpy(rows).to(dev)].contiguous()
+        self.new_kr = new_kr[torch.from_numpy(rows).to(dev)].contiguous()
+        self.new_seq = seq_idx[torch.from_numpy(rows).to(dev)].contiguous()
+        self.new_pos = pos[torch.from_numpy(rows).to(dev)].contiguous()
         del new_c, new_kr, seq_idx, pos
 
         # ---- outputs and workspace
@@ -127,6 +142,12 @@ class DecodeBuffers:
         B.absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uks[replica % len(self.w_uks)],
                    self.q_pos, self.q_abs, self.n_tok, stream)
 
+    def append(self, stream=None, replica: int = 0):
+        B.cache_append(self.dims, self.new_c, self.new_kr, self.new_seq, self.new_pos,
+                       self.page_table, self.batch, self.max_pages, self.max_len,
+                       self.cache_rows, self.w.rope, self.caches[replica],
+                       self.scales[replica], self.n_tok, stream)
+
     def attend(self, replica: int = 0, stream=None, num_splits: Optional[int] = None):
         ns = self.num_splits if num_splits is None else num_splits
         ws, wsb = self.workspace, self.ws_bytes
@@ -145,5 +166,6 @@ class DecodeBuffers:
 
     def step(self, replica: int = 0, stream=None):
         self.absorb(stream, replica)
+        self.append(stream, replica)
         self.attend(replica, stream)
         self.up_proj(stream, replica)

@@ -7,8 +7,9 @@ bits.  Exponent field 0 encodes subnormals (m/8) * 2^-6; fields 1..15 encode
 (1 + m/8) * 2^(e-7), except the all-ones pattern S.1111.111 which is NaN.
 There is no infinity; the largest finite magnitude is 448.  The pages ask for
 a KV cache of about 6 bits per element without naming a scheme ("DeepSeek-V2:
-Strong, Economical, Efficient", section 3.5, inference efficiency); the fp8
-cache with one fp32 scale per token is this build's stand-in for it.
+Strong, Economical, Efficient", section 3.2.3, training and inference
+efficiency); the fp8
+cache with one fp32 scale per token is the 8-bit format of that kind.
 
 Per-token quantisation rule of the fp8 cache (the quantised code is an integer
 decided in float32, the precision the kernel takes it in):

@@ -3,7 +3,7 @@ compare with the oracle.  Tolerances are the ones the workloads state:
 bf16 inputs with fp32 accumulation: rel-L2 <= 5e-3 and max-abs <= 2e-2;
 fp8 latent cache: rel-L2 <= 3e-2 (against the oracle on the dequantised
 cache).  The fp32 tiny workload (no tolerance stated) is gated on the same
-bf16 bounds and, as this build's own target, on rel-L2 <= 1e-5."""
+bf16 bounds and, as an internal target, on rel-L2 <= 1e-5."""
 from __future__ import annotations
 
 import sys

@@ -44,10 +44,15 @@ def _gates(w):
 
 
 def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision="bf16",
-                 max_abs=True):
+                 max_abs=True, top_abs=0):
+    """Step on the GPU, then compare the sampled rows (seqs x heads, all rows
+    when None) with the oracle.  top_abs > 0 also compares the top_abs
+    (query token, head) rows with the largest |o| of the GPU output (where an
+    error in the score of a dominant token shows most), each recomputed by
+    the oracle."""
     say(f"case {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout} "
         f"splits={w.num_splits if num_splits is None else num_splits} precision={precision} "
-        f"seqs={seqs} heads={heads}")
+        f"seqs={seqs} heads={heads} top_abs={top_abs}")
     gen = generate(w) if gen is None else gen
     buf = _buffers(w, gen, num_splits=num_splits, precision=precision)
     buf.step()
@@ -59,6 +64,17 @@ def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision=
     mask = sample_mask((w.batch * w.q_tokens, w.n_heads),
                        range(w.batch) if seqs is None else seqs,
                        range(w.n_heads) if heads is None else heads, w.q_tokens)
+    if top_abs > 0:
+        amax = np.abs(o).max(axis=2)
+        order = np.argsort(amax, axis=None)[::-1][:top_abs]
+        for flat in order:
+            n, i = divmod(int(flat), w.n_heads)
+            b = n // w.q_tokens
+            say(f"  largest |o|: token {n} (seq {b}) head {i}: {amax[n, i]:.3f}")
+            r1 = omla.decode_workload(gen, w, seqs=[b], heads=[i])
+            for k in ("o", "latent", "lse"):
+                ref[k][n, i] = r1[k][n, i]
+            mask[n, i] = True
     rel, mabs = _gates(w)
     if not max_abs:
         mabs = None
@@ -202,18 +218,24 @@ def test_decode_parity_fp32_mode(w):
 
 
 # ------------------------------------------------- full-size workloads
+# Full-size workloads: 8 sequences (all 4 of the long-context one) and 16
+# heads or more, every 8th head plus head 127 (each of the four 32-row waves of
+# a 128-row block), and the 8 rows of largest |o|.
+_H16 = list(range(0, 128, 8)) + [127]
 FULL = [
-    (WORKLOADS["v2_b32_l4k_bf16"], [0, 17, 31], [0, 1, 64, 127]),
-    (WORKLOADS["v2_b64_l8k_bf16"], [5, 63], [3, 100]),
-    (WORKLOADS["v2_fp8_t4_b64_l8k"], [0, 63], [0, 64, 127]),
-    (WORKLOADS["v2_long_b4_l128k_bf16"], [0, 3], [0, 77]),
-    (WORKLOADS["v2lite_b64_l8k_bf16"], [0, 31, 63], [0, 5, 15]),
+    (WORKLOADS["v2_b32_l4k_bf16"], [0, 4, 9, 13, 17, 22, 26, 31], _H16),
+    (WORKLOADS["v2_b64_l8k_bf16"], [0, 5, 14, 23, 32, 41, 50, 63], _H16),
+    (WORKLOADS["v2_fp8_t4_b64_l8k"], [0, 9, 18, 27, 36, 45, 54, 63], _H16),
+    (WORKLOADS["v2_long_b4_l128k_bf16"], [0, 1, 2, 3], [0, 8, 16, 24, 40, 56, 64, 72, 77, 88,
+                                                        96, 104, 112, 120, 127, 33]),
+    (WORKLOADS["v2lite_b64_l8k_bf16"], [0, 9, 18, 27, 31, 45, 54, 63], list(range(16))),
 ]
 
 
 @pytest.mark.parametrize("w,seqs,heads", FULL, ids=[f[0].name for f in FULL])
 def test_decode_parity_full_size(w, seqs, heads):
-    _run_compare(w, seqs=seqs, heads=heads, precision=PRECISION.get(w.name, "bf16"))
+    _run_compare(w, seqs=seqs, heads=heads, precision=PRECISION.get(w.name, "bf16"),
+                 top_abs=8)
 
 
 def test_bf16_mode_on_outlier_workloads():
@@ -229,8 +251,8 @@ def test_decode_parity_full_size_paged():
     w = WORKLOADS["v2_paged_b128_bf16"]
     gen = generate(w)
     L = gen["seq_lens"]
-    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 5})
-    _run_compare(w, gen=gen, seqs=seqs, heads=[0, 77, 127])
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 5, 20, 47, 66, 93, 120})
+    _run_compare(w, gen=gen, seqs=seqs, heads=_H16, top_abs=8)
 
 
 # ------------------------------------------------------ properties
@@ -366,7 +388,9 @@ def test_fp8_every_code_decodes_exactly(n_heads):
     row[:, 508:512] = codes[:4]
     buf.cache[:2] = torch.from_numpy(row).cuda()
     buf.kv_scale[:2] = 1.0
-    buf.step()
+    buf.absorb()                      # no append: the cache holds the rows written above
+    buf.attend()
+    buf.up_proj()
     torch.cuda.synchronize()
     lat = to_np(buf.latent)                       # [2, n_h, 512]
     exp = formats.e4m3_to_f64(row[:, :512])

@@ -194,7 +194,7 @@ def test_scale_is_pre_absorption_head_dim():
     assert abs(out["lse"][0, 0] - math.log(1 + math.exp(s1))) < 1e-14
 
 
-# ------------------------------------------------------- absorption identity (L312)
+# ---- absorption identity ("DeepSeek-V2: Strong, Economical, Efficient", 2.1.2, App. C)
 def _absorbed(p):
     """Absorbed evaluation (DeepSeek-V2 Appendix C: W^UK folded into the query,
     W^UV applied after the latent-space sum), written independently."""
@@ -405,6 +405,30 @@ def test_kv_cache_accounting_matches_pages():
     assert mla_el / (2 * w.d_head) == e["gqa_equivalent_groups"]
     assert 2 * mla_el == e["bf16_bytes_per_token"]
     assert mla_el + 4 == e["fp8_bytes_per_token_with_fp32_scale"]
+
+
+def test_cache_row_index_hand_computed_slots():
+    """The slot map of the cache layouts, against slots worked out by hand.
+
+    Paged, 4-token pages, two sequences with shuffled pages: sequence 0 owns
+    pages [2, 0] (tokens 0-3 -> rows 8-11, tokens 4-7 -> rows 0-3), sequence 1
+    owns pages [1, 3] (tokens 0-3 -> rows 4-7, tokens 4-7 -> rows 12-15).
+    Contiguous with max_len 10: row = 10 * seq + pos."""
+    pt = np.array([[2, 0], [1, 3]])
+    seq = np.array([0, 0, 0, 1, 1, 1, 1])
+    pos = np.array([0, 3, 5, 0, 3, 4, 7])
+    assert mla.cache_row_index(seq, pos, pt, 4, 0).tolist() == [8, 11, 1, 4, 7, 12, 15]
+    assert mla.cache_row_index(seq, pos, None, 4, 10).tolist() == [0, 3, 5, 10, 13, 14, 17]
+    # 64-token pages: token 130 of a sequence with pages [5, 1, 3] is entry 2
+    # of page 3 (130 = 2 * 64 + 2) -> row 3 * 64 + 2 = 194; token 63 -> row 383
+    pt64 = np.array([[5, 1, 3]])
+    assert mla.cache_row_index(np.array([0, 0, 0]), np.array([130, 63, 64]), pt64, 64,
+                               0).tolist() == [194, 383, 64]
+    # every (sequence, position) of a full table lands on its own slot
+    all_seq = np.repeat([0, 1], 8)
+    all_pos = np.tile(np.arange(8), 2)
+    slots = mla.cache_row_index(all_seq, all_pos, pt, 4, 0)
+    assert sorted(slots.tolist()) == list(range(16))
 
 
 # ------------------------------------------- absorbed query and up-projection
