@@ -21,7 +21,7 @@ PREC_BF16, PREC_FP32 = 0, 1
 PRECISION_CODES = {"bf16": PREC_BF16, "fp32": PREC_FP32}
 
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
-            "mla_decode_attn", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
+            "mla_decode_attn", "mla_decode_attn_noalloc", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
             "mla_kv_produce_workspace_size", "mla_kv_produce",
             "mla_status_string", "mla_version")
 
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                               ctypes.POINTER(sz)]
     lib.mla_decode_attn.argtypes = [pdims, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
                                     i32, vp, sz, vp, vp, vp]
+    lib.mla_decode_attn_noalloc.argtypes = [pdims, vp, vp, vp, vp, i32, i32, vp, vp, i32, i32,
+                                            i32, vp, vp, vp]
     lib.mla_up_proj_v.argtypes = [pdims, vp, vp, vp, i32, i32, vp]
     lib.mla_out_proj_workspace_size.argtypes = [pdims, i32, i32, i32, ctypes.POINTER(sz)]
     lib.mla_out_proj.argtypes = [pdims, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp]
@@ -186,6 +188,24 @@ def decode_attn(dims: MLADims, q_abs, cache, kv_scale, page_table, max_pages: in
                                int(q_tokens), int(num_splits), _ptr(workspace), int(ws_bytes),
                                _ptr(out_latent), _ptr(out_lse), _stream(stream)),
            "mla_decode_attn")
+
+
+NOALLOC_MAX_WORKSPACE = 96 << 20      # bytes of the library's own split workspace
+
+
+def decode_attn_noalloc(dims: MLADims, q_abs, cache, kv_scale, page_table, max_pages: int,
+                        max_len: int, seq_lens, seq_lens_host: Sequence[int], q_tokens: int,
+                        num_splits: int, out_latent, out_lse, stream=None, _lens_cache=None):
+    """mla_decode_attn with the split workspace in the library's device array."""
+    lib = load_library()
+    lens = _lens_cache if _lens_cache is not None else _lens_host(seq_lens_host)
+    _check(lib.mla_decode_attn_noalloc(ctypes.byref(dims), _ptr(q_abs), _ptr(cache),
+                                       _ptr(kv_scale), _ptr(page_table), int(max_pages),
+                                       int(max_len), _ptr(seq_lens),
+                                       ctypes.cast(lens, ctypes.c_void_p), len(seq_lens_host),
+                                       int(q_tokens), int(num_splits), _ptr(out_latent),
+                                       _ptr(out_lse), _stream(stream)),
+           "mla_decode_attn_noalloc")
 
 
 def up_proj_v(dims: MLADims, latent, w_uv, out, n_tokens: int, stream=None,

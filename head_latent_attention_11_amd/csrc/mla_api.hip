@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "mla_common.hpp"
@@ -177,6 +178,36 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
 
 }  // namespace
 
+// Split-KV workspace of the allocation-free attention call
+// (mla_decode_attn_noalloc): one file-scope device array per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel or
+// a copy (on the host it is only a stand-in for the symbol): it uses the
+// device address that hipGetSymbolAddress returns, fetched once per device
+// and kept in scratch_ptr.  Every allocation-free call on a GPU shares that
+// GPU's array, so such calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = size_t(96) << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on the first
+// call on the device), or nullptr when the runtime cannot provide it.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 int32_t mla_version(void) { return kVersion; }
@@ -190,7 +221,7 @@ const char* mla_status_string(int32_t s) {
     case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MLA_ERR_SEQLEN: return "a sequence length is < 1, < T, or beyond the cache capacity";
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
-    case MLA_ERR_UNSUPPORTED: return "request not supported by this build";
+    case MLA_ERR_UNSUPPORTED: return "request not supported by the library";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
     case MLA_ERR_ARG: return "invalid count, size or flag argument";
     default: return "unknown status";
@@ -330,29 +361,40 @@ int32_t mla_decode_workspace_size(const mla_dims_t* dims, const int32_t* seq_len
   return MLA_OK;
 }
 
-int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* cache,
-                        const float* kv_scale, const int32_t* page_table, int32_t max_pages,
-                        int32_t max_len, const int32_t* seq_lens,
-                        const int32_t* seq_lens_host, int32_t batch, int32_t q_tokens,
-                        int32_t num_splits, void* workspace, size_t ws_bytes,
-                        float* out_latent, float* out_lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks and plan of an attention call (host only, no HIP call).
+int32_t check_decode(const mla_dims_t* dims, const void* q_abs, const void* cache,
+                     const float* kv_scale, const int32_t* page_table, int32_t max_pages,
+                     int32_t max_len, const int32_t* seq_lens, const int32_t* seq_lens_host,
+                     int32_t batch, int32_t q_tokens, int32_t num_splits, float* out_latent,
+                     float* out_lse, Plan* p) {
   int32_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!q_abs || !cache || !seq_lens || !seq_lens_host || !out_latent || !out_lse)
     return MLA_ERR_NULL;
   if (dims->kv_dtype == MLA_FP8_E4M3 && !kv_scale) return MLA_ERR_NULL;
-  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(out_latent) ||
-      !aligned16(out_lse) || (workspace && !aligned16(workspace)))
+  if (!aligned16(q_abs) || !aligned16(cache) || !aligned16(out_latent) || !aligned16(out_lse))
     return MLA_ERR_ALIGN;
-  Plan p;
-  st = make_plan(dims, seq_lens_host, batch, q_tokens, num_splits, &p);
+  st = make_plan(dims, seq_lens_host, batch, q_tokens, num_splits, p);
   if (st != MLA_OK) return st;
   const int64_t cap = page_table ? (int64_t)max_pages * kPage : (int64_t)max_len;
   if (page_table ? max_pages < 1 : max_len < 1) return MLA_ERR_ARG;
   for (int b = 0; b < batch; ++b)
     if (seq_lens_host[b] > cap) return MLA_ERR_SEQLEN;
-  if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return MLA_ERR_WORKSPACE;
+  return MLA_OK;
+}
 
+// The attention call once its arguments are checked and its workspace is
+// known to be large enough: kernel arguments, work-item table, launches.
+int32_t launch_decode_call(const mla_dims_t* dims, const Plan& p, const void* q_abs,
+                           const void* cache, const float* kv_scale,
+                           const int32_t* page_table, int32_t max_pages, int32_t max_len,
+                           const int32_t* seq_lens, const int32_t* seq_lens_host,
+                           int32_t batch, int32_t q_tokens, void* workspace,
+                           float* out_latent, float* out_lse, void* stream) {
   DecodeArgs a = {};
   a.q_abs = q_abs;
   a.cache = cache;
@@ -438,6 +480,50 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* c
     if (e != hipSuccess) return MLA_ERR_LAUNCH;
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* cache,
+                        const float* kv_scale, const int32_t* page_table, int32_t max_pages,
+                        int32_t max_len, const int32_t* seq_lens,
+                        const int32_t* seq_lens_host, int32_t batch, int32_t q_tokens,
+                        int32_t num_splits, void* workspace, size_t ws_bytes,
+                        float* out_latent, float* out_lse, void* stream) {
+  Plan p;
+  int32_t st = check_decode(dims, q_abs, cache, kv_scale, page_table, max_pages, max_len,
+                            seq_lens, seq_lens_host, batch, q_tokens, num_splits, out_latent,
+                            out_lse, &p);
+  if (st != MLA_OK) return st;
+  if (workspace && !aligned16(workspace)) return MLA_ERR_ALIGN;
+  if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes)) return MLA_ERR_WORKSPACE;
+  return launch_decode_call(dims, p, q_abs, cache, kv_scale, page_table, max_pages, max_len,
+                            seq_lens, seq_lens_host, batch, q_tokens, workspace, out_latent,
+                            out_lse, stream);
+}
+
+int32_t mla_decode_attn_noalloc(const mla_dims_t* dims, const void* q_abs, const void* cache,
+                                const float* kv_scale, const int32_t* page_table,
+                                int32_t max_pages, int32_t max_len, const int32_t* seq_lens,
+                                const int32_t* seq_lens_host, int32_t batch, int32_t q_tokens,
+                                int32_t num_splits, float* out_latent, float* out_lse,
+                                void* stream) {
+  Plan p;
+  int32_t st = check_decode(dims, q_abs, cache, kv_scale, page_table, max_pages, max_len,
+                            seq_lens, seq_lens_host, batch, q_tokens, num_splits, out_latent,
+                            out_lse, &p);
+  if (st != MLA_OK) return st;
+  if (p.ws_bytes > kScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0) {
+    ws = scratch_ptr();
+    if (!ws) return MLA_ERR_LAUNCH;
+  }
+  return launch_decode_call(dims, p, q_abs, cache, kv_scale, page_table, max_pages, max_len,
+                            seq_lens, seq_lens_host, batch, q_tokens, ws, out_latent, out_lse,
+                            stream);
 }
 
 int32_t mla_out_proj_workspace_size(const mla_dims_t* dims, int32_t d_model, int32_t n_tokens,

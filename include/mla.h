@@ -25,7 +25,8 @@
  *   - All pointers are DEVICE pointers unless the name ends in _host.
  *   - All tensors are dense, row-major, and start 16-byte aligned.
  *   - The caller allocates and owns every buffer, including the workspace.
- *     The library allocates no memory and keeps no state between calls.
+ *     The library allocates no memory and keeps no state between calls
+ *     (except the device array of mla_decode_attn_noalloc, below).
  *   - Every call enqueues work on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns without synchronising.  Results are ready when the
  *     stream reaches that point.
@@ -57,7 +58,7 @@ typedef enum mla_status {
   MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MLA_ERR_SEQLEN = -5,      /* some L_b < 1, L_b < T, or L_b beyond capacity */
   MLA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
-  MLA_ERR_UNSUPPORTED = -7, /* valid request this build does not implement */
+  MLA_ERR_UNSUPPORTED = -7, /* valid request the library does not implement */
   MLA_ERR_LAUNCH = -8,      /* the HIP runtime rejected a kernel launch */
   MLA_ERR_ARG = -9          /* a count, size or flag argument is invalid */
 } mla_status_t;
@@ -219,6 +220,28 @@ int32_t mla_decode_attn(const mla_dims_t* dims, const void* q_abs,
                         int32_t q_tokens, int32_t num_splits, void* workspace,
                         size_t ws_bytes, float* out_latent, float* out_lse,
                         void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Allocation-free attention call, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Computes exactly what
+ * mla_decode_attn computes, with the same kernels and the same split plan,
+ * but the split-KV partials live in a device array of the library
+ * (96 MiB per GPU, held from the first call on that GPU until the process
+ * ends) instead of a caller workspace.  Arguments and errors are those of
+ * mla_decode_attn without workspace / ws_bytes; a plan whose workspace
+ * (mla_decode_workspace_size) exceeds 96 MiB returns MLA_ERR_WORKSPACE and
+ * enqueues nothing.  The call itself allocates nothing.  All calls on one GPU
+ * share its array: calls that overlap on one GPU (e.g. on two streams
+ * without ordering between them) race and give undefined results.        */
+int32_t mla_decode_attn_noalloc(const mla_dims_t* dims, const void* q_abs,
+                                const void* cache, const float* kv_scale,
+                                const int32_t* page_table, int32_t max_pages,
+                                int32_t max_len, const int32_t* seq_lens,
+                                const int32_t* seq_lens_host, int32_t batch,
+                                int32_t q_tokens, int32_t num_splits,
+                                float* out_latent, float* out_lse,
+                                void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Value up-projection after the latent sum ("DeepSeek-V2", section 2.1.2 and

@@ -265,3 +265,20 @@ def test_dims_struct_layout_matches_header(tmp_path):
                                           text=True).stdout.split()]
     assert out[0] == ctypes.sizeof(binding.MLADims)
     assert out[1:] == [getattr(binding.MLADims, n).offset for n in names]
+
+
+def test_noalloc_rejects_plans_beyond_its_array(mla):
+    """mla_decode_attn_noalloc checks the plan's workspace against its
+    96 MiB device array on the host, before any HIP call."""
+    lib, b = mla
+    d = _v2(b)
+    lens = [65536] * 64
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    need = b.decode_workspace_size(d, lens, 1, 64)
+    assert need > b.NOALLOC_MAX_WORKSPACE
+    assert lib.mla_decode_attn_noalloc(ctypes.byref(d), FAKE, FAKE, None, None, 0, 65536, FAKE,
+                                       ctypes.cast(arr, ctypes.c_void_p), len(lens), 1, 64,
+                                       FAKE, FAKE, None) == WS
+    assert lib.mla_decode_attn_noalloc(ctypes.byref(d), None, FAKE, None, None, 0, 65536, FAKE,
+                                       ctypes.cast(arr, ctypes.c_void_p), len(lens), 1, 64,
+                                       FAKE, FAKE, None) == NULL
