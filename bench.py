@@ -291,7 +291,7 @@ class Timer:
     used round-robin, so each step reads them from HBM), timed with HIP
     events on the stream the graphs are launched on."""
 
-    def __init__(self, name):
+    def __init__(self, name, precision="auto"):
         import torch
         from head_latent_attention_11_amd.runner import DecodeBuffers
         from mla_inputs import WORKLOADS, generate
@@ -301,7 +301,7 @@ class Timer:
         self.cache_b, self.io_b, self.flops = algorithmic(w, self.seq_lens)
         self.replicas = reps = max(2, -(-768 * 2 ** 20 // max(self.cache_b, 1)))
         self.buf = DecodeBuffers(w, self.gen, device="cuda", poison=False, cache_replicas=reps,
-                                 weight_replicas=reps)
+                                 weight_replicas=reps, precision=precision)
         torch.cuda.synchronize()
         self.stream = torch.cuda.current_stream()
         buf = self.buf
@@ -428,6 +428,8 @@ def main():
                     help="skip the timings of the cache producer and of the output "
                          "projection around the step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precision", default="auto", choices=["auto", "bf16", "bf16x2", "fp32"],
+                    help="precision mode of the library (mla_dims_t.precision)")
     ap.add_argument("--no-side", action="store_true",
                     help="skip the companion (bf16, T=1) and DeepSeek-V2-Lite lines")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -441,7 +443,7 @@ def main():
 
     import torch
     torch.cuda.set_device(0)
-    t = Timer(args.workload)
+    t = Timer(args.workload, args.precision)
     w, buf, stream = t.w, t.buf, t.stream
     cache_b, io_b, flops = t.cache_b, t.io_b, t.flops
 
@@ -530,7 +532,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens,
                    "kv_len": w.kv_len or None, "n_heads": w.n_heads, "d_head": w.d_head,
                    "d_latent": w.d_latent, "d_rope": w.d_rope, "kv_dtype": w.kv_dtype,
-                   "layout": w.layout, "cache_replicas": t.replicas,
+                   "layout": w.layout, "precision": args.precision,
+                   "cache_replicas": t.replicas,
                    "steps_per_graph": STEPS_PER_GRAPH,
                    "step": "absorb_q + cache_append(B*T rows) + decode_attn + up_proj_v"},
         "step_us_events": round(ms_step_events * 1e3, 2),

@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(PKG, "libmla.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
-PREC_BF16, PREC_FP32 = 0, 1
-PRECISION_CODES = {"bf16": PREC_BF16, "fp32": PREC_FP32}
+PREC_AUTO, PREC_FP32, PREC_BF16, PREC_BF16X2 = 0, 1, 2, 3
+PRECISION_CODES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16,
+                   "bf16x2": PREC_BF16X2}
 
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_decode_attn_noalloc", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
@@ -48,7 +49,7 @@ class MLADims(ctypes.Structure):
     @classmethod
     def make(cls, n_heads, d_head, d_latent, d_rope, kv_dtype="bf16",
              q_dtype="bf16", softmax_scale=0.0, rope_base=0.0, page_size=64,
-             precision="bf16", yarn_factor=0.0, yarn_alpha=1.0, yarn_beta=32.0,
+             precision="auto", yarn_factor=0.0, yarn_alpha=1.0, yarn_beta=32.0,
              yarn_orig_len=4096, yarn_coef=0.0707):
         kv = DTYPE_CODES[kv_dtype] if isinstance(kv_dtype, str) else kv_dtype
         qd = DTYPE_CODES[q_dtype] if isinstance(q_dtype, str) else q_dtype
@@ -58,7 +59,7 @@ class MLADims(ctypes.Structure):
                    yarn_orig_len, yarn_coef)
 
     @classmethod
-    def from_workload(cls, w, precision="bf16"):
+    def from_workload(cls, w, precision="auto"):
         return cls.make(w.n_heads, w.d_head, w.d_latent, w.d_rope, w.kv_dtype,
                         w.q_dtype, 0.0, w.rope_base, w.page_size, precision,
                         w.yarn_factor, w.yarn_alpha, w.yarn_beta, w.yarn_orig_len,
@@ -66,6 +67,14 @@ class MLADims(ctypes.Structure):
 
     def qabs_is_f32(self) -> bool:
         return self.q_dtype == F32 or self.precision == PREC_FP32
+
+    def qabs_pairs(self) -> bool:
+        """q_abs holds (hi, lo) bf16 pairs per row (the layout rule of
+        mla_absorb_q in include/mla.h)."""
+        shape = (self.d_head == 128 and self.d_latent == 512 and self.d_rope == 64
+                 and self.q_dtype == BF16 and self.n_heads % 128 == 0)
+        return shape and (self.precision == PREC_BF16X2 or
+                          (self.precision == PREC_AUTO and self.kv_dtype == BF16))
 
 
 _lib = None

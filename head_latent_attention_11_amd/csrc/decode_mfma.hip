@@ -181,9 +181,10 @@ static_assert(QLOADS * 64 == ROWS_WG * (QROW / 16), "whole staged rows");
 
 // Staged query halves: 16-byte unit u holds row u / 37, unit u % 37 of the
 // half (unit 36 is the row padding: an out-of-range offset, zero-filled).
-__device__ inline uint32_t q_src_offset(int u, int half) {
+// Rows are q_row_bytes apart (query pairs: only the hi part is read).
+__device__ inline uint32_t q_src_offset(int u, int half, int q_row_bytes) {
   const int r = u / (QROW / 16), c = u - (QROW / 16) * r;
-  return c == QROW / 16 - 1 ? kOOB : uint32_t(r * (2 * D) + half * D + 16 * c);
+  return c == QROW / 16 - 1 ? kOOB : uint32_t(r * q_row_bytes + half * D + 16 * c);
 }
 
 template <bool FP8>
@@ -192,6 +193,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float s_scale[NBUF][TILE];
   __shared__ int s_restart;
+  __shared__ int s_escalate;
   __shared__ __attribute__((aligned(16))) uint8_t s_p[4 * 2 * 1024];   // P^T fragments
   __shared__ float s_inv[ROWS_WG];
 
@@ -391,10 +393,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   // wait, so their HBM latency overlaps the query staging.
   bf16x8 qf[D / 16];
   const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs +
-                                 ((size_t)b * rows + rb * ROWS_WG) * (2 * D));
+                                 ((size_t)b * rows + rb * ROWS_WG) * a.q_row_bytes);
   const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
-                     uint32_t(ROWS_WG * 2 * D), 0x00020000u};
+                     uint32_t(ROWS_WG * a.q_row_bytes), 0x00020000u};
   const uint32_t qlds = lds_ring + 2 * TILE_BYTES;
   // half p_: load n = wave + 4k (n < QLOADS) fills staging units 64n .. 64n+63
 #define MLA_Q_ISSUE(p_)                                                                    \
@@ -403,7 +405,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
       if (wave + 4 * k < QLOADS)                                                         \
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
                      :: "s"(qlds + 1024 * (wave + 4 * k)),                               \
-                        "v"(q_src_offset(64 * (wave + 4 * k) + lane, (p_))), "s"(qrs)    \
+                        "v"(q_src_offset(64 * (wave + 4 * k) + lane, (p_), a.q_row_bytes)), \
+                        "s"(qrs)                                                         \
                      : "memory");                                                        \
   } while (0)
   // half p_ -> qf[18 p_ .. 18 p_ + 17]
@@ -445,7 +448,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     MLA_DECODE_FIRST_TILE();                                                             \
   } while (0)
 
-  if (tid == 0) s_restart = 0;
+  if (tid == 0) { s_restart = 0; s_escalate = 0; }
   // first attempt: query half 0, tiles 0 and 1, query half 1
   MLA_Q_ISSUE(0);
   MLA_ISSUE_FIRST_TILES();
@@ -567,9 +570,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           for (int i = 0; i < 8; ++i) pk_prev[i] = pk[i];
           m_seen = fmaxf(m_seen, mt);
           if (mt > m_ref + 64.0f) s_restart = 1;
+          if (mt > a.esc_log2) s_escalate = 1;   // recomputed with split operands
           MLA_WAIT_ONE_TILE_IN_FLIGHT();     // tile it+1 landed (it+2 may fly)
           __syncthreads();
-          restart = __builtin_amdgcn_readfirstlane(s_restart);   // uniform: read after the barrier
+          restart = __builtin_amdgcn_readfirstlane(s_restart | s_escalate);   // uniform: after the barrier
           if (restart) break;
         }
         if (!restart) {
@@ -655,6 +659,12 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     }
     if (!restart) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load of this attempt in flight
+    if (__builtin_amdgcn_readfirstlane(s_escalate)) {
+      // A score past the escalation threshold: the split-operand kernel
+      // recomputes this item's rows; nothing is written here but the flag.
+      if (tid == 0) a.esc_flags[(size_t)item_id * a.fast_rb + rb] = 1;
+      return;
+    }
     __syncthreads();                  // everyone has read the flag
     if (tid == 0) s_restart = 0;
     m_ref = m_seen;
@@ -677,6 +687,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   // 32 rb + l32); each row's normaliser is with the wave that owns the row.
   // Each wave stages its part of the rows in LDS and writes it back with
   // 16-byte stores over runs of 256 (bf16) or 512 (fp32) contiguous bytes.
+  if (a.esc_flags && tid == 0) a.esc_flags[(size_t)item_id * a.fast_rb + rb] = 0;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   const float lse = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
@@ -724,7 +735,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     constexpr int SROW = 272;
     uint8_t* stg = &s_kv[0][0] + wave * (128 * SROW);
     const size_t g0 = (size_t)item_id * rows + row0;
-    uint8_t* dst = (uint8_t*)a.part_o + g0 * (2 * DC) + 256 * wave;
+    uint8_t* dst = (uint8_t*)a.part_o + g0 * a.part_row_bytes + 256 * wave;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
 #pragma unroll
@@ -744,7 +755,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #pragma unroll
     for (int n = 0; n < 32; ++n) {
       const int r = 4 * n + (lane >> 4);
-      *(u32x4*)(dst + (size_t)r * (2 * DC) + 16 * (lane & 15)) =
+      *(u32x4*)(dst + (size_t)r * a.part_row_bytes + 16 * (lane & 15)) =
           *(const u32x4*)(stg + r * SROW + 16 * (lane & 15));
     }
     if (h == 0) a.part_lse[(size_t)item_id * rows + own0 + l32] = lse;

@@ -468,7 +468,7 @@ void decode_small_kernel(DecodeArgs a, ItemTable tab) {
       if (wave == 0 && g == 0) a.out_lse[gr] = lse;
     } else {
       const size_t pr = (size_t)item_id * rows + row;
-      uint8_t* dst = (uint8_t*)a.part_o + (pr * kLatent + 128 * wave + 4 * g) * 2;
+      uint8_t* dst = (uint8_t*)a.part_o + pr * a.part_row_bytes + (128 * wave + 4 * g) * 2;
 #pragma unroll
       for (int cb = 0; cb < 8; ++cb) {
         const floatx4 v = o[nr][cb] * inv;

@@ -67,12 +67,16 @@ __device__ inline shortx4 lds_read_tr16(const uint16_t* p) {
       (shortx4 __attribute__((address_space(3)))*)(p));
 }
 
-template <typename OutT>
+// PAIRS (bf16 output only): each row is written as the pair hi = bf16(q),
+// lo = bf16(q - hi), hi in elements [0, D) and lo in [D, 2D) of a 2D row.
+template <typename OutT, bool PAIRS = false>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
     OutT* __restrict__ q_abs, int n_tok, int n_h, RopeFreq rope) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
+  constexpr int QROW = PAIRS ? 2 * D : D;     // elements per q_abs row
+  static_assert(!PAIRS || sizeof(OutT) == 2, "query pairs are bf16");
   __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kAbsLdsRow];
   __shared__ __attribute__((aligned(16))) unsigned char os[32 * kAbsOutRow];
@@ -138,11 +142,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
       if (q_pos) pos = q_pos[tok];
     }
     if (q_pos) rope_rot(x0, x1, pos, theta, &x0, &x1);
-    OutT* dst = q_abs + ((size_t)tok * n_h + head) * D + DC + 2 * rk;
+    OutT* dst = q_abs + ((size_t)tok * n_h + head) * QROW + DC + 2 * rk;
     if constexpr (sizeof(OutT) == 4) {
       *(float2*)dst = float2{x0, x1};
     } else {
-      *(uint32_t*)dst = pack_bf16x2(x0, x1);
+      const uint32_t hi = pack_bf16x2(x0, x1);
+      *(uint32_t*)dst = hi;
+      if constexpr (PAIRS)
+        *(uint32_t*)(dst + D) = pack_bf16x2(x0 - __builtin_bit_cast(float, hi << 16),
+                                            x1 - __builtin_bit_cast(float, hi & 0xFFFF0000u));
     }
   }
 #pragma unroll
@@ -181,21 +189,33 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     OutT* orow = (OutT*)(os + l32 * kAbsOutRow) + wave * 32;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      if constexpr (sizeof(OutT) == 4)
+      if constexpr (sizeof(OutT) == 4) {
         *(floatx4*)(orow + 8 * jj + 4 * h) =
             floatx4{acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
-      else
-        *(u32x2*)(orow + 8 * jj + 4 * h) = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
-                                                pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
+      } else {
+        const u32x2 hi = u32x2{pack_bf16x2(acc[4 * jj], acc[4 * jj + 1]),
+                               pack_bf16x2(acc[4 * jj + 2], acc[4 * jj + 3])};
+        *(u32x2*)(orow + 8 * jj + 4 * h) = hi;
+        if constexpr (PAIRS)          // lo parts: columns 128.. of the staging row
+          *(u32x2*)(orow + kAbsCols + 8 * jj + 4 * h) = u32x2{
+              pack_bf16x2(acc[4 * jj] - __builtin_bit_cast(float, hi[0] << 16),
+                          acc[4 * jj + 1] - __builtin_bit_cast(float, hi[0] & 0xFFFF0000u)),
+              pack_bf16x2(acc[4 * jj + 2] - __builtin_bit_cast(float, hi[1] << 16),
+                          acc[4 * jj + 3] - __builtin_bit_cast(float, hi[1] & 0xFFFF0000u))};
+      }
     }
     __syncthreads();
     // 32 tokens x 128 columns, 16-byte chunks, each token's run contiguous
-    constexpr int per_row = kAbsCols * (int)sizeof(OutT) / 16;
+    // (pairs: the hi run, then the lo run D elements further)
+    constexpr int run = kAbsCols * (int)sizeof(OutT) / 16;   // chunks per run
+    constexpr int per_row = PAIRS ? 2 * run : run;
 #pragma unroll
     for (int i = 0; i < 32 * per_row / 256; ++i) {
       const int ch = tid + 256 * i, t = ch / per_row, c = ch % per_row;
+      const int part = PAIRS ? c / run : 0, cc = PAIRS ? c % run : c;
       if (t0 + t < n_tok)
-        *(u32x4*)((unsigned char*)(q_abs + ((size_t)(t0 + t) * n_h + head) * D + cb * kAbsCols) + 16 * c) =
+        *(u32x4*)((unsigned char*)(q_abs + ((size_t)(t0 + t) * n_h + head) * QROW + part * D +
+                                   cb * kAbsCols) + 16 * cc) =
             *(const u32x4*)(os + t * kAbsOutRow + 16 * c);
     }
   }
@@ -368,16 +388,35 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const float* lse_p = a.part_lse + (size_t)first * rows + row;
   float* out = a.out_latent + (size_t)R * a.d_c;
   const int d0 = 8 * lane;                                // this lane's 8 dims
-  const size_t pstride = (size_t)rows * a.d_c;            // elements between splits
+  const uint8_t* pbase = (const uint8_t*)a.part_o + ((size_t)first * rows + row) * a.part_row_bytes;
+  const size_t pstride = (size_t)rows * a.part_row_bytes; // bytes between splits
+  // format of split s's partial: fp32 on the general path and for items
+  // recomputed with split operands, else bf16
+  const int32_t* flags = a.esc_flags ? a.esc_flags + (size_t)first * a.fast_rb + row / 128
+                                     : nullptr;
+  auto f32_of = [&](int sp) -> int {
+    return !a.part_bf16 ? 1 : (flags ? (flags[(size_t)sp * a.fast_rb] != 0) : 0);
+  };
+  auto bf16_lo = [](uint32_t x) { return __builtin_bit_cast(float, x << 16); };
+  auto bf16_hi = [](uint32_t x) { return __builtin_bit_cast(float, x & 0xFFFF0000u); };
   if (a.part_bf16 && ns <= 16) {
-    // Few splits: every load (LSEs and partials) is issued before any of
-    // them is used, so the row costs one memory latency.
+    // Few splits: every load (LSEs, formats and partials) is issued before
+    // any of them is used, so the row costs one memory latency.
     const float lse_l = (lane < ns) ? lse_p[(size_t)lane * rows] : -INFINITY;
-    const uint16_t* src = (const uint16_t*)a.part_o + ((size_t)first * rows + row) * a.d_c + d0;
-    u32x4 v[16];
+    const int f_l = (lane < ns) ? f32_of(lane) : 0;
+    u32x4 v0[16], v1[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s)
-      if (s < ns) v[s] = *(const u32x4*)(src + (size_t)s * pstride);
+    for (int sp = 0; sp < 16; ++sp) {
+      if (sp < ns) {
+        const uint8_t* src = pbase + (size_t)sp * pstride;
+        if (__shfl(f_l, sp, 64)) {
+          v0[sp] = *(const u32x4*)(src + 4 * d0);
+          v1[sp] = *(const u32x4*)(src + 4 * d0 + 16);
+        } else {
+          v0[sp] = *(const u32x4*)(src + 2 * d0);
+        }
+      }
+    }
     const float mx = wave_max(lse_l);
     if (mx == -INFINITY) {                                // no visible token at all
       *(floatx4*)(out + d0) = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -390,13 +429,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     const float w_l = e_l * (1.0f / wsum);
     floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if (s < ns) {
-        const float w = __shfl(w_l, s, 64);
-        acc0 += w * floatx4{__builtin_bit_cast(float, v[s][0] << 16), __builtin_bit_cast(float, v[s][0] & 0xFFFF0000u),
-                            __builtin_bit_cast(float, v[s][1] << 16), __builtin_bit_cast(float, v[s][1] & 0xFFFF0000u)};
-        acc1 += w * floatx4{__builtin_bit_cast(float, v[s][2] << 16), __builtin_bit_cast(float, v[s][2] & 0xFFFF0000u),
-                            __builtin_bit_cast(float, v[s][3] << 16), __builtin_bit_cast(float, v[s][3] & 0xFFFF0000u)};
+    for (int sp = 0; sp < 16; ++sp) {
+      if (sp < ns) {
+        const float w = __shfl(w_l, sp, 64);
+        if (__shfl(f_l, sp, 64)) {
+          acc0 += w * __builtin_bit_cast(floatx4, v0[sp]);
+          acc1 += w * __builtin_bit_cast(floatx4, v1[sp]);
+        } else {
+          acc0 += w * floatx4{bf16_lo(v0[sp][0]), bf16_hi(v0[sp][0]), bf16_lo(v0[sp][1]), bf16_hi(v0[sp][1])};
+          acc1 += w * floatx4{bf16_lo(v0[sp][2]), bf16_hi(v0[sp][2]), bf16_lo(v0[sp][3]), bf16_hi(v0[sp][3])};
+        }
       }
     }
     *(floatx4*)(out + d0) = acc0;
@@ -405,7 +447,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     return;
   }
   float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, lse_p[(size_t)s * rows]);
+  for (int sp = lane; sp < ns; sp += 64) mx = fmaxf(mx, lse_p[(size_t)sp * rows]);
   mx = wave_max(mx);
   if (mx == -INFINITY) {                                  // no visible token at all
     for (int d = d0; d < min(d0 + 8, a.d_c); d += 4) *(floatx4*)(out + d) = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -413,56 +455,30 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     return;
   }
   float wsum = 0.f;
-  for (int s = lane; s < ns; s += 64) wsum += expf(lse_p[(size_t)s * rows] - mx);
+  for (int sp = lane; sp < ns; sp += 64) wsum += expf(lse_p[(size_t)sp * rows] - mx);
   wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  if (a.part_bf16) {                                      // fast path: d_c = 512
-    const uint16_t* src = (const uint16_t*)a.part_o + ((size_t)first * rows + row) * a.d_c + d0;
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-      const int n = min(64, ns - s0);
-      const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
-      int s = 0;
-      for (; s + 4 <= n; s += 4) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(src + (size_t)(s0 + s + u) * pstride);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float w = __shfl(w_l, s + u, 64);
-          acc0 += w * floatx4{__builtin_bit_cast(float, v[u][0] << 16), __builtin_bit_cast(float, v[u][0] & 0xFFFF0000u),
-                              __builtin_bit_cast(float, v[u][1] << 16), __builtin_bit_cast(float, v[u][1] & 0xFFFF0000u)};
-          acc1 += w * floatx4{__builtin_bit_cast(float, v[u][2] << 16), __builtin_bit_cast(float, v[u][2] & 0xFFFF0000u),
-                              __builtin_bit_cast(float, v[u][3] << 16), __builtin_bit_cast(float, v[u][3] & 0xFFFF0000u)};
-        }
-      }
-      for (; s < n; ++s) {
-        const u32x4 v = *(const u32x4*)(src + (size_t)(s0 + s) * pstride);
-        const float w = __shfl(w_l, s, 64);
-        acc0 += w * floatx4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xFFFF0000u),
-                            __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xFFFF0000u)};
-        acc1 += w * floatx4{__builtin_bit_cast(float, v[2] << 16), __builtin_bit_cast(float, v[2] & 0xFFFF0000u),
-                            __builtin_bit_cast(float, v[3] << 16), __builtin_bit_cast(float, v[3] & 0xFFFF0000u)};
+  const bool has0 = d0 < a.d_c, has1 = d0 + 4 < a.d_c;    // general path: d_c % 4 == 0
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int n = min(64, ns - s0);
+    const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
+    const int f_l = (lane < n) ? f32_of(s0 + lane) : 0;
+    for (int sp = 0; sp < n; ++sp) {
+      const float w = __shfl(w_l, sp, 64);
+      const uint8_t* src = pbase + (size_t)(s0 + sp) * pstride;
+      if (__shfl(f_l, sp, 64)) {
+        if (has0) acc0 += w * *(const floatx4*)(src + 4 * d0);
+        if (has1) acc1 += w * *(const floatx4*)(src + 4 * d0 + 16);
+      } else {                                            // bf16 partials: d_c = 512
+        const u32x4 v = *(const u32x4*)(src + 2 * d0);
+        acc0 += w * floatx4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+        acc1 += w * floatx4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
       }
     }
-    *(floatx4*)(out + d0) = acc0;
-    *(floatx4*)(out + d0 + 4) = acc1;
-  } else {                                                // general path: fp32, d_c % 4 == 0
-    const float* src = (const float*)a.part_o + ((size_t)first * rows + row) * a.d_c;
-    const bool has0 = d0 < a.d_c, has1 = d0 + 4 < a.d_c;
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-      const int n = min(64, ns - s0);
-      const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
-      for (int s = 0; s < n; ++s) {
-        const float w = __shfl(w_l, s, 64);
-        const float* ps = src + (size_t)(s0 + s) * pstride;
-        if (has0) acc0 += w * *(const floatx4*)(ps + d0);
-        if (has1) acc1 += w * *(const floatx4*)(ps + d0 + 4);
-      }
-    }
-    if (has0) *(floatx4*)(out + d0) = acc0;
-    if (has1) *(floatx4*)(out + d0 + 4) = acc1;
   }
+  if (has0) *(floatx4*)(out + d0) = acc0;
+  if (has1) *(floatx4*)(out + d0 + 4) = acc1;
   if (lane == 0) a.out_lse[R] = mx + logf(wsum);
 }
 
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(256) void up_proj_general_kernel(
 }
 
 // ================================================================ launchers
-hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
+hipError_t launch_absorb(const mla_dims_t& d, bool fast, bool pairs, const void* q_nope,
                          const void* q_rope, const void* w_uk,
                          const int32_t* q_pos, void* q_abs, int n_tok,
                          RopeFreq rope, hipStream_t st) {
@@ -599,7 +615,12 @@ hipError_t launch_absorb(const mla_dims_t& d, bool fast, const void* q_nope,
     // to 256 workgroups in all
     const int groups = std::max(1, std::min((n_tok + 31) / 32, kNumCU / (4 * d.n_heads)));
     const dim3 grid(d.n_heads * 4, groups);
-    if (out_f32)
+    if (pairs)
+      hipLaunchKernelGGL((absorb_mfma_kernel<uint16_t, true>), grid, dim3(256), 0, st,
+                         (const uint16_t*)q_nope, (const uint16_t*)q_rope,
+                         (const uint16_t*)w_uk, q_pos, (uint16_t*)q_abs, n_tok,
+                         d.n_heads, rope);
+    else if (out_f32)
       hipLaunchKernelGGL(absorb_mfma_kernel<float>, grid, dim3(256), 0, st,
                          (const uint16_t*)q_nope, (const uint16_t*)q_rope,
                          (const uint16_t*)w_uk, q_pos, (float*)q_abs, n_tok,

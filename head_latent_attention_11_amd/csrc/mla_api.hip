@@ -12,7 +12,7 @@
 #include "mla_common.hpp"
 
 namespace mla {
-hipError_t launch_absorb(const mla_dims_t&, bool, const void*, const void*, const void*,
+hipError_t launch_absorb(const mla_dims_t&, bool, bool, const void*, const void*, const void*,
                          const int32_t*, void*, int, RopeFreq, hipStream_t);
 hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int32_t*,
                          const int32_t*, const int32_t*, int, int, int, long long, int,
@@ -29,6 +29,7 @@ static_assert(sizeof(DecodeArgs) + sizeof(ItemTable) <= 4096,
               "the attention kernel's arguments must stay within 4 KB");
 hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_small(const DecodeArgs&, const ItemTable&, int rows_wg, hipStream_t);
+hipError_t launch_decode_x2(const DecodeArgs&, const ItemTable&, int row_blocks, hipStream_t);
 }  // namespace mla
 
 using namespace mla;
@@ -53,7 +54,7 @@ int32_t check_dims(const mla_dims_t* d) {
     return MLA_ERR_DTYPE;
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return MLA_ERR_ARG;
-  if (d->precision != MLA_PREC_BF16 && d->precision != MLA_PREC_FP32) return MLA_ERR_ARG;
+  if (d->precision < MLA_PREC_AUTO || d->precision > MLA_PREC_BF16X2) return MLA_ERR_ARG;
   if (!isfinite(d->yarn_factor) || d->yarn_factor < 0.f) return MLA_ERR_ARG;
   if (d->yarn_factor > 1.f) {                        // context extension in use
     if (!(d->yarn_alpha > 0.f) || !(d->yarn_beta > d->yarn_alpha) || !isfinite(d->yarn_beta))
@@ -72,7 +73,7 @@ bool fast_shape(const mla_dims_t* d) {
 
 // Attention in blocks of 128 rows: 32 heads of one query token per wave.
 bool fast_decode(const mla_dims_t* d, int T) {
-  return fast_shape(d) && d->precision == MLA_PREC_BF16 &&
+  return fast_shape(d) && d->precision != MLA_PREC_FP32 &&
          (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) && d->n_heads % 32 == 0 &&
          ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
 }
@@ -81,13 +82,42 @@ bool fast_decode(const mla_dims_t* d, int T) {
 // row sub-block) for the other head counts that are multiples of 16, bf16
 // or fp8 cache.  Returns the rows per block, or 0.
 int small_decode_rows(const mla_dims_t* d, int T) {
-  if (!fast_shape(d) || d->precision != MLA_PREC_BF16 ||
+  if (!fast_shape(d) || d->precision == MLA_PREC_FP32 ||
       (d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3) || d->n_heads % 16 != 0 ||
       fast_decode(d, T))
     return 0;
   const int64_t rows = (int64_t)d->n_heads * T;
   return rows % 32 == 0 ? 32 : 16;
 }
+
+// Shapes whose absorbed query can be stored as (hi, lo) bf16 pairs and whose
+// attention can run with split operands: every T gives whole 128-row blocks.
+bool pairs_shape(const mla_dims_t* d) {
+  return fast_shape(d) && d->n_heads % 128 == 0;
+}
+
+// The absorbed query is stored as (hi, lo) pairs.
+bool qabs_pairs(const mla_dims_t* d) {
+  if (!pairs_shape(d)) return false;
+  return d->precision == MLA_PREC_BF16X2 ||
+         (d->precision == MLA_PREC_AUTO && d->kv_dtype == MLA_BF16);
+}
+
+// Work items may be escalated to split operands (precision AUTO).
+bool escalating(const mla_dims_t* d) {
+  return d->precision == MLA_PREC_AUTO && qabs_pairs(d);
+}
+
+// Split operands for every item (precision BF16X2); the shape must allow it.
+bool x2_only(const mla_dims_t* d) { return d->precision == MLA_PREC_BF16X2; }
+bool x2_supported(const mla_dims_t* d) {
+  return pairs_shape(d) && d->kv_dtype == MLA_BF16;
+}
+
+constexpr int kX2Rows = 64;            // query rows per split-operand workgroup
+// Escalation threshold: an item whose largest scaled score exceeds 7 in
+// natural-log units (7 log2(e) in the kernels' log2 units) is recomputed.
+constexpr float kEscalateNat = 7.0f;
 
 // Format of the absorbed query.
 int32_t qabs_dtype(const mla_dims_t* d) {
@@ -122,9 +152,13 @@ struct Plan {
   int num_splits;   // > 0: per-sequence equal splits
   int chunk;        // global chunk when num_splits == 0
   int n_items;
-  int row_blocks;
+  int row_blocks;   // row blocks per item of the main attention kernel
+  int fast_rb;      // 128-row blocks per item (escalation flags)
   bool any_split;
-  bool part_bf16;
+  bool part_bf16;   // partials in bf16 unless the item is escalated
+  bool escalate;    // precision AUTO with split-operand recomputation
+  size_t part_row_bytes;
+  size_t lse_bytes, part_bytes, flag_bytes;
   size_t ws_bytes;
 };
 
@@ -133,14 +167,20 @@ struct Plan {
 // chunk length for all sequences so that the work items fill the GPU about
 // once: chunk = ceil(total tokens * row blocks / 256 CUs), rounded up to 64
 // and at least 256 tokens.
+// Workspace: [LSE: items x rows fp32][partials: items x rows x
+// part_row_bytes][flags: items x rows/128 int32], each part 256-byte
+// aligned; LSE and partials only when some sequence is split, flags only
+// when items may escalate.
 int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
                   int num_splits, Plan* p) {
   if (B < 1 || T < 1 || T > 1024) return MLA_ERR_ARG;
   if (num_splits < 0 || num_splits > 4096) return MLA_ERR_ARG;
+  if (x2_only(d) && !x2_supported(d)) return MLA_ERR_UNSUPPORTED;
   const int small = small_decode_rows(d, T);
   const bool fast = fast_decode(d, T) || small > 0;   // matrix-core kernels
   const int64_t rows = (int64_t)d->n_heads * T;
-  const int64_t rb = small > 0 ? rows / small : fast ? rows / kRowsPerWorkgroup : rows;
+  const int64_t rb = x2_only(d) ? rows / kX2Rows
+                     : small > 0 ? rows / small : fast ? rows / kRowsPerWorkgroup : rows;
   int64_t total = 0;
   for (int b = 0; b < B; ++b) {
     if (lens[b] < 1 || lens[b] < T) return MLA_ERR_SEQLEN;
@@ -148,9 +188,13 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
   }
   p->num_splits = num_splits;
   p->row_blocks = (int)rb;
+  p->fast_rb = (int)(rows / kRowsPerWorkgroup);
   p->chunk = 0;
   if (num_splits == 0) {
-    const int64_t target_items = std::max<int64_t>(1, (kNumCU + rb - 1) / rb);
+    // split-operand workgroups do the work of 128-row ones on 64 rows:
+    // plan as for 128-row blocks
+    const int64_t rb_plan = x2_only(d) ? rows / kRowsPerWorkgroup : rb;
+    const int64_t target_items = std::max<int64_t>(1, (kNumCU + rb_plan - 1) / rb_plan);
     int64_t c = (total + target_items - 1) / target_items;
     c = ((c + kPage - 1) / kPage) * kPage;
     c = std::max<int64_t>(c, kMinChunk);
@@ -167,12 +211,17 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
   if (items * rb > INT32_MAX / 2) return MLA_ERR_ARG;
   p->n_items = (int)items;
   p->any_split = any;
-  // partials: fp32 LSE per (item, row), then the latent partials (bf16 on
-  // the matrix-core path, fp32 on the general path)
-  const size_t part_elem = fast ? 2 : 4;
-  const size_t lse_bytes = ((size_t)items * rows * sizeof(float) + 255) / 256 * 256;
-  p->part_bf16 = fast;
-  p->ws_bytes = any ? lse_bytes + (size_t)items * rows * d->d_latent * part_elem : 0;
+  p->escalate = escalating(d) && fast;
+  // partials: bf16 on the matrix-core paths (slots of fp32 size when an
+  // item may be recomputed with split operands, which writes fp32), fp32
+  // with split operands everywhere and on the general path
+  p->part_bf16 = fast && !x2_only(d);
+  p->part_row_bytes = (size_t)d->d_latent * ((p->part_bf16 && !p->escalate) ? 2 : 4);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  p->lse_bytes = any ? al((size_t)items * rows * sizeof(float)) : 0;
+  p->part_bytes = any ? al((size_t)items * rows * p->part_row_bytes) : 0;
+  p->flag_bytes = p->escalate ? al((size_t)items * p->fast_rb * sizeof(int32_t)) : 0;
+  p->ws_bytes = p->lse_bytes + p->part_bytes + p->flag_bytes;
   return MLA_OK;
 }
 
@@ -238,9 +287,10 @@ int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_r
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_abs) ||
       (q_rope && !aligned16(q_rope)))
     return MLA_ERR_ALIGN;
+  if (x2_only(dims) && !x2_supported(dims)) return MLA_ERR_UNSUPPORTED;
   const bool fast = fast_shape(dims);
-  return status_of(launch_absorb(*dims, fast, q_nope, q_rope, w_uk, q_pos, q_abs, n_tokens,
-                                 rope_of(dims), (hipStream_t)stream));
+  return status_of(launch_absorb(*dims, fast, qabs_pairs(dims), q_nope, q_rope, w_uk, q_pos,
+                                 q_abs, n_tokens, rope_of(dims), (hipStream_t)stream));
 }
 
 int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* new_kr,
@@ -365,6 +415,49 @@ int32_t mla_decode_workspace_size(const mla_dims_t* dims, const int32_t* seq_len
 
 namespace {
 
+// Work-item table of an attention launch whose workgroups handle row_blocks
+// blocks of rows per item (see ItemTable).  Empty (n = 0) when every
+// sequence has the same length (the kernels then compute the item from the
+// workgroup index) or when there are too many items (they locate them).
+ItemTable make_table(const Plan& p, int row_blocks, int batch, const int32_t* seq_lens_host,
+                     int uniform_len) {
+  ItemTable tab;
+  tab.n = 0;
+  tab.uniform_len = uniform_len;
+  if (uniform_len > 0 || p.n_items > kItemTable || batch >= (1 << 20)) return tab;
+  // items in sequence order with their token counts, then largest first
+  struct It { uint32_t key; int32_t id; int32_t size; };
+  std::vector<It> its;
+  its.reserve(p.n_items);
+  for (int b = 0; b < batch; ++b) {
+    const int L = seq_lens_host[b];
+    const int c = chunk_of(L, p.num_splits, p.chunk);
+    const int ns = splits_of(L, p.num_splits, p.chunk);
+    for (int sp = 0; sp < ns && sp < 4096; ++sp)
+      its.push_back({uint32_t(b) | (uint32_t(sp) << 20), (int32_t)its.size(),
+                     std::min(c, L - sp * c)});
+  }
+  if ((int64_t)its.size() != p.n_items) return tab;
+  std::stable_sort(its.begin(), its.end(),
+                   [](const It& x, const It& y) { return x.size > y.size; });
+  // Workgroup g runs table entry xcd_logical_index(g, G) / row_blocks: the
+  // entries are filled with the largest items in the order in which
+  // workgroups first reach them.
+  const int n = (int)its.size(), G = n * row_blocks;
+  std::vector<char> done(n, 0);
+  int next = 0;
+  for (int g = 0; g < G && next < n; ++g) {
+    const int i = xcd_logical_index(g, G) / row_blocks;
+    if (done[i]) continue;
+    done[i] = 1;
+    tab.seq_split[i] = its[next].key;
+    tab.item_id[i] = its[next].id;
+    ++next;
+  }
+  tab.n = (next == n) ? n : 0;
+  return tab;
+}
+
 // Argument checks and plan of an attention call (host only, no HIP call).
 int32_t check_decode(const mla_dims_t* dims, const void* q_abs, const void* cache,
                      const float* kv_scale, const int32_t* page_table, int32_t max_pages,
@@ -401,11 +494,16 @@ int32_t launch_decode_call(const mla_dims_t* dims, const Plan& p, const void* q_
   a.kv_scale = kv_scale;
   a.page_table = page_table;
   a.seq_lens = seq_lens;
-  const int64_t rows = (int64_t)dims->n_heads * q_tokens;
-  const size_t lse_bytes = ((size_t)p.n_items * rows * sizeof(float) + 255) / 256 * 256;
-  a.part_lse = p.any_split ? (float*)workspace : nullptr;
-  a.part_o = p.any_split ? (void*)((char*)workspace + lse_bytes) : nullptr;
+  char* ws = (char*)workspace;
+  a.part_lse = p.any_split ? (float*)ws : nullptr;
+  a.part_o = p.any_split ? (void*)(ws + p.lse_bytes) : nullptr;
+  a.esc_flags = p.escalate ? (int32_t*)(ws + p.lse_bytes + p.part_bytes) : nullptr;
   a.part_bf16 = p.part_bf16 ? 1 : 0;
+  a.part_row_bytes = (int32_t)p.part_row_bytes;
+  const int D = dims->d_latent + dims->d_rope;
+  a.q_row_bytes = (qabs_pairs(dims) ? 2 : 1) * D * (qabs_dtype(dims) == MLA_F32 ? 4 : 2);
+  a.fast_rb = p.fast_rb;
+  a.esc_log2 = p.escalate ? kEscalateNat * 1.4426950408889634f : INFINITY;
   a.out_latent = out_latent;
   a.out_lse = out_lse;
   a.B = batch;
@@ -432,45 +530,16 @@ int32_t launch_decode_call(const mla_dims_t* dims, const Plan& p, const void* q_
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   const int small_rows = small_decode_rows(dims, q_tokens);
-  if (fast_decode(dims, q_tokens) || small_rows > 0) {
-    ItemTable tab;
-    tab.n = 0;
-    tab.uniform_len = a.uniform_len;
-    if (a.uniform_len > 0) {
-    } else if (p.n_items <= kItemTable && batch < (1 << 20)) {
-      // items in sequence order with their token counts, then largest first
-      struct It { uint32_t key; int32_t id; int32_t size; };
-      std::vector<It> its;
-      its.reserve(p.n_items);
-      for (int b = 0; b < batch; ++b) {
-        const int L = seq_lens_host[b];
-        const int c = chunk_of(L, p.num_splits, p.chunk);
-        const int ns = splits_of(L, p.num_splits, p.chunk);
-        for (int sp = 0; sp < ns && sp < 4096; ++sp)
-          its.push_back({uint32_t(b) | (uint32_t(sp) << 20), (int32_t)its.size(),
-                         std::min(c, L - sp * c)});
-      }
-      if ((int64_t)its.size() == p.n_items) {
-        std::stable_sort(its.begin(), its.end(),
-                         [](const It& x, const It& y) { return x.size > y.size; });
-        // Workgroup g runs table entry xcd_logical_index(g, G) / row_blocks:
-        // the entries are filled with the largest items in the order in
-        // which workgroups first reach them.
-        const int n = (int)its.size(), G = n * p.row_blocks;
-        std::vector<char> done(n, 0);
-        int next = 0;
-        for (int g = 0; g < G && next < n; ++g) {
-          const int i = xcd_logical_index(g, G) / p.row_blocks;
-          if (done[i]) continue;
-          done[i] = 1;
-          tab.seq_split[i] = its[next].key;
-          tab.item_id[i] = its[next].id;
-          ++next;
-        }
-        tab.n = (next == n) ? n : 0;
-      }
-    }
+  const int64_t rows = (int64_t)dims->n_heads * q_tokens;
+  const int x2_rb = (int)(rows / kX2Rows);
+  if (x2_only(dims)) {
+    e = launch_decode_x2(a, make_table(p, x2_rb, batch, seq_lens_host, a.uniform_len), x2_rb, s);
+  } else if (fast_decode(dims, q_tokens) || small_rows > 0) {
+    const ItemTable tab = make_table(p, p.row_blocks, batch, seq_lens_host, a.uniform_len);
     e = small_rows > 0 ? launch_decode_small(a, tab, small_rows, s) : launch_decode_mfma(a, tab, s);
+    if (e == hipSuccess && p.escalate)     // items flagged by the kernel above
+      e = launch_decode_x2(a, make_table(p, x2_rb, batch, seq_lens_host, a.uniform_len), x2_rb,
+                           s);
   } else {
     e = launch_decode_general(a, s);
   }

@@ -129,15 +129,23 @@ __host__ __device__ inline int xcd_logical_index(int g, int G) {
 
 // Arguments of the attention kernels (passed by value).
 struct DecodeArgs {
-  const void* q_abs;          // [B*T, n_h, D] bf16 (fast) / q_dtype (general)
+  const void* q_abs;          // [B*T, n_h, D] bf16 (fast) / q_dtype (general);
+                              // query pairs: [B*T, n_h, 2, D] bf16 (hi, lo)
   const void* cache;          // contiguous [B, max_len, D] or paged
   const float* kv_scale;      // fp8: one float per cache row
   const int32_t* page_table;  // [B, max_pages] or nullptr
   const int32_t* seq_lens;    // [B]
-  void* part_o;               // [n_items, rows, d_c] partial latent outputs
-                              // (bf16 when part_bf16, else fp32)
+  void* part_o;               // [n_items, rows] partial latent outputs of d_c
+                              // elements, part_row_bytes apart (bf16 when
+                              // part_bf16 and the item is not escalated, else fp32)
   float* part_lse;            // [n_items, rows]
+  int32_t* esc_flags;         // [n_items, rows / 128] or nullptr: 1 = the item's
+                              // 128-row block is recomputed with split operands
   int32_t part_bf16;
+  int32_t part_row_bytes;     // bytes between consecutive partial rows
+  int32_t q_row_bytes;        // bytes between consecutive q_abs rows
+  int32_t fast_rb;            // 128-row blocks per item (flag index stride)
+  float esc_log2;             // escalation threshold on scaled scores (log2 units)
   float* out_latent;          // [B*T, n_h, d_c]
   float* out_lse;             // [B*T, n_h]
   int32_t B, T, n_h, d_c, d_r;

@@ -39,7 +39,7 @@ def to_device(arr: np.ndarray, kind: str, device) -> torch.Tensor:
 class DecodeBuffers:
     def __init__(self, w, gen: Dict[str, np.ndarray], device="cuda",
                  num_splits: Optional[int] = None, poison: bool = True,
-                 cache_replicas: int = 1, precision: str = "bf16",
+                 cache_replicas: int = 1, precision: str = "auto",
                  weight_replicas: int = 1):
         self.w = w
         self.device = torch.device(device)
@@ -120,7 +120,9 @@ class DecodeBuffers:
 
         # ---- outputs and workspace
         qabs_dtype = torch.float32 if self.dims.qabs_is_f32() else self.w_uk.dtype
-        self.q_abs = torch.empty((self.n_tok, w.n_heads, D), dtype=qabs_dtype, device=dev)
+        qshape = ((self.n_tok, w.n_heads, 2, D) if self.dims.qabs_pairs()
+                  else (self.n_tok, w.n_heads, D))
+        self.q_abs = torch.empty(qshape, dtype=qabs_dtype, device=dev)
         self.latent = torch.empty((self.n_tok, w.n_heads, w.d_latent), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.n_tok, w.n_heads), dtype=torch.float32, device=dev)
         # o is written in fp32: the parity gates are absolute (max-abs) and the

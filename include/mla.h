@@ -81,7 +81,7 @@ typedef struct mla_dims {
                           MLA_F32 or MLA_BF16 */
   float softmax_scale; /* 0 -> 1/sqrt(d_head + d_rope) */
   float rope_base;     /* RoPE base; 0 -> 10000 */
-  int32_t precision;   /* MLA_PREC_BF16 or MLA_PREC_FP32, see below */
+  int32_t precision;   /* an mla_precision_t, see below */
   /* Context extension of the RoPE parts (YaRN, which "DeepSeek-V2",
    * section 3, long context extension, applies to the decoupled key and
    * query only: s = 40, alpha = 1, beta = 32, 4K training context).
@@ -104,27 +104,42 @@ typedef struct mla_dims {
 } mla_dims_t;
 
 /* Arithmetic of the absorbed query and the attention (inputs and weights are
- * always read in q_dtype / kv_dtype):
- *   MLA_PREC_BF16: the absorbed query is stored in q_dtype and, on the
- *     matrix-core path, the softmax weights enter the P.C product as bf16
- *     (each rounded to 8 significant bits; the normaliser sums exactly the
- *     rounded weights).  Fastest; scores and weights carry bf16 rounding.
+ * always read in q_dtype / kv_dtype).  bf16 rounding of the absorbed query
+ * moves a score s by about 2^-9 of the query-key dot product, and rounding a
+ * softmax weight to bf16 moves it by up to 2^-9 of itself: invisible when
+ * the weights spread over many tokens, visible in the output when a few
+ * cache rows of large norm take most of the weight.
+ *   MLA_PREC_AUTO (default): the matrix-core kernels with bf16 operands.
+ *     With n_heads a multiple of 128 and a BF16 cache, the absorbed query
+ *     is stored as bf16 (hi, lo) pairs (hi = bf16(q), lo = bf16(q - hi)),
+ *     the attention reads hi, and a work item whose largest scaled score
+ *     exceeds 7 (natural-log units) is recomputed with split operands as in
+ *     MLA_PREC_BF16X2.  Otherwise the same as MLA_PREC_BF16.
  *   MLA_PREC_FP32: the absorbed query is stored as fp32 whatever q_dtype
- *     is, and scores, weights and the weighted sum are formed in fp32.  For
- *     inputs whose score range makes bf16 rounding of the query or of the
- *     weights visible in the output (e.g. a few cache rows far larger than
- *     the rest).                                                            */
+ *     is, and scores, weights and the weighted sum are formed in fp32 by
+ *     the general (scalar) kernel.  Any dims.
+ *   MLA_PREC_BF16: bf16 operands only (each softmax weight enters P.C
+ *     rounded to 8 significant bits; the normaliser sums exactly the
+ *     rounded weights).  Fastest; no recomputation.
+ *   MLA_PREC_BF16X2: every work item on matrix cores with split operands:
+ *     scores from the (hi, lo) query pair and weights as bf16 (hi, lo)
+ *     pairs, i.e. relative errors of about 2^-17 instead of 2^-9; split
+ *     partials in fp32.  Requires n_heads % 128 == 0 and a BF16 cache
+ *     (MLA_ERR_UNSUPPORTED otherwise).                                      */
 typedef enum mla_precision {
-  MLA_PREC_BF16 = 0,
-  MLA_PREC_FP32 = 1
+  MLA_PREC_AUTO = 0,
+  MLA_PREC_FP32 = 1,
+  MLA_PREC_BF16 = 2,
+  MLA_PREC_BF16X2 = 3
 } mla_precision_t;
 
 /* Supported combinations:
  *   matrix-core path: d_h = 128, d_c = 512, d_h^R = 64, q_dtype = BF16
  *       (absorption and up-projection: any n_h; the absorption also with
- *       MLA_PREC_FP32); attention with precision = MLA_PREC_BF16 and
+ *       MLA_PREC_FP32); attention with precision AUTO, BF16 or BF16X2 and
  *         n_h % 32 == 0, (n_h*T) % 128 == 0, kv_dtype = BF16 or FP8_E4M3
- *           (blocks of 128 query rows: DeepSeek-V2 / V3, 128 heads), or
+ *           (blocks of 128 query rows: DeepSeek-V2 / V3, 128 heads; split
+ *           operands in blocks of 64 rows, BF16 cache), or
  *         n_h % 16 == 0 otherwise, kv_dtype = BF16 or FP8_E4M3 (blocks of 16 or 32
  *           rows: e.g. DeepSeek-V2-Lite, 16 heads, T = 1..4);
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
@@ -145,8 +160,11 @@ typedef enum mla_precision {
  * q_nope [n_tokens, n_h, d_h], q_rope [n_tokens, n_h, d_h^R],
  * w_uk [n_h, d_h, d_c]: q_dtype.  q_pos [n_tokens] int32 or NULL.
  * q_abs [n_tokens, n_h, d_c + d_h^R]: q_dtype (F32 when precision is
- * MLA_PREC_FP32), written (round to nearest).
- * n_tokens >= 1.                                                          */
+ * MLA_PREC_FP32), written (round to nearest); with q_dtype BF16, d_h = 128,
+ * d_c = 512, d_h^R = 64, n_h % 128 == 0 and precision AUTO (BF16 cache) or
+ * BF16X2 it is [n_tokens, n_h, 2, d_c + d_h^R] bf16: hi = bf16(q) then
+ * lo = bf16(q - hi) of each row ("query pairs").
+ * n_tokens >= 1.  Errors: MLA_ERR_UNSUPPORTED for BF16X2 on other shapes.  */
 int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope,
                      const void* q_rope, const void* w_uk,
                      const int32_t* q_pos, void* q_abs, int32_t n_tokens,
@@ -187,7 +205,9 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c,
 /* ------------------------------------------------------------------------ */
 /* Workspace of mla_decode_attn for the given host copy of the lengths and
  * split request (same planner as mla_decode_attn).  *bytes receives the
- * exact size; 0 when no sequence is split.                                */
+ * exact size: the split partials when some sequence is split, plus one
+ * 4-byte flag per (work item, 128-row block) when precision AUTO may
+ * recompute items with split operands; 0 when neither applies.            */
 int32_t mla_decode_workspace_size(const mla_dims_t* dims,
                                   const int32_t* seq_lens_host, int32_t batch,
                                   int32_t q_tokens, int32_t num_splits,
@@ -201,9 +221,9 @@ int32_t mla_decode_workspace_size(const mla_dims_t* dims,
  *   out_latent[n, i, :] = sum_j softmax(s)_j * cache_row_j[0:d_c]
  *   out_lse[n, i]       = ln sum_j exp(s_j)
  *
- * q_abs [B*T, n_h, D] as written by mla_absorb_q (q_dtype, or F32 when
- * precision is MLA_PREC_FP32); cache as in mla_cache_append (kv_scale for
- * FP8 only).  seq_lens [B] int32 on the device; seq_lens_host: the same
+ * q_abs as written by mla_absorb_q with the same dims ([B*T, n_h, D] in
+ * q_dtype, F32 with MLA_PREC_FP32, or query pairs [B*T, n_h, 2, D]); cache
+ * as in mla_cache_append (kv_scale for FP8 only).  seq_lens [B] int32 on the device; seq_lens_host: the same
  * values on the host (used to plan the split-KV work; they must agree).
  * num_splits = 0: the library splits long sequences into KV chunks to fill
  * the GPU; num_splits = S > 0: each sequence is cut into at most S chunks of

@@ -86,8 +86,14 @@ def test_decode_validation(mla):
     assert _decode(lib, b, bad, [100]) == DIMS
     bad = _v2(b, softmax_scale=-1.0)
     assert _decode(lib, b, bad, [100]) == ARG
-    bad = _v2(b, precision=2)
+    bad = _v2(b, precision=4)
     assert _decode(lib, b, bad, [100]) == ARG                 # unknown precision mode
+    bad = _v2(b, precision=-1)
+    assert _decode(lib, b, bad, [100]) == ARG
+    # split operands need 128-head multiples and a bf16 cache
+    assert _decode(lib, b, _v2(b, n_heads=16, precision="bf16x2"), [100]) == UNSUP
+    assert _decode(lib, b, _v2(b, kv_dtype="fp8", precision="bf16x2"), [100],
+                   scale=FAKE) == UNSUP
     # paged: capacity is max_pages * 64
     assert _decode(lib, b, d, [200], pt=FAKE, max_pages=3) == SEQLEN
     assert _decode(lib, b, d, [200], pt=FAKE, max_pages=0) == ARG
@@ -200,7 +206,7 @@ def _ws(lib, dims, lens, T=1, splits=0):
 
 def test_split_planner_sizes(mla):
     lib, b = mla
-    d = _v2(b)
+    d = _v2(b, precision="bf16")          # bf16 operands only: bf16 partials
     rows, dc = 128, 512
     # 32 x 4096 tokens, 1 row block of 128 rows: chunk 512 -> 8 splits each
     st, n = _ws(lib, d, [4096] * 32)
@@ -239,6 +245,33 @@ def test_split_planner_sizes(mla):
     assert st == OK and n == 0
     st, _ = _ws(lib, d, [5], T=6)
     assert st == SEQLEN
+
+
+def test_split_planner_sizes_with_split_operands(mla):
+    """Precision AUTO (128 heads, bf16 cache): partial slots of fp32 size and
+    one flag per (item, 128-row block), each part 256-byte aligned; BF16X2:
+    fp32 partials, no flags; the items are planned as for 128-row blocks."""
+    lib, b = mla
+    rows, dc = 128, 512
+    auto = _v2(b)
+    assert auto.precision == 0
+    st, n = _ws(lib, auto, [4096] * 32)                        # 256 items of 512 tokens
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4 + 1024
+    st, n = _ws(lib, auto, [131072] * 4, splits=64)
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4 + 1024
+    st, n = _ws(lib, auto, [8192] * 64, T=4)                   # unsplit: flags only
+    assert st == OK and n == 64 * 4 * 4
+    st, n = _ws(lib, auto, [200])                              # one flag, 256-byte aligned
+    assert st == OK and n == 256
+    st, n = _ws(lib, _v2(b, kv_dtype="fp8"), [8192] * 64, T=4)  # fp8 cache: no escalation
+    assert st == OK and n == 0
+    x2 = _v2(b, precision="bf16x2")
+    st, n = _ws(lib, x2, [4096] * 32)
+    assert st == OK and n == 256 * rows * 4 + 256 * rows * dc * 4
+    st, n = _ws(lib, x2, [200])
+    assert st == OK and n == 0
+    st, _ = _ws(lib, _v2(b, n_heads=64, precision="bf16x2"), [4096])
+    assert st == UNSUP
 
 
 def test_dims_struct_layout_matches_header(tmp_path):

@@ -43,7 +43,7 @@ def _gates(w):
     return (REL_L2_FP8, None) if w.kv_dtype == "fp8" else (REL_L2_BF16, MAX_ABS_BF16)
 
 
-def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision="bf16",
+def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision="auto",
                  max_abs=True, top_abs=0):
     """Step on the GPU, then compare the sampled rows (seqs x heads, all rows
     when None) with the oracle.  top_abs > 0 also compares the top_abs
@@ -90,12 +90,9 @@ def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision=
 
 
 # ----------------------------------------------------------- small cases
-# Workloads whose score range makes bf16 rounding of the absorbed query and of
-# the softmax weights visible at the max-abs gate (1% of the cache rows scaled
-# by 8) are checked in the fp32 precision mode; the bf16 mode is checked on
-# them against the rel-L2 gate in test_bf16_mode_on_outlier_workloads.
-PRECISION = {"v2_outliers_split7": "fp32", "v2_long_b4_l128k_bf16": "fp32"}
-
+# Every case runs in the default precision mode (AUTO): on the workloads with
+# cache rows scaled by 8 the bf16 kernel hands its work items to the
+# split-operand kernel, and both gates hold there.
 SMALL = [
     WORKLOADS["tiny_fp32"],
     small_variant(V2, name="v2_ragged_auto", batch=4, kv_len=0, lengths=(1, 33, 700, 64)),
@@ -157,7 +154,7 @@ SMALL = [
 
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_decode_parity_small(w):
-    _run_compare(w, precision=PRECISION.get(w.name, "bf16"))
+    _run_compare(w)
 
 
 # Context extension (YaRN) of the RoPE parts, rotated by the library (query
@@ -234,17 +231,68 @@ FULL = [
 
 @pytest.mark.parametrize("w,seqs,heads", FULL, ids=[f[0].name for f in FULL])
 def test_decode_parity_full_size(w, seqs, heads):
-    _run_compare(w, seqs=seqs, heads=heads, precision=PRECISION.get(w.name, "bf16"),
-                 top_abs=8)
+    _run_compare(w, seqs=seqs, heads=heads, top_abs=8)
 
 
 def test_bf16_mode_on_outlier_workloads():
-    """The bf16 mode on the outlier workloads: within the rel-L2 gate (the
-    max-abs gate is the fp32 mode's, see PRECISION)."""
+    """The bf16-operand path alone (precision BF16: no recomputation) on the
+    outlier workloads: within the rel-L2 gate; its max-abs error is what the
+    split operands remove (both gates hold in the default mode above)."""
     w = SMALL[[x.name for x in SMALL].index("v2_outliers_split7")]
     _run_compare(w, precision="bf16", max_abs=False)
     w = WORKLOADS["v2_long_b4_l128k_bf16"]
-    _run_compare(w, seqs=[1], heads=[0, 127], precision="bf16", max_abs=False)
+    _run_compare(w, seqs=[0, 3], heads=[0, 77, 127], precision="bf16", max_abs=False)
+
+
+# The split-operand kernel on every item (precision BF16X2), both gates.
+X2 = [
+    small_variant(V2, name="x2_ragged_split5", batch=4, kv_len=0, lengths=(1, 33, 700, 64),
+                  num_splits=5),
+    small_variant(V2, name="x2_paged", batch=5, kv_len=0, lengths=(40, 900, 64, 65, 333),
+                  layout="paged"),
+    small_variant(V2, name="x2_t4_causal", batch=3, q_tokens=4, kv_len=0, lengths=(300, 4, 130),
+                  num_splits=2),
+    small_variant(V2, name="x2_outliers_split3", batch=2, kv_len=0, lengths=(3000, 2900),
+                  num_splits=3, outlier_frac=0.01, outlier_scale=8.0),
+    small_variant(V2, name="x2_rope_yarn", batch=2, kv_len=0, lengths=(4600, 900), rope=True,
+                  yarn_factor=40.0),
+]
+
+
+@pytest.mark.parametrize("w", X2, ids=[w.name for w in X2])
+def test_decode_parity_split_operands(w):
+    heads = [0, 31, 64, 127] if w.rope else None
+    _run_compare(w, heads=heads, precision="bf16x2")
+
+
+def _latent_lse(w, gen, precision, num_splits=None):
+    buf = _buffers(w, gen, precision=precision, num_splits=num_splits)
+    buf.absorb()
+    buf.attend()
+    torch.cuda.synchronize()
+    return to_np(buf.latent), to_np(buf.lse)
+
+
+def test_escalation_decisions():
+    """AUTO escalates exactly the items that need it.  On N(0,1) data (largest
+    scores ~4-5) no item is recomputed: the result is bit for bit that of the
+    bf16-operand path.  With 1% of the cache rows scaled by 8 every item holds
+    scores far past the threshold: the result is bit for bit that of the
+    split-operand path (same kernel, same fp32 partials, same combine)."""
+    w = small_variant(V2, name="esc_plain", batch=3, kv_len=0, lengths=(3000, 700, 1500),
+                      num_splits=3)
+    gen = generate(w)
+    a_lat, a_lse = _latent_lse(w, gen, "auto")
+    b_lat, b_lse = _latent_lse(w, gen, "bf16")
+    assert np.array_equal(a_lat, b_lat) and np.array_equal(a_lse, b_lse)
+    w = small_variant(V2, name="esc_outliers", batch=2, kv_len=0, lengths=(3000, 2900),
+                      num_splits=3, outlier_frac=0.01, outlier_scale=8.0)
+    gen = generate(w)
+    a_lat, a_lse = _latent_lse(w, gen, "auto")
+    x_lat, x_lse = _latent_lse(w, gen, "bf16x2")
+    assert np.array_equal(a_lat, x_lat) and np.array_equal(a_lse, x_lse)
+    b_lat, _ = _latent_lse(w, gen, "bf16")
+    assert not np.array_equal(a_lat, b_lat)
 
 
 def test_decode_parity_full_size_paged():
@@ -256,13 +304,14 @@ def test_decode_parity_full_size_paged():
 
 
 # ------------------------------------------------------ properties
-def test_split_invariance_and_determinism():
+@pytest.mark.parametrize("precision", ["bf16", "bf16x2"])
+def test_split_invariance_and_determinism(precision):
     w = small_variant(V2, name="split_inv", batch=2, kv_len=0, lengths=(2000, 1500))
     gen = generate(w)
     ref = omla.decode_workload(gen, w)
     outs = {}
     for ns in (1, 2, 7, 0):
-        buf = _buffers(w, gen, num_splits=ns)
+        buf = _buffers(w, gen, num_splits=ns, precision=precision)
         buf.step()
         torch.cuda.synchronize()
         outs[ns] = (to_np(buf.latent), to_np(buf.o))
@@ -271,14 +320,18 @@ def test_split_invariance_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(to_np(buf.latent), outs[ns][0])
         assert np.array_equal(to_np(buf.o), outs[ns][1])
-    # A split run stores each chunk's partial latent in bf16 before the LSE
-    # combine: one extra rounding of at most 2^-8 relative per element on top
-    # of the unsplit result, whose own operands are bf16.  The two results may
-    # therefore differ by up to about one bf16 unit roundoff (2^-8) in rel-L2.
+    # bf16 operands: a split run stores each chunk's partial latent in bf16
+    # before the LSE combine, one extra rounding of at most 2^-8 relative per
+    # element on top of the unsplit result, whose own operands are bf16: the
+    # two may differ by up to about one bf16 unit roundoff (2^-8) in rel-L2.
+    # Split operands: fp32 partials and ~2^-17 operand errors; the split and
+    # unsplit results differ only by fp32 rounding in the combine and in the
+    # accumulation order (bound 1e-5).
+    bound = 2.0 ** -8 if precision == "bf16" else 1e-5
     for ns in (2, 7, 0):
         r = rel_l2(outs[ns][0], outs[1][0])
         say(f"  splits={ns} vs unsplit: rel-L2 {r:.2e}")
-        assert r <= 2.0 ** -8
+        assert r <= bound
 
 
 def test_paged_equals_contiguous_bitwise():
@@ -305,7 +358,8 @@ def test_reference_restart_on_large_score_jump():
     2^64 (log2 units) forces the matrix-core kernel to restart its work item
     with a higher reference; the result must still match the oracle.  The
     rows scaled by 64 scale the bf16 operand rounding by 64 as well, so the
-    bf16 mode is held to the rel-L2 gate and the fp32 mode to both gates.
+    bf16-operand path is held to the rel-L2 gate, the split-operand and fp32
+    paths to both gates.
     For several heads the jump exceeds 128 (log2 units): without the restart
     their weights would overflow fp32, so a missed restart shows up as a
     non-finite output."""
@@ -316,7 +370,9 @@ def test_reference_restart_on_large_score_jump():
     c[1000 + 500] *= 64.0           # sequence 1
     from mla_inputs import bf16_bits_from_f32
     gen["c_kv"] = bf16_bits_from_f32(c.astype(np.float32))
-    _run_compare(w, gen=gen, max_abs=False)
+    _run_compare(w, gen=gen, precision="bf16", max_abs=False)   # restart of the bf16 kernel
+    _run_compare(w, gen=gen)        # AUTO: recomputed (and restarted) with split operands
+    _run_compare(w, gen=gen, precision="bf16x2")
     _run_compare(w, gen=gen, precision="fp32")
 
 
@@ -413,6 +469,22 @@ def test_absorb_q_parity(w):
     d = omla.logical_inputs(gen, w)
     ref = omla.absorbed_query(d["q_nope"], d["q_rope"], d["w_uk"])
     got = to_np(buf.q_abs)
+    if buf.dims.qabs_pairs():
+        # (hi, lo) pairs: hi is the bf16 rounding of the fp32 result and
+        # hi + lo carries it to ~2^-17 relative (fp32 accumulation beyond)
+        hi, lo = got[:, :, 0, :], got[:, :, 1, :]
+        check("q_abs hi", hi, ref, 4e-3)
+        assert np.all(np.abs(lo) <= np.abs(hi) * 2.0 ** -8 + 1e-30)
+        check("q_abs hi + lo", hi + lo, ref, 2e-5)
+        # elementwise: the lo rounding (2^-17 |q|) plus the fp32 accumulation
+        # of 128 products (at most 128 * 2^-24 of the sum of their
+        # magnitudes); the rotated RoPE part is a single fp32 rounding away
+        mag = np.abs(ref).copy()
+        for i in range(w.n_heads):
+            mag[:, i, :w.d_latent] = np.abs(d["q_nope"][:, i, :]) @ np.abs(d["w_uk"][i])
+        bound = 2.0 ** -17 * np.abs(ref) + 128 * 2.0 ** -24 * mag + 2.0 ** -24 * np.abs(ref)
+        assert np.all(np.abs(hi + lo - ref) <= 2 * bound + 1e-30)
+        return
     # q_abs is stored in the query format: bf16 rounding (2^-9 relative)
     tol = 1e-6 if w.q_dtype == "f32" else 4e-3
     check("q_abs", got, ref, tol)
