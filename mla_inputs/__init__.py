@@ -26,8 +26,9 @@ Draw recipe (every workload):
   * Outliers (long-context workload): round(frac * L) distinct token rows per
     sequence, uniform without replacement; only the c_KV row is multiplied by
     the outlier factor (a power of two, so exact in bf16).
-  * fp8-cache workload: the c_KV / k_R rows generated here are the bf16 source
-    rows that the cache-append step quantises; quantisation is not done here.
+  * fp8- and 6-bit-cache workloads: the c_KV / k_R rows generated here are
+    the bf16 source rows that the cache-append step quantises; quantisation is
+    not done here.
 """
 from __future__ import annotations
 
@@ -61,7 +62,7 @@ class Workload:
     kv_len: int = 0            # uniform length; 0 when len_range is used
     len_range: Tuple[int, int] = (0, 0)   # log-uniform [lo, hi]
     lengths: Tuple[int, ...] = ()          # explicit per-sequence lengths
-    kv_dtype: str = "bf16"     # "f32" | "bf16" | "fp8"
+    kv_dtype: str = "bf16"     # "f32" | "bf16" | "fp8" | "fp6"
     q_dtype: str = "bf16"      # "f32" | "bf16"
     layout: str = "contiguous"  # "contiguous" | "paged"
     page_size: int = 64
@@ -117,6 +118,12 @@ WORKLOADS: Dict[str, Workload] = {
             d_head=128, d_latent=512, d_rope=64, kv_len=8192, kv_dtype="fp8",
             description="fp8 e4m3 latent cache (per-token fp32 scale) + "
                         "4 causal query tokens: B=64, T=4, L=8192"),
+        Workload(
+            name="v2_fp6_t4_b64_l8k", batch=64, q_tokens=4, n_heads=128,
+            d_head=128, d_latent=512, d_rope=64, kv_len=8192, kv_dtype="fp6",
+            description="6-bit latent cache (E2M3 codes, one E8M0 power of two "
+                        "per 32 elements) + 4 causal query tokens: B=64, T=4, "
+                        "L=8192"),
         Workload(
             name="v2_b64_l8k_bf16", batch=64, q_tokens=1, n_heads=128,
             d_head=128, d_latent=512, d_rope=64, kv_len=8192,

@@ -185,8 +185,10 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload, seqs=None) -> Dict[str,
       * RoPE on q^R at the query positions and on k^R at the row positions
         when the workload carries raw (unrotated) RoPE parts;
       * for the fp8 cache, the per-token E4M3 quantisation of the source rows
-        (float32 decisions, see ``formats``) followed by exact dequantisation:
-        the dequantised cache *is* the attention input.
+        (float32 decisions, see ``formats``), for the 6-bit cache the E2M3
+        quantisation with one shared power of two per 32 elements, each
+        followed by exact dequantisation: the dequantised cache *is* the
+        attention input.
     ``seqs`` limits the cache rows decoded to those sequences (the returned
     row_offsets then index the compacted rows).
     """
@@ -228,6 +230,12 @@ def logical_inputs(gen: Dict[str, np.ndarray], workload, seqs=None) -> Dict[str,
         deq = formats.dequantize_rows_e4m3(codes, scales)
         c, kr = deq[:, :w.d_latent], deq[:, w.d_latent:]
         d["fp8_codes"], d["fp8_scales"] = codes, scales
+    elif w.kv_dtype == "fp6":
+        rows = np.concatenate([c, kr], axis=1).astype(np.float32)
+        codes, exps = formats.quantize_rows_mxfp6(rows)
+        deq = formats.dequantize_rows_mxfp6(codes, exps)
+        c, kr = deq[:, :w.d_latent], deq[:, w.d_latent:]
+        d["fp6_codes"], d["fp6_exps"] = codes, exps
     d["c_rows"], d["kr_rows"] = c, kr
     return d
 

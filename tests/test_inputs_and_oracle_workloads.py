@@ -123,3 +123,23 @@ def test_oracle_sampled_heads_match_full():
     part = mla.decode_workload(g, w, seqs=[1], heads=[3, 5])
     np.testing.assert_array_equal(part["o"][1, [3, 5]], full["o"][1, [3, 5]])
     assert np.isnan(part["o"][0]).all()
+
+
+def test_oracle_on_the_6bit_cache_workload():
+    """The 6-bit cache workload end to end in the oracle (scaled down): the
+    attention input is the dequantised cache, every value on its block's
+    E2M3 grid; its error against the bf16 source rows is that of E2M3 with
+    shared powers of two (relative RMS of a few percent: reported by the
+    benchmark, not a parity gate)."""
+    w = small_variant(WORKLOADS["v2_fp6_t4_b64_l8k"], batch=2, kv_len=96)
+    g = generate(w)
+    d = mla.logical_inputs(g, w)
+    rows = np.concatenate([d["c_rows"], d["kr_rows"]], axis=1)
+    scale = np.repeat(np.ldexp(1.0, d["fp6_exps"]), 32, axis=1)
+    on_grid = np.isin(rows / scale, formats.E2M3_TABLE)
+    assert on_grid.all()
+    src = np.concatenate([formats.bf16_to_f64(g["c_kv"]), formats.bf16_to_f64(g["k_r"])], axis=1)
+    rel = np.linalg.norm(rows - src) / np.linalg.norm(src)
+    assert 0.01 < rel < 0.08
+    out = mla.decode_workload(g, w, seqs=[1], heads=[0, 127])
+    assert np.all(np.isfinite(out["o"][4:8][:, [0, 127]]))

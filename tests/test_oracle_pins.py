@@ -621,3 +621,94 @@ def test_yarn_logit_factor_and_how_it_enters():
     b = mla.decode(t * qn, t * qr, wuk, wuv, C, KR, [0], [L], 1)
     for k in ("o", "latent", "lse"):
         np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------- 6-bit latent cache
+def test_e2m3_values_are_the_e4m3_values_on_the_e2m3_grid():
+    """E2M3 shares E4M3's 3 mantissa bits with a narrower exponent range: its
+    non-negative values are exactly the E4M3 values v in [0, 7.5] with 8 v
+    an integer (E2M3's subnormal spacing is 1/8).  The E4M3 side comes from
+    torch's float8_e4m3fn, independent of the E2M3 table."""
+    e4 = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    e4 = e4.numpy()
+    grid = sorted(v for v in e4 if 0 <= v <= 7.5 and float(v * 8).is_integer())
+    assert len(grid) == 32
+    np.testing.assert_array_equal(formats.E2M3_TABLE[:32], np.array(grid))
+    # sign bit: codes 32..63 are the negatives of 0..31
+    np.testing.assert_array_equal(formats.E2M3_TABLE[32:], -formats.E2M3_TABLE[:32])
+
+
+def test_e2m3_landmarks():
+    t = formats.E2M3_TABLE
+    assert t[0x1F] == 7.5 and t[0x01] == 0.125 and t[0x08] == 1.0 and t[0x3F] == -7.5
+    assert t[0x07] == 0.875 and t[0x10] == 2.0 and t[0x18] == 4.0 and t[0x19] == 4.5
+
+
+def test_mxfp6_golden_block():
+    with open(os.path.join(GOLDEN, "mxfp6_block_example.json")) as f:
+        g = json.load(f)
+    row = np.zeros((1, 576), dtype=np.float32)
+    row[0, :4] = g["block"]
+    codes, exps = formats.quantize_rows_mxfp6(row)
+    assert codes[0, :4].tolist() == g["expected_codes"]
+    assert exps[0, 0] == g["expected_exponent"]
+    assert np.all(exps[0, 1:] == g["expected_zero_block_exponent"])
+    np.testing.assert_array_equal(formats.dequantize_rows_mxfp6(codes, exps)[0, :4],
+                                  g["expected_values"])
+    packed = formats.pack_rows_mxfp6(codes, exps)
+    assert packed[0, :3].tolist() == g["expected_first_bytes"]
+    assert packed[0, 432] == g["expected_exponent_byte"]
+    assert packed.shape == (1, 452) and np.all(packed[0, 450:] == 0)
+
+
+def test_mxfp6_quantisation_bounds_and_idempotence():
+    """Per block: amax / 2^e lies in [4, 8); each element is within half a
+    grid step of its stored value (the step of E2M3 at the element's
+    magnitude, 1/8 below 2, 1/4 in [2, 4), 1/2 in [4, 8), times 2^e), or
+    saturated at 7.5 * 2^e from below 8 * 2^e; quantising the stored values
+    returns the same codes; codes are monotone in the input."""
+    rng = np.random.default_rng(5)
+    rows = (rng.standard_normal((64, 576)) * np.exp(rng.uniform(-6, 6, (64, 1)))).astype(np.float32)
+    rows[3, :32] = 0.0                                   # an all-zero block
+    codes, exps = formats.quantize_rows_mxfp6(rows)
+    blocks = rows.astype(np.float64).reshape(64, 18, 32)
+    amax = np.abs(blocks).max(axis=2)
+    ratio = amax / np.ldexp(1.0, exps)
+    nz = amax > 0
+    assert np.all((ratio[nz] >= 4) & (ratio[nz] < 8))
+    assert exps[3, 0] == -126
+    deq = formats.dequantize_rows_mxfp6(codes, exps).reshape(64, 18, 32)
+    y = np.abs(blocks) / np.ldexp(1.0, exps)[:, :, None]
+    step = np.where(y < 2, 0.125, np.where(y < 4, 0.25, 0.5))
+    err = np.abs(blocks - deq) / np.ldexp(1.0, exps)[:, :, None]
+    sat = y > 7.5
+    assert np.all(err[~sat] <= step[~sat] / 2 + 1e-12)
+    assert np.all(err[sat] < 0.5)
+    codes2, exps2 = formats.quantize_rows_mxfp6(deq.reshape(64, 576).astype(np.float32))
+    np.testing.assert_array_equal(codes2, codes)
+    xs = np.linspace(-7.5, 7.5, 4001)
+    v = formats.e2m3_to_f64(formats.e2m3_nearest_sat(xs))
+    assert np.all(np.diff(v) >= 0)
+
+
+def test_mxfp6_packing_bit_order():
+    """Code i of block k sits at bits 6 i .. 6 i + 5 of bytes 24 k .. 24 k + 23
+    read as one little-endian integer; byte 432 + k is e_k + 127."""
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 64, (3, 576)).astype(np.uint8)
+    exps = rng.integers(-126, 128, (3, 18)).astype(np.int32)
+    packed = formats.pack_rows_mxfp6(codes, exps)
+    for r in range(3):
+        for k in range(18):
+            word = int.from_bytes(bytes(packed[r, 24 * k:24 * k + 24]), "little")
+            for i in range(32):
+                assert (word >> (6 * i)) & 63 == codes[r, 32 * k + i]
+            assert int(packed[r, 432 + k]) == exps[r, k] + 127
+
+
+def test_mxfp6_bits_per_element():
+    """The 6-bit cache: 576 codes of 6 bits plus 18 block exponents of 8 bits
+    = 6.25 bits per element (the pages: about 6 bits per element on
+    average); 452 bytes per token row with 2 bytes of padding."""
+    assert (576 * 6 + 18 * 8) / 576 == 6.25
+    assert formats.MXFP6_ROW_BYTES == 452 and 576 * 6 // 8 + 18 + 2 == 452
