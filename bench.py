@@ -40,6 +40,7 @@ KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
                   ("decode_mfma.hip", "decode_mfma_asm.inc", "decode_small.hip",
                    "kernels_misc.hip", "mla_common.hpp", "plan_device.hpp", "mla_api.hip")]
 LITE_WORKLOAD = "v2lite_b64_l8k_bf16"   # DeepSeek-V2-Lite shapes (16 heads)
+FP6_WORKLOAD = "v2_fp6_t4_b64_l8k"      # the headline shape on the 6-bit cache
 
 
 def algorithmic(w, seq_lens):
@@ -47,8 +48,11 @@ def algorithmic(w, seq_lens):
     launch: the latent cache rows, the absorbed queries, the latent output
     and the LSE; 2 * rows * L * (d_c + d_h^R + d_c) flops per sequence."""
     D = w.d_latent + w.d_rope
-    esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
-    row_bytes = D * esz + (4 if w.kv_dtype == "fp8" else 0)
+    if w.kv_dtype == "fp6":
+        row_bytes = 452                  # 576 six-bit codes, 18 exponent bytes, 2 pad
+    else:
+        esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.kv_dtype]
+        row_bytes = D * esz + (4 if w.kv_dtype == "fp8" else 0)
     total_tokens = int(sum(seq_lens))
     q_bytes = w.batch * w.q_tokens * w.n_heads * D * (4 if w.q_dtype == "f32" else 2)
     out_bytes = w.batch * w.q_tokens * w.n_heads * (w.d_latent + 1) * 4
@@ -527,7 +531,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype in ("bf16", "fp8") else "f32",
+        "dtype": "bf16" if w.kv_dtype in ("bf16", "fp8", "fp6") else "f32",
         "data": "synthetic (seeded N(0,1) latent cache and queries, N(0,1/d_c) weights)",
         "config": {"workload": w.name, "batch": w.batch, "q_tokens": w.q_tokens,
                    "kv_len": w.kv_len or None, "n_heads": w.n_heads, "d_head": w.d_head,
@@ -556,6 +560,8 @@ def main():
             out["companion"] = side_line(COMPANION_WORKLOAD, args.steps)
         if w.name != LITE_WORKLOAD:
             out["v2lite"] = side_line(LITE_WORKLOAD, args.steps)
+        if w.name != FP6_WORKLOAD:
+            out["fp6_cache"] = side_line(FP6_WORKLOAD, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(t.w, t.gen, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -15,8 +15,9 @@ from typing import Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+F32, BF16, FP8_E4M3, FP6_E2M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp6": FP6_E2M3}
+FP6_ROW_BYTES = 452            # bytes per 6-bit cache row of 576 elements
 PREC_AUTO, PREC_FP32, PREC_BF16, PREC_BF16X2 = 0, 1, 2, 3
 PRECISION_CODES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16,
                    "bf16x2": PREC_BF16X2}

@@ -71,6 +71,11 @@ constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte chunks per thread (9)
 constexpr int RAW8 = 18944;              // fp8: raw tile (18 KB) at this offset of its slot
 constexpr int SCL8 = 37376;              // fp8: the tile's 32 token scales, end of the slot
 constexpr int NLD8 = TILE * D / 1024;    // fp8: 1 KB loads per raw tile (18)
+constexpr int ROW6 = 452;                // fp6: bytes per cache row (432 codes, 18 exponents, pad)
+constexpr int TILE6 = TILE * ROW6;       // fp6: raw tile (14464 bytes)
+constexpr int NLD6 = (TILE6 + 1023) / 1024;   // fp6: 1 KB loads per raw tile (15)
+constexpr int RAW6 = TILE_BYTES - NLD6 * 1024;  // fp6: raw tile at this offset of its slot
+constexpr int NBLK6 = TILE * D / 32;     // fp6: blocks of 32 elements per tile (576)
 constexpr int QROW = 592;                // LDS bytes per staged half query row (576 + 16 pad)
 constexpr int QLOADS = ROWS_WG * (QROW / 16) / 64;   // 1 KB loads per staged half (74)
 constexpr uint32_t kOOB = 0x40000000u;   // buffer offset past any valid range
@@ -187,9 +192,32 @@ __device__ inline uint32_t q_src_offset(int u, int half, int q_row_bytes) {
   return c == QROW / 16 - 1 ? kOOB : uint32_t(r * q_row_bytes + half * D + 16 * c);
 }
 
-template <bool FP8>
+// 32 E2M3 codes (6 dwords, code i at bits 6 i .. 6 i + 5) times 2^e -> 32
+// bf16 values, two per dword (even element in the low half).  Exact: every
+// E2M3 value times a power of two in range is a bf16 value.  The scale's
+// power-of-two part is what the instruction applies.
+__device__ inline void fp6x32_to_bf16x32(const uint32_t (&w)[6], float scale, u32x4 (&r)[4]) {
+  typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+  typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+  const u32x6 v = {w[0], w[1], w[2], w[3], w[4], w[5]};
+  u32x16 o;
+  // The conversion writes its 16 result registers over several cycles and
+  // a read issued right after it sees the old contents: 20 wait states
+  // separate it from the first use.
+  asm volatile("s_nop 1\n\tv_cvt_scalef32_pk32_bf16_fp6 %0, %1, %2\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3"
+               : "=&v"(o) : "v"(v), "v"(scale));
+  r[0] = u32x4{o[0], o[1], o[2], o[3]};
+  r[1] = u32x4{o[4], o[5], o[6], o[7]};
+  r[2] = u32x4{o[8], o[9], o[10], o[11]};
+  r[3] = u32x4{o[12], o[13], o[14], o[15]};
+}
+
+// KVK: cache kind, 0 = bf16, 1 = fp8 E4M3 with per-token scales, 2 = 6-bit
+// (E2M3 codes with one power of two per 32 elements).
+template <int KVK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
+  constexpr bool FP8 = KVK == 1, FP6 = KVK == 2, RAW = KVK != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float s_scale[NBUF][TILE];
   __shared__ int s_restart;
@@ -243,7 +271,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
 
   const uint8_t* cache = (const uint8_t*)a.cache;
-  constexpr int ROWB = FP8 ? D : 2 * D;                   // bytes per cache row
+  constexpr int ROWB = FP8 ? D : FP6 ? ROW6 : 2 * D;     // bytes per cache row
   const int seq_row0 = b * a.max_len;
   typedef __attribute__((address_space(4))) const int32_t* ConstI32;
   const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
@@ -278,6 +306,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const int qbase = 64 * wave + lane;
 #define MLA_VOFF(n_) tile_src_offset(qbase + 256 * (n_))
   u32x2 stg8[FP8 ? NSTG8 : 1];
+  uint32_t stg6[FP6 ? 2 : 1][7];                          // fp6: 6 code dwords + exponent byte
   const uint32_t lane16 = 16 * lane;                      // fp8: lane offset of raw loads
 
   // Issue the loads of the tile starting at token ts into ring slot buf.  A
@@ -302,7 +331,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ad__ >> 32)) & 0xFFFFu, \
                         (uint32_t)__builtin_amdgcn_readfirstlane(nv__ * ROWB),           \
                         0x00020000u};                                                    \
-    if constexpr (!FP8) {                                                                \
+    if constexpr (!RAW) {                                                                 \
       const uint32_t lb__ = lds_ring + (buf_) * TILE_BYTES + 1024 * wave;                \
       _Pragma("unroll") for (int n = 0; n < NLD - 1; ++n)                                \
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
@@ -311,6 +340,15 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
                      :: "s"(lds_ring + (buf_) * TILE_BYTES + 1024 * 36),                 \
                         "v"(MLA_VOFF(NLD - 1)), "s"(rs__) : "memory");                   \
+    } else if constexpr (FP6) {                                                          \
+      /* raw 6-bit rows (contiguous) into the slot's upper part; wave w issues */        \
+      /* loads w, w+4, ...; the tail of the last load is past the range (zeros) */      \
+      const uint32_t lb__ = lds_ring + (buf_) * TILE_BYTES + RAW6 + 1024 * wave;         \
+      _Pragma("unroll") for (int k = 0; k < (NLD6 + 3) / 4; ++k)                         \
+        if (wave + 4 * k < NLD6)                                                         \
+          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"     \
+                       :: "s"(lb__ + 4096 * k), "v"(lane16), "s"(rs__),                  \
+                          "s"(__builtin_amdgcn_readfirstlane(1024 * (wave + 4 * k))) : "memory"); \
     } else {                                                                             \
       /* raw fp8 rows (contiguous) into the slot's upper part; wave w issues */          \
       /* loads w, w+4, ...; wave 3 also the 32 token scales (128 bytes) */                \
@@ -349,6 +387,49 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     if (tid < TILE) {                                                                    \
       const float sc = *(const float*)(&s_kv[(buf_)][SCL8 + 4 * reg_token(tid & 15, tid >> 4)]); \
       s_scale[(buf_)][tid] = (sc == 0.f) ? 1.f : sc;                                     \
+    }                                                                                    \
+  } while (0)
+  // fp6: this thread's blocks q = tid, tid + 256 of the raw tile in slot buf
+  // (token q / 18, elements 32 (q % 18) ..): 6 code dwords and the exponent
+  // byte.  Blocks 512 .. 575 (tokens 28 .. 31) are wave 0's and are read in
+  // MLA_DECODE6 itself: their raw bytes lie past every bf16 row the other
+  // blocks write (rows 0 .. 28), and within wave 0 all reads precede all
+  // writes.
+#define MLA_READ_RAW6(buf_)                                                                \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                      \
+      const int q = tid + 256 * i;                                                       \
+      const int t = q / 18, k = q - 18 * (q / 18);                                       \
+      const uint8_t* src = &s_kv[(buf_)][RAW6 + ROW6 * t];                               \
+      _Pragma("unroll") for (int w = 0; w < 6; ++w)                                      \
+        stg6[i][w] = *(const uint32_t*)(src + 24 * k + 4 * w);                           \
+      stg6[i][6] = src[432 + k];                                                         \
+    }                                                                                    \
+  } while (0)
+  // fp6: decode the blocks into the slot's bf16 rows (the raw reads of
+  // blocks 0 .. 511 are done: a barrier separates the two); block (t, k) ->
+  // row t, dims 32 k ..
+#define MLA_DECODE6(buf_)                                                                  \
+  do {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < 3; ++i) {                                      \
+      const int q = tid + 256 * i;                                                       \
+      if (q < NBLK6) {                                                                   \
+        const int t = q / 18, k = q - 18 * (q / 18);                                     \
+        uint32_t cw[6], ex;                                                              \
+        if (i < 2) {                                                                     \
+          _Pragma("unroll") for (int w = 0; w < 6; ++w) cw[w] = stg6[i < 2 ? i : 0][w];  \
+          ex = stg6[i < 2 ? i : 0][6];                                                   \
+        } else {                                                                         \
+          const uint8_t* src = &s_kv[(buf_)][RAW6 + ROW6 * t];                           \
+          _Pragma("unroll") for (int w = 0; w < 6; ++w)                                  \
+            cw[w] = *(const uint32_t*)(src + 24 * k + 4 * w);                            \
+          ex = src[432 + k];                                                             \
+        }                                                                                \
+        u32x4 r[4];                                                                      \
+        fp6x32_to_bf16x32(cw, __builtin_bit_cast(float, ex << 23), r);                   \
+        uint8_t* dst = &s_kv[(buf_)][t * LROW + 64 * k];                                 \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) *(u32x4*)(dst + 16 * u) = r[u];   \
+      }                                                                                  \
     }                                                                                    \
   } while (0)
   // bf16: wait until at most one tile's loads of this wave are in flight
@@ -436,12 +517,18 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
         __syncthreads();                                                                 \
         MLA_DECODE8(0);                                                                  \
       }                                                                                  \
+    } else if constexpr (FP6) {                                                          \
+      if (ntiles > 0) {                                                                  \
+        MLA_READ_RAW6(0);                                                                \
+        __syncthreads();                                                                 \
+        MLA_DECODE6(0);                                                                  \
+      }                                                                                  \
     }                                                                                    \
   } while (0)
 #define MLA_PROLOGUE()                                                                     \
   do {                                                                                   \
     MLA_ISSUE_FIRST_TILES();                                                             \
-    if constexpr (FP8) {                                                                 \
+    if constexpr (RAW) {                                                                 \
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                   \
       __syncthreads();                                                                   \
     }                                                                                    \
@@ -458,9 +545,11 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     const int nt = min(ntiles, 2);
     if (nt == 2) {
       if constexpr (FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (FP6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     } else if (nt == 1) {
       if constexpr (FP8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (FP6) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -484,7 +573,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
     l_run = 0.f;
     int restart = 0;
-    if constexpr (!FP8) {
+    if constexpr (!RAW) {
       // Step it: scores of tile it; the PV product of tile it-1 with the
       // softmax of tile it interleaved (one assembly block); the loads of
       // tile it+2 spread through both blocks; wait for tile it+1.  Ring
@@ -574,6 +663,74 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           MLA_WAIT_ONE_TILE_IN_FLIGHT();     // tile it+1 landed (it+2 may fly)
           __syncthreads();
           restart = __builtin_amdgcn_readfirstlane(s_restart | s_escalate);   // uniform: after the barrier
+          if (restart) break;
+        }
+        if (!restart) {
+          put_p(s_p, wave, lane, pk_prev);
+          __syncthreads();
+          pvd_tile(s_kv[(ntiles - 1) & 3] + pv_off, s_p + 16 * lane, o);
+        }
+      }
+    } else if constexpr (FP6) {
+      // The step of the fp8 path with 6-bit tiles: raw tile it+1 (copied
+      // during step it-1) is read after the scores of step it and decoded in
+      // place after its first barrier (each block of 32 codes with its power
+      // of two, exact in bf16), while tile it+2 is copied.  No per-token
+      // scale: the softmax is the bf16 one.
+      if (ntiles > 0) {
+        __syncthreads();
+        uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        for (int it = 0; it < ntiles; ++it) {
+          const int ts = t0 + it * TILE;
+          MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
+          put_p(s_p, wave, lane, pk_prev);   // weights of tile it-1 (zero at step 0)
+          const floatx16 s_cur = qk_tile(s_kv[it & 3] + qk_off, qf);
+          MLA_READ_RAW6((it + 1) & 3);       // after the scores: no staging registers in them
+          __syncthreads();                   // weights of tile it-1 in; raw tile it+1 read
+          MLA_DECODE6((it + 1) & 3);
+          float sv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
+          if (ts + TILE - 1 > lim) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (ts + reg_token(r, h) > lim) sv[r] = kNegInf;
+          }
+          float mt;
+          if (m_ref == kNegInf) {
+            float tmp0;
+            asm volatile(MLA_ASM_SOFTMAX_MAX
+                         : "=&v"(mt), "=&v"(tmp0)
+                         : "v"(sv[0]), "v"(sv[1]), "v"(sv[2]), "v"(sv[3]), "v"(sv[4]),
+                           "v"(sv[5]), "v"(sv[6]), "v"(sv[7]), "v"(sv[8]), "v"(sv[9]),
+                           "v"(sv[10]), "v"(sv[11]), "v"(sv[12]), "v"(sv[13]), "v"(sv[14]),
+                           "v"(sv[15]), "v"(a.scale_log2));
+            m_ref = mt;                          // O and l are still zero here
+          }
+          const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
+          const uint32_t vb = (uint32_t)(uintptr_t)(s_kv[(it > 0 ? it - 1 : 0) & 3] + pv_off);
+          const uint32_t pb = (uint32_t)(uintptr_t)(s_p + 16 * lane);
+          uint32_t pk[8];
+          float tmp;
+          asm volatile(MLA_ASM_PVD_SOFTMAX_TILE
+                       : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
+                         "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
+                         "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
+                         "+a"(o[15]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3]),
+                         "+v"(sv[4]), "+v"(sv[5]), "+v"(sv[6]), "+v"(sv[7]), "+v"(sv[8]),
+                         "+v"(sv[9]), "+v"(sv[10]), "+v"(sv[11]), "+v"(sv[12]), "+v"(sv[13]),
+                         "+v"(sv[14]), "+v"(sv[15]), "=&v"(pk[0]), "=&v"(pk[1]), "=&v"(pk[2]),
+                         "=&v"(pk[3]), "=&v"(pk[4]), "=&v"(pk[5]), "=&v"(pk[6]), "=&v"(pk[7]),
+                         "=&v"(mt), "=&v"(tmp), "+v"(l_run)
+                       : "v"(vb), "v"(pb), "v"(neg_m), "v"(a.scale_log2)
+                       : "memory", MLA_ASM_PVD_CLOBBERS);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pk_prev[i] = pk[i];
+          m_seen = fmaxf(m_seen, mt);
+          if (mt > m_ref + 64.0f) s_restart = 1;
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // raw tile it+2 landed
+          __syncthreads();
+          restart = __builtin_amdgcn_readfirstlane(s_restart);   // uniform: read after the barrier
           if (restart) break;
         }
         if (!restart) {
@@ -676,6 +833,8 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #undef MLA_DECODE_FIRST_TILE
 #undef MLA_READ_RAW8
 #undef MLA_DECODE8
+#undef MLA_READ_RAW6
+#undef MLA_DECODE6
 #undef MLA_WAIT_ONE_TILE_IN_FLIGHT
 #undef MLA_TILE_RSRC
 #undef MLA_VOFF
@@ -766,9 +925,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const ItemTable& tab, hipStre
   // a.row_blocks counts blocks of ROWS_WG query rows
   const int grid = a.n_items * a.row_blocks;
   if (a.kv_dtype == MLA_FP8_E4M3)
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(grid), dim3(256), 0, st, a, tab);
+    hipLaunchKernelGGL(decode_mfma_kernel<1>, dim3(grid), dim3(256), 0, st, a, tab);
+  else if (a.kv_dtype == MLA_FP6_E2M3)
+    hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3(grid), dim3(256), 0, st, a, tab);
+    hipLaunchKernelGGL(decode_mfma_kernel<0>, dim3(grid), dim3(256), 0, st, a, tab);
   return hipGetLastError();
 }
 

@@ -258,6 +258,7 @@ if __name__ == "__main__":
     txt.append(f"#define MLA_ASM_QK_CLOBBERS {clobbers(QK_TMP, 32)}\n")
     txt.append(emit("MLA_ASM_PVD_TILE", pvd()))
     txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_DMA", pvd(True, True)))
+    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE", pvd(True, False, False)))
     txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_FP8", pvd(True, False, True)))
     txt.append(f"#define MLA_ASM_PVD_CLOBBERS {clobbers(PVD_VBUF, 256 - PVD_VBUF)}\n")
     txt.append(f"#define MLA_ASM_PVD_FP8_CLOBBERS {clobbers(212, 44)}\n")

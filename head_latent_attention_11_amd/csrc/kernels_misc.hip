@@ -328,6 +328,31 @@ __global__ __launch_bounds__(256) void append_kernel(
       uint16_t* dst = (uint16_t*)cache + row * D;
 #pragma unroll
       for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = f32_to_bf16_bits(v[k]);
+    } else if (KV == MLA_FP6_E2M3) {
+      // D = 576: element lane + 64 k is element lane % 32 of block 2 k +
+      // lane / 32, so each block is one half-wave at one k
+      uint8_t* dst = (uint8_t*)cache + row * kMxRowBytes;
+      const int i = lane & 31;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        float am = fabsf(v[k]);
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+        const int ex = mx_block_exponent(am);
+        const uint32_t c = f32_to_e2m3(ldexpf(v[k], -ex));   // exact scaling
+        const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64);
+        const uint32_t c3 = __shfl_down(c, 3, 64);
+        const int blk = 2 * k + (lane >> 5);
+        if ((i & 3) == 0) {                  // codes i .. i+3: 24 bits, 3 bytes
+          const uint32_t w = c | (c1 << 6) | (c2 << 12) | (c3 << 18);
+          uint8_t* p = dst + 24 * blk + 3 * (i >> 2);
+          p[0] = uint8_t(w);
+          p[1] = uint8_t(w >> 8);
+          p[2] = uint8_t(w >> 16);
+        }
+        if (i == 0) dst[432 + blk] = uint8_t(ex + 127);
+      }
+      if (lane == 0) { dst[450] = 0; dst[451] = 0; }
     } else {
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -668,6 +693,8 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
   if (d.kv_dtype == MLA_F32) MLA_APPEND(float, MLA_F32);
   else if (d.kv_dtype == MLA_BF16 && !src_f32) MLA_APPEND(uint16_t, MLA_BF16);
   else if (d.kv_dtype == MLA_BF16) MLA_APPEND(float, MLA_BF16);
+  else if (d.kv_dtype == MLA_FP6_E2M3 && !src_f32) MLA_APPEND(uint16_t, MLA_FP6_E2M3);
+  else if (d.kv_dtype == MLA_FP6_E2M3) MLA_APPEND(float, MLA_FP6_E2M3);
   else if (!src_f32) MLA_APPEND(uint16_t, MLA_FP8_E4M3);
   else MLA_APPEND(float, MLA_FP8_E4M3);
 #undef MLA_APPEND

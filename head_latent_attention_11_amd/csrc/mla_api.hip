@@ -50,7 +50,8 @@ int32_t check_dims(const mla_dims_t* d) {
   if (d->d_rope < 0 || d->d_rope > 128 || (d->d_rope & 1)) return MLA_ERR_DIMS;
   if (d->page_size != kPage) return MLA_ERR_DIMS;
   if (d->q_dtype != MLA_F32 && d->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  if (d->kv_dtype != MLA_F32 && d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3)
+  if (d->kv_dtype != MLA_F32 && d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3 &&
+      d->kv_dtype != MLA_FP6_E2M3)
     return MLA_ERR_DTYPE;
   if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return MLA_ERR_ARG;
   if (!(d->rope_base >= 0.f) || !isfinite(d->rope_base)) return MLA_ERR_ARG;
@@ -74,8 +75,9 @@ bool fast_shape(const mla_dims_t* d) {
 // Attention in blocks of 128 rows: 32 heads of one query token per wave.
 bool fast_decode(const mla_dims_t* d, int T) {
   return fast_shape(d) && d->precision != MLA_PREC_FP32 &&
-         (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3) && d->n_heads % 32 == 0 &&
-         ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
+         (d->kv_dtype == MLA_BF16 || d->kv_dtype == MLA_FP8_E4M3 ||
+          d->kv_dtype == MLA_FP6_E2M3) &&
+         d->n_heads % 32 == 0 && ((int64_t)d->n_heads * T) % kRowsPerWorkgroup == 0;
 }
 
 // Attention in blocks of 16 or 32 rows (16 heads of one query token per
@@ -176,6 +178,7 @@ int32_t make_plan(const mla_dims_t* d, const int32_t* lens, int B, int T,
   if (B < 1 || T < 1 || T > 1024) return MLA_ERR_ARG;
   if (num_splits < 0 || num_splits > 4096) return MLA_ERR_ARG;
   if (x2_only(d) && !x2_supported(d)) return MLA_ERR_UNSUPPORTED;
+  if (d->kv_dtype == MLA_FP6_E2M3 && !fast_decode(d, T)) return MLA_ERR_UNSUPPORTED;
   const int small = small_decode_rows(d, T);
   const bool fast = fast_decode(d, T) || small > 0;   // matrix-core kernels
   const int64_t rows = (int64_t)d->n_heads * T;
@@ -307,6 +310,8 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* 
   } else if (kv_scale) {
     return MLA_ERR_ARG;
   }
+  if (dims->kv_dtype == MLA_FP6_E2M3 && dims->d_latent + dims->d_rope != 576)
+    return MLA_ERR_UNSUPPORTED;
   if (n_rows < 1 || batch < 1 || cache_rows < 1) return MLA_ERR_ARG;
   if (apply_rope != 0 && apply_rope != 1) return MLA_ERR_ARG;
   if (page_table) {
@@ -336,6 +341,8 @@ static int32_t check_append(const mla_dims_t* dims, const int32_t* seq_idx, cons
   } else if (kv_scale) {
     return MLA_ERR_ARG;
   }
+  if (dims->kv_dtype == MLA_FP6_E2M3 && dims->d_latent + dims->d_rope != 576)
+    return MLA_ERR_UNSUPPORTED;
   if (n_rows < 1 || batch < 1 || cache_rows < 1) return MLA_ERR_ARG;
   if (apply_rope != 0 && apply_rope != 1) return MLA_ERR_ARG;
   if (page_table) {

@@ -80,6 +80,40 @@ __host__ __device__ inline uint32_t f32_to_e4m3(float x) {
   return code | sign;
 }
 
+// float -> nearest E2M3 code (ties to the even code), magnitudes from 7.5
+// up saturating to 7.5; the sign bit of x becomes bit 5.  |x| < 8 in use.
+__host__ __device__ inline uint32_t f32_to_e2m3(float x) {
+  union { uint32_t u; float f; } v;
+  v.f = x;
+  const uint32_t sign = (v.u >> 26) & 0x20u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 7.5f)) {
+    code = 0x1F;
+  } else if (a < 1.0f) {                     // subnormal grid m/8 (m = 8 is 1.0)
+    code = uint32_t(rintf(a * 8.0f));
+  } else {
+    union { uint32_t u; float f; } w;
+    w.f = a;
+    const int E = int((w.u >> 23) & 0xFF) - 127;   // 0, 1 or 2
+    uint32_t e = uint32_t(E + 1);
+    uint32_t q = uint32_t(rintf((ldexpf(a, -E) - 1.0f) * 8.0f));
+    if (q == 8) { q = 0; ++e; }
+    code = (e << 3) | q;                     // a < 7.5 keeps this <= 0x1F
+  }
+  return code | sign;
+}
+
+// Shared exponent of a block of 32 elements of the 6-bit cache:
+// floor(log2 amax) - 2 kept in [-126, 127] (-126 for amax = 0).
+__host__ __device__ inline int mx_block_exponent(float amax) {
+  union { uint32_t u; float f; } v;
+  v.f = amax;
+  const int e = int((v.u >> 23) & 0xFF) - 127 - 2;
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+constexpr int kMxRowBytes = 452;     // 6-bit cache row: 432 code bytes, 18 exponents, 2 pad
+
 // ------------------------------------------------------------------ RoPE
 // Frequencies of the interleaved pairs (2k, 2k+1): theta_k = base^(-2k/d),
 // and with context extension (factor > 1, YaRN's NTK-by-parts rule) pair k,

@@ -85,6 +85,12 @@ class DecodeBuffers:
                 if poison:
                     cache.fill_(0x7F)                       # E4M3 NaN
                     scale.fill_(float("nan"))
+            elif w.kv_dtype == "fp6":
+                cache = torch.empty((self.cache_rows, B.FP6_ROW_BYTES), dtype=torch.uint8,
+                                    device=dev)
+                scale = None
+                if poison:
+                    cache.fill_(0xFF)                       # exponent byte 255: infinite scale
             else:
                 cache = torch.empty((self.cache_rows, D), dtype=_TORCH_STORE[w.kv_dtype], device=dev)
                 scale = None

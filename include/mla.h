@@ -66,7 +66,10 @@ typedef enum mla_status {
 typedef enum mla_dtype {
   MLA_F32 = 0,      /* IEEE binary32 */
   MLA_BF16 = 1,     /* bfloat16 */
-  MLA_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("e4m3fn", max 448), KV cache only */
+  MLA_FP8_E4M3 = 2, /* OCP FP8 E4M3 ("e4m3fn", max 448), KV cache only */
+  MLA_FP6_E2M3 = 3  /* 6-bit cache (KV cache only, d_c + d_h^R = 576): OCP
+                       microscaling FP6 E2M3 codes (max 7.5) with one E8M0
+                       power of two per 32 elements, see mla_cache_append */
 } mla_dtype_t;
 
 /* Problem dimensions and number formats (a plain value struct). */
@@ -76,7 +79,8 @@ typedef struct mla_dims {
   int32_t d_latent;    /* d_c   (KV compression dim) */
   int32_t d_rope;      /* d_h^R (decoupled RoPE dim, even) */
   int32_t page_size;   /* tokens per page of a paged cache; must be 64 */
-  int32_t kv_dtype;    /* cache format: MLA_F32, MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t kv_dtype;    /* cache format: MLA_F32, MLA_BF16, MLA_FP8_E4M3 or
+                          MLA_FP6_E2M3 */
   int32_t q_dtype;     /* format of queries, weights, q_abs and o:
                           MLA_F32 or MLA_BF16 */
   float softmax_scale; /* 0 -> 1/sqrt(d_head + d_rope) */
@@ -142,6 +146,8 @@ typedef enum mla_precision {
  *           operands in blocks of 64 rows, BF16 cache), or
  *         n_h % 16 == 0 otherwise, kv_dtype = BF16 or FP8_E4M3 (blocks of 16 or 32
  *           rows: e.g. DeepSeek-V2-Lite, 16 heads, T = 1..4);
+ *       kv_dtype = FP6_E2M3: the 128-row blocks only (MLA_ERR_UNSUPPORTED
+ *       for other shapes and for MLA_PREC_FP32 / MLA_PREC_BF16X2);
  *   general path: any n_h >= 1, d_h <= 256, d_c <= 512 (a multiple of 4),
  *       d_h^R <= 128 (even),
  *       every q_dtype / kv_dtype combination (e.g. the all-fp32 problems).
@@ -194,7 +200,19 @@ int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope,
  * kv_dtype FP8_E4M3: per row, s = amax|row| / 448 (float32, s = 1 if the row
  * is zero); each element stores the E4M3 code nearest to x / s (ties to
  * even, saturating at 448); kv_scale[row] = s.  kv_scale must be NULL for
- * other formats.                                                          */
+ * other formats.
+ *
+ * kv_dtype FP6_E2M3 (the ~6-bit cache of "DeepSeek-V2", section 3.2.3,
+ * training and inference efficiency, whose scheme the page leaves open):
+ * each cache row is 452 bytes.  Elements are taken in blocks of 32 (18
+ * blocks of the 576); block k has the shared exponent e_k = floor(log2
+ * amax_k) - 2 kept in [-126, 127] (-126 for an all-zero block), so amax_k /
+ * 2^e_k lies in [4, 8), and each element stores the E2M3 code nearest to
+ * x / 2^e_k (ties to the even code, saturating at 7.5; sign = the sign bit
+ * of x).  Bytes 24k .. 24k+23 hold block k's 32 codes, code i at bits
+ * 6i .. 6i+5 of those bytes read as one little-endian integer; byte 432 + k
+ * holds e_k + 127; bytes 450 and 451 are zero.  A stored element is
+ * decode(code) * 2^e_k: 6.25 bits per element with the exponents.        */
 int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c,
                          const void* new_kr, const int32_t* seq_idx,
                          const int32_t* pos, const int32_t* page_table,

@@ -315,3 +315,21 @@ def test_noalloc_rejects_plans_beyond_its_array(mla):
     assert lib.mla_decode_attn_noalloc(ctypes.byref(d), None, FAKE, None, None, 0, 65536, FAKE,
                                        ctypes.cast(arr, ctypes.c_void_p), len(lens), 1, 64,
                                        FAKE, FAKE, None) == NULL
+
+
+def test_six_bit_cache_validation(mla):
+    """The 6-bit cache: 128-row attention blocks only, rows of 576 elements,
+    no per-row scale array."""
+    lib, b = mla
+    fp6 = _v2(b, kv_dtype="fp6")
+    assert fp6.kv_dtype == 3
+    st, n = _ws(lib, fp6, [8192] * 64, T=4)                  # unsplit, no flags
+    assert st == OK and n == 0
+    assert _decode(lib, b, _v2(b, n_heads=16, kv_dtype="fp6"), [100]) == UNSUP
+    assert _decode(lib, b, _v2(b, kv_dtype="fp6", precision="fp32"), [100]) == UNSUP
+    assert _decode(lib, b, _v2(b, kv_dtype="fp6", precision="bf16x2"), [100]) == UNSUP
+    one = (ctypes.c_int32 * 1)(0)
+    ap = lambda d, scale: lib.mla_cache_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 1, 0,
+                                               64, 64, 0, FAKE, scale, 1, None)
+    assert ap(fp6, FAKE) == ARG                                # no scale array
+    assert ap(b.MLADims.make(128, 128, 256, 64, kv_dtype="fp6"), None) == UNSUP   # D != 576

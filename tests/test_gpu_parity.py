@@ -40,7 +40,9 @@ def _buffers(w, gen, **kw):
 
 
 def _gates(w):
-    return (REL_L2_FP8, None) if w.kv_dtype == "fp8" else (REL_L2_BF16, MAX_ABS_BF16)
+    # quantised caches (fp8, 6-bit): the rel-L2 gate of the fp8 cache, against
+    # the oracle on the dequantised cache
+    return (REL_L2_FP8, None) if w.kv_dtype in ("fp8", "fp6") else (REL_L2_BF16, MAX_ABS_BF16)
 
 
 def _run_compare(w, gen=None, seqs=None, heads=None, num_splits=None, precision="auto",
@@ -143,6 +145,15 @@ SMALL = [
                   kv_len=0, lengths=(520, 100, 4), kv_dtype="fp8", layout="paged"),
     small_variant(V2, name="n32_fp8_t1", batch=3, n_heads=32, kv_len=0, lengths=(333, 65, 1000),
                   kv_dtype="fp8"),
+    # the 6-bit cache (E2M3 codes, one power of two per 32 elements)
+    small_variant(V2, name="fp6_t1_ragged", batch=4, kv_len=0, lengths=(1, 33, 700, 64),
+                  kv_dtype="fp6"),
+    small_variant(V2, name="fp6_t4_split3", batch=4, q_tokens=4, kv_len=0,
+                  lengths=(300, 77, 4, 130), kv_dtype="fp6", num_splits=3),
+    small_variant(V2, name="fp6_t1_paged", batch=3, kv_len=0, lengths=(100, 520, 31),
+                  kv_dtype="fp6", layout="paged"),
+    small_variant(V2, name="fp6_t2_rope_yarn", batch=2, q_tokens=2, kv_len=0,
+                  lengths=(4600, 900), kv_dtype="fp6", rope=True, yarn_factor=40.0),
     small_variant(V2, name="general_n8_fp8", batch=2, n_heads=8, kv_len=0, lengths=(50, 300),
                   kv_dtype="fp8"),
     small_variant(WORKLOADS["tiny_fp32"], name="tiny_fp32_bf16cache", kv_dtype="bf16",
@@ -223,6 +234,7 @@ FULL = [
     (WORKLOADS["v2_b32_l4k_bf16"], [0, 4, 9, 13, 17, 22, 26, 31], _H16),
     (WORKLOADS["v2_b64_l8k_bf16"], [0, 5, 14, 23, 32, 41, 50, 63], _H16),
     (WORKLOADS["v2_fp8_t4_b64_l8k"], [0, 9, 18, 27, 36, 45, 54, 63], _H16),
+    (WORKLOADS["v2_fp6_t4_b64_l8k"], [0, 9, 18, 27, 36, 45, 54, 63], _H16),
     (WORKLOADS["v2_long_b4_l128k_bf16"], [0, 1, 2, 3], [0, 8, 16, 24, 40, 56, 64, 72, 77, 88,
                                                         96, 104, 112, 120, 127, 33]),
     (WORKLOADS["v2lite_b64_l8k_bf16"], [0, 9, 18, 27, 31, 45, 54, 63], list(range(16))),
@@ -378,7 +390,7 @@ def test_reference_restart_on_large_score_jump():
 
 # --------------------------------------------------- append, bit exact
 @pytest.mark.parametrize("layout", ["contiguous", "paged"])
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp6", "f32"])
 def test_cache_append_bit_exact(layout, kv):
     w = small_variant(V2, name=f"append_{kv}_{layout}", batch=3, kv_len=0,
                       lengths=(65, 200, 3), layout=layout, kv_dtype=kv,
@@ -395,6 +407,10 @@ def test_cache_append_bit_exact(layout, kv):
         got = cache.numpy()[rows]
         assert np.array_equal(got, d["fp8_codes"])
         assert np.array_equal(buf.kv_scale.cpu().numpy()[rows], d["fp8_scales"])
+    elif kv == "fp6":
+        d = omla.logical_inputs(gen, w)
+        got = cache.numpy()[rows]
+        assert np.array_equal(got, formats.pack_rows_mxfp6(d["fp6_codes"], d["fp6_exps"]))
     elif kv == "bf16":
         got = cache.view(torch.int16).numpy().view(np.uint16)[rows]
         assert np.array_equal(got, np.concatenate([gen["c_kv"], gen["k_r"]], 1))
@@ -407,6 +423,8 @@ def test_cache_append_bit_exact(layout, kv):
     rest = cache.numpy()[~written] if kv != "bf16" else cache.float().numpy()[~written]
     if kv == "fp8":
         assert np.all(rest == 0x7F)
+    elif kv == "fp6":
+        assert np.all(rest == 0xFF)
     else:
         assert np.all(np.isnan(rest))
 
@@ -450,6 +468,38 @@ def test_fp8_every_code_decodes_exactly(n_heads):
     torch.cuda.synchronize()
     lat = to_np(buf.latent)                       # [2, n_h, 512]
     exp = formats.e4m3_to_f64(row[:, :512])
+    for b in range(2):
+        assert np.array_equal(lat[b], np.broadcast_to(exp[b], lat[b].shape)), b
+
+
+def test_fp6_every_code_decodes_exactly():
+    """L = 1: the latent output is the stored row itself.  Rows built from
+    all 64 E2M3 codes under block exponents from -20 to +20 (18 blocks a
+    row) must come back as their exact values.  The query is zero, so every
+    score is 0 and the weight exactly 1 (with rows this large a nonzero
+    query gives scores near 1e8, where the weight 2^(s - max) is 1 only to
+    within the rounding of s)."""
+    from head_latent_attention_11_amd.runner import DecodeBuffers
+    w = small_variant(V2, name="codes6", batch=2, kv_len=0, lengths=(1, 1), kv_dtype="fp6")
+    gen = generate(w)
+    buf = DecodeBuffers(w, gen)
+    codes = np.zeros((2, 576), dtype=np.uint8)
+    codes[0] = np.arange(576) % 64
+    codes[1] = (63 - np.arange(576)) % 64
+    exps = np.zeros((2, 18), dtype=np.int32)
+    exps[0] = np.arange(18) - 9
+    exps[1] = np.linspace(-20, 20, 18).astype(np.int32)
+    row = formats.pack_rows_mxfp6(codes, exps)
+    rows = omla.cache_row_index(np.array([0, 1]), np.array([0, 0]), None, 64, buf.max_len)
+    for r in range(2):
+        buf.cache[int(rows[r])] = torch.from_numpy(row[r]).cuda()
+    buf.q_nope.zero_()
+    buf.q_rope.zero_()
+    buf.absorb()                      # no append: the cache holds the rows written above
+    buf.attend()
+    torch.cuda.synchronize()
+    lat = to_np(buf.latent)
+    exp = formats.dequantize_rows_mxfp6(codes, exps)[:, :512]
     for b in range(2):
         assert np.array_equal(lat[b], np.broadcast_to(exp[b], lat[b].shape)), b
 
