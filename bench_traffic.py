@@ -17,7 +17,7 @@ then, anywhere:
 FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch.  Each is scaled by the
 factor that makes the copy kernel's reading equal its true size (copy bytes
 read, resp. written), and the attention call's traffic is the sum over its
-kernels (decode_mfma_kernel or decode_general_kernel, and combine_kernel).
+kernels (the decode kernels the plan launched, and combine_kernel).
 Writes profiles/decode_traffic.json (read by bench.py, which uses it only
 when the workload and the kernel sources match) and a short summary.
 """
@@ -31,7 +31,8 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-ATTN_KERNELS = ("decode_mfma_kernel", "decode_general_kernel", "combine_kernel")
+ATTN_KERNELS = ("decode_mfma_kernel", "decode_small_kernel", "decode_x2_kernel",
+                "decode_general_kernel", "combine_kernel")
 COPY_KERNEL = "copyBuffer"
 
 
