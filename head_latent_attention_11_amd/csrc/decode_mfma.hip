@@ -28,11 +28,10 @@
 //     bf16 tiles move HBM -> LDS with buffer loads that write LDS directly
 //     (no VGPR staging); a load range that ends at the last valid token makes
 //     the hardware write zeros for masked tokens, so they enter the PV
-//     product as exact zeros.  Raw fp8 tiles are copied the same way into
-//     the upper half of their slot and decoded in place to bf16 (exact: every
-//     E4M3 value is a bf16 value) one step before they are used; the
-//     per-token scale multiplies the score and the PV weight, so the fp8
-//     values enter the bf16 MFMA exactly.
+//     product as exact zeros.  Raw 6-bit tiles are copied the same way into
+//     the upper part of their slot and decoded in place to bf16 (exact) one
+//     step before they are used.  fp8 tiles have a kernel of their own
+//     (decode_fp8.hip) that converts its operands in registers.
 //   * S^T = K Q^T (v_mfma_f32_32x32x16_bf16) puts one row's 16 token scores
 //     in each lane: the per-row max and sum need no cross-lane reduction
 //     except with the partner lane (lane ^ 32).  The packed weights are then
@@ -52,6 +51,7 @@
 //     The result is exact for any reference: LSE = m_ref + log2(sum p).
 #include <math.h>
 
+#include "decode_tile.hpp"
 #include "mla_common.hpp"
 #include "plan_device.hpp"
 
@@ -67,10 +67,6 @@ constexpr int NLOADS = 37;               // direct loads of 64 x 16 B per tile
 constexpr int TILE_BYTES = NLOADS * 1024;
 constexpr int NLD = 10;                  // loads per wave per tile (wave 0: 10, others: 9)
 constexpr int NCH = 72;                  // 16-byte chunks per bf16 row
-constexpr int NSTG8 = TILE * NCH / 256;  // fp8: 8-byte chunks per thread (9)
-constexpr int RAW8 = 18944;              // fp8: raw tile (18 KB) at this offset of its slot
-constexpr int SCL8 = 37376;              // fp8: the tile's 32 token scales, end of the slot
-constexpr int NLD8 = TILE * D / 1024;    // fp8: 1 KB loads per raw tile (18)
 constexpr int ROW6 = 452;                // fp6: bytes per cache row (432 codes, 18 exponents, pad)
 constexpr int TILE6 = TILE * ROW6;       // fp6: raw tile (14464 bytes)
 constexpr int NLD6 = (TILE6 + 1023) / 1024;   // fp6: 1 KB loads per raw tile (15)
@@ -98,16 +94,6 @@ __device__ inline float pair_max32(float x) {
   float lo = x, hi = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
   return fmaxf(lo, hi);
-}
-
-// 8 E4M3 codes -> 8 bf16 values (exact: every E4M3 value is a bf16 value).
-__device__ inline u32x4 fp8x8_to_bf16x8(u32x2 v) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
-  return r;
 }
 
 // One tile's S^T[token, head] for the wave's 32 heads (36 MFMAs over the
@@ -156,20 +142,11 @@ __device__ __forceinline__ void put_p(uint8_t* s_p, int wave, int lane, const ui
   *(u32x4*)(d + 1024) = u32x4{pk[4], pk[5], pk[6], pk[7]};
 }
 
-// Score-row order inside a tile.  MFMA row m of the scores (the K operand
-// row read by lane m % 32) is tile row tile_row(m) = 16 (m/16) + (m/4)%4 +
-// 4 (m%4).  The transposed PV reads of a half-wave then cover four tile rows
-// p, p+4, p+8, p+12 (64 bytes each), which at the 1168-byte row pitch fall
-// in four disjoint quarters of the 64 LDS banks; the score-operand reads of
-// 16 lanes still cover 16 rows of distinct residues mod 16 (distinct bank
-// groups).  Score register r of a lane in half h (row m = 8(r/4) + 4h +
-// r%4) holds token tile_row(m).
-__device__ __forceinline__ int tile_row(int m) {
-  return 16 * (m >> 4) + ((m >> 2) & 3) + 4 * (m & 3);
-}
-__device__ __forceinline__ int reg_token(int r, int h) {
-  return tile_row(8 * (r >> 2) + 4 * h + (r & 3));
-}
+// Score-row order inside a tile: tile_row(m) (decode_tile.hpp).  The
+// transposed PV reads of a half-wave cover four tile rows p, p+4, p+8, p+12
+// (64 bytes each), which at the 1168-byte row pitch fall in four disjoint
+// quarters of the 64 LDS banks; the score-operand reads of 16 lanes cover 16
+// rows of distinct residues mod 16 (distinct bank groups).
 
 // LDS source offset mapping of a tile (rows at a pitch of 73 granules of 16
 // bytes): granule u of the slot holds granule u % 73 of token row u / 73,
@@ -212,14 +189,14 @@ __device__ inline void fp6x32_to_bf16x32(const uint32_t (&w)[6], float scale, u3
   r[3] = u32x4{o[12], o[13], o[14], o[15]};
 }
 
-// KVK: cache kind, 0 = bf16, 1 = fp8 E4M3 with per-token scales, 2 = 6-bit
-// (E2M3 codes with one power of two per 32 elements).
+// KVK: cache kind, 0 = bf16, 2 = 6-bit (E2M3 codes with one power of two
+// per 32 elements).
 template <int KVK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
-  constexpr bool FP8 = KVK == 1, FP6 = KVK == 2, RAW = KVK != 0;
+  static_assert(KVK == 0 || KVK == 2, "fp8 tiles run on decode_fp8_kernel");
+  constexpr bool FP6 = KVK == 2, RAW = KVK != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_scale[NBUF][TILE];
   __shared__ int s_restart;
   __shared__ int s_escalate;
   __shared__ __attribute__((aligned(16))) uint8_t s_p[4 * 2 * 1024];   // P^T fragments
@@ -271,7 +248,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
 
   const uint8_t* cache = (const uint8_t*)a.cache;
-  constexpr int ROWB = FP8 ? D : FP6 ? ROW6 : 2 * D;     // bytes per cache row
+  constexpr int ROWB = FP6 ? ROW6 : 2 * D;               // bytes per cache row
   const int seq_row0 = b * a.max_len;
   typedef __attribute__((address_space(4))) const int32_t* ConstI32;
   const ConstI32 ptab = a.page_table ? (ConstI32)(a.page_table + (size_t)b * a.max_pages) : nullptr;
@@ -298,16 +275,13 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   // chunk q % 73 of its row (chunk 72 is the row padding, filled with zero
   // by an out-of-range offset).  Load n of wave w fills chunks
   // 64 (w + 4n) .. +63; the last (37th) load of a tile belongs to wave 0.
-  // fp8: 8-byte chunk ci = tid + 256 i of the tile goes to LDS bytes
-  // 16 ci + 16 (ci / 72) as 8 bf16.
   // LDS chunk q = 64 (w + 4n) + lane  <-  memory chunk q - q/73 of the tile
   // (q/73 = (449 q) >> 15 for q < 2368); the padding chunk of each row and
   // chunks past the tile take an out-of-range offset.
   const int qbase = 64 * wave + lane;
 #define MLA_VOFF(n_) tile_src_offset(qbase + 256 * (n_))
-  u32x2 stg8[FP8 ? NSTG8 : 1];
   uint32_t stg6[FP6 ? 2 : 1][7];                          // fp6: 6 code dwords + exponent byte
-  const uint32_t lane16 = 16 * lane;                      // fp8: lane offset of raw loads
+  const uint32_t lane16 = 16 * lane;                      // fp6: lane offset of raw loads
 
   // Issue the loads of the tile starting at token ts into ring slot buf.  A
   // tile never crosses a page (ts is a multiple of 32, pages hold 64 tokens).
@@ -349,44 +323,6 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"     \
                        :: "s"(lb__ + 4096 * k), "v"(lane16), "s"(rs__),                  \
                           "s"(__builtin_amdgcn_readfirstlane(1024 * (wave + 4 * k))) : "memory"); \
-    } else {                                                                             \
-      /* raw fp8 rows (contiguous) into the slot's upper part; wave w issues */          \
-      /* loads w, w+4, ...; wave 3 also the 32 token scales (128 bytes) */                \
-      const uint32_t lb__ = lds_ring + (buf_) * TILE_BYTES + RAW8 + 1024 * wave;         \
-      _Pragma("unroll") for (int k = 0; k < (NLD8 + 3) / 4; ++k)                         \
-        if (wave + 4 * k < NLD8)                                                         \
-          asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"     \
-                       :: "s"(lb__ + 4096 * k), "v"(lane16), "s"(rs__),                  \
-                          "s"(__builtin_amdgcn_readfirstlane(1024 * (wave + 4 * k))) : "memory"); \
-      if (wave == 3) {                                                                   \
-        const uint64_t sa__ = (uint64_t)(a.kv_scale + r0__);                             \
-        const u32x4 ss__ = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa__),    \
-                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa__ >> 32)) & 0xFFFFu, \
-                            (uint32_t)__builtin_amdgcn_readfirstlane(nv__ * 4), 0x00020000u}; \
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"          \
-                     :: "s"(lds_ring + (buf_) * TILE_BYTES + SCL8),                      \
-                        "v"(uint32_t(lane < TILE ? 4 * lane : kOOB)), "s"(ss__) : "memory"); \
-      }                                                                                  \
-    }                                                                                    \
-  } while (0)
-  // fp8: this thread's raw chunks of the tile in slot buf (8 bytes each)
-#define MLA_READ_RAW8(buf_)                                                                \
-  do {                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < NSTG8; ++i)                                    \
-      stg8[i] = *(const u32x2*)(&s_kv[(buf_)][RAW8 + 8 * (tid + 256 * i)]);              \
-  } while (0)
-  // fp8: decode them into the slot's bf16 rows (every wave's raw reads are
-  // done: a barrier separates the two) and put the token scales in
-  // score-register order (a masked token's zero scale becomes 1)
-#define MLA_DECODE8(buf_)                                                                  \
-  do {                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < NSTG8; ++i) {                                  \
-      const int ci = tid + 256 * i;                                                      \
-      *(u32x4*)(&s_kv[(buf_)][16 * ci + 16 * (ci / NCH)]) = fp8x8_to_bf16x8(stg8[i]);    \
-    }                                                                                    \
-    if (tid < TILE) {                                                                    \
-      const float sc = *(const float*)(&s_kv[(buf_)][SCL8 + 4 * reg_token(tid & 15, tid >> 4)]); \
-      s_scale[(buf_)][tid] = (sc == 0.f) ? 1.f : sc;                                     \
     }                                                                                    \
   } while (0)
   // fp6: this thread's blocks q = tid, tid + 256 of the raw tile in slot buf
@@ -501,7 +437,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
 
-  // Prologue of an attempt: issue tiles 0 and 1; fp8: once they have
+  // Prologue of an attempt: issue tiles 0 and 1; 6-bit: once they have
   // landed (vmcnt(0) and a barrier), tile 0 is decoded right away, tile 1
   // in step 0.
 #define MLA_ISSUE_FIRST_TILES()                                                            \
@@ -511,13 +447,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   } while (0)
 #define MLA_DECODE_FIRST_TILE()                                                            \
   do {                                                                                   \
-    if constexpr (FP8) {                                                                 \
-      if (ntiles > 0) {                                                                  \
-        MLA_READ_RAW8(0);                                                                \
-        __syncthreads();                                                                 \
-        MLA_DECODE8(0);                                                                  \
-      }                                                                                  \
-    } else if constexpr (FP6) {                                                          \
+    if constexpr (FP6) {                                                                 \
       if (ntiles > 0) {                                                                  \
         MLA_READ_RAW6(0);                                                                \
         __syncthreads();                                                                 \
@@ -544,12 +474,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
     // after it (the fewest any wave issues per tile) stay in flight
     const int nt = min(ntiles, 2);
     if (nt == 2) {
-      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (FP6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      if constexpr (FP6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
     } else if (nt == 1) {
-      if constexpr (FP8) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if constexpr (FP6) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+      if constexpr (FP6) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -672,11 +600,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
         }
       }
     } else if constexpr (FP6) {
-      // The step of the fp8 path with 6-bit tiles: raw tile it+1 (copied
-      // during step it-1) is read after the scores of step it and decoded in
-      // place after its first barrier (each block of 32 codes with its power
-      // of two, exact in bf16), while tile it+2 is copied.  No per-token
-      // scale: the softmax is the bf16 one.
+      // The bf16 step with 6-bit tiles: raw tile it+1 (copied during step
+      // it-1) is read after the scores of step it and decoded in place after
+      // its first barrier (each block of 32 codes with its power of two,
+      // exact in bf16), while tile it+2 is copied.
       if (ntiles > 0) {
         __syncthreads();
         uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
@@ -739,80 +666,6 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
           pvd_tile(s_kv[(ntiles - 1) & 3] + pv_off, s_p + 16 * lane, o);
         }
       }
-    } else {
-      // The same step as for bf16.  Raw fp8 tiles are copied into the upper
-      // part of their ring slot; tile it+1 (copied during step it-1) is read
-      // at the start of step it and decoded in place after its first barrier,
-      // while tile it+2 is copied.  The token scales are applied in the
-      // softmax: the scores are multiplied by them first, the PV weights
-      // after it.  s_scale holds a tile's 32 scales in score-register order
-      // (16 per lane half).
-      if (ntiles > 0) {
-        __syncthreads();
-        uint32_t pk_prev[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        for (int it = 0; it < ntiles; ++it) {
-          const int ts = t0 + it * TILE;
-          MLA_READ_RAW8((it + 1) & 3);
-          MLA_ISSUE_TILE(ts + 2 * TILE, (it + 2) & 3);
-          put_p(s_p, wave, lane, pk_prev);   // weights of tile it-1 (zero at step 0)
-          const floatx16 s_cur = qk_tile(s_kv[it & 3] + qk_off, qf);
-          __syncthreads();                   // weights of tile it-1 in; raw tile it+1 read
-          MLA_DECODE8((it + 1) & 3);
-          const float* kvp = &s_scale[it & 3][16 * h];   // this lane's token scales
-          float sv[16];                      // raw scores (scaled in the sequence)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[r] = s_cur[r];
-          if (ts + TILE - 1 > lim) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (ts + reg_token(r, h) > lim) sv[r] = kNegInf;
-          }
-          float mt;
-          if (m_ref == kNegInf) {
-            float tmp0, sc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[r] = sv[r] * kvp[r];   // as in the sequence
-            asm volatile(MLA_ASM_SOFTMAX_MAX
-                         : "=&v"(mt), "=&v"(tmp0)
-                         : "v"(sc[0]), "v"(sc[1]), "v"(sc[2]), "v"(sc[3]), "v"(sc[4]),
-                           "v"(sc[5]), "v"(sc[6]), "v"(sc[7]), "v"(sc[8]), "v"(sc[9]),
-                           "v"(sc[10]), "v"(sc[11]), "v"(sc[12]), "v"(sc[13]), "v"(sc[14]),
-                           "v"(sc[15]), "v"(a.scale_log2));
-            m_ref = mt;                          // O and l are still zero here
-          }
-          const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
-          const uint32_t vb = (uint32_t)(uintptr_t)(s_kv[(it > 0 ? it - 1 : 0) & 3] + pv_off);
-          const uint32_t pb = (uint32_t)(uintptr_t)(s_p + 16 * lane);
-          const uint32_t kb = (uint32_t)(uintptr_t)kvp;
-          uint32_t pk[8];
-          float tmp;
-          asm volatile(MLA_ASM_PVD_SOFTMAX_TILE_FP8
-                       : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
-                         "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
-                         "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
-                         "+a"(o[15]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3]),
-                         "+v"(sv[4]), "+v"(sv[5]), "+v"(sv[6]), "+v"(sv[7]), "+v"(sv[8]),
-                         "+v"(sv[9]), "+v"(sv[10]), "+v"(sv[11]), "+v"(sv[12]), "+v"(sv[13]),
-                         "+v"(sv[14]), "+v"(sv[15]), "=&v"(pk[0]), "=&v"(pk[1]), "=&v"(pk[2]),
-                         "=&v"(pk[3]), "=&v"(pk[4]), "=&v"(pk[5]), "=&v"(pk[6]), "=&v"(pk[7]),
-                         "=&v"(mt), "=&v"(tmp), "+v"(l_run)
-                       : "v"(vb), "v"(pb), "v"(neg_m), "v"(a.scale_log2), "v"(kb)
-                       : "memory", MLA_ASM_PVD_FP8_CLOBBERS);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pk_prev[i] = pk[i];
-          m_seen = fmaxf(m_seen, mt);
-          if (mt > m_ref + 64.0f) s_restart = 1;
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // raw tile it+2 landed
-          __syncthreads();
-          restart = __builtin_amdgcn_readfirstlane(s_restart);   // uniform: read after the barrier
-          if (restart) break;
-        }
-        if (!restart) {
-          put_p(s_p, wave, lane, pk_prev);
-          __syncthreads();
-          pvd_tile(s_kv[(ntiles - 1) & 3] + pv_off, s_p + 16 * lane, o);
-        }
-      }
     }
     if (!restart) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load of this attempt in flight
@@ -831,8 +684,6 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #undef MLA_PROLOGUE
 #undef MLA_ISSUE_FIRST_TILES
 #undef MLA_DECODE_FIRST_TILE
-#undef MLA_READ_RAW8
-#undef MLA_DECODE8
 #undef MLA_READ_RAW6
 #undef MLA_DECODE6
 #undef MLA_WAIT_ONE_TILE_IN_FLIGHT
@@ -840,93 +691,18 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
 #undef MLA_VOFF
 #undef MLA_PAGE
 
-  // ---- normalise and write (the final output, or this split's partial).
-  // Wave w holds O^T for its 128 latent dims and all 128 rows (block
-  // 4 db + rb: dims 128 w + 32 db + 8 (r/4) + 4h + r%4 in register r, row
-  // 32 rb + l32); each row's normaliser is with the wave that owns the row.
-  // Each wave stages its part of the rows in LDS and writes it back with
-  // 16-byte stores over runs of 256 (bf16) or 512 (fp32) contiguous bytes.
-  if (a.esc_flags && tid == 0) a.esc_flags[(size_t)item_id * a.fast_rb + rb] = 0;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = (l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  const float lse = (l_tot > 0.f) ? (m_ref + log2f(l_tot)) * 0.69314718055994531f : kNegInf;
-  if (h == 0) s_inv[32 * wave + l32] = inv;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile loads past the end still write LDS
-  __syncthreads();                                   // the ring is free; s_inv is in
-  float inv_rb[4];
-#pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) inv_rb[r4] = s_inv[32 * r4 + l32];
-  const int row0 = rb * ROWS_WG;                     // first row of the workgroup
-  const int own0 = row0 + 32 * wave;                 // first row this wave owns
-  if (ns == 1) {
-    // fp32 rows: 512 bytes per row from this wave, two passes of 64 rows
-    constexpr int SROW = 528;
-    uint8_t* stg = &s_kv[0][0] + wave * (64 * SROW);
-    const size_t g0 = (size_t)b * rows + row0;
-    uint8_t* dst = (uint8_t*)(a.out_latent + g0 * DC) + 512 * wave;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-#pragma unroll
-      for (int r2 = 0; r2 < 2; ++r2) {
-        const int r4 = 2 * p + r2;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const floatx16& ob = o[4 * db + r4];
-            const floatx4 v = {ob[4 * jj], ob[4 * jj + 1], ob[4 * jj + 2], ob[4 * jj + 3]};
-            *(floatx4*)(stg + (32 * r2 + l32) * SROW + 4 * (32 * db + 8 * jj + 4 * h)) = v * inv_rb[r4];
-          }
-        }
-      }
-      // 64 rows x 512 bytes: one store covers two rows
-#pragma unroll
-      for (int n = 0; n < 32; ++n) {
-        const int r = 2 * n + (lane >> 5);
-        *(floatx4*)(dst + (size_t)(64 * p + r) * (4 * DC) + 16 * (lane & 31)) =
-            *(const floatx4*)(stg + r * SROW + 16 * (lane & 31));
-      }
-    }
-    if (h == 0) a.out_lse[(size_t)b * rows + own0 + l32] = lse;
-  } else {
-    // split partial, normalised, stored as bf16 (combined in fp32): 256
-    // bytes per row from this wave, all 128 rows at once
-    constexpr int SROW = 272;
-    uint8_t* stg = &s_kv[0][0] + wave * (128 * SROW);
-    const size_t g0 = (size_t)item_id * rows + row0;
-    uint8_t* dst = (uint8_t*)a.part_o + g0 * a.part_row_bytes + 256 * wave;
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const floatx16& ob = o[4 * db + r4];
-          const float w = inv_rb[r4];
-          const bf16x2 p01 = {(__bf16)(ob[4 * jj] * w), (__bf16)(ob[4 * jj + 1] * w)};
-          const bf16x2 p23 = {(__bf16)(ob[4 * jj + 2] * w), (__bf16)(ob[4 * jj + 3] * w)};
-          *(u32x2*)(stg + (32 * r4 + l32) * SROW + 2 * (32 * db + 8 * jj + 4 * h)) =
-              u32x2{__builtin_bit_cast(uint32_t, p01), __builtin_bit_cast(uint32_t, p23)};
-        }
-      }
-    }
-    // 128 rows x 256 bytes: one store covers four rows
-#pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      const int r = 4 * n + (lane >> 4);
-      *(u32x4*)(dst + (size_t)r * a.part_row_bytes + 16 * (lane & 15)) =
-          *(const u32x4*)(stg + r * SROW + 16 * (lane & 15));
-    }
-    if (h == 0) a.part_lse[(size_t)item_id * rows + own0 + l32] = lse;
-  }
+  // ---- normalise and write (the final output, or this split's partial)
+  store_rows(a, o, l_run, m_ref, &s_kv[0][0], s_inv, b, rb, item_id, ns, rows, tid);
 }
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, const ItemTable& tab, hipStream_t st);
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, const ItemTable& tab, hipStream_t st) {
   // a.row_blocks counts blocks of ROWS_WG query rows
   const int grid = a.n_items * a.row_blocks;
   if (a.kv_dtype == MLA_FP8_E4M3)
-    hipLaunchKernelGGL(decode_mfma_kernel<1>, dim3(grid), dim3(256), 0, st, a, tab);
-  else if (a.kv_dtype == MLA_FP6_E2M3)
+    return launch_decode_fp8(a, tab, st);
+  if (a.kv_dtype == MLA_FP6_E2M3)
     hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
   else
     hipLaunchKernelGGL(decode_mfma_kernel<0>, dim3(grid), dim3(256), 0, st, a, tab);

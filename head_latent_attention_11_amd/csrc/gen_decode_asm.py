@@ -128,7 +128,7 @@ def softmax_valu(S, PK, MT, TMP, LRUN, NEGM, SCALE):
     return max_valu(S, MT, TMP, SCALE) + weights_valu(S, PK, LRUN, NEGM, SCALE)
 
 
-def pvd(with_softmax=False, with_dma=False, fp8=False):
+def pvd(with_softmax=False, with_dma=False):
     """PV product of one tile for this wave's 128 latent dims and all 128
     query rows of the workgroup: O^T[dims, rows] += C^T[dims, tok] P^T[tok,
     rows], 32 MFMAs (4 dim blocks x 4 row blocks x 2 token halves).  The
@@ -136,7 +136,7 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
     the waves that own the rows); each weight fragment is read once and used
     for 4 MFMAs, each transposed C^T fragment read once and used for 4.
     with_softmax: the softmax of the current tile is interleaved (two vector
-    instructions per MFMA, four for the longer fp8 softmax).
+    instructions per MFMA).
 
     operands: %0..%15 O blocks (block 4 db + rb: dims 32 db of the wave's
     128, rows 32 rb), %16..%31 the current tile's scores s_0..s_15 (in;
@@ -146,26 +146,14 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
     tile + the wave's dim offset), %44 this lane's P fragment address, %45
     -m_ref, %46 the scale (log2 domain).  with_dma: %47 buffer descriptor,
     %48 LDS base of this wave's loads, %49..%52 lane offsets of loads 5..8.
-    fp8 (no loads): %16..%31 are the raw scores; %47 is the address of this
-    lane's 16 token scales in LDS (read into v[212:227]); the sequence
-    multiplies the scores by them first.
     Without the softmax only %0..%15, %16 (= transposed-read base) and %17
     (= P fragment address) are used.
     Fixed registers: P fragments v[224:255], C^T fragment buffers
-    v[PVD_VBUF:223].  fp8 (which also holds the staged next tile): P
-    fragments v[240:255], the second token half's fragments read into them 4
-    MFMAs after the first half's last use, 3 C^T buffers v[228:239], token
-    scales v[212:227].
+    v[PVD_VBUF:223].
     """
     vbase, pbase = ("%43", "%44") if with_softmax else ("%16", "%17")
     valu = []
-    if with_softmax and fp8:
-        kv = lambda r: f"v{212 + r}"
-        valu = ([f"v_mul_f32 %{16 + r}, %{16 + r}, {kv(r)}" for r in range(16)]
-                + max_valu(lambda r: f"%{16 + r}", "%40", "%41", "%46")
-                + weights_valu_fp8(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
-                                   "%42", "%45", "%46", kv))
-    elif with_softmax:
+    if with_softmax:
         valu = softmax_valu(lambda r: f"%{16 + r}", lambda i: f"%{32 + i}",
                             "%40", "%41", "%42", "%45", "%46")
     out, issued = [], []
@@ -180,10 +168,10 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
         out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
 
     def pfrag(rb, ks):
-        return 240 + 4 * rb if fp8 else 224 + 4 * (4 * ks + rb)
+        return 224 + 4 * (4 * ks + rb)
 
     def vbuf(g):
-        return (228 + 4 * (g % 3)) if fp8 else PVD_VBUF + 4 * (g % PVD_NVBUF)
+        return PVD_VBUF + 4 * (g % PVD_NVBUF)
 
     def vread(g):
         ks, db = g // 4, g % 4
@@ -197,18 +185,12 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
         r = pfrag(rb, ks)
         read(("P", rb, ks), [f"ds_read_b128 v[{r}:{r + 3}], {pbase} offset:{1024 * (2 * rb + ks)}"])
 
-    if fp8 and with_softmax:
-        for q in range(4):
-            read("K", [f"ds_read_b128 v[{212 + 4 * q}:{215 + 4 * q}], %47 offset:{16 * q}"])
     for rb in range(4):
         pread(rb, 0)
     for g in range(PVD_AHEAD):
         vread(g)
-    if not fp8:
-        for rb in range(4):
-            pread(rb, 1)
-    if fp8 and with_softmax:
-        wait_for({"K"})                       # the scales, before the first scaling
+    for rb in range(4):
+        pread(rb, 1)
     vi = 0
     for _ in range(PVD_LEAD):                 # independent softmax work first
         if vi < len(valu):
@@ -222,12 +204,219 @@ def pvd(with_softmax=False, with_dma=False, fp8=False):
         wait_for({("V", g), ("P", rb, ks)})
         out.append(f"v_mfma_f32_32x32x16_bf16 %{4 * db + rb}, v[{vbuf(g)}:{vbuf(g) + 3}], "
                    f"v[{pfrag(rb, ks)}:{pfrag(rb, ks) + 3}], %{4 * db + rb}")
-        if fp8 and 12 <= i < 16:
-            pread(i - 12, 1)                  # after the last use of P(rb, 0)
         if with_dma and i % 8 == 3 and i // 8 < PV_DMA:
             k = i // 8
             out += dma(QK_DMA + k, "%47", "%48", f"%{49 + k}")
-        take = (4 if fp8 else 2) if i < 31 else len(valu) - vi
+        take = 2 if i < 31 else len(valu) - vi
+        for _ in range(take):
+            if vi < len(valu):
+                out.append(valu[vi])
+                vi += 1
+    assert vi == len(valu)
+    return out
+
+
+# ---------------------------------------------------------------- fp8 tiles
+# The fp8 kernel (decode_fp8.hip) keeps raw E4M3 tiles in LDS (rows of 576
+# codes at a pitch of LROW8 bytes) and converts the MFMA operands in
+# registers with v_cvt_scalef32_pk_bf16_fp8 (two codes per instruction, exact:
+# every E4M3 value is a bf16 value).  A vector write needs two wait states
+# before a matrix instruction reads it as an operand; the sequences keep at
+# least that many instructions in between.
+LROW8 = 592          # LDS bytes per fp8 token row (576 + 16 pad)
+QK8_AHEAD = 3        # raw 16-byte reads in flight ahead of the current pair
+QK8_DMA = 4          # tile loads interleaved with the score sequence
+QK8_RAW = 224        # 4 raw read buffers v[224:239]
+QK8_CVT = 240        # 4 converted operand buffers v[240:255]
+PV8_P = 240          # P fragments v[240:255]
+PV8_CVT = 232        # 2 converted C^T fragment buffers v[232:239]
+PV8_RAW = 226        # 3 raw C^T fragment buffers v[226:231]
+PV8_KV = 210         # the tile's 16 token scales v[210:225] (with the softmax)
+
+
+def cvt8(dst, src, hi):
+    sel = " op_sel:[1,0,0]" if hi else ""
+    return f"v_cvt_scalef32_pk_bf16_fp8 v{dst}, v{src}, 1.0{sel}"
+
+
+def qk8():
+    """Scores of one raw fp8 tile for the wave's 32 query rows: S^T[tok, row]
+    = K Q^T, 36 MFMAs in pairs.  Lane l reads 16 codes of token row l%32 at
+    dims 32kk + 16(l/32) (one ds_read_b128 per pair kk); the first 8 become
+    the A operand of MFMA 2kk, the last 8 that of MFMA 2kk+1, so MFMA 2kk
+    takes dims {32kk + 0..7, 32kk + 16..23} and MFMA 2kk+1 the others (the
+    query fragments are laid out to match).  The pair kk+1 is converted
+    while the pair kk runs.
+
+    operands: %0 S (floatx16, out), %1 base address of this lane's reads,
+    %2..%37 query fragments, %38 buffer descriptor of the tile being loaded,
+    %39 LDS base of this wave's loads of it, %40..%43 lane offsets of its
+    loads 0..3 (one after every fourth MFMA pair)."""
+    out, issued = [], []
+    npair = 18
+
+    def raw(kk):
+        return QK8_RAW + 4 * (kk % 4)
+
+    def conv(i):
+        return QK8_CVT + 4 * (i % 4)
+
+    def read(kk):
+        r = raw(kk)
+        out.append(f"ds_read_b128 v[{r}:{r + 3}], %1 offset:{32 * kk}")
+        issued.append(kk)
+
+    def wait(kk):
+        last = issued.index(kk)
+        out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
+
+    def convert(kk, half):
+        r, c = raw(kk), conv(2 * kk + half)
+        return [cvt8(c, r + 2 * half, False), cvt8(c + 1, r + 2 * half, True),
+                cvt8(c + 2, r + 2 * half + 1, False), cvt8(c + 3, r + 2 * half + 1, True)]
+
+    for kk in range(QK8_AHEAD):
+        read(kk)
+    wait(0)
+    out += convert(0, 0) + convert(0, 1)
+    for kk in range(npair):
+        if kk + QK8_AHEAD < npair:
+            read(kk + QK8_AHEAD)
+        for half in range(2):
+            i = 2 * kk + half
+            c = "0" if i == 0 else "%0"
+            out.append(f"v_mfma_f32_32x32x16_bf16 %0, v[{conv(i)}:{conv(i) + 3}], %{2 + i}, {c}")
+            if kk + 1 < npair:
+                if half == 0:
+                    wait(kk + 1)
+                out += convert(kk + 1, half)
+        if kk % 4 == 1 and kk // 4 < QK8_DMA:
+            n = kk // 4
+            out += dma(n, "%38", "%39", f"%{40 + n}")
+    return out
+
+
+def softmax8_valu(S, KV, MT, TMP, LRUN, NEGM, SCALE):
+    """Softmax of one fp8 tile (no masked token): the raw scores times their
+    token scales, the scaled max of the row (for the restart check), p_r =
+    2^(s_r * scale - m_ref); the normaliser sums the bf16-rounded p_r (pairs
+    packed into TMP, then a dot product with (1, 1)), and the PV weights p_r
+    times the token scale (the cache codes enter the MFMA unscaled) are
+    packed to bf16 pairs into S(0..7).  Each v_exp result is read at least
+    two instructions later."""
+    seq = [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
+    seq += max_valu(S, MT, TMP, SCALE)
+    fma = [f"v_fma_f32 {S(r)}, {S(r)}, {SCALE}, {NEGM}" for r in range(16)]
+    exp = [f"v_exp_f32 {S(r)}, {S(r)}" for r in range(16)]
+    seq += fma[:2]
+    for r in range(2, 16):
+        seq += [fma[r], exp[r - 2]]
+    seq += exp[14:]
+    seq.append("s_nop 1")
+    for i in range(8):
+        seq += [f"v_cvt_pk_bf16_f32 {TMP}, {S(2 * i)}, {S(2 * i + 1)}",
+                f"v_dot2c_f32_bf16 {LRUN}, 0x3f803f80, {TMP}"]
+    seq += [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
+    seq += [f"v_cvt_pk_bf16_f32 {S(i)}, {S(2 * i)}, {S(2 * i + 1)}" for i in range(8)]
+    return seq
+
+
+def pv8(with_softmax=True):
+    """PV product of one raw fp8 tile for this wave's 128 latent dims and
+    all 128 rows: O^T[dims, rows] += C^T[dims, tok] P^T[tok, rows], 32 MFMAs
+    (4 dim blocks x 4 row blocks x 2 token halves).  C^T fragment (ks, db)
+    comes from one ds_read_b64_tr_b8 per lane (8 codes: one latent dim of 8
+    tokens) and 4 conversions; it feeds 4 MFMAs.  The weight fragments of
+    all row blocks come from the LDS P buffer of the previous tile.
+
+    with_softmax: the softmax of the current tile (softmax8_valu) is
+    interleaved.  operands: %0..%15 O blocks (block 4 db + rb), %16..%31 the
+    current tile's raw scores (in; out: the packed PV weights in
+    %16..%23), %32 the scaled max (out), %33 a temporary, %34 the running
+    normaliser (in/out), %35 this lane's C^T read address (slot of the
+    previous tile + lane offset), %36 this lane's P fragment address
+    (previous tile's P buffer), %37 the address of this lane's 16 token
+    scales (read into v[210:225]), %38 -m_ref, %39 the scale (log2 domain),
+    %40 a scalar flag: nonzero zeroes the O blocks first (one MFMA of zero
+    operands and a zero accumulator input per block, skipped by a branch
+    inside the sequence otherwise).
+    Without the softmax: %0..%15, %16 the C^T address, %17 the P address."""
+    if with_softmax:
+        kv = lambda r: f"v{PV8_KV + r}"
+        valu = softmax8_valu(lambda r: f"%{16 + r}", kv, "%32", "%33", "%34", "%38", "%39")
+        vaddr, paddr = "%35", "%36"
+    else:
+        valu = []
+        vaddr, paddr = "%16", "%17"
+    out, issued = [], []
+
+    def read(name, instr):
+        out.append(instr)
+        issued.append(name)
+
+    def wait_for(names):
+        last = max(i for i, n in enumerate(issued) if n in names)
+        out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
+
+    def raw(g):
+        return PV8_RAW + 2 * (g % 3)
+
+    def conv(g):
+        return PV8_CVT + 4 * (g % 2)
+
+    def vread(g):
+        ks, db = g // 4, g % 4
+        read(("V", g), f"ds_read_b64_tr_b8 v[{raw(g)}:{raw(g) + 1}], {vaddr} "
+                       f"offset:{16 * LROW8 * ks + 32 * db}")
+
+    def pread(rb, ks):
+        r = PV8_P + 4 * rb
+        read(("P", rb, ks), f"ds_read_b128 v[{r}:{r + 3}], {paddr} offset:{1024 * (2 * rb + ks)}")
+
+    def convert(g):
+        r, c = raw(g), conv(g)
+        return [cvt8(c, r, False), cvt8(c + 1, r, True), cvt8(c + 2, r + 1, False),
+                cvt8(c + 3, r + 1, True)]
+
+    if with_softmax:
+        z = PV8_P + 12
+        out += ["s_cmp_eq_u32 %40, 0", "s_cbranch_scc1 MLA_PV8_NZ%=",
+                f"v_mov_b32 v{z}, 0", f"v_mov_b32 v{z + 1}, 0", f"v_mov_b32 v{z + 2}, 0",
+                f"v_mov_b32 v{z + 3}, 0", "s_nop 1"]
+        out += [f"v_mfma_f32_32x32x16_bf16 %{i}, v[{z}:{z + 3}], v[{z}:{z + 3}], 0"
+                for i in range(16)]
+        out += ["s_nop 7", "s_nop 7", "MLA_PV8_NZ%=:"]
+        for q in range(4):
+            read("K", f"ds_read_b128 v[{PV8_KV + 4 * q}:{PV8_KV + 4 * q + 3}], %37 offset:{16 * q}")
+    vread(0)
+    for rb in range(4):
+        pread(rb, 0)
+    vread(1)
+    vread(2)
+    vi = 0
+    if with_softmax:
+        wait_for({"K"})                       # the scales, before the first scaling
+    for _ in range(6):                        # independent softmax work first
+        if vi < len(valu):
+            out.append(valu[vi])
+            vi += 1
+    wait_for({("V", 0)})
+    out += convert(0)
+    for i in range(32):
+        ks, db, rb = i // 16, (i // 4) % 4, i % 4
+        g = i // 4
+        if rb == 0:
+            wait_for({("P", rr, ks) for rr in range(4)} if i in (0, 16) else {("V", g)})
+        out.append(f"v_mfma_f32_32x32x16_bf16 %{4 * db + rb}, v[{conv(g)}:{conv(g) + 3}], "
+                   f"v[{PV8_P + 4 * rb}:{PV8_P + 4 * rb + 3}], %{4 * db + rb}")
+        if 12 <= i < 16:
+            pread(i - 12, 1)                  # after the last use of P(rb, 0)
+        if rb == 1 and g + 1 < 8:
+            wait_for({("V", g + 1)})
+            out += convert(g + 1)             # read by MFMA 4(g+1), >= 2 instructions later
+        if rb == 2 and g + 3 < 8:
+            vread(g + 3)                      # into the buffer of fragment g, converted already
+        take = 3 if i < 31 else len(valu) - vi
         for _ in range(take):
             if vi < len(valu):
                 out.append(valu[vi])
@@ -258,9 +447,14 @@ if __name__ == "__main__":
     txt.append(f"#define MLA_ASM_QK_CLOBBERS {clobbers(QK_TMP, 32)}\n")
     txt.append(emit("MLA_ASM_PVD_TILE", pvd()))
     txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_DMA", pvd(True, True)))
-    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE", pvd(True, False, False)))
-    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE_FP8", pvd(True, False, True)))
+    txt.append(emit("MLA_ASM_PVD_SOFTMAX_TILE", pvd(True, False)))
     txt.append(f"#define MLA_ASM_PVD_CLOBBERS {clobbers(PVD_VBUF, 256 - PVD_VBUF)}\n")
-    txt.append(f"#define MLA_ASM_PVD_FP8_CLOBBERS {clobbers(212, 44)}\n")
     txt.append(emit_plain("MLA_ASM_SOFTMAX_MAX", softmax_max()))
+    txt.append(emit("MLA_ASM_QK8_TILE", qk8()))
+    txt.append(f"#define MLA_ASM_QK8_CLOBBERS {clobbers(QK8_RAW, 32)}\n")
+    txt.append(emit("MLA_ASM_PV8_SOFTMAX_TILE", pv8(True)))
+    txt.append(emit("MLA_ASM_PV8_TILE", pv8(False)))
+    txt.append(f"#define MLA_ASM_PV8_CLOBBERS {clobbers(PV8_RAW, 256 - PV8_RAW)}\n")
+    txt.append(f"#define MLA_ASM_PV8_SOFTMAX_CLOBBERS {clobbers(PV8_KV, 256 - PV8_KV)}\n")
+
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))

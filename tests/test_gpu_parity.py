@@ -388,6 +388,24 @@ def test_reference_restart_on_large_score_jump():
     _run_compare(w, gen=gen, precision="fp32")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "fp6"])
+def test_reference_restart_quantised_caches(kv):
+    """The restart of the quantised-cache kernels: rows scaled by 64 before
+    the cache is written (their scale absorbs the factor), late in each
+    sequence, with T = 4 causal rows; the fp8 kernel answers a restart with
+    a pass that finds every row's largest score and a second pass from that
+    reference.  The quantised caches are held to their rel-L2 gate."""
+    w = small_variant(V2, name=f"restart_{kv}", batch=2, q_tokens=4, kv_len=0,
+                      lengths=(1000, 900), kv_dtype=kv)
+    gen = generate(w)
+    c = formats.bf16_to_f64(gen["c_kv"])
+    c[700] *= 64.0
+    c[1000 + 500] *= 64.0
+    from mla_inputs import bf16_bits_from_f32
+    gen["c_kv"] = bf16_bits_from_f32(c.astype(np.float32))
+    _run_compare(w, gen=gen, max_abs=False)
+
+
 # --------------------------------------------------- append, bit exact
 @pytest.mark.parametrize("layout", ["contiguous", "paged"])
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "fp6", "f32"])
