@@ -37,8 +37,9 @@ COPY_CEILING_BYTES = 2 ** 30            # plain device copy reported as the prac
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 _CSRC = os.path.join(ROOT, "head_latent_attention_11_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
-                  ("decode_mfma.hip", "decode_mfma_asm.inc", "decode_small.hip", "decode_x2.hip",
-                   "kernels_misc.hip", "mla_common.hpp", "plan_device.hpp", "mla_api.hip")]
+                  ("decode_mfma.hip", "decode_fp8.hip", "decode_mfma_asm.inc", "decode_small.hip",
+                   "decode_x2.hip", "decode_tile.hpp", "kernels_misc.hip", "mla_common.hpp",
+                   "plan_device.hpp", "mla_api.hip")]
 LITE_WORKLOAD = "v2lite_b64_l8k_bf16"   # DeepSeek-V2-Lite shapes (16 heads)
 FP6_WORKLOAD = "v2_fp6_t4_b64_l8k"      # the headline shape on the 6-bit cache
 

@@ -31,7 +31,7 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-ATTN_KERNELS = ("decode_mfma_kernel", "decode_small_kernel", "decode_x2_kernel",
+ATTN_KERNELS = ("decode_mfma_kernel", "decode_fp8_kernel", "decode_small_kernel", "decode_x2_kernel",
                 "decode_general_kernel", "combine_kernel")
 COPY_KERNEL = "copyBuffer"
 

@@ -290,8 +290,7 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
 
   floatx16 o[DC / 32];
   float m_ref = kNegInf, m_seen = kNegInf, l_run = 0.f;
-  const uint32_t pw = lds0 + PBUF + 2048 * wave + 16 * lane;   // this lane's weights (+ 8 KB per buffer)
-  const uint32_t pr = lds0 + PBUF + 16 * lane;                 // this lane's weight reads
+  const uint32_t pr = lds0 + PBUF + 16 * lane;   // this lane's weight fragments (+ 8 KB per buffer)
 
 #pragma unroll
   for (int i = 0; i < DC / 32; ++i) o[i] = floatx16{};
@@ -356,15 +355,14 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
         }
         kva = lds0 + KVW + 128 * wave + 64 * h;
       }
-      float mt, tmp;
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_ref == kNegInf) != 0, 0)) {
         // the first tile in which the row sees a token sets the reference
         const float* kvp = (const float*)(s_lds + (kva - lds0));
-        float sc16[16];
+        float sc16[16], mt, tmp0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc16[r] = sv[r] * kvp[r];   // as in the sequence
         asm volatile(MLA_ASM_SOFTMAX_MAX
-                     : "=&v"(mt), "=&v"(tmp)
+                     : "=&v"(mt), "=&v"(tmp0)
                      : "v"(sc16[0]), "v"(sc16[1]), "v"(sc16[2]), "v"(sc16[3]), "v"(sc16[4]),
                        "v"(sc16[5]), "v"(sc16[6]), "v"(sc16[7]), "v"(sc16[8]), "v"(sc16[9]),
                        "v"(sc16[10]), "v"(sc16[11]), "v"(sc16[12]), "v"(sc16[13]),
@@ -374,9 +372,12 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
       const float neg_m = (m_ref == kNegInf) ? 0.f : -m_ref;
       // The PV product of tile it-1 with the softmax of tile it interleaved
       // (step 0: O is zeroed first, then tile 0 times the zeroed weight
-      // buffer 1 adds exact zeros); the weights come back packed in sv[0..7].
+      // buffer 1 adds exact zeros); the sequence writes this wave's weights
+      // of tile it into P buffer it%2.
       const uint32_t vb = lds0 + (it == 0 ? 0 : sp * SLOT) + pv_off;
       const uint32_t pb = pr + 8192 * ((it + 1) & 1);
+      const uint32_t pw = pr + 8192 * (it & 1) + 2048 * wave;   // this lane's weights of tile it
+      float tmp;
       asm volatile(MLA_ASM_PV8_SOFTMAX_TILE
                    : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
                      "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
@@ -384,27 +385,22 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
                      "+a"(o[15]), "+v"(sv[0]), "+v"(sv[1]), "+v"(sv[2]), "+v"(sv[3]),
                      "+v"(sv[4]), "+v"(sv[5]), "+v"(sv[6]), "+v"(sv[7]), "+v"(sv[8]),
                      "+v"(sv[9]), "+v"(sv[10]), "+v"(sv[11]), "+v"(sv[12]), "+v"(sv[13]),
-                     "+v"(sv[14]), "+v"(sv[15]), "=&v"(mt), "=&v"(tmp), "+v"(l_run)
+                     "+v"(sv[14]), "+v"(sv[15]), "=&v"(tmp), "+v"(l_run)
                    : "v"(vb), "v"(pb), "v"(kva), "v"(neg_m), "v"(a.scale_log2),
-                     "s"(__builtin_amdgcn_readfirstlane(it == 0 ? 1 : 0))
+                     "s"(__builtin_amdgcn_readfirstlane(it == 0 ? 1 : 0)), "v"(pw)
                    : "memory", MLA_ASM_PV8_SOFTMAX_CLOBBERS);
-      uint32_t pk[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pk[i] = __builtin_bit_cast(uint32_t, sv[i]);
-      // this wave's weights of tile it (row block w, token halves 0 and 1)
-      {
-        uint8_t* d = s_lds + PBUF + 8192 * (it & 1) + 2048 * wave + 16 * lane;
-        *(u32x4*)d = u32x4{pk[0], pk[1], pk[2], pk[3]};
-        *(u32x4*)(d + 1024) = u32x4{pk[4], pk[5], pk[6], pk[7]};
-      }
-      m_seen = fmaxf(m_seen, mt);
-      if (CHECK && mt > m_ref + 64.0f) s_restart = 1;
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"((AHEAD - 1) * LPT) : "memory");   // tile it+1 landed
       __syncthreads();
-      if constexpr (CHECK) {
-        if (__builtin_expect(__builtin_amdgcn_readfirstlane(s_restart) != 0, 0)) return true;
-      }
       sc = (sc + 1 == NB) ? 0 : sc + 1;
+    }
+    if constexpr (CHECK) {
+      // A weight above 2^64 (a score more than 64 above the row's
+      // reference, the overflow risk) leaves a normaliser above 2^64: either
+      // partial of a row above 2^63, or not finite, asks for a restart.
+      if (__builtin_amdgcn_ballot_w64(!(l_run <= 0x1p63f)) != 0 && lane == 0) s_restart = 1;
+      __syncthreads();
+      const bool again = __builtin_amdgcn_readfirstlane(s_restart) != 0;
+      return again;
     }
     return false;
   };

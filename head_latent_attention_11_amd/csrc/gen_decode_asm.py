@@ -239,7 +239,7 @@ def cvt8(dst, src, hi):
     return f"v_cvt_scalef32_pk_bf16_fp8 v{dst}, v{src}, 1.0{sel}"
 
 
-def qk8():
+def qk8(with_dma=True):
     """Scores of one raw fp8 tile for the wave's 32 query rows: S^T[tok, row]
     = K Q^T, 36 MFMAs in pairs.  Lane l reads 16 codes of token row l%32 at
     dims 32kk + 16(l/32) (one ds_read_b128 per pair kk); the first 8 become
@@ -290,34 +290,40 @@ def qk8():
                 if half == 0:
                     wait(kk + 1)
                 out += convert(kk + 1, half)
-        if kk % 4 == 1 and kk // 4 < QK8_DMA:
+        if with_dma and kk % 4 == 1 and kk // 4 < QK8_DMA:
             n = kk // 4
             out += dma(n, "%38", "%39", f"%{40 + n}")
     return out
 
 
-def softmax8_valu(S, KV, MT, TMP, LRUN, NEGM, SCALE):
-    """Softmax of one fp8 tile (no masked token): the raw scores times their
-    token scales, the scaled max of the row (for the restart check), p_r =
-    2^(s_r * scale - m_ref); the normaliser sums the bf16-rounded p_r (pairs
-    packed into TMP, then a dot product with (1, 1)), and the PV weights p_r
-    times the token scale (the cache codes enter the MFMA unscaled) are
-    packed to bf16 pairs into S(0..7).  Each v_exp result is read at least
-    two instructions later."""
-    seq = [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
-    seq += max_valu(S, MT, TMP, SCALE)
+def softmax8_valu(S, KV, TMP, LRUN, NEGM, SCALE, PWADDR):
+    """Softmax of one fp8 tile: the raw scores times their token scales, p_r
+    = 2^(s_r * scale - m_ref) against the row's fixed reference (no max:
+    overflow is checked once per pass, on the normaliser).  The normaliser
+    sums the bf16-rounded p_r (pairs packed in place, then two interleaved
+    dot products with (1, 1) into LRUN and TMP).  The PV weights p_r times
+    the token scale (the cache codes enter the MFMA unscaled) go into the
+    scale registers, are packed to bf16 pairs in place (KV(0..7)) and
+    written to this wave's P fragments at PWADDR (token halves 0 and 1).
+    Each v_exp result is read at least two instructions later."""
     fma = [f"v_fma_f32 {S(r)}, {S(r)}, {SCALE}, {NEGM}" for r in range(16)]
     exp = [f"v_exp_f32 {S(r)}, {S(r)}" for r in range(16)]
+    seq = [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
     seq += fma[:2]
     for r in range(2, 16):
         seq += [fma[r], exp[r - 2]]
     seq += exp[14:]
-    seq.append("s_nop 1")
-    for i in range(8):
-        seq += [f"v_cvt_pk_bf16_f32 {TMP}, {S(2 * i)}, {S(2 * i + 1)}",
-                f"v_dot2c_f32_bf16 {LRUN}, 0x3f803f80, {TMP}"]
-    seq += [f"v_mul_f32 {S(r)}, {S(r)}, {KV(r)}" for r in range(16)]
+    seq += [f"v_mov_b32 {TMP}, 0", "s_nop 1"]
+    seq += [f"v_mul_f32 {KV(r)}, {S(r)}, {KV(r)}" for r in range(16)]
     seq += [f"v_cvt_pk_bf16_f32 {S(i)}, {S(2 * i)}, {S(2 * i + 1)}" for i in range(8)]
+    for j in range(4):
+        seq += [f"v_dot2c_f32_bf16 {LRUN}, 0x3f803f80, {S(2 * j)}",
+                f"v_dot2c_f32_bf16 {TMP}, 0x3f803f80, {S(2 * j + 1)}"]
+    seq += [f"v_cvt_pk_bf16_f32 {KV(i)}, {KV(2 * i)}, {KV(2 * i + 1)}" for i in range(8)]
+    seq += [f"v_add_f32 {LRUN}, {LRUN}, {TMP}"]
+    k0 = KV(0)[1:]
+    seq += [f"ds_write_b128 {PWADDR}, v[{k0}:{int(k0) + 3}]",
+            f"ds_write_b128 {PWADDR}, v[{int(k0) + 4}:{int(k0) + 7}] offset:1024"]
     return seq
 
 
@@ -330,21 +336,22 @@ def pv8(with_softmax=True):
     all row blocks come from the LDS P buffer of the previous tile.
 
     with_softmax: the softmax of the current tile (softmax8_valu) is
-    interleaved.  operands: %0..%15 O blocks (block 4 db + rb), %16..%31 the
-    current tile's raw scores (in; out: the packed PV weights in
-    %16..%23), %32 the scaled max (out), %33 a temporary, %34 the running
-    normaliser (in/out), %35 this lane's C^T read address (slot of the
-    previous tile + lane offset), %36 this lane's P fragment address
-    (previous tile's P buffer), %37 the address of this lane's 16 token
-    scales (read into v[210:225]), %38 -m_ref, %39 the scale (log2 domain),
-    %40 a scalar flag: nonzero zeroes the O blocks first (one MFMA of zero
-    operands and a zero accumulator input per block, skipped by a branch
-    inside the sequence otherwise).
+    interleaved, front-loaded so that its weight writes leave the LDS queue
+    before the sequence ends.  operands: %0..%15 O blocks (block 4 db +
+    rb), %16..%31 the current tile's raw scores (in; clobbered), %32 a
+    temporary, %33 the running normaliser (in/out), %34 this lane's C^T
+    read address (slot of the previous tile + lane offset), %35 this lane's
+    P fragment address (previous tile's P buffer), %36 the address of this
+    lane's 16 token scales (read into v[210:225]), %37 -m_ref, %38 the
+    scale (log2 domain), %39 a scalar flag: nonzero zeroes the O blocks
+    first (one MFMA of zero operands and a zero accumulator input per
+    block, skipped by a branch inside the sequence otherwise), %40 this
+    lane's address in the P buffer of the current tile.
     Without the softmax: %0..%15, %16 the C^T address, %17 the P address."""
     if with_softmax:
         kv = lambda r: f"v{PV8_KV + r}"
-        valu = softmax8_valu(lambda r: f"%{16 + r}", kv, "%32", "%33", "%34", "%38", "%39")
-        vaddr, paddr = "%35", "%36"
+        valu = softmax8_valu(lambda r: f"%{16 + r}", kv, "%32", "%33", "%37", "%38", "%40")
+        vaddr, paddr = "%34", "%35"
     else:
         valu = []
         vaddr, paddr = "%16", "%17"
@@ -380,14 +387,14 @@ def pv8(with_softmax=True):
 
     if with_softmax:
         z = PV8_P + 12
-        out += ["s_cmp_eq_u32 %40, 0", "s_cbranch_scc1 MLA_PV8_NZ%=",
+        out += ["s_cmp_eq_u32 %39, 0", "s_cbranch_scc1 MLA_PV8_NZ%=",
                 f"v_mov_b32 v{z}, 0", f"v_mov_b32 v{z + 1}, 0", f"v_mov_b32 v{z + 2}, 0",
                 f"v_mov_b32 v{z + 3}, 0", "s_nop 1"]
         out += [f"v_mfma_f32_32x32x16_bf16 %{i}, v[{z}:{z + 3}], v[{z}:{z + 3}], 0"
                 for i in range(16)]
         out += ["s_nop 7", "s_nop 7", "MLA_PV8_NZ%=:"]
         for q in range(4):
-            read("K", f"ds_read_b128 v[{PV8_KV + 4 * q}:{PV8_KV + 4 * q + 3}], %37 offset:{16 * q}")
+            read("K", f"ds_read_b128 v[{PV8_KV + 4 * q}:{PV8_KV + 4 * q + 3}], %36 offset:{16 * q}")
     vread(0)
     for rb in range(4):
         pread(rb, 0)
@@ -396,10 +403,18 @@ def pv8(with_softmax=True):
     vi = 0
     if with_softmax:
         wait_for({"K"})                       # the scales, before the first scaling
+    def put_valu():
+        nonlocal vi
+        x = valu[vi]
+        vi += 1
+        if x.startswith("ds_write"):
+            read(("W", vi), x)                # counted by lgkmcnt like the reads
+        else:
+            out.append(x)
+
     for _ in range(6):                        # independent softmax work first
         if vi < len(valu):
-            out.append(valu[vi])
-            vi += 1
+            put_valu()
     wait_for({("V", 0)})
     out += convert(0)
     for i in range(32):
@@ -416,11 +431,10 @@ def pv8(with_softmax=True):
             out += convert(g + 1)             # read by MFMA 4(g+1), >= 2 instructions later
         if rb == 2 and g + 3 < 8:
             vread(g + 3)                      # into the buffer of fragment g, converted already
-        take = 3 if i < 31 else len(valu) - vi
+        take = 4 if i < 31 else len(valu) - vi
         for _ in range(take):
             if vi < len(valu):
-                out.append(valu[vi])
-                vi += 1
+                put_valu()
     assert vi == len(valu)
     return out
 
