@@ -483,7 +483,8 @@ def main():
     roof = roofline(bytes_alg, flops, attn_s)
     tr = traffic_for_current_kernel(w.name)
     roof["traffic"] = tr["hbm_bytes_per_launch"] if tr else None
-    roof["kernel"] = ("mla_decode_attn (decode_mfma_kernel, or decode_small_kernel for "
+    roof["kernel"] = ("mla_decode_attn (decode_fp8_kernel for fp8 caches, else decode_mfma_kernel; "
+                      "decode_small_kernel for "
                       "query-row counts that are no multiple of 128, + combine_kernel when "
                       "split), per call, HIP-event timed over back-to-back graph replays")
     roof["bytes_alg_per_launch"] = bytes_alg
