@@ -25,6 +25,7 @@ PRECISION_CODES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16,
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_decode_attn_noalloc", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
             "mla_kv_produce_workspace_size", "mla_kv_produce",
+            "mla_out_proj_pack", "mla_out_proj_packed",
             "mla_status_string", "mla_version")
 
 
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_up_proj_v.argtypes = [pdims, vp, vp, vp, i32, i32, vp]
     lib.mla_out_proj_workspace_size.argtypes = [pdims, i32, i32, i32, ctypes.POINTER(sz)]
     lib.mla_out_proj.argtypes = [pdims, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp]
+    lib.mla_out_proj_pack.argtypes = [pdims, vp, i32, vp, vp]
+    lib.mla_out_proj_packed.argtypes = [pdims, vp, vp, i32, vp, i32, i32, vp, sz, vp]
     lib.mla_kv_produce_workspace_size.argtypes = [pdims, i32, i32, ctypes.POINTER(sz)]
     lib.mla_kv_produce.argtypes = [pdims, vp, i32, vp, vp, ctypes.c_float, vp, vp, vp, i32, i32,
                                    i32, i64, i32, vp, vp, i32, vp, sz, vp]
@@ -253,6 +256,26 @@ def out_proj(dims: MLADims, o, w_o, d_model: int, u, n_tokens: int, workspace, w
     _check(lib.mla_out_proj(ctypes.byref(dims), _ptr(o), int(o_dtype), _ptr(w_o), int(d_model),
                             _ptr(u), int(u_dtype), int(n_tokens), _ptr(workspace), int(ws_bytes),
                             _stream(stream)), "mla_out_proj")
+
+
+def out_proj_pack(dims: MLADims, w_o, d_model: int, w_packed, stream=None):
+    """W^O [d_model, n_h d_h] bf16 -> the panel layout of mla_out_proj_packed."""
+    lib = load_library()
+    _check(lib.mla_out_proj_pack(ctypes.byref(dims), _ptr(w_o), int(d_model), _ptr(w_packed),
+                                 _stream(stream)), "mla_out_proj_pack")
+
+
+def out_proj_packed(dims: MLADims, o, w_packed, d_model: int, u, n_tokens: int, workspace,
+                    ws_bytes: int, stream=None, u_dtype: Optional[int] = None):
+    """u = W^O [o_1; ...; o_{n_h}] with W^O in the panel layout (o bf16); u's
+    dtype defaults to that of the tensor (float32 -> F32, else BF16)."""
+    lib = load_library()
+    import torch
+    if u_dtype is None:
+        u_dtype = F32 if (not isinstance(u, int) and u.dtype == torch.float32) else BF16
+    _check(lib.mla_out_proj_packed(ctypes.byref(dims), _ptr(o), _ptr(w_packed), int(d_model),
+                                   _ptr(u), int(u_dtype), int(n_tokens), _ptr(workspace),
+                                   int(ws_bytes), _stream(stream)), "mla_out_proj_packed")
 
 
 def kv_produce_workspace_size(dims: MLADims, d_model: int, n_rows: int) -> int:

@@ -21,7 +21,9 @@ hipError_t launch_append(const mla_dims_t&, const void*, const void*, const int3
 hipError_t launch_combine(const DecodeArgs&, hipStream_t);
 size_t gemm_xwt_workspace(int, int, int, int, int);
 hipError_t launch_gemm_xwt(const void*, int, const void*, int, void*, bool, int, int, int, void*,
-                           hipStream_t);
+                           hipStream_t, bool packed = false);
+bool gemm_xwt_packable(int, int, int, int);
+hipError_t launch_gemm_pack(const void*, void*, int, int, hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
 hipError_t launch_decode_mfma(const DecodeArgs&, const ItemTable&, hipStream_t);
@@ -630,6 +632,43 @@ int32_t mla_out_proj(const mla_dims_t* dims, const void* o, int32_t o_dtype, con
   if (need > 0 && (!workspace || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   return status_of(launch_gemm_xwt(o, o_dtype, w_o, dims->q_dtype, u, u_dtype == MLA_F32,
                                    n_tokens, d_model, K, workspace, (hipStream_t)stream));
+}
+
+int32_t mla_out_proj_pack(const mla_dims_t* dims, const void* w_o, int32_t d_model,
+                          void* w_packed, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!w_o || !w_packed) return MLA_ERR_NULL;
+  if (d_model < 1) return MLA_ERR_ARG;
+  if (dims->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  const int K = dims->n_heads * dims->d_head;
+  if (!gemm_xwt_packable(d_model, K, MLA_BF16, MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(w_o) || !aligned16(w_packed)) return MLA_ERR_ALIGN;
+  const char* a = (const char*)w_o;
+  const char* b = (const char*)w_packed;
+  const size_t n = (size_t)d_model * K * 2;
+  if (a < b + n && b < a + n) return MLA_ERR_ARG;             // overlapping buffers
+  return status_of(launch_gemm_pack(w_o, w_packed, d_model, K, (hipStream_t)stream));
+}
+
+int32_t mla_out_proj_packed(const mla_dims_t* dims, const void* o, const void* w_packed,
+                            int32_t d_model, void* u, int32_t u_dtype, int32_t n_tokens,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!o || !w_packed || !u) return MLA_ERR_NULL;
+  if (dims->q_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (u_dtype != MLA_F32 && u_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d_model < 1 || n_tokens < 1) return MLA_ERR_ARG;
+  const int K = dims->n_heads * dims->d_head;
+  if (!gemm_xwt_packable(d_model, K, MLA_BF16, MLA_BF16)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(o) || !aligned16(w_packed) || !aligned16(u) ||
+      (workspace && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  const size_t need = gemm_xwt_workspace(d_model, K, n_tokens, MLA_BF16, MLA_BF16);
+  if (!workspace || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  return status_of(launch_gemm_xwt(o, MLA_BF16, w_packed, MLA_BF16, u, u_dtype == MLA_F32,
+                                   n_tokens, d_model, K, workspace, (hipStream_t)stream, true));
 }
 
 int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent, const void* w_uv,

@@ -349,6 +349,33 @@ int32_t mla_out_proj(const mla_dims_t* dims, const void* o, int32_t o_dtype,
                      int32_t n_tokens, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* The output projection with W^O in a panel layout that the library writes
+ * once (e.g. when the weights are loaded), so that each 32-row strip of
+ * W^O streams from contiguous memory: element (f, k) of W^O [d_model, K]
+ * (K = n_h*d_h) sits at element
+ *     ((f / 32) * (K / 64) + k / 64) * 2048 + (f % 32) * 64 + k % 64
+ * of w_packed, i.e. 32 x 64 panels of 4 KB, each strip of 32 rows stored as
+ * its K/64 panels in order.  Same equation as mla_out_proj (the "DeepSeek-V3
+ * Technical Report" notes, MLA section), and the same sums in the same order,
+ * so its u is bit-identical to mla_out_proj's for the same inputs.
+ *
+ * mla_out_proj_pack: w_o [d_model, K] bf16 row-major -> w_packed (same size,
+ * d_model*K*2 bytes, caller-owned, must not overlap w_o).
+ * mla_out_proj_packed: o [n_tokens, n_h, d_h] bf16; w_packed as written by
+ * mla_out_proj_pack; u [n_tokens, d_model] in u_dtype (MLA_F32 or MLA_BF16);
+ * workspace/ws_bytes: at least mla_out_proj_workspace_size(dims, d_model,
+ * n_tokens, MLA_BF16, ...) bytes.
+ * Both need q_dtype = MLA_BF16 (else MLA_ERR_DTYPE), d_model % 32 == 0, K %
+ * 256 == 0 and d_model*K*2 < 2^31 (else MLA_ERR_UNSUPPORTED).  Other errors:
+ * MLA_ERR_NULL, MLA_ERR_ARG (d_model or n_tokens < 1, overlapping pack
+ * buffers), MLA_ERR_ALIGN, MLA_ERR_WORKSPACE; nothing is enqueued on an
+ * error.                                                                  */
+int32_t mla_out_proj_pack(const mla_dims_t* dims, const void* w_o, int32_t d_model,
+                          void* w_packed, void* stream);
+int32_t mla_out_proj_packed(const mla_dims_t* dims, const void* o, const void* w_packed,
+                            int32_t d_model, void* u, int32_t u_dtype, int32_t n_tokens,
+                            void* workspace, size_t ws_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

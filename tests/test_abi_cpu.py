@@ -123,6 +123,35 @@ def test_out_proj_validation(mla):
     assert op(ctypes.byref(d), FAKE, 1, FAKE, 5120, FAKE, 0, 32, FAKE, 1024, None) == WS
 
 
+def test_out_proj_packed_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    d32 = _v2(b, q_dtype="f32")
+    W2 = FAKE + (1 << 30)               # a second buffer, clear of FAKE's 168 MB
+    pk = lib.mla_out_proj_pack
+    assert pk(ctypes.byref(d), None, 5120, W2, None) == NULL
+    assert pk(ctypes.byref(d), FAKE, 5120, None, None) == NULL
+    assert pk(ctypes.byref(d), FAKE, 0, W2, None) == ARG
+    assert pk(ctypes.byref(d32), FAKE, 5120, W2, None) == DTYPE
+    assert pk(ctypes.byref(d), FAKE, 5136, W2, None) == UNSUP       # d_model % 32 != 0
+    assert pk(ctypes.byref(d), FAKE, 65536, W2, None) == UNSUP      # 2 GiB of W^O
+    assert pk(ctypes.byref(d), MIS, 5120, W2, None) == ALIGN
+    assert pk(ctypes.byref(d), FAKE, 5120, FAKE + 4096, None) == ARG  # overlapping
+    op = lib.mla_out_proj_packed
+    big = 1 << 30
+    assert op(ctypes.byref(d), None, FAKE, 5120, FAKE, 0, 32, FAKE, big, None) == NULL
+    assert op(ctypes.byref(d), FAKE, None, 5120, FAKE, 0, 32, FAKE, big, None) == NULL
+    assert op(ctypes.byref(d), FAKE, FAKE, 5120, None, 0, 32, FAKE, big, None) == NULL
+    assert op(ctypes.byref(d32), FAKE, FAKE, 5120, FAKE, 0, 32, FAKE, big, None) == DTYPE
+    assert op(ctypes.byref(d), FAKE, FAKE, 5120, FAKE, 2, 32, FAKE, big, None) == DTYPE
+    assert op(ctypes.byref(d), FAKE, FAKE, 5120, FAKE, 0, 0, FAKE, big, None) == ARG
+    assert op(ctypes.byref(d), FAKE, FAKE, 0, FAKE, 0, 32, FAKE, big, None) == ARG
+    assert op(ctypes.byref(d), FAKE, FAKE, 5136, FAKE, 0, 32, FAKE, big, None) == UNSUP
+    assert op(ctypes.byref(d), FAKE, MIS, 5120, FAKE, 0, 32, FAKE, big, None) == ALIGN
+    assert op(ctypes.byref(d), FAKE, FAKE, 5120, FAKE, 0, 32, None, 0, None) == WS
+    assert op(ctypes.byref(d), FAKE, FAKE, 5120, FAKE, 0, 32, FAKE, 1024, None) == WS
+
+
 def test_kv_produce_validation(mla):
     lib, b = mla
     d = _v2(b)

@@ -692,6 +692,57 @@ def test_out_proj_parity(w, n_tok, u_kind):
 
 
 
+OUT_PROJ_PACKED = [
+    (V2, 32, "f32"),            # one token tile, 5-wave workgroups
+    (V2, 45, "bf16"),           # a ragged second token tile (groups of 4 tiles)
+    (V2, 256, "f32"),           # groups of 8 token tiles
+    (small_variant(V2, name="v2_d256", d_model=256), 7, "f32"),      # 128-row feature blocks
+    (small_variant(V2, name="v2_d352", d_model=352), 300, "bf16"),   # partial last block
+]
+
+
+def _panel_layout(w_rm):
+    """The documented panel layout of mla_out_proj_packed, from the row-major
+    matrix: element (f, k) at ((f/32)(K/64) + k/64) 2048 + (f%32) 64 + k%64."""
+    d, K = w_rm.shape
+    return w_rm.reshape(d // 32, 32, K // 64, 64).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("w,n_tok,u_kind", OUT_PROJ_PACKED,
+                         ids=[f"{c[0].name}-{c[1]}-{c[2]}" for c in OUT_PROJ_PACKED])
+def test_out_proj_packed_parity(w, n_tok, u_kind):
+    """mla_out_proj_pack writes the documented panel layout (bit-exact), and
+    mla_out_proj_packed gives the same u, bit for bit, as mla_out_proj on the
+    row-major W^O, and matches the oracle."""
+    from head_latent_attention_11_amd import binding as B
+    from head_latent_attention_11_amd.runner import to_device
+    from mla_inputs import bf16_bits_from_f32, output_weights
+    say(f"case out_proj_packed {w.name}: n_tok={n_tok} d_model={w.d_model} u={u_kind}")
+    rng = np.random.default_rng(93)
+    o_st = bf16_bits_from_f32(rng.standard_normal((n_tok, w.n_heads, w.d_head)).astype(np.float32))
+    w_o = output_weights(w)
+    dims = B.MLADims.from_workload(w)
+    o_d = to_device(o_st, "bf16", "cuda")
+    w_d = to_device(w_o, "bf16", "cuda")
+    w_p = torch.full_like(w_d, float("nan"))
+    B.out_proj_pack(dims, w_d, w.d_model, w_p)
+    torch.cuda.synchronize()
+    got_p = w_p.view(torch.int16).cpu().numpy().reshape(-1)
+    assert np.array_equal(got_p, _panel_layout(w_o.view(np.int16))), "panel layout differs"
+    udt = torch.float32 if u_kind == "f32" else torch.bfloat16
+    wsb = B.out_proj_workspace_size(dims, w.d_model, n_tok, B.BF16)
+    ws = torch.full(((wsb + 15) // 16 * 4,), float("nan"), dtype=torch.float32, device="cuda")
+    u_p = torch.full((n_tok, w.d_model), float("nan"), dtype=udt, device="cuda")
+    u_r = torch.full((n_tok, w.d_model), float("nan"), dtype=udt, device="cuda")
+    B.out_proj_packed(dims, o_d, w_p, w.d_model, u_p, n_tok, ws, wsb)
+    torch.cuda.synchronize()
+    B.out_proj(dims, o_d, w_d, w.d_model, u_r, n_tok, ws, wsb)
+    torch.cuda.synchronize()
+    assert torch.equal(u_p, u_r), "packed and row-major projections differ"
+    ref = omla.output_project(formats.bf16_to_f64(o_st), formats.bf16_to_f64(w_o))
+    check("u", to_np(u_p), ref, 1e-5 if u_kind == "f32" else 4e-3)
+
+
 # ------------------------------ cache producer: [RMSNorm(W^DKV h) ; RoPE(W^KR h)]
 PRODUCE = [
     (V2, "contiguous", True),
