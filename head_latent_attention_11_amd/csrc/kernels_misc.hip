@@ -254,9 +254,123 @@ __global__ __launch_bounds__(256) void absorb_general_kernel(
 }
 
 // ================================================================ append
+// Cache slot of new row r (sequence seq_idx[r], position pos[r]), or -1 when
+// the row is skipped (sequence or position out of range, unmapped page, slot
+// past the cache).
+__device__ inline long long append_slot(const int32_t* __restrict__ seq_idx,
+                                        const int32_t* __restrict__ pos,
+                                        const int32_t* __restrict__ page_table, int B,
+                                        int max_pages, int max_len, long long cache_rows, int r) {
+  const int sq = seq_idx[r], p = pos[r];
+  if (sq < 0 || sq >= B || p < 0) return -1;
+  long long row;
+  if (page_table) {
+    if (p / kPage >= max_pages) return -1;
+    const int page = page_table[(size_t)sq * max_pages + p / kPage];
+    if (page < 0) return -1;
+    row = (long long)page * kPage + p % kPage;
+  } else {
+    if (p >= max_len) return -1;
+    row = (long long)sq * max_len + p;
+  }
+  return row < cache_rows ? row : -1;
+}
+
+// One wave writes cache slot `row` from a new row whose element e of c^KV is
+// ld_c(e) and element q of k^R is ld_kr(q): optional RoPE of k^R at position
+// p, optional RMS norm of the c^KV part (c_i * g_i / sqrt(mean(c^2) + eps)),
+// then the cache format (fp32, bf16, 6-bit blocks, or fp8 with a row scale).
+template <int KV, typename LdC, typename LdKr>
+__device__ inline void append_row(LdC ld_c, LdKr ld_kr, int lane, long long row, int p,
+                                  int apply_rope, void* __restrict__ cache,
+                                  float* __restrict__ kv_scale, int d_c, int d_r, RopeFreq rope,
+                                  const float* __restrict__ norm_gain, float norm_eps) {
+  const int D = d_c + d_r;
+  // gather this lane's elements (at most 10 per lane: D <= 640)
+  float v[10];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int e = lane + 64 * k;
+    float x = 0.f;
+    if (e < d_c) {
+      x = ld_c(e);
+    } else if (e < D) {
+      const int q = e - d_c;
+      if (apply_rope) {
+        const int kp = q >> 1;
+        float x0 = ld_kr(2 * kp);
+        float x1 = ld_kr(2 * kp + 1);
+        float y0, y1;
+        rope_pair(x0, x1, p, kp, d_r, rope, &y0, &y1);
+        x = (q & 1) ? y1 : y0;
+      } else {
+        x = ld_kr(q);
+      }
+    }
+    v[k] = x;
+  }
+  if (norm_gain) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 10; ++k)
+      if (lane + 64 * k < d_c) ss = fmaf(v[k], v[k], ss);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss / float(d_c) + norm_eps);
+#pragma unroll
+    for (int k = 0; k < 10; ++k)
+      if (lane + 64 * k < d_c) v[k] = v[k] * inv * norm_gain[lane + 64 * k];
+  }
+#pragma unroll
+  for (int k = 0; k < 10; ++k) amax = fmaxf(amax, fabsf(v[k]));
+  if (KV == MLA_F32) {
+    float* dst = (float*)cache + row * D;
+#pragma unroll
+    for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = v[k];
+  } else if (KV == MLA_BF16) {
+    uint16_t* dst = (uint16_t*)cache + row * D;
+#pragma unroll
+    for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = f32_to_bf16_bits(v[k]);
+  } else if (KV == MLA_FP6_E2M3) {
+    // D = 576: element lane + 64 k is element lane % 32 of block 2 k +
+    // lane / 32, so each block is one half-wave at one k
+    uint8_t* dst = (uint8_t*)cache + row * kMxRowBytes;
+    const int i = lane & 31;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      float am = fabsf(v[k]);
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      const int ex = mx_block_exponent(am);
+      const uint32_t c = f32_to_e2m3(ldexpf(v[k], -ex));   // exact scaling
+      const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64);
+      const uint32_t c3 = __shfl_down(c, 3, 64);
+      const int blk = 2 * k + (lane >> 5);
+      if ((i & 3) == 0) {                  // codes i .. i+3: 24 bits, 3 bytes
+        const uint32_t w = c | (c1 << 6) | (c2 << 12) | (c3 << 18);
+        uint8_t* q = dst + 24 * blk + 3 * (i >> 2);
+        q[0] = uint8_t(w);
+        q[1] = uint8_t(w >> 8);
+        q[2] = uint8_t(w >> 16);
+      }
+      if (i == 0) dst[432 + blk] = uint8_t(ex + 127);
+    }
+    if (lane == 0) { dst[450] = 0; dst[451] = 0; }
+  } else {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float sc = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
+    uint8_t* dst = (uint8_t*)cache + row * D;
+#pragma unroll
+    for (int k = 0; k < 10; ++k)
+      if (lane + 64 * k < D) dst[lane + 64 * k] = uint8_t(f32_to_e4m3(__fdiv_rn(v[k], sc)));
+    if (lane == 0) kv_scale[row] = sc;
+  }
+}
+
 // One wave per new row.  Source rows are F32 or BF16, row r of new_c at
-// r * c_stride (elements), of new_kr at r * kr_stride.  With norm_gain, the
-// c^KV part is RMS-normalised first: c_i * g_i / sqrt(mean(c^2) + eps).
+// r * c_stride (elements), of new_kr at r * kr_stride.
 template <typename SrcT, int KV>
 __global__ __launch_bounds__(256) void append_kernel(
     const SrcT* __restrict__ new_c, const SrcT* __restrict__ new_kr,
@@ -266,104 +380,56 @@ __global__ __launch_bounds__(256) void append_kernel(
     float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, RopeFreq rope,
     int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps) {
   const int lane = threadIdx.x & 63;
-  const int D = d_c + d_r;
   for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += gridDim.x * 4) {
-    const int sq = seq_idx[r], p = pos[r];
-    if (sq < 0 || sq >= B || p < 0) continue;
-    long long row;
-    if (page_table) {
-      if (p / kPage >= max_pages) continue;
-      const int page = page_table[(size_t)sq * max_pages + p / kPage];
-      if (page < 0) continue;
-      row = (long long)page * kPage + p % kPage;
-    } else {
-      if (p >= max_len) continue;
-      row = (long long)sq * max_len + p;
-    }
-    if (row >= cache_rows) continue;
-
-    // gather this lane's elements (at most 10 per lane: D <= 640)
-    float v[10];
-    float amax = 0.f;
-#pragma unroll
-    for (int k = 0; k < 10; ++k) {
-      const int e = lane + 64 * k;
-      float x = 0.f;
-      if (e < d_c) {
-        x = load_f(new_c, (size_t)r * c_stride + e);
-      } else if (e < D) {
-        const int q = e - d_c;
-        if (apply_rope) {
-          const int kp = q >> 1;
-          float x0 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp);
-          float x1 = load_f(new_kr, (size_t)r * kr_stride + 2 * kp + 1);
-          float y0, y1;
-          rope_pair(x0, x1, p, kp, d_r, rope, &y0, &y1);
-          x = (q & 1) ? y1 : y0;
-        } else {
-          x = load_f(new_kr, (size_t)r * kr_stride + q);
-        }
-      }
-      v[k] = x;
-    }
-    if (norm_gain) {
-      float ss = 0.f;
-#pragma unroll
-      for (int k = 0; k < 10; ++k)
-        if (lane + 64 * k < d_c) ss = fmaf(v[k], v[k], ss);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-      const float inv = 1.0f / sqrtf(ss / float(d_c) + norm_eps);
-#pragma unroll
-      for (int k = 0; k < 10; ++k)
-        if (lane + 64 * k < d_c) v[k] = v[k] * inv * norm_gain[lane + 64 * k];
-    }
-#pragma unroll
-    for (int k = 0; k < 10; ++k) amax = fmaxf(amax, fabsf(v[k]));
-    if (KV == MLA_F32) {
-      float* dst = (float*)cache + row * D;
-#pragma unroll
-      for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = v[k];
-    } else if (KV == MLA_BF16) {
-      uint16_t* dst = (uint16_t*)cache + row * D;
-#pragma unroll
-      for (int k = 0; k < 10; ++k) if (lane + 64 * k < D) dst[lane + 64 * k] = f32_to_bf16_bits(v[k]);
-    } else if (KV == MLA_FP6_E2M3) {
-      // D = 576: element lane + 64 k is element lane % 32 of block 2 k +
-      // lane / 32, so each block is one half-wave at one k
-      uint8_t* dst = (uint8_t*)cache + row * kMxRowBytes;
-      const int i = lane & 31;
-#pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        float am = fabsf(v[k]);
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
-        const int ex = mx_block_exponent(am);
-        const uint32_t c = f32_to_e2m3(ldexpf(v[k], -ex));   // exact scaling
-        const uint32_t c1 = __shfl_down(c, 1, 64), c2 = __shfl_down(c, 2, 64);
-        const uint32_t c3 = __shfl_down(c, 3, 64);
-        const int blk = 2 * k + (lane >> 5);
-        if ((i & 3) == 0) {                  // codes i .. i+3: 24 bits, 3 bytes
-          const uint32_t w = c | (c1 << 6) | (c2 << 12) | (c3 << 18);
-          uint8_t* p = dst + 24 * blk + 3 * (i >> 2);
-          p[0] = uint8_t(w);
-          p[1] = uint8_t(w >> 8);
-          p[2] = uint8_t(w >> 16);
-        }
-        if (i == 0) dst[432 + blk] = uint8_t(ex + 127);
-      }
-      if (lane == 0) { dst[450] = 0; dst[451] = 0; }
-    } else {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-      const float s = (amax == 0.f) ? 1.0f : __fdiv_rn(amax, 448.0f);
-      uint8_t* dst = (uint8_t*)cache + row * D;
-#pragma unroll
-      for (int k = 0; k < 10; ++k)
-        if (lane + 64 * k < D) dst[lane + 64 * k] = uint8_t(f32_to_e4m3(__fdiv_rn(v[k], s)));
-      if (lane == 0) kv_scale[row] = s;
-    }
+    const long long row = append_slot(seq_idx, pos, page_table, B, max_pages, max_len,
+                                      cache_rows, r);
+    if (row < 0) continue;
+    const SrcT* c = new_c + (size_t)r * c_stride;
+    const SrcT* kr = new_kr + (size_t)r * kr_stride;
+    append_row<KV>([&](int e) { return load_f(c, e); }, [&](int q) { return load_f(kr, q); },
+                   lane, row, pos[r], apply_rope, cache, kv_scale, d_c, d_r, rope, norm_gain,
+                   norm_eps);
   }
+}
+
+// The cache producer's second half: one workgroup per new row sums the
+// projection's K-block partials of the row (part [nkb, n_rows, D] fp32, in
+// K-block order) into LDS, then wave 0 appends the row as append_kernel does.
+template <int KV>
+__global__ __launch_bounds__(192) void produce_append_kernel(
+    const float* __restrict__ part, int nkb, const int32_t* __restrict__ seq_idx,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ page_table, int B,
+    int max_pages, int max_len, long long cache_rows, int apply_rope,
+    void* __restrict__ cache, float* __restrict__ kv_scale, int n_rows, int d_c, int d_r,
+    RopeFreq rope, const float* __restrict__ norm_gain, float norm_eps) {
+  __shared__ __attribute__((aligned(16))) float srow[640];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const long long row = append_slot(seq_idx, pos, page_table, B, max_pages, max_len,
+                                    cache_rows, r);
+  if (row < 0) return;                 // uniform over the workgroup
+  const int D = d_c + d_r;             // D % 4 == 0
+  const size_t kstride = (size_t)n_rows * D;
+  if (4 * tid < D) {
+    // every K block's partial is loaded before any is added (at most 16 in
+    // flight), then summed in K-block order
+    const float* src = part + (size_t)r * D + 4 * tid;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < nkb; k0 += 16) {
+      floatx4 v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k0 + k < nkb) v[k] = *(const floatx4*)(src + (k0 + k) * kstride);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k0 + k < nkb) acc += v[k];
+    }
+    *(floatx4*)(srow + 4 * tid) = acc;
+  }
+  __syncthreads();
+  if (tid < 64)
+    append_row<KV>([&](int e) { return srow[e]; }, [&](int q) { return srow[d_c + q]; }, tid,
+                   row, pos[r], apply_rope, cache, kv_scale, d_c, d_r, rope, norm_gain,
+                   norm_eps);
 }
 
 // =============================================================== combine
@@ -698,6 +764,24 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
   else if (!src_f32) MLA_APPEND(uint16_t, MLA_FP8_E4M3);
   else MLA_APPEND(float, MLA_FP8_E4M3);
 #undef MLA_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_produce_append(const mla_dims_t& d, const float* part, int nkb,
+                                 const int32_t* seq_idx, const int32_t* pos,
+                                 const int32_t* page_table, int B, int max_pages, int max_len,
+                                 long long cache_rows, int apply_rope, void* cache,
+                                 float* kv_scale, int n_rows, RopeFreq rope, hipStream_t st,
+                                 const float* norm_gain, float norm_eps) {
+#define MLA_PRODUCE(KV)                                                                       \
+  hipLaunchKernelGGL((produce_append_kernel<KV>), dim3(n_rows), dim3(192), 0, st, part, nkb,  \
+                     seq_idx, pos, page_table, B, max_pages, max_len, cache_rows, apply_rope, \
+                     cache, kv_scale, n_rows, d.d_latent, d.d_rope, rope, norm_gain, norm_eps)
+  if (d.kv_dtype == MLA_F32) MLA_PRODUCE(MLA_F32);
+  else if (d.kv_dtype == MLA_BF16) MLA_PRODUCE(MLA_BF16);
+  else if (d.kv_dtype == MLA_FP6_E2M3) MLA_PRODUCE(MLA_FP6_E2M3);
+  else MLA_PRODUCE(MLA_FP8_E4M3);
+#undef MLA_PRODUCE
   return hipGetLastError();
 }
 

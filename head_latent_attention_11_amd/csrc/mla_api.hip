@@ -23,6 +23,11 @@ size_t gemm_xwt_workspace(int, int, int, int, int);
 hipError_t launch_gemm_xwt(const void*, int, const void*, int, void*, bool, int, int, int, void*,
                            hipStream_t, bool packed = false);
 bool gemm_xwt_packable(int, int, int, int);
+bool gemm_xwt_fast(int, int, int, int);
+int gemm_xwt_nkb(int, int);
+hipError_t launch_produce_append(const mla_dims_t&, const float*, int, const int32_t*,
+                                 const int32_t*, const int32_t*, int, int, int, long long, int,
+                                 void*, float*, int, RopeFreq, hipStream_t, const float*, float);
 hipError_t launch_gemm_pack(const void*, void*, int, int, hipStream_t);
 hipError_t launch_up_proj(const mla_dims_t&, bool, const float*, const void*, void*, bool,
                           int, hipStream_t);
@@ -358,8 +363,14 @@ static int32_t check_append(const mla_dims_t* dims, const int32_t* seq_idx, cons
   return MLA_OK;
 }
 
-static size_t produce_rows_bytes(const mla_dims_t* d, int32_t n_rows) {
-  return ((size_t)n_rows * (d->d_latent + d->d_rope) * sizeof(float) + 255) / 256 * 256;
+// Workspace of the producer: the projection's K-block partials (matrix-core
+// path, summed inside the append kernel) or the projected rows in fp32
+// (general path).
+static size_t produce_ws_bytes(const mla_dims_t* d, int32_t d_model, int32_t n_rows) {
+  const int D = d->d_latent + d->d_rope;
+  if (gemm_xwt_fast(D, d_model, d->q_dtype, d->q_dtype))
+    return gemm_xwt_workspace(D, d_model, n_rows, d->q_dtype, d->q_dtype);
+  return (size_t)n_rows * D * sizeof(float);
 }
 
 int32_t mla_kv_produce_workspace_size(const mla_dims_t* dims, int32_t d_model, int32_t n_rows,
@@ -368,9 +379,7 @@ int32_t mla_kv_produce_workspace_size(const mla_dims_t* dims, int32_t d_model, i
   if (st != MLA_OK) return st;
   if (!bytes) return MLA_ERR_NULL;
   if (d_model < 1 || n_rows < 1) return MLA_ERR_ARG;
-  const int D = dims->d_latent + dims->d_rope;
-  *bytes = produce_rows_bytes(dims, n_rows) +
-           gemm_xwt_workspace(D, d_model, n_rows, dims->q_dtype, dims->q_dtype);
+  *bytes = produce_ws_bytes(dims, d_model, n_rows);
   return MLA_OK;
 }
 
@@ -392,14 +401,24 @@ int32_t mla_kv_produce(const mla_dims_t* dims, const void* h, int32_t d_model,
       (workspace && !aligned16(workspace)))
     return MLA_ERR_ALIGN;
   const int D = dims->d_latent + dims->d_rope;
-  const size_t rows_b = produce_rows_bytes(dims, n_rows);
-  const size_t need = rows_b + gemm_xwt_workspace(D, d_model, n_rows, dims->q_dtype,
-                                                  dims->q_dtype);
-  if (!workspace || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!workspace || ws_bytes < produce_ws_bytes(dims, d_model, n_rows))
+    return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (gemm_xwt_fast(D, d_model, dims->q_dtype, dims->q_dtype)) {
+    // two launches: the projection's K-block partials, then their sum,
+    // the norm, RoPE and the store, one workgroup per row
+    hipError_t e = launch_gemm_xwt(h, dims->q_dtype, w_dkv_kr, dims->q_dtype, nullptr, true,
+                                   n_rows, D, d_model, workspace, s);
+    if (e != hipSuccess) return MLA_ERR_LAUNCH;
+    return status_of(launch_produce_append(*dims, (const float*)workspace,
+                                           gemm_xwt_nkb(D, d_model), seq_idx, pos, page_table,
+                                           batch, max_pages, max_len, cache_rows, apply_rope,
+                                           cache, kv_scale, n_rows, rope_of(dims), s, norm_gain,
+                                           norm_eps));
+  }
   float* rows = (float*)workspace;
   hipError_t e = launch_gemm_xwt(h, dims->q_dtype, w_dkv_kr, dims->q_dtype, rows, true, n_rows,
-                                 D, d_model, (char*)workspace + rows_b, s);
+                                 D, d_model, nullptr, s);
   if (e != hipSuccess) return MLA_ERR_LAUNCH;
   return status_of(launch_append(*dims, rows, rows + dims->d_latent, seq_idx, pos, page_table,
                                  batch, max_pages, max_len, cache_rows, apply_rope, cache,

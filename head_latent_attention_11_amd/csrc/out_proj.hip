@@ -476,10 +476,15 @@ hipError_t launch_gemm_pack(const void* w, void* w_packed, int d_out, int K, hip
   return hipGetLastError();
 }
 
+int gemm_xwt_nkb(int d_out, int K) { return gemm_plan(d_out, K).nkb; }
+
+// The matrix-core path: partial sums [nkb, n_tok, d_out] fp32 into
+// workspace, then (when out != nullptr) their sum into out.
 hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtype,
                            void* out, bool out_f32, int n_tok, int d_out, int K,
                            void* workspace, hipStream_t st, bool packed) {
   if (packed && !gemm_xwt_packable(d_out, K, x_dtype, w_dtype)) return hipErrorInvalidValue;
+  if (!out && !gemm_xwt_fast(d_out, K, x_dtype, w_dtype)) return hipErrorInvalidValue;
   if (gemm_xwt_fast(d_out, K, x_dtype, w_dtype)) {
     // one token tile with a 6-slot ring for at most 32 tokens, groups of 4
     // token tiles with a 4-slot ring up to 128 tokens, else groups of 8
@@ -505,6 +510,7 @@ hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtyp
     if (packed) { MLA_OPK_ALL(true) } else { MLA_OPK_ALL(false) }
 #undef MLA_OPK_ALL
 #undef MLA_OPK
+    if (!out) return hipGetLastError();
     const size_t n4 = (size_t)n_tok * d_out / 4;
     const dim3 rgrid((unsigned)((n4 + 255) / 256));
     if (out_f32)

@@ -313,7 +313,8 @@ int32_t mla_up_proj_v(const mla_dims_t* dims, const float* latent,
  * batch, max_pages, max_len, cache_rows, apply_rope, cache, kv_scale, n_rows:
  * as mla_cache_append (rows whose slot falls outside the cache are skipped).
  * workspace/ws_bytes: at least mla_kv_produce_workspace_size() bytes (the
- * projected rows in fp32, and the projection's partial sums).  Errors: those
+ * projection's fp32 partial sums over K blocks, or its fp32 rows when the
+ * operands are fp32).  Errors: those
  * of mla_cache_append, MLA_ERR_ARG for d_model < 1 or a negative or
  * non-finite norm_eps, MLA_ERR_WORKSPACE; nothing is enqueued on an error.  */
 int32_t mla_kv_produce_workspace_size(const mla_dims_t* dims, int32_t d_model,
