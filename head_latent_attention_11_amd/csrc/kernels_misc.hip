@@ -280,35 +280,43 @@ __device__ inline long long append_slot(const int32_t* __restrict__ seq_idx,
 // ld_c(e) and element q of k^R is ld_kr(q): optional RoPE of k^R at position
 // p, optional RMS norm of the c^KV part (c_i * g_i / sqrt(mean(c^2) + eps)),
 // then the cache format (fp32, bf16, 6-bit blocks, or fp8 with a row scale).
+// Every load of the row (and of the norm gains) is issued before the first
+// is used, at clamped indices, and the lane's elements are selected after:
+// loads inside per-element branches would each wait for the previous one.
 template <int KV, typename LdC, typename LdKr>
 __device__ inline void append_row(LdC ld_c, LdKr ld_kr, int lane, long long row, int p,
                                   int apply_rope, void* __restrict__ cache,
                                   float* __restrict__ kv_scale, int d_c, int d_r, RopeFreq rope,
                                   const float* __restrict__ norm_gain, float norm_eps) {
   const int D = d_c + d_r;
-  // gather this lane's elements (at most 10 per lane: D <= 640)
+  // element lane + 64 k (at most 10 per lane: D <= 640)
+  float xc[10], xa[10], xb[10], gn[10];
+#pragma unroll
+  for (int k = 0; k < 10; ++k) {
+    const int e = lane + 64 * k;
+    const int q = min(max(e - d_c, 0), d_r - 1);
+    xc[k] = ld_c(min(e, d_c - 1));
+    xa[k] = ld_kr(apply_rope ? (q & ~1) : q);          // the pair's first element, or q
+    xb[k] = ld_kr(apply_rope ? (q | 1) : q);           // the pair's second element
+    gn[k] = norm_gain ? norm_gain[min(e, d_c - 1)] : 1.f;
+  }
   float v[10];
   float amax = 0.f;
 #pragma unroll
   for (int k = 0; k < 10; ++k) {
     const int e = lane + 64 * k;
     float x = 0.f;
-    if (e < d_c) {
-      x = ld_c(e);
-    } else if (e < D) {
-      const int q = e - d_c;
+    if (64 * k < D && 64 * k + 63 >= d_c) {           // the wave holds k^R elements here
+      const int q = min(max(e - d_c, 0), d_r - 1);
+      float y = xa[k];
       if (apply_rope) {
-        const int kp = q >> 1;
-        float x0 = ld_kr(2 * kp);
-        float x1 = ld_kr(2 * kp + 1);
         float y0, y1;
-        rope_pair(x0, x1, p, kp, d_r, rope, &y0, &y1);
-        x = (q & 1) ? y1 : y0;
-      } else {
-        x = ld_kr(q);
+        rope_pair(xa[k], xb[k], p, q >> 1, d_r, rope, &y0, &y1);
+        y = (q & 1) ? y1 : y0;
       }
+      x = (e >= d_c && e < D) ? y : 0.f;
     }
-    v[k] = x;
+    v[k] = (e < d_c) ? xc[k] : x;
   }
   if (norm_gain) {
     float ss = 0.f;
@@ -320,7 +328,7 @@ __device__ inline void append_row(LdC ld_c, LdKr ld_kr, int lane, long long row,
     const float inv = 1.0f / sqrtf(ss / float(d_c) + norm_eps);
 #pragma unroll
     for (int k = 0; k < 10; ++k)
-      if (lane + 64 * k < d_c) v[k] = v[k] * inv * norm_gain[lane + 64 * k];
+      if (lane + 64 * k < d_c) v[k] = v[k] * inv * gn[k];
   }
 #pragma unroll
   for (int k = 0; k < 10; ++k) amax = fmaxf(amax, fabsf(v[k]));
