@@ -134,12 +134,12 @@ int32_t qabs_dtype(const mla_dims_t* d) {
 }
 
 RopeFreq rope_of(const mla_dims_t* d) {
-  RopeFreq r;
-  r.base = d->rope_base > 0.f ? d->rope_base : 10000.f;
-  r.factor = d->yarn_factor > 1.f ? d->yarn_factor : 1.f;
-  r.alpha = d->yarn_alpha;
-  r.beta = d->yarn_beta;
-  r.orig_len = (float)d->yarn_orig_len;
+  RopeFreq r{};
+  const double base = d->rope_base > 0.f ? d->rope_base : 10000.f;
+  const double factor = d->yarn_factor > 1.f ? d->yarn_factor : 1.f;
+  for (int k = 0; k < d->d_rope / 2 && k < kMaxRopePairs; ++k)
+    r.theta[k] = rope_theta_host(k, d->d_rope, base, factor, d->yarn_alpha, d->yarn_beta,
+                                 (double)d->yarn_orig_len);
   return r;
 }
 

@@ -119,21 +119,26 @@ constexpr int kMxRowBytes = 452;     // 6-bit cache row: 432 code bytes, 18 expo
 // and with context extension (factor > 1, YaRN's NTK-by-parts rule) pair k,
 // which turns r_k = orig_len theta_k / (2 pi) times over the original
 // context, takes (1 - g) theta_k / factor + g theta_k with g = clamp((r_k -
-// alpha) / (beta - alpha), 0, 1).  Computed in double precision.
+// alpha) / (beta - alpha), 0, 1).  Computed in double precision on the host,
+// once per call, and handed to the kernels as a table (a power in double
+// precision per rotated pair would dominate the append of a decode step).
+constexpr int kMaxRopePairs = 64;     // d_rope <= 128
 struct RopeFreq {
-  float base;
-  float factor;     // <= 1: no extension
-  float alpha, beta;
-  float orig_len;
+  double theta[kMaxRopePairs];
 };
 
-__host__ __device__ inline double rope_theta(int k, int d, const RopeFreq& rf) {
-  const double theta = pow((double)rf.base, -2.0 * (double)k / (double)d);
-  if (!(rf.factor > 1.0f)) return theta;
-  const double turns = (double)rf.orig_len * theta / 6.283185307179586;
-  double g = (turns - (double)rf.alpha) / ((double)rf.beta - (double)rf.alpha);
+inline double rope_theta_host(int k, int d, double base, double factor, double alpha,
+                              double beta, double orig_len) {
+  const double theta = pow(base, -2.0 * (double)k / (double)d);
+  if (!(factor > 1.0)) return theta;
+  const double turns = orig_len * theta / 6.283185307179586;
+  double g = (turns - alpha) / (beta - alpha);
   g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
-  return (1.0 - g) * theta / (double)rf.factor + g * theta;
+  return (1.0 - g) * theta / factor + g * theta;
+}
+
+__host__ __device__ inline double rope_theta(int k, int /*d*/, const RopeFreq& rf) {
+  return rf.theta[k];
 }
 
 // ------------------------------------------------------------ split planner
