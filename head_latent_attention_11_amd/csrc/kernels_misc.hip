@@ -54,6 +54,7 @@ template <> __device__ inline void store_f<uint16_t>(uint16_t* p, size_t i, floa
 // written as one contiguous run.
 constexpr int kAbsCols = 128, kAbsDh = 128, kAbsLdsRow = kAbsCols + 8;
 constexpr int kAbsOutRow = 528;       // bytes per token row of the output staging
+constexpr int kAbsRopeBatch = 8;      // RoPE pairs of a thread whose loads fly together
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
@@ -89,20 +90,25 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   // the blocks of 32 tokens t0 = 32 (y + k gridDim.y).
   // The RoPE part q_abs[..., 512:576] is shared out over the head's
   // workgroups: pair p = 256 cb + tid + 1024 (y + u gridDim.y) (token p / 32,
-  // pair k = p % 32 = tid % 32 for every u).  The first pair's inputs are
-  // loaded before the W^UK block (loads complete in order) and rotated while
-  // it is in flight.
+  // pair k = p % 32 = tid % 32 for every u), kAbsRopeBatch pairs of a thread
+  // at a time.  A batch's inputs are loaded at clamped indices, with no
+  // branch around the loads (so that they are in flight together), the
+  // first batch before the W^UK block; its rotations run while that block
+  // is in flight.
   const int n_pairs = n_tok * (DR / 2), rk = tid & 31;
   const int p_first = 1024 * blockIdx.y + cb * 256 + tid, p_step = 1024 * gridDim.y;
   const int t_first = 32 * blockIdx.y, t_step = 32 * gridDim.y;
-  float rx0 = 0.f, rx1 = 0.f;
-  int rpos = 0;
-  if (p_first < n_pairs) {
-    const uint16_t* src = q_rope + ((size_t)(p_first >> 5) * n_h + head) * DR + 2 * rk;
-    rx0 = bf16_bits_to_f32(src[0]);
-    rx1 = bf16_bits_to_f32(src[1]);
-    if (q_pos) rpos = q_pos[p_first >> 5];
-  }
+  uint32_t rxy[kAbsRopeBatch];         // the pair's two bf16 inputs
+  int rpos[kAbsRopeBatch];
+  auto load_pairs = [&](int p0) {
+#pragma unroll
+    for (int u = 0; u < kAbsRopeBatch; ++u) {
+      const int tok = min(p0 + u * p_step, n_pairs - 1) >> 5;
+      rxy[u] = *(const uint32_t*)(q_rope + ((size_t)tok * n_h + head) * DR + 2 * rk);
+      rpos[u] = q_pos ? q_pos[tok] : 0;
+    }
+  };
+  load_pairs(p_first);
 
   // query block loader: 32 tokens x 128 d_h = 512 chunks of 16 bytes
   auto load_q = [&](int t0, u32x4* qv) {
@@ -131,26 +137,25 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     stg[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
   const double theta = q_pos ? rope_theta(rk, DR, rope) : 0.0;
-  for (int p = p_first; p < n_pairs; p += p_step) {
-    const int tok = p >> 5;
-    float x0 = rx0, x1 = rx1;
-    int pos = rpos;
-    if (p != p_first) {
-      const uint16_t* src = q_rope + ((size_t)tok * n_h + head) * DR + 2 * rk;
-      x0 = bf16_bits_to_f32(src[0]);
-      x1 = bf16_bits_to_f32(src[1]);
-      if (q_pos) pos = q_pos[tok];
-    }
-    if (q_pos) rope_rot(x0, x1, pos, theta, &x0, &x1);
-    OutT* dst = q_abs + ((size_t)tok * n_h + head) * QROW + DC + 2 * rk;
-    if constexpr (sizeof(OutT) == 4) {
-      *(float2*)dst = float2{x0, x1};
-    } else {
-      const uint32_t hi = pack_bf16x2(x0, x1);
-      *(uint32_t*)dst = hi;
-      if constexpr (PAIRS)
-        *(uint32_t*)(dst + D) = pack_bf16x2(x0 - __builtin_bit_cast(float, hi << 16),
-                                            x1 - __builtin_bit_cast(float, hi & 0xFFFF0000u));
+  for (int p0 = p_first; p0 < n_pairs; p0 += kAbsRopeBatch * p_step) {
+    if (p0 != p_first) load_pairs(p0);
+#pragma unroll
+    for (int u = 0; u < kAbsRopeBatch; ++u) {
+      const int p = p0 + u * p_step;
+      float x0 = bf16_bits_to_f32(uint16_t(rxy[u])), x1 = bf16_bits_to_f32(uint16_t(rxy[u] >> 16));
+      if (q_pos) rope_rot(x0, x1, rpos[u], theta, &x0, &x1);
+      if (p < n_pairs) {
+        OutT* dst = q_abs + ((size_t)(p >> 5) * n_h + head) * QROW + DC + 2 * rk;
+        if constexpr (sizeof(OutT) == 4) {
+          *(float2*)dst = float2{x0, x1};
+        } else {
+          const uint32_t hi = pack_bf16x2(x0, x1);
+          *(uint32_t*)dst = hi;
+          if constexpr (PAIRS)
+            *(uint32_t*)(dst + D) = pack_bf16x2(x0 - __builtin_bit_cast(float, hi << 16),
+                                                x1 - __builtin_bit_cast(float, hi & 0xFFFF0000u));
+        }
+      }
     }
   }
 #pragma unroll
