@@ -625,13 +625,15 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
     const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
     wv[i] = *(const u32x4*)(wsrc + (size_t)r * DC + c8);
   }
-  floatx4 v[8];                        // 32 rows x 128 chunks of 4 floats
+  // 32 rows x 128 chunks of 4 floats.  Rows past the end read the last
+  // token's row (their outputs are not stored), with no branch around the
+  // loads, so that the block in flight is not waited for early.
+  floatx4 v[8];
   auto load_latent = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int ch = tid + 512 * i, t = ch >> 7, c4 = (ch & 127) * 4;
-      v[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (t0 + t < n_tok) v[i] = *(const floatx4*)(latent + ((size_t)(t0 + t) * n_h + head) * DC + c4);
+      const int ch = tid + 512 * i, t = min(t0 + (ch >> 7), n_tok - 1), c4 = (ch & 127) * 4;
+      v[i] = *(const floatx4*)(latent + ((size_t)t * n_h + head) * DC + c4);
     }
   };
   // blockIdx.y splits the tokens when there are few heads: group y takes
