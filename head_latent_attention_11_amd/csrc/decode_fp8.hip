@@ -97,7 +97,8 @@ __device__ inline uint32_t fp8_tile_offset(int u) {
 }
 
 // Staged query halves: 16-byte unit u holds row u / 37, unit u % 37 of the
-// half (unit 36 is the row padding).  Rows are q_row_bytes apart.
+// half (unit 36 is the row padding).  Rows are q_row_bytes apart (a
+// constant at the call, so the offsets fold).
 __device__ inline uint32_t fp8_q_offset(int u, int half, int q_row_bytes) {
   const int r = u / (QROW / 16), c = u - (QROW / 16) * r;
   return c == QROW / 16 - 1 ? kOOB : uint32_t(r * q_row_bytes + half * D + 16 * c);
@@ -163,6 +164,10 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
   if (pg_regs) {
     if (lane < pg_n) pg_lo = a.page_table[(size_t)b * a.max_pages + pg_first + lane];
     if (64 + lane < pg_n) pg_hi = a.page_table[(size_t)b * a.max_pages + pg_first + 64 + lane];
+    // wait for them here, before the query and tile loads: the compiler
+    // does not count the assembly loads and would otherwise wait for all of
+    // them (vmcnt(0)) at the first use of a page id
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 #define MLA_PAGE(ts_)                                                                      \
   (pg_regs ? __builtin_amdgcn_readlane(((ts_) / kPage - pg_first) < 64 ? pg_lo : pg_hi,   \
@@ -244,17 +249,17 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
   // dims through ring slots 2..5 while tiles 0 and 1 load into slots 0, 1.
   bf16x8 qf[D / 16];
   const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs +
-                                 ((size_t)b * rows + rb * ROWS_WG) * a.q_row_bytes);
+                                 ((size_t)b * rows + rb * ROWS_WG) * (2 * D));
   const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
-                     uint32_t(ROWS_WG * a.q_row_bytes), 0x00020000u};
+                     uint32_t(ROWS_WG * (2 * D)), 0x00020000u};
 #define MLA_Q_ISSUE(p_)                                                                    \
   do {                                                                                   \
     _Pragma("unroll") for (int n__ = 0; n__ < (QLOADS + 3) / 4; ++n__)                   \
       if (wave + 4 * n__ < QLOADS)                                                       \
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
                      :: "s"(lds0 + QSTAGE + 1024 * (wave + 4 * n__)),                    \
-                        "v"(fp8_q_offset(64 * (wave + 4 * n__) + lane, (p_), a.q_row_bytes)), \
+                        "v"(fp8_q_offset(64 * (wave + 4 * n__) + lane, (p_), (2 * D))), \
                         "s"(qrs)                                                         \
                      : "memory");                                                        \
   } while (0)
@@ -480,6 +485,7 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
 hipError_t launch_decode_fp8(const DecodeArgs& a, const ItemTable& tab, hipStream_t st) {
   // a.row_blocks counts blocks of 128 query rows
   const int grid = a.n_items * a.row_blocks;
+  if (a.q_row_bytes != 2 * D) return hipErrorInvalidValue;   // plain bf16 query rows only
   hipLaunchKernelGGL(decode_fp8_kernel, dim3(grid), dim3(256), 0, st, a, tab);
   return hipGetLastError();
 }

@@ -163,11 +163,7 @@ static_assert(QLOADS * 64 == ROWS_WG * (QROW / 16), "whole staged rows");
 
 // Staged query halves: 16-byte unit u holds row u / 37, unit u % 37 of the
 // half (unit 36 is the row padding: an out-of-range offset, zero-filled).
-// Rows are q_row_bytes apart (query pairs: only the hi part is read).
-__device__ inline uint32_t q_src_offset(int u, int half, int q_row_bytes) {
-  const int r = u / (QROW / 16), c = u - (QROW / 16) * r;
-  return c == QROW / 16 - 1 ? kOOB : uint32_t(r * q_row_bytes + half * D + 16 * c);
-}
+// Rows are QRB bytes apart (query pairs: only the hi part is read).
 
 // 32 E2M3 codes (6 dwords, code i at bits 6 i .. 6 i + 5) times 2^e -> 32
 // bf16 values, two per dword (even element in the low half).  Exact: every
@@ -190,11 +186,13 @@ __device__ inline void fp6x32_to_bf16x32(const uint32_t (&w)[6], float scale, u3
 }
 
 // KVK: cache kind, 0 = bf16, 2 = 6-bit (E2M3 codes with one power of two
-// per 32 elements).
-template <int KVK>
+// per 32 elements).  QRB: bytes between query rows (2 D, or 4 D for query
+// pairs), a constant so that the staging offsets fold.
+template <int KVK, int QRB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   static_assert(KVK == 0 || KVK == 2, "fp8 tiles run on decode_fp8_kernel");
+  static_assert(QRB == 2 * D || QRB == 4 * D, "plain bf16 rows or query pairs");
   constexpr bool FP6 = KVK == 2, RAW = KVK != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
   __shared__ int s_restart;
@@ -263,6 +261,10 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   if (pg_regs) {
     if (lane < pg_n) pg_lo = a.page_table[(size_t)b * a.max_pages + pg_first + lane];
     if (64 + lane < pg_n) pg_hi = a.page_table[(size_t)b * a.max_pages + pg_first + 64 + lane];
+    // wait for them here, before the query and tile loads: the compiler
+    // does not count the assembly loads and would otherwise wait for all of
+    // them (vmcnt(0)) at the first use of a page id
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
   // page id of the tile starting at token ts (ts inside the item)
@@ -410,21 +412,37 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   // wait, so their HBM latency overlaps the query staging.
   bf16x8 qf[D / 16];
   const uint64_t qa = (uint64_t)((const uint8_t*)a.q_abs +
-                                 ((size_t)b * rows + rb * ROWS_WG) * a.q_row_bytes);
+                                 ((size_t)b * rows + rb * ROWS_WG) * QRB);
   const u32x4 qrs = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qa),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(qa >> 32)) & 0xFFFFu,
-                     uint32_t(ROWS_WG * a.q_row_bytes), 0x00020000u};
+                     uint32_t(ROWS_WG * QRB), 0x00020000u};
   const uint32_t qlds = lds_ring + 2 * TILE_BYTES;
+  const int qu0 = 64 * wave + lane;                       // staging unit of load 0
   // half p_: load n = wave + 4k (n < QLOADS) fills staging units 64n .. 64n+63
+  // Loads k < QLOADS / 4 exist for every wave (wave + 4 k <= 3 + 4 (QLOADS / 4 - 1)
+  // < QLOADS) and are issued with no test: a bound test per load splits them
+  // into blocks, and the compiler then waits for all loads in flight before
+  // each one.  The staging unit u = 64 (wave + 4 k) + lane of load k is kept
+  // as row u / 37 and unit u % 37 and stepped by 256 = 6 * 37 + 34 units per
+  // load (32-bit adds and selects only).
+#define MLA_Q_LOAD(p_, n_, r_, c_)                                                         \
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"              \
+               :: "s"(qlds + 1024 * (n_)),                                                \
+                  "v"((c_) == QROW / 16 - 1 ? kOOB                                        \
+                                            : uint32_t((r_) * QRB + (p_) * D + 16 * (c_))), \
+                  "s"(qrs) : "memory")
 #define MLA_Q_ISSUE(p_)                                                                    \
   do {                                                                                   \
-    _Pragma("unroll") for (int k = 0; k < (QLOADS + 3) / 4; ++k)                         \
-      if (wave + 4 * k < QLOADS)                                                         \
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"        \
-                     :: "s"(qlds + 1024 * (wave + 4 * k)),                               \
-                        "v"(q_src_offset(64 * (wave + 4 * k) + lane, (p_), a.q_row_bytes)), \
-                        "s"(qrs)                                                         \
-                     : "memory");                                                        \
+    int r__ = qu0 / (QROW / 16), c__ = qu0 - (QROW / 16) * r__;                          \
+    _Pragma("unroll") for (int k = 0; k < QLOADS / 4; ++k) {                             \
+      MLA_Q_LOAD(p_, wave + 4 * k, r__, c__);                                            \
+      c__ += 256 % (QROW / 16);                                                          \
+      r__ += 256 / (QROW / 16);                                                          \
+      const bool wrap__ = c__ >= QROW / 16;                                              \
+      c__ = wrap__ ? c__ - QROW / 16 : c__;                                              \
+      r__ = wrap__ ? r__ + 1 : r__;                                                      \
+    }                                                                                    \
+    if (wave < QLOADS % 4) MLA_Q_LOAD(p_, wave + 4 * (QLOADS / 4), r__, c__);            \
   } while (0)
   // half p_ -> qf[18 p_ .. 18 p_ + 17]
 #define MLA_Q_READ(p_)                                                                     \
@@ -495,6 +513,7 @@ void decode_mfma_kernel(DecodeArgs a, ItemTable tab) {
   MLA_DECODE_FIRST_TILE();
 #undef MLA_Q_ISSUE
 #undef MLA_Q_READ
+#undef MLA_Q_LOAD
 
   for (;;) {                          // attempts (a restart is rare)
 #pragma unroll
@@ -702,10 +721,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, const ItemTable& tab, hipStre
   const int grid = a.n_items * a.row_blocks;
   if (a.kv_dtype == MLA_FP8_E4M3)
     return launch_decode_fp8(a, tab, st);
-  if (a.kv_dtype == MLA_FP6_E2M3)
-    hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(grid), dim3(256), 0, st, a, tab);
+  if (a.kv_dtype == MLA_FP6_E2M3 && a.q_row_bytes == 2 * D)
+    hipLaunchKernelGGL((decode_mfma_kernel<2, 2 * D>), dim3(grid), dim3(256), 0, st, a, tab);
+  else if (a.kv_dtype == MLA_BF16 && a.q_row_bytes == 2 * D)
+    hipLaunchKernelGGL((decode_mfma_kernel<0, 2 * D>), dim3(grid), dim3(256), 0, st, a, tab);
+  else if (a.kv_dtype == MLA_BF16 && a.q_row_bytes == 4 * D)
+    hipLaunchKernelGGL((decode_mfma_kernel<0, 4 * D>), dim3(grid), dim3(256), 0, st, a, tab);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<0>, dim3(grid), dim3(256), 0, st, a, tab);
+    return hipErrorInvalidValue;     // no other query layout reaches this kernel
   return hipGetLastError();
 }
 

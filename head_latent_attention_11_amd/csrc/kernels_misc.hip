@@ -470,7 +470,8 @@ __device__ inline int wave_sum_i(int v) {
 
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int R = blockIdx.x * 4 + (threadIdx.x >> 6);      // global row (nq * n_h + head)
+  // global row (nq * n_h + head), one per wave
+  const int R = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int rows = a.n_h * a.T;
   if (R >= a.B * rows) return;
   const int b = R / rows, row = R % rows;
@@ -504,22 +505,27 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   auto bf16_lo = [](uint32_t x) { return __builtin_bit_cast(float, x << 16); };
   auto bf16_hi = [](uint32_t x) { return __builtin_bit_cast(float, x & 0xFFFF0000u); };
   if (a.part_bf16 && ns <= 16) {
-    // Few splits: every load (LSEs, formats and partials) is issued before
-    // any of them is used, so the row costs one memory latency.
+    // Few splits: every load (LSEs and partials) is issued before any of
+    // them is used, so the row costs one memory latency.  Bit s of fmask:
+    // split s holds fp32 (the item was recomputed with split operands), in
+    // a slot of fp32 size; the mask is the same for the whole wave, so the
+    // format choices are scalar branches outside the loads.
     const float lse_l = (lane < ns) ? lse_p[(size_t)lane * rows] : -INFINITY;
-    const int f_l = (lane < ns) ? f32_of(lane) : 0;
+    const uint64_t fmask = flags ? __ballot(lane < ns && flags[(size_t)lane * a.fast_rb] != 0) : 0;
     u32x4 v0[16], v1[16];
+    if (fmask == 0) {
 #pragma unroll
-    for (int sp = 0; sp < 16; ++sp) {
-      if (sp < ns) {
-        const uint8_t* src = pbase + (size_t)sp * pstride;
-        if (__shfl(f_l, sp, 64)) {
-          v0[sp] = *(const u32x4*)(src + 4 * d0);
-          v1[sp] = *(const u32x4*)(src + 4 * d0 + 16);
-        } else {
-          v0[sp] = *(const u32x4*)(src + 2 * d0);
+      for (int sp = 0; sp < 16; ++sp)
+        if (sp < ns) v0[sp] = *(const u32x4*)(pbase + (size_t)sp * pstride + 2 * d0);
+    } else {
+      // bf16 entries read 16 bytes past their 16 (inside the fp32-size slot)
+#pragma unroll
+      for (int sp = 0; sp < 16; ++sp)
+        if (sp < ns) {
+          const uint8_t* src = pbase + (size_t)sp * pstride + (((fmask >> sp) & 1) ? 4 * d0 : 2 * d0);
+          v0[sp] = *(const u32x4*)src;
+          v1[sp] = *(const u32x4*)(src + 16);
         }
-      }
     }
     const float mx = wave_max(lse_l);
     if (mx == -INFINITY) {                                // no visible token at all
@@ -535,8 +541,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int sp = 0; sp < 16; ++sp) {
       if (sp < ns) {
-        const float w = __shfl(w_l, sp, 64);
-        if (__shfl(f_l, sp, 64)) {
+        const float w = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), sp));
+        if ((fmask >> sp) & 1) {
           acc0 += w * __builtin_bit_cast(floatx4, v0[sp]);
           acc1 += w * __builtin_bit_cast(floatx4, v1[sp]);
         } else {

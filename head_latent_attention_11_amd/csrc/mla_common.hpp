@@ -23,6 +23,10 @@ constexpr int kPage = 64;            // tokens per page of a paged cache
 constexpr int kNumCU = 256;          // MI355X compute units
 constexpr int kNumXCD = 8;           // accelerator complex dies (own L2 each)
 constexpr int kMinChunk = 256;       // smallest automatic KV chunk (tokens)
+// s_waitcnt immediate that waits for every vector-memory load and nothing
+// else (gfx9 encoding: vmcnt in bits 3:0 and 15:14 = 0, expcnt 6:4 = 7,
+// lgkmcnt 11:8 = 15)
+constexpr int kWaitVm0 = 0x0F70;
 
 // ---------------------------------------------------------------- formats
 __host__ __device__ inline float bf16_bits_to_f32(uint16_t b) {
