@@ -496,12 +496,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const uint8_t* pbase = (const uint8_t*)a.part_o + ((size_t)first * rows + row) * a.part_row_bytes;
   const size_t pstride = (size_t)rows * a.part_row_bytes; // bytes between splits
   // format of split s's partial: fp32 on the general path and for items
-  // recomputed with split operands, else bf16
+  // recomputed with split operands (flag set), else bf16
   const int32_t* flags = a.esc_flags ? a.esc_flags + (size_t)first * a.fast_rb + row / 128
                                      : nullptr;
-  auto f32_of = [&](int sp) -> int {
-    return !a.part_bf16 ? 1 : (flags ? (flags[(size_t)sp * a.fast_rb] != 0) : 0);
-  };
   auto bf16_lo = [](uint32_t x) { return __builtin_bit_cast(float, x << 16); };
   auto bf16_hi = [](uint32_t x) { return __builtin_bit_cast(float, x & 0xFFFF0000u); };
   if (a.part_bf16 && ns <= 16) {
@@ -570,21 +567,40 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   wsum = wave_sum(wsum);
   const float inv = 1.0f / wsum;
   floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const bool has0 = d0 < a.d_c, has1 = d0 + 4 < a.d_c;    // general path: d_c % 4 == 0
-  for (int s0 = 0; s0 < ns; s0 += 64) {
-    const int n = min(64, ns - s0);
+  // general path: d_c % 4 == 0; lanes past d_c read the row's first bytes
+  // (in bounds) and never store
+  const bool has0 = d0 < a.d_c, has1 = d0 + 4 < a.d_c;
+  const int off0 = has0 ? 4 * d0 : 0, off1 = has1 ? 4 * d0 + 16 : 0;
+  // Splits in batches of 16: every partial load of a batch is issued before
+  // any of them is used.  A split's format (bit s of fmask: fp32, else bf16
+  // with d_c = 512) only selects its addresses, so the loads carry no branch;
+  // a bf16 entry loads its 16 bytes twice.  Slots past the batch's n splits
+  // read its last split again (same format) with weight 0.
+  for (int s0 = 0; s0 < ns; s0 += 16) {
+    const int n = min(16, ns - s0);
     const float w_l = (lane < n) ? expf(lse_p[(size_t)(s0 + lane) * rows] - mx) * inv : 0.f;
-    const int f_l = (lane < n) ? f32_of(s0 + lane) : 0;
-    for (int sp = 0; sp < n; ++sp) {
-      const float w = __shfl(w_l, sp, 64);
-      const uint8_t* src = pbase + (size_t)(s0 + sp) * pstride;
-      if (__shfl(f_l, sp, 64)) {
-        if (has0) acc0 += w * *(const floatx4*)(src + 4 * d0);
-        if (has1) acc1 += w * *(const floatx4*)(src + 4 * d0 + 16);
-      } else {                                            // bf16 partials: d_c = 512
-        const u32x4 v = *(const u32x4*)(src + 2 * d0);
-        acc0 += w * floatx4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-        acc1 += w * floatx4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+    const uint64_t fmask = !a.part_bf16 ? ~0ull
+                           : flags ? __ballot(lane < n && flags[(size_t)(s0 + lane) * a.fast_rb] != 0)
+                                   : 0ull;
+    u32x4 v0[16], v1[16];
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) {
+      const int sc = min(sp, n - 1);
+      const uint8_t* src = pbase + (size_t)(s0 + sc) * pstride;
+      const bool f32 = (fmask >> sc) & 1;
+      v0[sp] = *(const u32x4*)(src + (f32 ? off0 : 2 * d0));
+      v1[sp] = *(const u32x4*)(src + (f32 ? off1 : 2 * d0));
+    }
+#pragma unroll
+    for (int sp = 0; sp < 16; ++sp) {
+      const float w = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), sp));
+      if ((fmask >> min(sp, n - 1)) & 1) {
+        acc0 += w * __builtin_bit_cast(floatx4, v0[sp]);
+        acc1 += w * __builtin_bit_cast(floatx4, v1[sp]);
+      } else {
+        acc0 += w * floatx4{bf16_lo(v0[sp][0]), bf16_hi(v0[sp][0]), bf16_lo(v0[sp][1]), bf16_hi(v0[sp][1])};
+        acc1 += w * floatx4{bf16_lo(v0[sp][2]), bf16_hi(v0[sp][2]), bf16_lo(v0[sp][3]), bf16_hi(v0[sp][3])};
       }
     }
   }
