@@ -25,7 +25,7 @@ PRECISION_CODES = {"auto": PREC_AUTO, "fp32": PREC_FP32, "bf16": PREC_BF16,
 EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_decode_attn_noalloc", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
             "mla_kv_produce_workspace_size", "mla_kv_produce",
-            "mla_out_proj_pack", "mla_out_proj_packed",
+            "mla_out_proj_pack", "mla_out_proj_packed", "mla_check_page_table",
             "mla_status_string", "mla_version")
 
 
@@ -112,6 +112,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    i32, i64, i32, vp, vp, i32, vp, sz, vp]
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_check_page_table.argtypes = [pdims, vp, i32, vp, i32, i64, vp, vp]
     lib.mla_version.argtypes = []
     for f in EXPORTED:
         if f not in ("mla_status_string",):
@@ -219,6 +220,17 @@ def decode_attn_noalloc(dims: MLADims, q_abs, cache, kv_scale, page_table, max_p
                                        int(q_tokens), int(num_splits), _ptr(out_latent),
                                        _ptr(out_lse), _stream(stream)),
            "mla_decode_attn_noalloc")
+
+
+def check_page_table(dims: MLADims, page_table, max_pages: int, seq_lens, batch: int,
+                     n_pages: int, result, stream=None):
+    """Device range check of a page table; result: int32[4] on the device
+    (out-of-range entries, first flat index or -1, its value, bad lengths)."""
+    lib = load_library()
+    _check(lib.mla_check_page_table(ctypes.byref(dims), _ptr(page_table), int(max_pages),
+                                    _ptr(seq_lens), int(batch), int(n_pages), _ptr(result),
+                                    _stream(stream)),
+           "mla_check_page_table")
 
 
 def up_proj_v(dims: MLADims, latent, w_uv, out, n_tokens: int, stream=None,

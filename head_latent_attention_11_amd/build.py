@@ -50,24 +50,33 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out_dir: str | None = None,
+          host_flags: tuple = ()) -> str:
+    """Compile every source and link the library; returns its path.
+
+    out_dir: build folder and library location (default: in-tree libmla.so).
+    host_flags: extra flags for the host side only (each passed as
+    `-Xarch_host <flag>`, e.g. sanitizers); device code is unchanged."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir = BUILD if out_dir is None else os.path.join(out_dir, "_build")
+    lib = LIB if out_dir is None else os.path.join(out_dir, "libmla.so")
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs]
+    objs = [os.path.join(build_dir, f[:-4] + ".o") for f in srcs]
+    host = [a for f in host_flags for a in ("-Xarch_host", f)]
 
     def compile_one(args):
         src, obj = args
-        _run([hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-              "-o", obj], verbose)
+        _run([hipcc, *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), *host, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
 
     jobs = min(len(srcs), max(1, (os.cpu_count() or 4)), 16)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *host, *objs, "-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@
 // "DeepSeek-V3 Technical Report" notes, MLA section (head-block layout of
 // W^UK / W^UV; attention-output equation whose sum over tokens is what the
 // split combine re-associates).
+#include <limits.h>
 #include <math.h>
 
 #include "mla_common.hpp"
@@ -820,6 +821,62 @@ hipError_t launch_produce_append(const mla_dims_t& d, const float* part, int nkb
   else if (d.kv_dtype == MLA_FP6_E2M3) MLA_PRODUCE(MLA_FP6_E2M3);
   else MLA_PRODUCE(MLA_FP8_E4M3);
 #undef MLA_PRODUCE
+  return hipGetLastError();
+}
+
+// ============================================================ page-table check
+// Debug aid: every page id that a sequence's length makes the kernels read
+// (entries p < ceil(L_b / page) of row b) must lie in [0, n_pages).  One
+// workgroup walks the table (a debug path: no speed needed, and a single
+// workgroup can set its own result without a clearing launch).
+// result: [0] out-of-range entries, [1] flat index b * max_pages + p of the
+// first (-1 if none), [2] its value (0 if none), [3] sequences whose length
+// is < 0 or > max_pages * page (their whole row is checked).
+__global__ __launch_bounds__(1024) void page_table_check_kernel(
+    const int32_t* __restrict__ pt, int max_pages, const int32_t* __restrict__ lens, int batch,
+    long long n_pages, int32_t* __restrict__ result) {
+  __shared__ int s_count, s_first, s_badlen;
+  if (threadIdx.x == 0) {
+    s_count = 0;
+    s_first = INT_MAX;
+    s_badlen = 0;
+  }
+  __syncthreads();
+  int count = 0, first = INT_MAX, badlen = 0;
+  const long long total = (long long)batch * max_pages;
+  for (long long i = threadIdx.x; i < total; i += blockDim.x) {
+    const int b = (int)(i / max_pages), p = (int)(i - (long long)b * max_pages);
+    const int L = lens[b];
+    const bool len_ok = L >= 0 && (long long)L <= (long long)max_pages * kPage;
+    if (p == 0 && !len_ok) ++badlen;
+    const int used = len_ok ? (L + kPage - 1) / kPage : max_pages;
+    if (p < used) {
+      const int v = pt[i];
+      if (v < 0 || (long long)v >= n_pages) {
+        ++count;
+        first = min(first, (int)i);
+      }
+    }
+  }
+  if (count) {
+    atomicAdd(&s_count, count);
+    atomicMin(&s_first, first);
+  }
+  if (badlen) atomicAdd(&s_badlen, badlen);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    result[0] = s_count;
+    result[1] = s_count ? s_first : -1;
+    result[2] = s_count ? pt[s_first] : 0;
+    result[3] = s_badlen;
+  }
+}
+
+hipError_t launch_page_table_check(const int32_t* pt, int max_pages, const int32_t* lens,
+                                   int batch, long long n_pages, int32_t* result,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(page_table_check_kernel, dim3(1), dim3(1024), 0, st, pt, max_pages, lens,
+                     batch, n_pages, result);
   return hipGetLastError();
 }
 

@@ -37,6 +37,8 @@ static_assert(sizeof(DecodeArgs) + sizeof(ItemTable) <= 4096,
 hipError_t launch_decode_general(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_small(const DecodeArgs&, const ItemTable&, int rows_wg, hipStream_t);
 hipError_t launch_decode_x2(const DecodeArgs&, const ItemTable&, int row_blocks, hipStream_t);
+hipError_t launch_page_table_check(const int32_t*, int, const int32_t*, int, long long,
+                                   int32_t*, hipStream_t);
 }  // namespace mla
 
 using namespace mla;
@@ -270,6 +272,20 @@ void* scratch_ptr() {
 extern "C" {
 
 int32_t mla_version(void) { return kVersion; }
+
+int32_t mla_check_page_table(const mla_dims_t* dims, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                             int64_t n_pages, int32_t* result, void* stream) {
+  const int32_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!page_table || !seq_lens || !result) return MLA_ERR_NULL;
+  if (batch < 1 || max_pages < 1 || n_pages < 1) return MLA_ERR_ARG;
+  if ((int64_t)batch * max_pages > INT32_MAX) return MLA_ERR_ARG;
+  if (launch_page_table_check(page_table, max_pages, seq_lens, batch, (long long)n_pages,
+                              result, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
 
 const char* mla_status_string(int32_t s) {
   switch (s) {

@@ -377,6 +377,28 @@ int32_t mla_out_proj_packed(const mla_dims_t* dims, const void* o, const void* w
                             int32_t d_model, void* u, int32_t u_dtype, int32_t n_tokens,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Page-table range check (debug aid).  The cache rows of the "DeepSeek-V2"
+ * page, section 2.1.3, are found through the page table of the paged layout
+ * described at mla_cache_append; the attention and producer kernels do not
+ * range-check the page ids they read (an id outside the cache is undefined
+ * behaviour).  A caller that does not trust a table (debug builds, tables
+ * built by other code) runs this check on the device first.
+ *
+ * page_table [batch, max_pages] int32 and seq_lens [batch] int32 (device).
+ * For each sequence b the entries p < ceil(L_b / page_size) are checked to
+ * lie in [0, n_pages); a length outside [0, max_pages * page_size] is
+ * counted and the whole row is checked.  result (device int32[4], written by
+ * the call; no clearing needed): [0] entries out of range, [1] flat index
+ * b * max_pages + p of the first of them (-1 if none), [2] its value (0 if
+ * none), [3] sequences with an out-of-range length.  One workgroup reads the
+ * whole table: for debugging, not for the serving loop.
+ * Errors: MLA_ERR_NULL, MLA_ERR_ARG (batch, max_pages or n_pages < 1, or
+ * batch * max_pages > 2^31 - 1), dims errors as everywhere.               */
+int32_t mla_check_page_table(const mla_dims_t* dims, const int32_t* page_table,
+                             int32_t max_pages, const int32_t* seq_lens, int32_t batch,
+                             int64_t n_pages, int32_t* result, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* mla_status_string(int32_t status);
 

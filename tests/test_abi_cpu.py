@@ -152,6 +152,20 @@ def test_out_proj_packed_validation(mla):
     assert op(ctypes.byref(d), FAKE, FAKE, 5120, FAKE, 0, 32, FAKE, 1024, None) == WS
 
 
+def test_page_table_check_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    chk = lib.mla_check_page_table
+    assert chk(None, FAKE, 8, FAKE, 4, 100, FAKE, None) == NULL
+    assert chk(ctypes.byref(d), None, 8, FAKE, 4, 100, FAKE, None) == NULL
+    assert chk(ctypes.byref(d), FAKE, 8, None, 4, 100, FAKE, None) == NULL
+    assert chk(ctypes.byref(d), FAKE, 8, FAKE, 4, 100, None, None) == NULL
+    assert chk(ctypes.byref(d), FAKE, 0, FAKE, 4, 100, FAKE, None) == ARG
+    assert chk(ctypes.byref(d), FAKE, 8, FAKE, 0, 100, FAKE, None) == ARG
+    assert chk(ctypes.byref(d), FAKE, 8, FAKE, 4, 0, FAKE, None) == ARG
+    assert chk(ctypes.byref(d), FAKE, 1 << 16, FAKE, 1 << 16, 100, FAKE, None) == ARG
+
+
 def test_kv_produce_validation(mla):
     lib, b = mla
     d = _v2(b)

@@ -828,3 +828,111 @@ def test_kv_produce_parity(w, layout, norm):
         written[slot] = True
         assert np.all(np.isnan(c[~written])), "a slot outside the new rows was written"
         check("rows", got, ref, 1e-5 if w.kv_dtype == "f32" else 4e-3)
+
+
+# ------------------------------------------------------ debug aids
+def _page_check_expected(pt, lens, n_pages):
+    """Host count of the page-table check: out-of-range ids among each row's
+    used entries (all entries when the length is out of range)."""
+    batch, max_pages = pt.shape
+    count, first, badlen = 0, -1, 0
+    for b in range(batch):
+        L = int(lens[b])
+        ok = 0 <= L <= max_pages * 64
+        badlen += 0 if ok else 1
+        used = (L + 63) // 64 if ok else max_pages
+        for p in range(used):
+            v = int(pt[b, p])
+            if v < 0 or v >= n_pages:
+                count += 1
+                if first < 0:
+                    first = b * max_pages + p
+    return [count, first, int(pt.reshape(-1)[first]) if count else 0, badlen]
+
+
+@pytest.mark.parametrize("batch,max_pages,n_pages", [(37, 50, 900), (1000, 600, 100000)])
+def test_page_table_check(batch, max_pages, n_pages):
+    """mla_check_page_table on a valid table, then with out-of-range ids
+    planted in used entries (counted), in unused entries past a sequence's
+    length (not counted) and with out-of-range lengths."""
+    from head_latent_attention_11_amd import binding as B
+    say(f"case page check: batch={batch} max_pages={max_pages} n_pages={n_pages}")
+    dims = B.MLADims.make(128, 128, 512, 64)
+    rng = np.random.default_rng(batch)
+    lens = rng.integers(1, max_pages * 64 + 1, size=batch).astype(np.int32)
+    pt = rng.integers(0, n_pages, size=(batch, max_pages)).astype(np.int32)
+    result = torch.full((4,), 12345, dtype=torch.int32, device="cuda")
+
+    def run(pt_h, lens_h):
+        B.check_page_table(dims, torch.from_numpy(pt_h).cuda(), max_pages,
+                           torch.from_numpy(lens_h).cuda(), batch, n_pages, result)
+        torch.cuda.synchronize()
+        return result.cpu().tolist()
+
+    assert run(pt, lens) == [0, -1, 0, 0]
+    bad = pt.copy()
+    lens2 = lens.copy()
+    used = (lens2 + 63) // 64
+    for k, b in enumerate(rng.choice(batch, size=min(batch, 12), replace=False)):
+        p = int(rng.integers(0, used[b]))
+        bad[b, p] = [-1, n_pages, n_pages + 7, -(1 << 30)][k % 4]
+        if used[b] < max_pages:                       # past the length: not read, not counted
+            bad[b, int(used[b])] = -5
+    lens2[rng.integers(0, batch)] = -3
+    lens2[rng.integers(0, batch)] = max_pages * 64 + 1
+    want = _page_check_expected(bad, lens2, n_pages)
+    got = run(bad, lens2)
+    say(f"  planted: got {got}, host count {want}")
+    assert got == want and got[0] > 0
+
+
+GUARD = 4096
+GUARD_BYTE = 0xA5
+
+
+def _guarded_like(t):
+    """A tensor of t's shape, dtype and contents inside a larger allocation
+    whose GUARD bytes before and after hold a fixed byte."""
+    nbytes = t.numel() * t.element_size()
+    raw = torch.full((nbytes + 2 * GUARD,), GUARD_BYTE, dtype=torch.uint8, device=t.device)
+    view = raw[GUARD:GUARD + nbytes].view(t.dtype).view(t.shape)
+    view.copy_(t)
+    return raw, view
+
+
+@pytest.mark.parametrize("w", [
+    small_variant(V2, name="canary_split5", batch=4, kv_len=0, lengths=(1, 33, 700, 64),
+                  num_splits=5),
+    small_variant(V2, name="canary_split40_paged", batch=3, kv_len=0, lengths=(2600, 64, 1300),
+                  num_splits=40, layout="paged"),
+    small_variant(V2, name="canary_fp8_t4", batch=4, q_tokens=4, kv_len=0,
+                  lengths=(300, 77, 4, 130), kv_dtype="fp8", num_splits=3),
+    small_variant(V2, name="canary_lite_n16", batch=4, n_heads=16, kv_len=0,
+                  lengths=(1, 33, 700, 64), num_splits=4),
+], ids=lambda w: w.name)
+def test_output_guard_canaries(w):
+    """Every buffer a decode step writes (absorbed query, cache with its
+    scales, split workspace, latent, LSE, output) sits between guard bytes;
+    after the step the guards are unchanged and the output still passes the
+    oracle comparison."""
+    say(f"case canaries {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout}")
+    gen = generate(w)
+    buf = _buffers(w, gen)
+    raws = {}
+    for name in ("q_abs", "latent", "lse", "o"):
+        raws[name], view = _guarded_like(getattr(buf, name))
+        setattr(buf, name, view)
+    if buf.workspace is not None:
+        raws["workspace"], buf.workspace = _guarded_like(buf.workspace)
+    raws["cache"], buf.caches[0] = _guarded_like(buf.caches[0])
+    if buf.scales[0] is not None:
+        raws["scales"], buf.scales[0] = _guarded_like(buf.scales[0])
+    buf.step()
+    torch.cuda.synchronize()
+    for name, raw in raws.items():
+        head = raw[:GUARD].cpu().numpy()
+        tail = raw[-GUARD:].cpu().numpy()
+        assert np.all(head == GUARD_BYTE) and np.all(tail == GUARD_BYTE), f"{name}: guard overwritten"
+    ref = omla.decode_workload(gen, w)
+    rel, mabs = _gates(w)
+    check("o", to_np(buf.o), ref["o"], rel, mabs)
