@@ -664,16 +664,24 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
   // the blocks of 32 tokens t0 = 32 (y + k gridDim.y)
   const int t_first = 32 * blockIdx.y, t_step = 32 * gridDim.y;
   load_latent(t_first);
-  for (int t0 = t_first; t0 < n_tok; t0 += t_step) {
-    if (t0 == t_first) {
+  // W^UV into LDS, then each wave's A operands (its 16 d_h rows, all 512
+  // latent dims: 64 VGPRs) into registers once: they are the same for every
+  // token block, and reading them from LDS per block was a third of the
+  // block's LDS traffic
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
-        *(u32x4*)(sw + r * kUpRow + c8) = wv[i];
-      }
-    } else {
-      __syncthreads();                 // the previous block's reads are done
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int ch = tid + 512 * i, r = ch >> 6, c8 = (ch & 63) * 8;
+    *(u32x4*)(sw + r * kUpRow + c8) = wv[i];
+  }
+  __syncthreads();
+  bf16x8 af[DC / 32];
+  {
+    const uint16_t* pa = sw + (16 * mi + r16) * kUpRow + 8 * g;
+#pragma unroll
+    for (int s = 0; s < DC / 32; ++s) af[s] = *(const bf16x8*)(pa + 32 * s);
+  }
+  for (int t0 = t_first; t0 < n_tok; t0 += t_step) {
+    if (t0 != t_first) __syncthreads();   // the previous block's reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int ch = tid + 512 * i, t = ch >> 7, c4 = (ch & 127) * 4;
@@ -692,15 +700,13 @@ __global__ __launch_bounds__(512) void up_proj_mfma_kernel(
     __syncthreads();
 
     floatx4 acc_hi = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* pa = sw + (16 * mi + r16) * kUpRow + 8 * g;
     const int bo = (16 * ni + r16) * kUpRow + 8 * g;
 #pragma unroll
     for (int s = 0; s < DC / 32; ++s) {
-      const bf16x8 a = *(const bf16x8*)(pa + 32 * s);
       const bf16x8 bh = *(const bf16x8*)(sh + bo + 32 * s);
       const bf16x8 bl = *(const bf16x8*)(sl + bo + 32 * s);
-      acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc_hi, 0, 0, 0);
-      acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc_lo, 0, 0, 0);
+      acc_hi = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bh, acc_hi, 0, 0, 0);
+      acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bl, acc_lo, 0, 0, 0);
     }
     // acc[e]: d_h row 64 half + 16 mi + 4 g + e, token t0 + 16 ni + r16
     const int tok = t0 + 16 * ni + r16;
