@@ -9,6 +9,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_common.hpp"
 #include "plan_device.hpp"
 
@@ -17,12 +19,19 @@ namespace mla {
 // ============================================================ RoPE helper
 // Interleaved pairs (2k, 2k+1) rotated by pos * theta_k (rope_theta, with
 // or without context extension); angle and rotation in double precision.
+// The angle pos * theta is formed and reduced to [-pi, pi] in double
+// (positions up to 2^17 times frequencies near 1 need that: an fp32 angle of
+// 1e5 rad has a unit roundoff of ~0.008 rad); sine, cosine and the rotation
+// then run in fp32 (relative error ~1e-7).  Double-precision sine and cosine
+// per pair made the rotations a large part of the absorption.
 __device__ inline void rope_rot(float x0, float x1, int pos, double theta, float* y0, float* y1) {
-  double ang = (double)pos * theta;
-  double s, c;
-  sincos(ang, &s, &c);
-  *y0 = (float)((double)x0 * c - (double)x1 * s);
-  *y1 = (float)((double)x0 * s + (double)x1 * c);
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0.15915494309189535);            // turns: ang / (2 pi)
+  const float r = (float)fma(-k, 6.283185307179586, ang);      // in [-pi, pi]
+  float s, c;
+  sincosf(r, &s, &c);
+  *y0 = x0 * c - x1 * s;
+  *y1 = x0 * s + x1 * c;
 }
 __device__ inline void rope_pair(float x0, float x1, int pos, int k, int d,
                                  const RopeFreq& rf, float* y0, float* y1) {
@@ -111,13 +120,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   };
   load_pairs(p_first);
 
-  // query block loader: 32 tokens x 128 d_h = 512 chunks of 16 bytes
+  // query block loader: 32 tokens x 128 d_h = 512 chunks of 16 bytes.
+  // Tokens past n_tok load the last token again (never stored), so no branch
+  // surrounds the loads.
   auto load_q = [&](int t0, u32x4* qv) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int ch = tid + 256 * i, t = ch >> 4, c8 = (ch & 15) * 8;
-      qv[i] = u32x4{0u, 0u, 0u, 0u};
-      if (t0 + t < n_tok) qv[i] = *(const u32x4*)(q_nope + ((size_t)(t0 + t) * n_h + head) * kAbsDh + c8);
+      const int ch = tid + 256 * i, c8 = (ch & 15) * 8;
+      const int t = min(t0 + (ch >> 4), n_tok - 1);
+      qv[i] = *(const u32x4*)(q_nope + ((size_t)t * n_h + head) * kAbsDh + c8);
     }
   };
   auto store_q = [&](const u32x4* qv) {
@@ -178,7 +189,13 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     af[k] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
   }
 
-  for (int t0 = t_first; t0 < n_tok; t0 += t_step) {
+  // One block of 32 tokens.  FULL blocks (all 32 tokens exist) store their
+  // rows with no per-lane test: stores share the memory counter with loads,
+  // and stores under a per-lane branch make the compiler wait for every
+  // store in flight (the previous block's copy-out) before it stages the
+  // next query block.  Only the last, partial block tests its tokens.
+  auto block = [&](int t0, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     if (t0 > t_first) {                // next query block (loaded during the last one)
       __syncthreads();                 // the last block's operand reads and copy-out are done
       store_q(qv);
@@ -219,12 +236,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     for (int i = 0; i < 32 * per_row / 256; ++i) {
       const int ch = tid + 256 * i, t = ch / per_row, c = ch % per_row;
       const int part = PAIRS ? c / run : 0, cc = PAIRS ? c % run : c;
-      if (t0 + t < n_tok)
+      if (FULL || t0 + t < n_tok)
         *(u32x4*)((unsigned char*)(q_abs + ((size_t)(t0 + t) * n_h + head) * QROW + part * D +
                                    cb * kAbsCols) + 16 * cc) =
             *(const u32x4*)(os + t * kAbsOutRow + 16 * c);
     }
-  }
+  };
+  int t0 = t_first;
+  for (; t0 + 32 <= n_tok; t0 += t_step) block(t0, std::true_type{});
+  if (t0 < n_tok) block(t0, std::false_type{});
 }
 
 // =================================================== absorb: general path
