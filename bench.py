@@ -2,8 +2,9 @@
 """Benchmark of one MLA decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic inputs:
-    mla_absorb_q -> mla_cache_append (the B*T new rows) -> mla_decode_attn
-    (split-KV attention + LSE combine) -> mla_up_proj_v
+    mla_absorb_append (mla_absorb_q and mla_cache_append of the B*T new rows,
+    one launch) -> mla_decode_attn (split-KV attention + LSE combine)
+    -> mla_up_proj_v
 with every input already resident in HBM.  The latent cache (>= 768 MB in
 total) and W^UK / W^UV are replicated and the replicas are used round-robin,
 so each step reads its cache and weights from HBM rather than from the
@@ -568,7 +569,7 @@ def main():
                    "layout": w.layout, "precision": args.precision,
                    "cache_replicas": t.replicas,
                    "steps_per_graph": STEPS_PER_GRAPH,
-                   "step": "absorb_q + cache_append(B*T rows) + decode_attn + up_proj_v"},
+                   "step": "absorb_append (absorb_q + cache_append of B*T rows) + decode_attn + up_proj_v"},
         "step_us_events": round(ms_step_events * 1e3, 2),
         "step_us_median_p10_p90": [round(ps["median"] * 1e6, 2), round(ps["p10"] * 1e6, 2),
                                    round(ps["p90"] * 1e6, 2)],

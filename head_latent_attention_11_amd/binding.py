@@ -26,6 +26,7 @@ EXPORTED = ("mla_absorb_q", "mla_cache_append", "mla_decode_workspace_size",
             "mla_decode_attn", "mla_decode_attn_noalloc", "mla_up_proj_v", "mla_out_proj_workspace_size", "mla_out_proj",
             "mla_kv_produce_workspace_size", "mla_kv_produce",
             "mla_out_proj_pack", "mla_out_proj_packed", "mla_check_page_table",
+            "mla_absorb_append",
             "mla_status_string", "mla_version")
 
 
@@ -113,6 +114,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_check_page_table.argtypes = [pdims, vp, i32, vp, i32, i64, vp, vp]
+    lib.mla_absorb_append.argtypes = [pdims, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32,
+                                      i32, i32, i64, i32, vp, vp, i32, vp]
     lib.mla_version.argtypes = []
     for f in EXPORTED:
         if f not in ("mla_status_string",):
@@ -220,6 +223,21 @@ def decode_attn_noalloc(dims: MLADims, q_abs, cache, kv_scale, page_table, max_p
                                        int(q_tokens), int(num_splits), _ptr(out_latent),
                                        _ptr(out_lse), _stream(stream)),
            "mla_decode_attn_noalloc")
+
+
+def absorb_append(dims: MLADims, q_nope, q_rope, w_uk, q_pos, q_abs, n_tokens: int,
+                  new_c, new_kr, seq_idx, pos, page_table, batch: int, max_pages: int,
+                  max_len: int, cache_rows: int, apply_rope: bool, cache, kv_scale,
+                  n_rows: int, stream=None):
+    """mla_absorb_q and mla_cache_append in one call (one launch on their fast paths)."""
+    lib = load_library()
+    _check(lib.mla_absorb_append(ctypes.byref(dims), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                 _ptr(q_pos), _ptr(q_abs), int(n_tokens), _ptr(new_c),
+                                 _ptr(new_kr), _ptr(seq_idx), _ptr(pos), _ptr(page_table),
+                                 int(batch), int(max_pages), int(max_len), int(cache_rows),
+                                 int(bool(apply_rope)), _ptr(cache), _ptr(kv_scale),
+                                 int(n_rows), _stream(stream)),
+           "mla_absorb_append")
 
 
 def check_page_table(dims: MLADims, page_table, max_pages: int, seq_lens, batch: int,

@@ -80,18 +80,22 @@ __device__ inline shortx4 lds_read_tr16(const uint16_t* p) {
 
 // PAIRS (bf16 output only): each row is written as the pair hi = bf16(q),
 // lo = bf16(q - hi), hi in elements [0, D) and lo in [D, 2D) of a 2D row.
-template <typename OutT, bool PAIRS = false>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(
+// One workgroup's share (bx: head * 4 + column block; by of gy: token
+// group), as a function so that the absorption can also run inside the
+// combined absorption + append launch.
+template <typename OutT, bool PAIRS>
+__device__ __forceinline__ void absorb_mfma_block(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
-    OutT* __restrict__ q_abs, int n_tok, int n_h, RopeFreq rope) {
+    OutT* __restrict__ q_abs, int n_tok, int n_h, const RopeFreq& rope, int bx, int by,
+    int gy) {
   constexpr int DC = 512, DR = 64, D = DC + DR;
   constexpr int QROW = PAIRS ? 2 * D : D;     // elements per q_abs row
   static_assert(!PAIRS || sizeof(OutT) == 2, "query pairs are bf16");
   __shared__ __attribute__((aligned(16))) uint16_t ws[kAbsDh * kAbsLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * kAbsLdsRow];
   __shared__ __attribute__((aligned(16))) unsigned char os[32 * kAbsOutRow];
-  const int head = blockIdx.x >> 2, cb = blockIdx.x & 3;
+  const int head = bx >> 2, cb = bx & 3;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, j = lane & 15;
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   // first batch before the W^UK block; its rotations run while that block
   // is in flight.
   const int n_pairs = n_tok * (DR / 2), rk = tid & 31;
-  const int p_first = 1024 * blockIdx.y + cb * 256 + tid, p_step = 1024 * gridDim.y;
-  const int t_first = 32 * blockIdx.y, t_step = 32 * gridDim.y;
+  const int p_first = 1024 * by + cb * 256 + tid, p_step = 1024 * gy;
+  const int t_first = 32 * by, t_step = 32 * gy;
   uint32_t rxy[kAbsRopeBatch];         // the pair's two bf16 inputs
   int rpos[kAbsRopeBatch];
   auto load_pairs = [&](int p0) {
@@ -245,6 +249,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   int t0 = t_first;
   for (; t0 + 32 <= n_tok; t0 += t_step) block(t0, std::true_type{});
   if (t0 < n_tok) block(t0, std::false_type{});
+}
+
+template <typename OutT, bool PAIRS = false>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
+    OutT* __restrict__ q_abs, int n_tok, int n_h, RopeFreq rope) {
+  absorb_mfma_block<OutT, PAIRS>(q_nope, q_rope, w_uk, q_pos, q_abs, n_tok, n_h, rope,
+                                 blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // =================================================== absorb: general path
@@ -405,16 +418,18 @@ __device__ inline void append_row(LdC ld_c, LdKr ld_kr, int lane, long long row,
 
 // One wave per new row.  Source rows are F32 or BF16, row r of new_c at
 // r * c_stride (elements), of new_kr at r * kr_stride.
+// Rows block * 4 + wave, + nblocks * 4, ... (one row per wave at a time).
 template <typename SrcT, int KV>
-__global__ __launch_bounds__(256) void append_kernel(
+__device__ __forceinline__ void append_rows(
     const SrcT* __restrict__ new_c, const SrcT* __restrict__ new_kr,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
     long long cache_rows, int apply_rope, void* __restrict__ cache,
-    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, RopeFreq rope,
-    int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps) {
+    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, const RopeFreq& rope,
+    int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps,
+    int block, int nblocks) {
   const int lane = threadIdx.x & 63;
-  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < n_rows; r += gridDim.x * 4) {
+  for (int r = block * 4 + (threadIdx.x >> 6); r < n_rows; r += nblocks * 4) {
     const long long row = append_slot(seq_idx, pos, page_table, B, max_pages, max_len,
                                       cache_rows, r);
     if (row < 0) continue;
@@ -424,6 +439,44 @@ __global__ __launch_bounds__(256) void append_kernel(
                    lane, row, pos[r], apply_rope, cache, kv_scale, d_c, d_r, rope, norm_gain,
                    norm_eps);
   }
+}
+
+template <typename SrcT, int KV>
+__global__ __launch_bounds__(256) void append_kernel(
+    const SrcT* __restrict__ new_c, const SrcT* __restrict__ new_kr,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
+    long long cache_rows, int apply_rope, void* __restrict__ cache,
+    float* __restrict__ kv_scale, int n_rows, int d_c, int d_r, RopeFreq rope,
+    int c_stride, int kr_stride, const float* __restrict__ norm_gain, float norm_eps) {
+  append_rows<SrcT, KV>(new_c, new_kr, seq_idx, pos, page_table, B, max_pages, max_len,
+                        cache_rows, apply_rope, cache, kv_scale, n_rows, d_c, d_r, rope,
+                        c_stride, kr_stride, norm_gain, norm_eps, blockIdx.x, gridDim.x);
+}
+
+// The step's absorption and cache append in one launch (they read and write
+// disjoint buffers).  Every workgroup runs one (column block, token group)
+// share of the absorption; before it, workgroup b's four waves append rows
+// 4b .. 4b + 3 (and 4 (b + k * workgroups) .. for more rows), so the append
+// takes no workgroup slots of its own: the absorption's LDS allows two
+// workgroups per CU, and extra append workgroups would push absorption
+// workgroups into a second round.  bf16 query and rows, bf16 absorbed query
+// (or query pairs), bf16 / fp8 / 6-bit cache.
+template <bool PAIRS, int KV>
+__global__ __launch_bounds__(256) void absorb_append_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int32_t* __restrict__ q_pos,
+    uint16_t* __restrict__ q_abs, int n_tok, int n_h, int abs_x, int abs_y,
+    const uint16_t* __restrict__ new_c, const uint16_t* __restrict__ new_kr,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const int32_t* __restrict__ page_table, int B, int max_pages, int max_len,
+    long long cache_rows, int apply_rope, void* __restrict__ cache,
+    float* __restrict__ kv_scale, int n_rows, RopeFreq rope) {
+  append_rows<uint16_t, KV>(new_c, new_kr, seq_idx, pos, page_table, B, max_pages, max_len,
+                            cache_rows, apply_rope, cache, kv_scale, n_rows, 512, 64, rope, 512,
+                            64, nullptr, 0.f, blockIdx.x, gridDim.x);
+  absorb_mfma_block<uint16_t, PAIRS>(q_nope, q_rope, w_uk, q_pos, q_abs, n_tok, n_h, rope,
+                                     blockIdx.x % abs_x, blockIdx.x / abs_x, abs_y);
 }
 
 // The cache producer's second half: one workgroup per new row sums the
@@ -829,6 +882,39 @@ hipError_t launch_append(const mla_dims_t& d, const void* new_c, const void* new
   else if (!src_f32) MLA_APPEND(uint16_t, MLA_FP8_E4M3);
   else MLA_APPEND(float, MLA_FP8_E4M3);
 #undef MLA_APPEND
+  return hipGetLastError();
+}
+
+// One launch for the absorption and the append when both take their fast
+// paths (see absorb_append_kernel); returns hipErrorInvalidValue otherwise.
+hipError_t launch_absorb_append(const mla_dims_t& d, bool pairs, const void* q_nope,
+                                const void* q_rope, const void* w_uk, const int32_t* q_pos,
+                                void* q_abs, int n_tok, const void* new_c, const void* new_kr,
+                                const int32_t* seq_idx, const int32_t* pos,
+                                const int32_t* page_table, int B, int max_pages, int max_len,
+                                long long cache_rows, int apply_rope, void* cache,
+                                float* kv_scale, int n_rows, RopeFreq rope, hipStream_t st) {
+  const int abs_y = std::max(1, std::min((n_tok + 31) / 32, kNumCU / (4 * d.n_heads)));
+  const int abs_x = 4 * d.n_heads;
+  const long long total = (long long)abs_x * abs_y;
+  if (total > INT_MAX) return hipErrorInvalidValue;
+#define MLA_AA(P, KV)                                                                         \
+  hipLaunchKernelGGL((absorb_append_kernel<P, KV>), dim3((unsigned)total), dim3(256), 0, st,  \
+                     (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, \
+                     q_pos, (uint16_t*)q_abs, n_tok, d.n_heads, abs_x, abs_y,                 \
+                     (const uint16_t*)new_c, (const uint16_t*)new_kr, seq_idx, pos,           \
+                     page_table, B, max_pages, max_len, cache_rows, apply_rope, cache,        \
+                     kv_scale, n_rows, rope)
+  if (d.kv_dtype == MLA_BF16) {
+    if (pairs) MLA_AA(true, MLA_BF16); else MLA_AA(false, MLA_BF16);
+  } else if (d.kv_dtype == MLA_FP8_E4M3) {
+    if (pairs) MLA_AA(true, MLA_FP8_E4M3); else MLA_AA(false, MLA_FP8_E4M3);
+  } else if (d.kv_dtype == MLA_FP6_E2M3) {
+    if (pairs) MLA_AA(true, MLA_FP6_E2M3); else MLA_AA(false, MLA_FP6_E2M3);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef MLA_AA
   return hipGetLastError();
 }
 

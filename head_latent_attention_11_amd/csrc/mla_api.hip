@@ -39,6 +39,10 @@ hipError_t launch_decode_small(const DecodeArgs&, const ItemTable&, int rows_wg,
 hipError_t launch_decode_x2(const DecodeArgs&, const ItemTable&, int row_blocks, hipStream_t);
 hipError_t launch_page_table_check(const int32_t*, int, const int32_t*, int, long long,
                                    int32_t*, hipStream_t);
+hipError_t launch_absorb_append(const mla_dims_t&, bool, const void*, const void*, const void*,
+                                const int32_t*, void*, int, const void*, const void*,
+                                const int32_t*, const int32_t*, const int32_t*, int, int, int,
+                                long long, int, void*, float*, int, RopeFreq, hipStream_t);
 }  // namespace mla
 
 using namespace mla;
@@ -303,9 +307,14 @@ const char* mla_status_string(int32_t s) {
   }
 }
 
-int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
-                     const void* w_uk, const int32_t* q_pos, void* q_abs,
-                     int32_t n_tokens, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of mla_absorb_q and mla_cache_append (shared with the
+// combined call).
+int32_t check_absorb_call(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                          const void* w_uk, const void* q_abs, int32_t n_tokens) {
   int32_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!q_nope || !w_uk || !q_abs || (dims->d_rope > 0 && !q_rope)) return MLA_ERR_NULL;
@@ -314,16 +323,14 @@ int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_r
       (q_rope && !aligned16(q_rope)))
     return MLA_ERR_ALIGN;
   if (x2_only(dims) && !x2_supported(dims)) return MLA_ERR_UNSUPPORTED;
-  const bool fast = fast_shape(dims);
-  return status_of(launch_absorb(*dims, fast, qabs_pairs(dims), q_nope, q_rope, w_uk, q_pos,
-                                 q_abs, n_tokens, rope_of(dims), (hipStream_t)stream));
+  return MLA_OK;
 }
 
-int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* new_kr,
-                         const int32_t* seq_idx, const int32_t* pos,
-                         const int32_t* page_table, int32_t batch, int32_t max_pages,
-                         int32_t max_len, int64_t cache_rows, int32_t apply_rope,
-                         void* cache, float* kv_scale, int32_t n_rows, void* stream) {
+int32_t check_append_call(const mla_dims_t* dims, const void* new_c, const void* new_kr,
+                          const int32_t* seq_idx, const int32_t* pos,
+                          const int32_t* page_table, int32_t batch, int32_t max_pages,
+                          int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                          const void* cache, const float* kv_scale, int32_t n_rows) {
   int32_t st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (!new_c || !seq_idx || !pos || !cache || (dims->d_rope > 0 && !new_kr))
@@ -346,6 +353,64 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* 
   if (dims->d_latent + dims->d_rope > 640) return MLA_ERR_DIMS;
   if (!aligned16(new_c) || !aligned16(cache) || (new_kr && !aligned16(new_kr)))
     return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_absorb_append(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                          const void* w_uk, const int32_t* q_pos, void* q_abs,
+                          int32_t n_tokens, const void* new_c, const void* new_kr,
+                          const int32_t* seq_idx, const int32_t* pos,
+                          const int32_t* page_table, int32_t batch, int32_t max_pages,
+                          int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                          void* cache, float* kv_scale, int32_t n_rows, void* stream) {
+  int32_t st = check_absorb_call(dims, q_nope, q_rope, w_uk, q_abs, n_tokens);
+  if (st != MLA_OK) return st;
+  st = check_append_call(dims, new_c, new_kr, seq_idx, pos, page_table, batch, max_pages,
+                         max_len, cache_rows, apply_rope, cache, kv_scale, n_rows);
+  if (st != MLA_OK) return st;
+  const RopeFreq rope = rope_of(dims);
+  const hipStream_t s = (hipStream_t)stream;
+  const bool fast = fast_shape(dims);
+  const bool one_launch = fast && dims->precision != MLA_PREC_FP32 &&
+                          (dims->kv_dtype == MLA_BF16 || dims->kv_dtype == MLA_FP8_E4M3 ||
+                           dims->kv_dtype == MLA_FP6_E2M3);
+  if (one_launch)
+    return status_of(launch_absorb_append(*dims, qabs_pairs(dims), q_nope, q_rope, w_uk, q_pos,
+                                          q_abs, n_tokens, new_c, new_kr, seq_idx, pos,
+                                          page_table, batch, max_pages, max_len, cache_rows,
+                                          apply_rope, cache, kv_scale, n_rows, rope, s));
+  st = status_of(launch_absorb(*dims, fast, qabs_pairs(dims), q_nope, q_rope, w_uk, q_pos,
+                               q_abs, n_tokens, rope, s));
+  if (st != MLA_OK) return st;
+  return status_of(launch_append(*dims, new_c, new_kr, seq_idx, pos, page_table, batch,
+                                 max_pages, max_len, cache_rows, apply_rope, cache, kv_scale,
+                                 n_rows, rope, s, dims->kv_dtype == MLA_F32, dims->d_latent,
+                                 dims->d_rope, nullptr, 0.f));
+}
+
+int32_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                     const void* w_uk, const int32_t* q_pos, void* q_abs,
+                     int32_t n_tokens, void* stream) {
+  const int32_t st = check_absorb_call(dims, q_nope, q_rope, w_uk, q_abs, n_tokens);
+  if (st != MLA_OK) return st;
+  const bool fast = fast_shape(dims);
+  return status_of(launch_absorb(*dims, fast, qabs_pairs(dims), q_nope, q_rope, w_uk, q_pos,
+                                 q_abs, n_tokens, rope_of(dims), (hipStream_t)stream));
+}
+
+int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c, const void* new_kr,
+                         const int32_t* seq_idx, const int32_t* pos,
+                         const int32_t* page_table, int32_t batch, int32_t max_pages,
+                         int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                         void* cache, float* kv_scale, int32_t n_rows, void* stream) {
+  const int32_t st = check_append_call(dims, new_c, new_kr, seq_idx, pos, page_table, batch,
+                                       max_pages, max_len, cache_rows, apply_rope, cache,
+                                       kv_scale, n_rows);
+  if (st != MLA_OK) return st;
   return status_of(launch_append(*dims, new_c, new_kr, seq_idx, pos, page_table, batch,
                                  max_pages, max_len, cache_rows, apply_rope, cache,
                                  kv_scale, n_rows, rope_of(dims), (hipStream_t)stream,

@@ -5,12 +5,12 @@
 cache with ``mla_cache_append`` (so the cache bytes are written by the
 library's own append kernel), and runs the decode step
 
-    mla_absorb_q -> mla_cache_append -> mla_decode_attn (split-KV + combine)
-    -> mla_up_proj_v
+    mla_absorb_append (mla_absorb_q + mla_cache_append in one call)
+    -> mla_decode_attn (split-KV + combine) -> mla_up_proj_v
 
-on the current torch stream (the step also appends its B*T new rows with
-``mla_cache_append`` before the attention call).  No arithmetic of the
-method happens here.
+on the current torch stream (the step appends its B*T new rows before the
+attention call; absorb() and append() run the two separately).  No
+arithmetic of the method happens here.
 """
 from __future__ import annotations
 
@@ -172,8 +172,15 @@ class DecodeBuffers:
         B.up_proj_v(self.dims, self.latent, self.w_uvs[replica % len(self.w_uvs)], self.o,
                     self.n_tok, stream)
 
+    def absorb_append(self, stream=None, replica: int = 0):
+        """absorb() and append() as one library call (mla_absorb_append)."""
+        B.absorb_append(self.dims, self.q_nope, self.q_rope, self.w_uks[replica % len(self.w_uks)],
+                        self.q_pos, self.q_abs, self.n_tok, self.new_c, self.new_kr,
+                        self.new_seq, self.new_pos, self.page_table, self.batch,
+                        self.max_pages, self.max_len, self.cache_rows, self.w.rope,
+                        self.caches[replica], self.scales[replica], self.n_tok, stream)
+
     def step(self, replica: int = 0, stream=None):
-        self.absorb(stream, replica)
-        self.append(stream, replica)
+        self.absorb_append(stream, replica)
         self.attend(replica, stream)
         self.up_proj(stream, replica)

@@ -221,6 +221,27 @@ int32_t mla_cache_append(const mla_dims_t* dims, const void* new_c,
                          float* kv_scale, int32_t n_rows, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The decode step's two producers in one call: the query absorption of
+ * mla_absorb_q ("DeepSeek-V2", section 2.1.2 and Appendix C; RoPE of q^R,
+ * section 2.1.3) and the cache append of mla_cache_append (the cached c^KV
+ * and k^R of section 2.1.3).  Arguments, layouts, results and errors are
+ * those of the two calls (first the absorption's arguments, then the
+ * append's); both are validated before anything is launched, and the
+ * results are bit-identical to calling mla_absorb_q then mla_cache_append.
+ * When both take their fast paths (d_h = 128, d_c = 512, d_h^R = 64,
+ * q_dtype BF16, precision other than MLA_PREC_FP32, cache BF16, FP8_E4M3 or
+ * FP6_E2M3) they run as one launch, since neither reads what the other
+ * writes; otherwise as the two launches in that order.  q_abs must not
+ * overlap the cache, its scales or the append's inputs.                   */
+int32_t mla_absorb_append(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                          const void* w_uk, const int32_t* q_pos, void* q_abs,
+                          int32_t n_tokens, const void* new_c, const void* new_kr,
+                          const int32_t* seq_idx, const int32_t* pos,
+                          const int32_t* page_table, int32_t batch, int32_t max_pages,
+                          int32_t max_len, int64_t cache_rows, int32_t apply_rope,
+                          void* cache, float* kv_scale, int32_t n_rows, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Workspace of mla_decode_attn for the given host copy of the lengths and
  * split request (same planner as mla_decode_attn).  *bytes receives the
  * exact size: the split partials when some sequence is split, plus one

@@ -221,6 +221,18 @@ static void rejected_calls() {
           "check table too large");
   }
 
+  {
+    int32_t* ip = (int32_t*)buf;
+    CHECK(mla_absorb_append(nullptr, p, p, p, nullptr, p, 4, p, p, ip, ip, nullptr, 2, 0, 64, 128,
+                            0, p, nullptr, 4, nullptr) == MLA_ERR_NULL, "absorb_append NULL dims");
+    CHECK(mla_absorb_append(&d, p, p, p, nullptr, p, 0, p, p, ip, ip, nullptr, 2, 0, 64, 128, 0,
+                            p, nullptr, 4, nullptr) == MLA_ERR_ARG, "absorb_append 0 tokens");
+    CHECK(mla_absorb_append(&d, p, p, p, nullptr, p, 4, p, p, ip, ip, nullptr, 2, 0, 64, 128, 0,
+                            odd, nullptr, 4, nullptr) == MLA_ERR_ALIGN, "absorb_append cache");
+    CHECK(mla_absorb_append(&d, p, p, p, nullptr, p, 4, p, p, ip, ip, nullptr, 2, 0, 64, 100, 0,
+                            p, nullptr, 4, nullptr) == MLA_ERR_ARG, "absorb_append capacity");
+  }
+
   for (int32_t s = 5; s >= -12; --s) {
     const char* t = mla_status_string(s);
     CHECK(t != nullptr && strlen(t) > 0, "status string %d", s);

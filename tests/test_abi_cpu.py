@@ -166,6 +166,30 @@ def test_page_table_check_validation(mla):
     assert chk(ctypes.byref(d), FAKE, 1 << 16, FAKE, 1 << 16, 100, FAKE, None) == ARG
 
 
+def test_absorb_append_validation(mla):
+    lib, b = mla
+    d = _v2(b)
+    aa = lib.mla_absorb_append
+
+    def call(q_nope=FAKE, w_uk=FAKE, q_abs=FAKE, n_tok=4, new_c=FAKE, cache=FAKE, scale=None,
+             n_rows=4, dims=d):
+        return aa(ctypes.byref(dims) if dims is not None else None, q_nope, FAKE, w_uk, None,
+                  q_abs, n_tok, new_c, FAKE, FAKE, FAKE, None, 2, 0, 64, 128, 0, cache, scale,
+                  n_rows, None)
+    assert call(dims=None) == NULL
+    assert call(q_nope=None) == NULL
+    assert call(q_abs=None) == NULL
+    assert call(new_c=None) == NULL
+    assert call(cache=None) == NULL
+    assert call(n_tok=0) == ARG
+    assert call(n_rows=0) == ARG
+    assert call(q_abs=MIS) == ALIGN
+    assert call(cache=MIS) == ALIGN
+    assert call(scale=FAKE) == ARG                     # scales only with an fp8 cache
+    d8 = _v2(b, kv_dtype="fp8")
+    assert call(dims=d8) == NULL                        # fp8 cache without scales
+
+
 def test_kv_produce_validation(mla):
     lib, b = mla
     d = _v2(b)

@@ -936,3 +936,39 @@ def test_output_guard_canaries(w):
     ref = omla.decode_workload(gen, w)
     rel, mabs = _gates(w)
     check("o", to_np(buf.o), ref["o"], rel, mabs)
+
+
+@pytest.mark.parametrize("w", [
+    small_variant(V2, name="aa_bf16_pairs", batch=4, kv_len=0, lengths=(1, 33, 700, 64)),
+    small_variant(V2, name="aa_fp8_t4", batch=4, q_tokens=4, kv_len=0, lengths=(300, 77, 4, 130),
+                  kv_dtype="fp8"),
+    small_variant(V2, name="aa_fp6_paged", batch=3, q_tokens=2, kv_len=0, lengths=(100, 520, 64),
+                  kv_dtype="fp6", layout="paged"),
+    small_variant(V2, name="aa_lite_n16_paged", batch=4, n_heads=16, kv_len=0,
+                  lengths=(1, 33, 700, 64), layout="paged"),
+    WORKLOADS["tiny_fp32"],
+], ids=lambda w: w.name)
+def test_absorb_append_matches_separate_calls(w):
+    """mla_absorb_append (one launch on the fast paths, two otherwise) writes
+    the same bytes as mla_absorb_q followed by mla_cache_append: the absorbed
+    query and every cache byte and scale, with cache and query pre-filled
+    with a byte pattern so that only the step's new rows are written."""
+    say(f"case absorb_append {w.name}: B={w.batch} T={w.q_tokens} kv={w.kv_dtype} layout={w.layout}")
+    gen = generate(w)
+    bufs = [_buffers(w, gen), _buffers(w, gen)]
+    for buf in bufs:
+        buf.q_abs.view(torch.uint8).fill_(0x5A)
+        buf.caches[0].view(torch.uint8).fill_(0x5A)
+        if buf.scales[0] is not None:
+            buf.scales[0].fill_(0.5)
+    bufs[0].absorb()
+    bufs[0].append()
+    bufs[1].absorb_append()
+    torch.cuda.synchronize()
+    a, b = bufs
+    assert torch.equal(a.q_abs.view(torch.uint8), b.q_abs.view(torch.uint8)), "absorbed query"
+    assert torch.equal(a.caches[0].view(torch.uint8), b.caches[0].view(torch.uint8)), "cache"
+    assert not torch.equal(a.caches[0].view(torch.uint8),
+                           torch.full_like(a.caches[0].view(torch.uint8), 0x5A)), "rows written"
+    if a.scales[0] is not None:
+        assert torch.equal(a.scales[0], b.scales[0]), "scales"
