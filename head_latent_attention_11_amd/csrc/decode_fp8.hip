@@ -309,7 +309,10 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
   auto run_steps = [&](auto check) __attribute__((always_inline)) -> bool {
     constexpr bool CHECK = decltype(check)::value;
     int sc = 0;                       // slot of tile it
-    for (int it = 0; it <= ntiles; ++it) {
+    // One step as two sequences, with the masking and reference code
+    // between them: the first step and tiles that reach past the wave's
+    // visibility limit.
+    auto step_split = [&](int it) __attribute__((always_inline)) {
       const int ts = t0 + it * TILE;
       const int si = (sc + AHEAD >= NB) ? sc + AHEAD - NB : sc + AHEAD;   // tile it + AHEAD
       const int sp = (sc == 0) ? NB - 1 : sc - 1;                         // tile it - 1
@@ -397,7 +400,51 @@ void decode_fp8_kernel(DecodeArgs a, ItemTable tab) {
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"((AHEAD - 1) * LPT) : "memory");   // tile it+1 landed
       __syncthreads();
       sc = (sc + 1 == NB) ? 0 : sc + 1;
-    }
+    };
+    // One step of a tile none of whose tokens is masked, after the first
+    // (every row's reference is set): scores, PV product and softmax in one
+    // sequence, so the PV operand reads go out under the last score MFMAs.
+    auto step_fused = [&](int it) __attribute__((always_inline)) {
+      const int ts = t0 + it * TILE;
+      const int si = (sc + AHEAD >= NB) ? sc + AHEAD - NB : sc + AHEAD;   // tile it + AHEAD
+      const int sp = (sc == 0) ? NB - 1 : sc - 1;                         // tile it - 1
+      MLA_TILE_RSRC(ts + AHEAD * TILE, rs_n, rss_n);
+      const uint32_t lb_n = __builtin_amdgcn_readfirstlane(lds0 + si * SLOT + 1024 * wave);
+      const uint32_t ad = lds0 + sc * SLOT + qk_off;
+      const uint32_t vb = lds0 + sp * SLOT + pv_off;
+      const uint32_t pb = pr + 8192 * ((it + 1) & 1);
+      const uint32_t pw = pr + 8192 * (it & 1) + 2048 * wave;
+      const uint32_t kva = lds0 + sc * SLOT + SCL + 64 * h;
+      const float neg_m = -m_ref;
+      float tmp;
+      asm volatile(MLA_ASM_STEP8_TILE
+                   : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]),
+                     "+a"(o[5]), "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]),
+                     "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]),
+                     "+a"(o[15]), "+v"(l_run), "=&v"(tmp)
+                   : "v"(ad), "v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
+                     "v"(qf[5]), "v"(qf[6]), "v"(qf[7]), "v"(qf[8]), "v"(qf[9]),
+                     "v"(qf[10]), "v"(qf[11]), "v"(qf[12]), "v"(qf[13]), "v"(qf[14]),
+                     "v"(qf[15]), "v"(qf[16]), "v"(qf[17]), "v"(qf[18]), "v"(qf[19]),
+                     "v"(qf[20]), "v"(qf[21]), "v"(qf[22]), "v"(qf[23]), "v"(qf[24]),
+                     "v"(qf[25]), "v"(qf[26]), "v"(qf[27]), "v"(qf[28]), "v"(qf[29]),
+                     "v"(qf[30]), "v"(qf[31]), "v"(qf[32]), "v"(qf[33]), "v"(qf[34]),
+                     "v"(qf[35]), "s"(rs_n), "s"(lb_n), "v"(voff[0]), "v"(voff[1]),
+                     "v"(voff[2]), "v"(voff[3]), "v"(vb), "v"(pb), "v"(kva), "v"(neg_m),
+                     "v"(a.scale_log2), "v"(pw)
+                   : "memory", MLA_ASM_STEP8_CLOBBERS);
+      MLA_ISSUE_FIFTH(si, rs_n, rss_n);
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"((AHEAD - 1) * LPT) : "memory");   // tile it+1 landed
+      __syncthreads();
+      sc = (sc + 1 == NB) ? 0 : sc + 1;
+    };
+    // tiles 0 .. nfull-1 hold no token past this wave's limit
+    const int nfull = __builtin_amdgcn_readfirstlane(max(0, (lim - t0 + 1) / TILE));
+    const int fused_end = min(nfull, ntiles + 1);
+    step_split(0);
+    int it = 1;
+    for (; it < fused_end; ++it) step_fused(it);
+    for (; it <= ntiles; ++it) step_split(it);
     if constexpr (CHECK) {
       // A weight above 2^64 (a score more than 64 above the row's
       // reference, the overflow risk) leaves a normaliser above 2^64: either

@@ -439,6 +439,158 @@ def pv8(with_softmax=True):
     return out
 
 
+PV8_S = 194          # the current tile's scores v[194:209] (fused step only)
+
+
+def step8():
+    """A whole steady-state step of the fp8 kernel as one sequence: the
+    scores of tile it (as qk8, into the fixed registers v[194:209]), then the
+    PV product of tile it-1 with the softmax of tile it interleaved (as pv8).
+    Being one sequence lets the PV product's first operand reads go out
+    while the last score MFMAs run, each into a buffer whose last reader has
+    been issued: the token scales and C^T fragment 0 once the raw buffer of
+    score pair 16 is converted, fragments 1 and 2 once that of pair 17 is,
+    and weight fragment rb right after score MFMA 32 + rb, the last reader
+    of its register quad.  The PV MFMAs then follow the score MFMAs with no
+    LDS round trip in between.  For tiles with no masked token after the
+    first one (the row references are set); the others take the two
+    sequences with the kernel's masking code between them.
+
+    operands: %0..%15 O blocks (block 4 db + rb), %16 the running
+    normaliser (in/out), %17 a temporary, %18 base address of this lane's
+    score reads (slot of tile it), %19..%54 query fragments, %55 buffer
+    descriptor of the tile being loaded, %56 LDS base of this wave's loads
+    of it, %57..%60 lane offsets of its loads 0..3, %61 this lane's C^T read
+    address (slot of tile it-1), %62 this lane's P fragment address (buffer
+    of tile it-1), %63 the address of this lane's 16 token scales of tile
+    it, %64 -m_ref, %65 the scale (log2 domain), %66 this lane's address in
+    the P buffer of tile it."""
+    S = lambda r: f"v{PV8_S + r}"
+    kv = lambda r: f"v{PV8_KV + r}"
+    valu = softmax8_valu(S, kv, "%17", "%16", "%64", "%65", "%66")
+    sreg = f"v[{PV8_S}:{PV8_S + 15}]"
+    out, issued = [], []
+
+    def read(name, instr):
+        out.append(instr)
+        issued.append(name)
+
+    def wait_for(names):
+        last = max(i for i, n in enumerate(issued) if n in names)
+        out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - last)})")
+
+    # ---- scores (qk8 with the PV prologue reads hoisted into its tail)
+    def qraw(kk):
+        return QK8_RAW + 4 * (kk % 4)
+
+    def qconv(i):
+        return QK8_CVT + 4 * (i % 4)
+
+    def qread(kk):
+        r = qraw(kk)
+        read(("Q", kk), f"ds_read_b128 v[{r}:{r + 3}], %18 offset:{32 * kk}")
+
+    def qconvert(kk, half):
+        r, c = qraw(kk), qconv(2 * kk + half)
+        return [cvt8(c, r + 2 * half, False), cvt8(c + 1, r + 2 * half, True),
+                cvt8(c + 2, r + 2 * half + 1, False), cvt8(c + 3, r + 2 * half + 1, True)]
+
+    def vraw(g):
+        return PV8_RAW + 2 * (g % 3)
+
+    def vconv(g):
+        return PV8_CVT + 4 * (g % 2)
+
+    def vread(g):
+        ks, db = g // 4, g % 4
+        read(("V", g), f"ds_read_b64_tr_b8 v[{vraw(g)}:{vraw(g) + 1}], %61 "
+                       f"offset:{16 * LROW8 * ks + 32 * db}")
+
+    def pread(rb, ks):
+        r = PV8_P + 4 * rb
+        read(("P", rb, ks), f"ds_read_b128 v[{r}:{r + 3}], %62 offset:{1024 * (2 * rb + ks)}")
+
+    def vconvert(g):
+        r, c = vraw(g), vconv(g)
+        return [cvt8(c, r, False), cvt8(c + 1, r, True), cvt8(c + 2, r + 1, False),
+                cvt8(c + 3, r + 1, True)]
+
+    npair = 18
+    for kk in range(QK8_AHEAD):
+        qread(kk)
+    wait_for({("Q", 0)})
+    out += qconvert(0, 0) + qconvert(0, 1)
+    for kk in range(npair):
+        if kk + QK8_AHEAD < npair:
+            qread(kk + QK8_AHEAD)
+        for half in range(2):
+            i = 2 * kk + half
+            c = "0" if i == 0 else sreg
+            out.append(f"v_mfma_f32_32x32x16_bf16 {sreg}, v[{qconv(i)}:{qconv(i) + 3}], "
+                       f"%{19 + i}, {c}")
+            if kk + 1 < npair:
+                if half == 0:
+                    wait_for({("Q", kk + 1)})
+                out += qconvert(kk + 1, half)
+            if i >= 32:
+                pread(i - 32, 0)              # its quad's last reader (MFMA i) is issued
+            if i == 31:                       # raw quads of pairs 14..16 are converted
+                for q in range(4):
+                    read("K", f"ds_read_b128 v[{PV8_KV + 4 * q}:{PV8_KV + 4 * q + 3}], "
+                              f"%63 offset:{16 * q}")
+                vread(0)
+            if i == 33:                       # ... and that of pair 17
+                vread(1)
+                vread(2)
+        if kk % 4 == 1 and kk // 4 < QK8_DMA:
+            n = kk // 4
+            out += dma(n, "%55", "%56", f"%{57 + n}")
+
+    # ---- PV product of tile it-1 with the softmax of tile it
+    vi = 0
+
+    def put_valu():
+        nonlocal vi
+        x = valu[vi]
+        vi += 1
+        if x.startswith("ds_write"):
+            read(("W", vi), x)                # counted by lgkmcnt like the reads
+        else:
+            out.append(x)
+
+    wait_for({("V", 0)})
+    out += vconvert(0)
+    for i in range(32):
+        ks, db, rb = i // 16, (i // 4) % 4, i % 4
+        g = i // 4
+        if i < 4 or 16 <= i < 20:
+            wait_for({("P", rb, ks)})
+        elif rb == 0:
+            wait_for({("V", g)})
+        out.append(f"v_mfma_f32_32x32x16_bf16 %{4 * db + rb}, v[{vconv(g)}:{vconv(g) + 3}], "
+                   f"v[{PV8_P + 4 * rb}:{PV8_P + 4 * rb + 3}], %{4 * db + rb}")
+        if 12 <= i < 16:
+            pread(i - 12, 1)                  # after the last use of P(rb, 0)
+        if rb == 1 and g + 1 < 8:
+            wait_for({("V", g + 1)})
+            out += vconvert(g + 1)            # read by MFMA 4(g+1), >= 2 instructions later
+        if rb == 2 and g + 3 < 8:
+            vread(g + 3)                      # into the buffer of fragment g, converted already
+        if i == 1:
+            # the scores' last MFMA ended before PV MFMA 1 started; the
+            # nops cover the matrix-result-to-vector-read distance besides
+            out.append("s_nop 7")
+            out.append("s_nop 7")
+            wait_for({"K"})
+        if i >= 1:
+            take = 4 if i < 31 else len(valu) - vi
+            for _ in range(take):
+                if vi < len(valu):
+                    put_valu()
+    assert vi == len(valu)
+    return out
+
+
 def clobbers(base, n):
     return ", ".join(f'"v{base + i}"' for i in range(n))
 
@@ -470,5 +622,7 @@ if __name__ == "__main__":
     txt.append(emit("MLA_ASM_PV8_TILE", pv8(False)))
     txt.append(f"#define MLA_ASM_PV8_CLOBBERS {clobbers(PV8_RAW, 256 - PV8_RAW)}\n")
     txt.append(f"#define MLA_ASM_PV8_SOFTMAX_CLOBBERS {clobbers(PV8_KV, 256 - PV8_KV)}\n")
+    txt.append(emit("MLA_ASM_STEP8_TILE", step8()))
+    txt.append(f"#define MLA_ASM_STEP8_CLOBBERS {clobbers(PV8_S, 256 - PV8_S)}\n")
 
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))
