@@ -115,6 +115,18 @@ SMALL = [
                   lengths=(300, 77, 4, 130), kv_dtype="fp8", num_splits=3),
     small_variant(V2, name="fp8_t1_paged", batch=2, kv_len=0, lengths=(100, 520),
                   kv_dtype="fp8", layout="paged"),
+    # 128-row blocks holding several query tokens (32 or 64 heads): the waves
+    # of a workgroup reach their visibility limits at different tiles, so they
+    # switch from the fused steady-state step to the split step at different
+    # steps between the same barriers
+    small_variant(V2, name="fp8_n32_t4", batch=4, n_heads=32, q_tokens=4, kv_len=0,
+                  lengths=(300, 97, 4, 1000), kv_dtype="fp8"),
+    small_variant(V2, name="fp8_n64_t2_split3", batch=3, n_heads=64, q_tokens=2, kv_len=0,
+                  lengths=(700, 130, 2), kv_dtype="fp8", num_splits=3),
+    # lengths on tile boundaries: every tile of the item fully visible, and
+    # one token past a boundary
+    small_variant(V2, name="fp8_t1_tile_edges", batch=3, kv_len=0, lengths=(512, 65, 32),
+                  kv_dtype="fp8"),
     # head counts with no multiple of 128 rows: the 16/32/64-row kernel
     small_variant(V2, name="lite_n16_ragged", batch=4, n_heads=16, kv_len=0,
                   lengths=(1, 33, 700, 64)),
