@@ -491,7 +491,11 @@ hipError_t launch_gemm_xwt(const void* x, int x_dtype, const void* w, int w_dtyp
     // token tiles (W streamed once per 256 tokens) with a 3-slot ring
     const GemmPlan p = gemm_plan(d_out, K);
     const int nw = p.nw, kb = p.kb;
-    const int mt = (n_tok <= 32) ? 1 : (n_tok <= 128) ? 4 : 8;
+    int mt = (n_tok <= 32) ? 1 : (n_tok <= 128) ? 4 : 8;
+    // groups of 8 token tiles that would leave more than half of the CUs
+    // idle (few feature blocks, e.g. the 576 rows of the cache producer):
+    // groups of 4, twice the workgroups, W streamed once per 128 tokens
+    if (mt == 8 && (int64_t)p.nfb * p.nkb * ((n_tok + 255) / 256) < kNumCU / 2) mt = 4;
     const int ntg = (n_tok + 32 * mt - 1) / (32 * mt);
     const dim3 grid(p.nfb * p.nkb * ntg);
     const uint16_t* xp = (const uint16_t*)x;
