@@ -213,6 +213,16 @@ def test_small_rows_long_paged_item():
     _run_compare(w, heads=[0, 5, 15])
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_long_paged_item_128_rows(kv):
+    """The same on the 128-row kernels: an unsplit 9000-token paged item
+    reads its page ids per tile with scalar loads, between the step
+    sequences (fp8: also between the fused steady-state steps)."""
+    w = small_variant(V2, name=f"long_item_{kv}", batch=2, kv_len=0, lengths=(9000, 300),
+                      layout="paged", num_splits=1, kv_dtype=kv)
+    _run_compare(w, heads=[0, 37, 127])
+
+
 def test_small_rows_items_located_on_device():
     """More work items than the host's item table holds, lengths not all
     equal: the 16-row kernel locates each item from the lengths itself."""
