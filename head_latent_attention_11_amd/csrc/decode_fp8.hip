@@ -46,6 +46,12 @@
 //     wave's loads of tile it+1; barrier.  The loads of tile it+5 go to the
 //     slot of tile it-2, whose last reader (PV in step it-1) every wave has
 //     finished at the barrier that ended step it-1.
+//   * Steps whose tile has no masked token, after the first, run the scores
+//     and the PV product with the softmax as one inline-assembly sequence:
+//     the PV product's first operand reads go out under the last score
+//     MFMAs.  Step 0 and the masked tail keep two sequences with the masking
+//     and reference code between them; the three parts run one after
+//     another (no branch around a block that writes O).
 //   * Softmax against a fixed per-row reference with rare restarts, as in
 //     the bf16 kernel (exact for any reference: LSE = m_ref + log2 sum p).
 #include <math.h>
