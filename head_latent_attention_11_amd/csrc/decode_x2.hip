@@ -82,6 +82,10 @@ template <int N>
 __device__ __forceinline__ void x2_wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 }  // namespace
 
+// Software-pipelined step bodies (gen_decode_asm.py): the split-operand
+// score sequence, MLA_ASM_QKX2_TILE.
+#include "decode_mfma_asm.inc"
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_x2_kernel(DecodeArgs a, ItemTable tab, int row_blocks) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_kv[NBUF][TILE_BYTES];
@@ -142,6 +146,10 @@ void decode_x2_kernel(DecodeArgs a, ItemTable tab, int row_blocks) {
       qh[ks] = *(const bf16x8*)(qsrc + 64 * ks);
       ql[ks] = *(const bf16x8*)(qsrc + 2 * D + 64 * ks);
     }
+    // landed here, before any tile load: the compiler does not count the
+    // assembly loads, and its first use of a fragment (the score sequence,
+    // inside the step loop) would otherwise wait for every load in flight
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
   }
 
   const uint32_t lds_ring = (uint32_t)(uintptr_t)&s_kv[0][0];
@@ -211,15 +219,24 @@ void decode_x2_kernel(DecodeArgs a, ItemTable tab, int row_blocks) {
       const int ts = t0 + it * TILE;
 
       // ---- scores S^T = K (Q_hi + Q_lo)^T for the wave's 16 rows
-      floatx4 sh[2] = {}, sl[2] = {};
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 k = *(const bf16x8*)(slot + (16 * tb + qk_off) * LROW + 64 * ks + 16 * g);
-          sh[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qh[ks], sh[tb], 0, 0, 0);
-          sl[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, ql[ks], sl[tb], 0, 0, 0);
-        }
+      // (a generated sequence: five operand reads stay in flight, where the
+      // compiler waited for each read before its two MFMAs; the hi query
+      // fragments and the first nine lo ones are read from accumulation
+      // registers, which hold them next to O (236 of 256), the other lo ones
+      // from vector registers)
+      floatx4 sh[2], sl[2];
+      {
+        const uint32_t ad = (uint32_t)(uintptr_t)(slot + qk_off * LROW + 16 * g);
+        asm volatile(MLA_ASM_QKX2_TILE
+                     : "=&v"(sh[0]), "=&v"(sh[1]), "=&v"(sl[0]), "=&v"(sl[1])
+                     : "v"(ad), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(qh[4]),
+                       "a"(qh[5]), "a"(qh[6]), "a"(qh[7]), "a"(qh[8]), "a"(qh[9]), "a"(qh[10]),
+                       "a"(qh[11]), "a"(qh[12]), "a"(qh[13]), "a"(qh[14]), "a"(qh[15]),
+                       "a"(qh[16]), "a"(qh[17]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]),
+                       "a"(ql[4]), "a"(ql[5]), "a"(ql[6]), "a"(ql[7]), "a"(ql[8]), "v"(ql[9]),
+                       "v"(ql[10]), "v"(ql[11]), "v"(ql[12]), "v"(ql[13]), "v"(ql[14]),
+                       "v"(ql[15]), "v"(ql[16]), "v"(ql[17])
+                     : "memory", MLA_ASM_QKX2_CLOBBERS);
       }
       // score (tb, i): token ts + 16 tb + 4 i + g of row qrow
       float x[8];

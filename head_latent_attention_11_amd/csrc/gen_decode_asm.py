@@ -591,6 +591,52 @@ def step8():
     return out
 
 
+# ------------------------------------------------------ split-operand scores
+X2_AHEAD = 5         # tile-operand reads in flight ahead of the current pair
+X2_RAW = 232         # 6 read buffers v[232:255]
+
+
+def qkx2():
+    """Scores of one bf16 tile for a split-operand wave's 16 query rows:
+    S^T[tok, row] = K (Q_hi + Q_lo)^T with v_mfma_f32_16x16x32_bf16, tokens
+    as M in two blocks of 16, the hi and lo parts of the query in separate
+    accumulators (4 in all).  Read n (n = 2 ks + tb) fetches the 8 dims
+    32 ks + 8 (l/16) .. +7 of this lane's token row of block tb and feeds the
+    hi and the lo MFMA of (ks, tb); five reads stay in flight ahead.
+
+    operands: %0 %1 S_hi of token blocks 0 and 1, %2 %3 S_lo (floatx4, out),
+    %4 base address of this lane's reads (token block 0, dim group l/16),
+    %5..%22 Q_hi fragments (ks = 0..17), %23..%40 Q_lo fragments."""
+    out, issued = [], []
+    nbuf = X2_AHEAD + 1
+
+    def buf(n):
+        return X2_RAW + 4 * (n % nbuf)
+
+    def read(n):
+        ks, tb = n // 2, n % 2
+        r = buf(n)
+        out.append(f"ds_read_b128 v[{r}:{r + 3}], %4 offset:{16 * LROW * tb + 64 * ks}")
+        issued.append(n)
+
+    def wait(n):
+        out.append(f"s_waitcnt lgkmcnt({min(15, len(issued) - 1 - issued.index(n))})")
+
+    nread = 2 * (QK_STEPS // 2)
+    for n in range(X2_AHEAD):
+        read(n)
+    for n in range(nread):
+        ks, tb = n // 2, n % 2
+        wait(n)
+        r = buf(n)
+        for part, (acc, q) in enumerate(((tb, 5 + ks), (2 + tb, 23 + ks))):
+            c = "0" if ks == 0 else f"%{acc}"
+            out.append(f"v_mfma_f32_16x16x32_bf16 %{acc}, v[{r}:{r + 3}], %{q}, {c}")
+        if n + X2_AHEAD < nread:
+            read(n + X2_AHEAD)                # into the buffer of read n-1, consumed
+    return out
+
+
 def clobbers(base, n):
     return ", ".join(f'"v{base + i}"' for i in range(n))
 
@@ -623,6 +669,8 @@ if __name__ == "__main__":
     txt.append(f"#define MLA_ASM_PV8_CLOBBERS {clobbers(PV8_RAW, 256 - PV8_RAW)}\n")
     txt.append(f"#define MLA_ASM_PV8_SOFTMAX_CLOBBERS {clobbers(PV8_KV, 256 - PV8_KV)}\n")
     txt.append(emit("MLA_ASM_STEP8_TILE", step8()))
+    txt.append(emit("MLA_ASM_QKX2_TILE", qkx2()))
+    txt.append(f"#define MLA_ASM_QKX2_CLOBBERS {clobbers(X2_RAW, 256 - X2_RAW)}\n")
     txt.append(f"#define MLA_ASM_STEP8_CLOBBERS {clobbers(PV8_S, 256 - PV8_S)}\n")
 
     open("decode_mfma_asm.inc", "w").write("\n".join(txt))
