@@ -15,9 +15,11 @@ and are waited for by the kernel) and finishes with enough independent
 cycles for a vector instruction to read the matrix results.
 
 Run from this directory after changing the tile layout constants below
-(they must match decode_mfma.hip):  python3 gen_decode_asm.py
+(they must match decode_mfma.hip, decode_fp8.hip and decode_x2.hip: LROW is
+also the row pitch of the split-operand kernel's tiles):
+python3 gen_decode_asm.py
 """
-LROW = 1168          # LDS bytes per token row
+LROW = 1168          # LDS bytes per bf16 token row (also decode_x2.hip)
 QK_STEPS = 36        # 576 / 16 dims per v_mfma_f32_32x32x16_bf16
 QK_AHEAD = 6         # reads in flight ahead of the current MFMA
 QK_BUFS = 8
